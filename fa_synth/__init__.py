@@ -1,0 +1,251 @@
+"""Seeded synthetic inputs for varlen attention.
+
+This module serves both the oracle side (tests, the CPU baseline) and the GPU
+side (parity tests, the bench).  It holds no attention arithmetic: only
+cumulative-offset construction, Gaussian draws and the bf16 rounding of those
+draws, so that both sides receive bit-identical inputs.
+
+Workload shapes follow the FlashAttention pages:
+  * cumulative offsets of length batch+1, e.g. [0, 128, 300] for lengths 128
+    and 172 (friki.work, "Mecanismo cu_seqlens en FlashAttention",
+    section "Estructuras de datos clave");
+  * the ragged pair q=[0, 200, 1024] / k=[0, 300, 1024] with 12 heads of
+    dimension 64 (same page, section "Ejemplo de uso con PyTorch");
+  * sequence lengths 512 to 16k at 16k total tokens per batch, head dimension
+    64 and 128, causal and not (iplexlaw.co.kr, "FlashAttention-2 GPU work
+    partitioning", section on the roughly 2x kernel speed-up).
+
+Draw recipe: numpy ``default_rng(seed)`` (PCG64); for the ragged 64k batch the
+sequence lengths are drawn first; then Q, K and V are drawn in that order as
+i.i.d. N(0, 1) float32 arrays of shape [tokens, heads, head_dim]; bf16
+workloads round each draw to bf16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "bf16_rne_bits",
+    "bf16_bits_to_f32",
+    "cu_from_lengths",
+    "loguniform_lengths",
+    "workload_tiny",
+    "workload_ragged_qk",
+    "workload_dense",
+    "workload_sweep",
+    "workload_ragged64k",
+    "workload_custom",
+    "all_parity_workloads",
+    "draw_qkv",
+    "SWEEP_SEQLENS",
+    "SWEEP_HEAD_DIMS",
+]
+
+SWEEP_SEQLENS = (512, 1024, 2048, 4096, 8192, 16384)
+SWEEP_HEAD_DIMS = (64, 128)
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding of inputs (bit arithmetic; no ml_dtypes in this image)
+# --------------------------------------------------------------------------
+def bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even).
+
+    Returns the uint16 bit patterns.  Inputs are finite Gaussian draws, so no
+    NaN/Inf handling is needed; finite inputs that overflow become +-inf as
+    IEEE rounding prescribes.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    rounded = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 values of bf16 bit patterns."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# cumulative offsets
+# --------------------------------------------------------------------------
+def cu_from_lengths(lengths: Sequence[int]) -> np.ndarray:
+    """int32 cumulative offsets [0, L0, L0+L1, ...] of length batch+1."""
+    out = np.zeros(len(lengths) + 1, dtype=np.int64)
+    out[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    if out[-1] > np.iinfo(np.int32).max:
+        raise ValueError("total length exceeds int32")
+    return out.astype(np.int32)
+
+
+def loguniform_lengths(rng: np.random.Generator, total: int, lo: int, hi: int) -> List[int]:
+    """Lengths round(exp(U(ln lo, ln hi))) drawn until they reach ``total``.
+
+    The last length is clipped so that the lengths sum to exactly ``total``
+    (it may therefore fall below ``lo``).
+    """
+    lengths: List[int] = []
+    acc = 0
+    a, b = math.log(lo), math.log(hi)
+    while acc < total:
+        L = int(round(math.exp(rng.uniform(a, b))))
+        L = max(1, min(L, total - acc))
+        lengths.append(L)
+        acc += L
+    return lengths
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    cu_q: Tuple[int, ...]
+    cu_k: Tuple[int, ...]
+    heads: int
+    head_dim: int
+    dtype: str  # "f32" or "bf16"
+    seed: int
+    causal_modes: Tuple[bool, ...]
+    lengths_from_rng: bool = False  # ragged 64k: lengths come from the same generator
+
+    @property
+    def batch(self) -> int:
+        return len(self.cu_q) - 1
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_q[-1])
+
+    @property
+    def total_k(self) -> int:
+        return int(self.cu_k[-1])
+
+    @property
+    def lengths_q(self) -> List[int]:
+        return [self.cu_q[i + 1] - self.cu_q[i] for i in range(self.batch)]
+
+    @property
+    def lengths_k(self) -> List[int]:
+        return [self.cu_k[i + 1] - self.cu_k[i] for i in range(self.batch)]
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return max(self.lengths_q) if self.batch else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return max(self.lengths_k) if self.batch else 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def describe(self) -> dict:
+        return {
+            "workload": self.name,
+            "batch": self.batch,
+            "total_q": self.total_q,
+            "total_k": self.total_k,
+            "heads": self.heads,
+            "head_dim": self.head_dim,
+            "dtype": self.dtype,
+            "seed": self.seed,
+        }
+
+
+def workload_tiny() -> Workload:
+    """batch 2, cu=[0,128,300] for q and k, 2 heads, d=64, fp32, non-causal."""
+    cu = (0, 128, 300)
+    return Workload("tiny_fp32_h2_d64", cu, cu, 2, 64, "f32", 0, (False,))
+
+
+def workload_ragged_qk() -> Workload:
+    """cu_q=[0,200,1024], cu_k=[0,300,1024], 12 heads, d=64, bf16, both masks."""
+    return Workload("ragged_qk_h12_d64", (0, 200, 1024), (0, 300, 1024), 12, 64, "bf16", 1,
+                    (False, True))
+
+
+def workload_dense() -> Workload:
+    """8 sequences of 2048 tokens, 16 heads, d=128, bf16, both masks."""
+    cu = tuple(int(x) for x in cu_from_lengths([2048] * 8))
+    return Workload("dense_8x2048_h16_d128", cu, cu, 16, 128, "bf16", 2, (False, True))
+
+
+def workload_sweep(seqlen: int, head_dim: int) -> Workload:
+    """16k total tokens: batch = 16384/seqlen, heads = 2048/head_dim, bf16."""
+    if seqlen not in SWEEP_SEQLENS or head_dim not in SWEEP_HEAD_DIMS:
+        raise ValueError("sweep point outside the 512..16k x {64,128} grid")
+    batch = 16384 // seqlen
+    heads = 2048 // head_dim
+    idx = SWEEP_SEQLENS.index(seqlen) * len(SWEEP_HEAD_DIMS) + SWEEP_HEAD_DIMS.index(head_dim)
+    cu = tuple(int(x) for x in cu_from_lengths([seqlen] * batch))
+    return Workload(f"sweep_L{seqlen}_d{head_dim}_h{heads}", cu, cu, heads, head_dim, "bf16",
+                    300 + idx, (False, True))
+
+
+def workload_ragged64k(seed: int = 4, total: int = 65536) -> Workload:
+    """64k tokens, lengths log-uniform in [64, 8192], 32 heads, d=128, bf16, causal."""
+    rng = np.random.default_rng(seed)
+    lengths = loguniform_lengths(rng, total, 64, 8192)
+    cu = tuple(int(x) for x in cu_from_lengths(lengths))
+    return Workload(f"ragged64k_h32_d128_causal_seed{seed}", cu, cu, 32, 128, "bf16", seed,
+                    (True,), lengths_from_rng=True)
+
+
+def workload_custom(name: str, lengths_q: Sequence[int], lengths_k: Optional[Sequence[int]],
+                    heads: int, head_dim: int, dtype: str, seed: int,
+                    causal_modes: Tuple[bool, ...] = (False, True)) -> Workload:
+    """Any ragged shape (used for edge cases: empty sequences, tails, Lq != Lk)."""
+    cu_q = tuple(int(x) for x in cu_from_lengths(lengths_q))
+    cu_k = cu_q if lengths_k is None else tuple(int(x) for x in cu_from_lengths(lengths_k))
+    return Workload(name, cu_q, cu_k, heads, head_dim, dtype, seed, causal_modes)
+
+
+def all_parity_workloads() -> List[Workload]:
+    out = [workload_tiny(), workload_ragged_qk(), workload_dense()]
+    out += [workload_sweep(L, d) for L in SWEEP_SEQLENS for d in SWEEP_HEAD_DIMS]
+    out.append(workload_ragged64k())
+    return out
+
+
+def draw_qkv(wl: Workload, heads: Optional[Sequence[int]] = None) -> dict:
+    """Draw Q, K, V for a workload.
+
+    Returns float32 arrays ``q``, ``k``, ``v`` (values exactly representable
+    in bf16 when the workload is bf16) and, for bf16, the uint16 bit arrays
+    ``q_bits``, ``k_bits``, ``v_bits`` that are handed to the device.
+    ``heads`` optionally keeps a subset of heads (the full tensors are still
+    drawn so that the values do not depend on the subset).
+    """
+    rng = np.random.default_rng(wl.seed)
+    if wl.lengths_from_rng:
+        lengths = loguniform_lengths(rng, wl.total_q, 64, 8192)
+        if tuple(cu_from_lengths(lengths)) != tuple(wl.cu_q):
+            raise RuntimeError("length draw does not reproduce the workload")
+    shape_q = (wl.total_q, wl.heads, wl.head_dim)
+    shape_k = (wl.total_k, wl.heads, wl.head_dim)
+    out = {}
+    for name, shape in (("q", shape_q), ("k", shape_k), ("v", shape_k)):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if wl.dtype == "bf16":
+            bits = bf16_rne_bits(x)
+            del x
+            x = bf16_bits_to_f32(bits).reshape(shape)
+            bits = bits.reshape(shape)
+            if heads is not None:
+                bits = np.ascontiguousarray(bits[:, list(heads), :])
+            out[name + "_bits"] = bits
+        elif wl.dtype != "f32":
+            raise ValueError(wl.dtype)
+        if heads is not None:
+            x = np.ascontiguousarray(x[:, list(heads), :])
+        out[name] = x
+    return out

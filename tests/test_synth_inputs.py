@@ -1,0 +1,58 @@
+"""Seeded input generation: bf16 rounding and workload shapes (CPU)."""
+import numpy as np
+import torch
+
+from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, all_parity_workloads, bf16_bits_to_f32,
+                      bf16_rne_bits, cu_from_lengths, draw_qkv, workload_ragged64k, workload_ragged_qk,
+                      workload_sweep, workload_tiny)
+
+
+def test_bf16_rounding_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10 ** rng.uniform(-3, 3),
+                        np.array([1.0, -1.0, 0.0, 1.00390625, 1.01171875, 3.0e38], dtype=np.float32)])
+    x = x.astype(np.float32)
+    ours = bf16_rne_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(bf16_bits_to_f32(ours), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_ties_round_to_even():
+    # 1 + 2^-8 is halfway between bf16 1.0 and 1 + 2^-7: ties go to the even mantissa (1.0)
+    assert bf16_bits_to_f32(bf16_rne_bits(np.array([1.00390625], np.float32)))[0] == 1.0
+    # 1 + 3*2^-8 is halfway between 1+2^-7 and 1+2^-6: goes to 1 + 2^-6 (even)
+    assert bf16_bits_to_f32(bf16_rne_bits(np.array([1.01171875], np.float32)))[0] == 1.015625
+
+
+def test_workload_shapes():
+    t = workload_tiny()
+    assert t.cu_q == (0, 128, 300) and t.heads == 2 and t.head_dim == 64 and t.dtype == "f32"
+    r = workload_ragged_qk()
+    assert r.lengths_q == [200, 824] and r.lengths_k == [300, 724] and r.heads == 12
+    for L in SWEEP_SEQLENS:
+        for d in SWEEP_HEAD_DIMS:
+            w = workload_sweep(L, d)
+            assert w.total_q == 16384 and w.heads * d == 2048 and w.batch * L == 16384
+    g = workload_ragged64k()
+    lens = g.lengths_q
+    assert sum(lens) == 65536 and all(64 <= L <= 8192 for L in lens[:-1]) and 1 <= lens[-1] <= 8192
+    assert g.heads == 32 and g.head_dim == 128 and g.causal_modes == (True,)
+    assert len({w.name for w in all_parity_workloads()}) == len(all_parity_workloads())
+
+
+def test_draws_are_seeded_and_bf16_exact():
+    w = workload_ragged_qk()
+    a = draw_qkv(w)
+    b = draw_qkv(w)
+    for n in "qkv":
+        assert np.array_equal(a[n], b[n])
+        assert np.array_equal(bf16_bits_to_f32(a[n + "_bits"]).reshape(a[n].shape), a[n])
+    sub = draw_qkv(w, heads=[0, 11])
+    assert np.array_equal(sub["k"], a["k"][:, [0, 11]])
+    assert abs(float(a["q"].mean())) < 0.01 and abs(float(a["q"].std()) - 1) < 0.01
+
+
+def test_cu_from_lengths():
+    assert cu_from_lengths([128, 172]).tolist() == [0, 128, 300]
+    assert cu_from_lengths([]).tolist() == [0]
