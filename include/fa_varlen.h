@@ -1,0 +1,177 @@
+/*
+ * fa_varlen.h -- C ABI of libfa_varlen.so: exact attention forward over packed
+ * variable-length sequences on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (FlashAttention pages):
+ *   * Sequences are packed back to back with no padding and addressed by
+ *     cumulative offsets of length batch+1; offsets [0,128,300] mean two
+ *     sequences of 128 and 172 tokens (friki.work, "Mecanismo cu_seqlens en
+ *     FlashAttention", sections "Estructuras de datos clave" and "Lógica de
+ *     cálculo de longitud").  A sequence's first row is its offset times the
+ *     row stride (same page, "Optimización de acceso a memoria").
+ *   * For every sequence b and head h the result is the exact attention
+ *     softmax(scale * Q K^T, optional causal mask) V; the tiled method never
+ *     writes the score matrix to HBM and keeps a running (online) softmax
+ *     whose statistics and partial outputs are rescaled block by block
+ *     (iplexlaw.co.kr, "FlashAttention-2 GPU work partitioning", section
+ *     "Bloques pequeños, normalización global"; slavadubrov.com, "O que
+ *     FlashAttention muda na inferência", section "Separar o armazenamento
+ *     do cálculo").
+ *   * Work is split over (sequence, head, query block) so that long sequences
+ *     in small batches still fill the GPU (iplexlaw.co.kr, section "Tres
+ *     mejoras en la utilización de la GPU").
+ *   * Causal masking may be combined with variable lengths (friki.work,
+ *     section "Integración con máscaras causales y caché paginada").
+ *
+ * Readings the pages leave open, fixed here:
+ *   * causal alignment is bottom-right: query i of a sequence (0-based) sees
+ *     key j iff j <= i + Lk - Lq;
+ *   * a query row that sees no key gets out = 0 and lse = -inf;
+ *   * lse is the natural log of sum_j exp(scale * q_i . k_j) over visible j.
+ *
+ * Conventions shared by every entry point
+ *   * Device pointers live on the current HIP device (hipSetDevice before the
+ *     call).  The caller owns every buffer; the library keeps no pointer
+ *     after a call returns and holds no state across calls.
+ *   * `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All device work is enqueued on it; calls return before it runs.
+ *   * Every function returns an fa_status.  On a validation error nothing is
+ *     launched and no buffer is touched.  Faults raised by device work
+ *     surface at the caller's next synchronisation on the stream.
+ *   * cu_seqlens contents are a precondition, not checked on the device:
+ *     cu[0] == 0, non-decreasing, cu[batch] <= total rows, and every length
+ *     at most the max_seqlen passed.  fa_varlen_check_cu_seqlens validates
+ *     them on the device for callers that want a check.
+ */
+#ifndef FA_VARLEN_H_
+#define FA_VARLEN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v and out. */
+typedef enum fa_dtype {
+  FA_DTYPE_F32 = 0,  /* IEEE float32; arithmetic in float32 throughout */
+  FA_DTYPE_BF16 = 1  /* bfloat16 in and out; float32 accumulation */
+} fa_dtype;
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,       /* a required pointer is NULL */
+  FA_ERR_DTYPE = 2,      /* dtype is not an fa_dtype */
+  FA_ERR_SHAPE = 3,      /* negative size, zero heads, or max_seqlen > rows */
+  FA_ERR_HEAD_DIM = 4,   /* head_dim not supported (64 and 128 are) */
+  FA_ERR_ALIGN = 5,      /* a pointer is not aligned as documented */
+  FA_ERR_ARG = 6,        /* softmax_scale not finite and > 0, causal not 0/1, bad block_m */
+  FA_ERR_HIP = 7,        /* the HIP runtime reported an error (no device, launch failure) */
+  FA_ERR_TOO_LARGE = 8   /* the launch grid would exceed 2^31 workgroups */
+} fa_status;
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/*
+ * Query-block height BM and key-block height BN used by fa_varlen_fwd for a
+ * (head_dim, dtype) pair.  BM is the block height of the work-item map
+ * (fa_varlen_tile_map): every work item covers at most BM query rows of one
+ * sequence.
+ * Returns FA_ERR_NULL, FA_ERR_DTYPE or FA_ERR_HEAD_DIM on bad arguments.
+ * Host only; launches nothing.
+ */
+int fa_varlen_block_sizes(int32_t head_dim, int32_t dtype, int32_t* block_m, int32_t* block_n);
+
+/*
+ * Work-item map of the ragged batch (the sequence-dimension split described
+ * in iplexlaw.co.kr, "FlashAttention-2 GPU work partitioning", section "Tres
+ * mejoras en la utilización de la GPU"; lengths per friki.work, section
+ * "Lógica de cálculo de longitud"):
+ *   blk_start[0] = 0,
+ *   blk_start[b+1] = blk_start[b] + ceil((cu_seqlens_q[b+1] - cu_seqlens_q[b]) / block_m).
+ * Work item t belongs to the sequence b with blk_start[b] <= t < blk_start[b+1]
+ * and covers its query rows (t - blk_start[b]) * block_m ... + block_m - 1,
+ * clipped to the sequence, so no item straddles two sequences.
+ *
+ *   cu_seqlens_q  device, int32 [batch + 1], 4-byte aligned
+ *   batch         >= 0
+ *   block_m       1 .. 4096
+ *   blk_start     device, int32 [batch + 1], written (4-byte aligned)
+ * A negative length (precondition violation) counts as 0 blocks.
+ */
+int fa_varlen_tile_map(const int32_t* cu_seqlens_q, int32_t batch, int32_t block_m,
+                       int32_t* blk_start, void* stream);
+
+/*
+ * Exact attention forward over packed variable-length sequences.
+ *
+ *   q             device [total_q, num_heads, head_dim], contiguous, dtype
+ *   k, v          device [total_k, num_heads, head_dim], contiguous, dtype
+ *   cu_seqlens_q  device int32 [batch + 1] query offsets
+ *   cu_seqlens_k  device int32 [batch + 1] key/value offsets
+ *   max_seqlen_q  >= every query length (sizes the launch; 0..total_q)
+ *   max_seqlen_k  >= every key length (0..total_k)
+ *   softmax_scale finite, > 0; multiplies q.k before the softmax
+ *   causal        0 or 1 (bottom-right alignment, see above)
+ *   out           device [total_q, num_heads, head_dim], dtype, written for
+ *                 rows < cu_seqlens_q[batch]; other rows untouched
+ *   lse           device float32 [num_heads, total_q], natural-log
+ *                 log-sum-exp per (head, query row); same rows as out
+ *   batch, total_q, total_k, num_heads, head_dim, dtype   sizes and type
+ *   stream        hipStream_t or NULL
+ *
+ * head_dim must be 64 or 128 (FA_ERR_HEAD_DIM otherwise).  q, k, v and out
+ * must be 16-byte aligned, lse and cu_seqlens 4-byte aligned (the offsets
+ * are best kept 32-byte aligned, as any hipMalloc'd buffer is).
+ * Scratch: a (batch+1)-entry int32 work-item map is allocated and freed
+ * stream-ordered (hipMallocAsync / hipFreeAsync) on `stream`.
+ * Reentrant: concurrent calls on different streams do not interfere.
+ */
+int fa_varlen_fwd(const void* q, const void* k, const void* v,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int32_t max_seqlen_q, int32_t max_seqlen_k,
+                  float softmax_scale, int32_t causal,
+                  void* out, float* lse,
+                  int32_t batch, int32_t total_q, int32_t total_k,
+                  int32_t num_heads, int32_t head_dim, int32_t dtype,
+                  void* stream);
+
+/*
+ * The same forward pass with a work-item map the caller already built with
+ * fa_varlen_tile_map (block_m from fa_varlen_block_sizes for this head_dim
+ * and dtype), e.g. once per batch and reused by every layer.  Launches only
+ * the attention kernel and allocates nothing.
+ *   blk_start     device int32 [batch + 1], 4-byte aligned, read only
+ * Other arguments and errors as fa_varlen_fwd.  A map built with another
+ * block_m is a precondition violation (rows are then skipped or repeated).
+ */
+int fa_varlen_fwd_mapped(const void* q, const void* k, const void* v,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int32_t max_seqlen_q, int32_t max_seqlen_k,
+                         float softmax_scale, int32_t causal,
+                         void* out, float* lse,
+                         int32_t batch, int32_t total_q, int32_t total_k,
+                         int32_t num_heads, int32_t head_dim, int32_t dtype,
+                         const int32_t* blk_start, void* stream);
+
+/*
+ * Device-side check of the cu_seqlens preconditions (friki.work, section
+ * "Estructuras de datos clave": batch+1 cumulative offsets).  Writes to
+ * `flags` (device int32 [1]) a bit mask, 0 when valid:
+ *   1  cu[0] != 0            2  cu decreases somewhere
+ *   4  cu[batch] > total     8  some length exceeds max_seqlen
+ * for either array (q bits in 0..3, k bits shifted left by 4).
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [batch + 1]
+ *   flags                       device int32 [1], overwritten
+ */
+int fa_varlen_check_cu_seqlens(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t* flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_VARLEN_H_ */

@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/fa_varlen.h declares, and host validation returns the documented
+status codes before any HIP call is made (so nothing here launches work)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import variable_length_flashattention_cu_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_varlen.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.library_path()),
+                                reason="libfa_varlen.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["fa_status_string", "fa_varlen_block_sizes", "fa_varlen_tile_map",
+                            "fa_varlen_fwd", "fa_varlen_fwd_mapped", "fa_varlen_check_cu_seqlens"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(9):
+        s = fa.fa_status_string(code)
+        assert isinstance(s, str) and s
+    assert fa.fa_status_string(12345) == "unknown status"
+    assert fa.fa_status_string(0) == "ok"
+
+
+def test_block_sizes():
+    for d in (64, 128):
+        for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16):
+            bm, bn = fa.fa_varlen_block_sizes(d, dt)
+            assert bm > 0 and bn > 0 and bm % 32 == 0 and bn % 32 == 0
+    with pytest.raises(fa.FaVarlenError) as e:
+        fa.fa_varlen_block_sizes(96, fa.FA_DTYPE_BF16)
+    assert e.value.status == 4
+    with pytest.raises(fa.FaVarlenError) as e:
+        fa.fa_varlen_block_sizes(64, 7)
+    assert e.value.status == 2
+    lib = fa.load_library()
+    assert lib.fa_varlen_block_sizes(64, 1, None, None) == 1
+
+
+# Fake device addresses: validation rejects every call below before any
+# pointer is dereferenced or any HIP call is made.
+A16 = 0x10000
+A4 = 0x10004
+
+
+def call_fwd(**over):
+    args = dict(q=A16, k=A16, v=A16, cu_q=A16, cu_k=A16, max_q=8, max_k=8, scale=0.125, causal=0, out=A16,
+                lse=A16, batch=1, total_q=8, total_k=8, heads=2, head_dim=64, dtype=1)
+    args.update(over)
+    lib = fa.load_library()
+    return lib.fa_varlen_fwd(args["q"], args["k"], args["v"], args["cu_q"], args["cu_k"], args["max_q"],
+                             args["max_k"], args["scale"], args["causal"], args["out"], args["lse"],
+                             args["batch"], args["total_q"], args["total_k"], args["heads"], args["head_dim"],
+                             args["dtype"], None)
+
+
+def call_mapped(**over):
+    args = dict(q=A16, k=A16, v=A16, cu_q=A16, cu_k=A16, max_q=8, max_k=8, scale=0.125, causal=0, out=A16,
+                lse=A16, batch=1, total_q=8, total_k=8, heads=2, head_dim=64, dtype=1, blk=A16)
+    args.update(over)
+    lib = fa.load_library()
+    return lib.fa_varlen_fwd_mapped(args["q"], args["k"], args["v"], args["cu_q"], args["cu_k"], args["max_q"],
+                                    args["max_k"], args["scale"], args["causal"], args["out"], args["lse"],
+                                    args["batch"], args["total_q"], args["total_k"], args["heads"],
+                                    args["head_dim"], args["dtype"], args["blk"], None)
+
+
+@pytest.mark.parametrize("call", [call_fwd, call_mapped])
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(cu_q=None), 1), (dict(cu_k=None), 1),
+    (dict(out=None), 1), (dict(lse=None), 1),
+    (dict(dtype=2), 2), (dict(dtype=-1), 2),
+    (dict(head_dim=96), 4), (dict(head_dim=256), 4), (dict(head_dim=0), 4),
+    (dict(batch=-1), 3), (dict(total_q=-1), 3), (dict(heads=0), 3), (dict(max_q=9), 3), (dict(max_k=9), 3),
+    (dict(max_q=-1), 3),
+    (dict(scale=0.0), 6), (dict(scale=-1.0), 6), (dict(scale=math.inf), 6), (dict(scale=math.nan), 6),
+    (dict(causal=2), 6), (dict(causal=-1), 6),
+    (dict(q=A16 + 8), 5), (dict(k=A16 + 2), 5), (dict(v=A16 + 4), 5), (dict(out=A16 + 8), 5),
+    (dict(lse=A16 + 2), 5), (dict(cu_q=A16 + 1), 5), (dict(cu_k=A16 + 2), 5),
+])
+def test_fwd_validation(call, over, code):
+    assert call(**over) == code
+
+
+def test_mapped_needs_map():
+    assert call_mapped(blk=None) == 1
+    assert call_mapped(blk=A16 + 2) == 5
+
+
+def test_lse_and_offsets_need_only_4_byte_alignment():
+    # with only 4-byte alignment on lse/offsets and an empty batch, nothing is launched: FA_OK
+    assert call_fwd(lse=A4, cu_q=A4, cu_k=A4, batch=0, max_q=0, max_k=0) == 0
+    assert call_mapped(lse=A4, cu_q=A4, cu_k=A4, batch=0, max_q=0, max_k=0, blk=A4) == 0
+
+
+def test_empty_problems_launch_nothing():
+    assert call_fwd(batch=0, max_q=0, max_k=0) == 0
+    assert call_fwd(total_q=0, max_q=0) == 0  # no query rows
+    assert call_mapped(total_q=0, max_q=0) == 0
+
+
+def test_grid_too_large():
+    # 2^31-1 rows, one head per ... heads chosen so that work items x heads overflow int32
+    big = 2**31 - 1
+    assert call_fwd(total_q=big, total_k=8, max_q=big, heads=2**20, head_dim=64) == 8
+
+
+def test_tile_map_validation():
+    lib = fa.load_library()
+    assert lib.fa_varlen_tile_map(None, 1, 128, A16, None) == 1
+    assert lib.fa_varlen_tile_map(A16, 1, 128, None, None) == 1
+    assert lib.fa_varlen_tile_map(A16, -1, 128, A16, None) == 3
+    assert lib.fa_varlen_tile_map(A16, 1, 0, A16, None) == 6
+    assert lib.fa_varlen_tile_map(A16, 1, 5000, A16, None) == 6
+    assert lib.fa_varlen_tile_map(A16 + 1, 1, 128, A16, None) == 5
+
+
+def test_check_cu_validation():
+    lib = fa.load_library()
+    assert lib.fa_varlen_check_cu_seqlens(None, A16, 1, 8, 8, 8, 8, A16, None) == 1
+    assert lib.fa_varlen_check_cu_seqlens(A16, A16, -1, 8, 8, 8, 8, A16, None) == 3
+    assert lib.fa_varlen_check_cu_seqlens(A16, A16, 1, 8, 8, 8, 8, A16 + 2, None) == 5
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_LIB", None)
+    monkeypatch.setattr(fa, "_PKG_DIR", str(tmp_path))
+    with pytest.raises(fa.FaVarlenError, match="not built"):
+        fa.load_library()
+    with pytest.raises(fa.FaVarlenError, match="not built"):
+        fa.fa_varlen_block_sizes(64, 1)

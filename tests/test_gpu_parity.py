@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path, called through the C ABI, against the oracle.
+
+Bar (from the method's exactness up to floating-point order): the work-item
+map is bit-exact; out and lse agree to max-abs 2e-2 for bf16 inputs (fp32
+accumulation, bf16 probabilities and output) and 1e-5 for fp32 inputs; rows
+with no visible key give lse = -inf exactly and out = 0.
+
+Configurations: the tiny fp32 batch, the ragged q/k batch and the dense
+8x2048 batch are compared in full; the 16k-token sweep and the ragged 64k
+batch (the sizes and launch configuration the bench times) are compared on
+sampled rows and heads.  Edge cases: empty sequences, single tokens, ragged
+tails, Lq != Lk with causal masks, hundreds of short sequences, poisoned and
+guarded output buffers, determinism.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, draw_qkv, workload_custom, workload_dense,
+                      workload_ragged64k, workload_ragged_qk, workload_sweep, workload_tiny)
+from oracle import attention_fwd, attention_rows, tile_map
+from tests._gpu_util import TOL, compare, host, run_gpu, sample_rows, say, to_device
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import variable_length_flashattention_cu_amd as m
+    m.load_library()  # raises if the HIP library is missing: no fallback exists
+    return m
+
+
+def full_parity(fa, wl, causal):
+    say(f"case {wl.name} causal={causal} dtype={wl.dtype}")
+    data = draw_qkv(wl)
+    t = to_device(data, wl)
+    o, l = host(*run_gpu(wl, t, causal))
+    ref_o, ref_l = attention_fwd(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
+    n = wl.total_q
+    return compare(o[:n], l[:, :n], ref_o[:n], ref_l[:, :n], TOL[wl.dtype], wl.name)
+
+
+# ---------------------------------------------------------------- tile map
+def test_tile_map_bit_exact(fa):
+    rng = np.random.default_rng(100)
+    cases = [[0, 128, 300], [0, 200, 1024], [0, 300, 1024], [0], [0, 0, 0], [0, 5, 5, 300, 300]]
+    for _ in range(20):
+        lens = rng.integers(0, 700, size=int(rng.integers(1, 40)))
+        cases.append([0] + np.cumsum(lens).tolist())
+    lens = rng.integers(0, 300, size=1000)  # several scan chunks of 256
+    cases.append([0] + np.cumsum(lens).tolist())
+    bms = sorted({fa.fa_varlen_block_sizes(d, dt)[0] for d in (64, 128) for dt in (0, 1)} | {1, 64, 256})
+    for cu in cases:
+        cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
+        for bm in bms:
+            got = fa.fa_varlen_tile_map(cu_t, bm).cpu().numpy()
+            assert np.array_equal(got, tile_map(cu, bm)), (cu[:5], bm)
+
+
+# ---------------------------------------------------------------- configurations, full comparison
+def test_tiny_fp32(fa):
+    full_parity(fa, workload_tiny(), False)
+
+
+def test_tiny_fp32_causal(fa):
+    full_parity(fa, workload_tiny(), True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_qk(fa, causal):
+    full_parity(fa, workload_ragged_qk(), causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_8x2048(fa, causal):
+    full_parity(fa, workload_dense(), causal)
+
+
+# ---------------------------------------------------------------- full sizes, sampled rows
+def sampled_parity(fa, wl, causal, heads, seed):
+    say(f"case {wl.name} causal={causal} (sampled rows, heads {heads})")
+    data = draw_qkv(wl)
+    t = to_device(data, wl)
+    o, l = host(*run_gpu(wl, t, causal))
+    bm = fa.fa_varlen_block_sizes(wl.head_dim, 1 if wl.dtype == "bf16" else 0)[0]
+    rows = sample_rows(wl, bm, np.random.default_rng(seed))
+    ref_o, ref_l = attention_rows(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal, rows,
+                                  heads)
+    compare(o[rows][:, heads], l[heads][:, rows], ref_o, ref_l, TOL[wl.dtype], wl.name)
+    assert not np.isnan(o[:wl.total_q]).any() and not np.isnan(l[:, :wl.total_q]).any()
+
+
+@pytest.mark.parametrize("seqlen", SWEEP_SEQLENS)
+@pytest.mark.parametrize("head_dim", SWEEP_HEAD_DIMS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_sweep_sampled(fa, seqlen, head_dim, causal):
+    wl = workload_sweep(seqlen, head_dim)
+    sampled_parity(fa, wl, causal, [0, wl.heads // 2, wl.heads - 1], seed=seqlen + head_dim)
+
+
+def test_ragged64k_sampled(fa):
+    wl = workload_ragged64k()
+    sampled_parity(fa, wl, True, [0, 17, 31], seed=4)
+
+
+# ---------------------------------------------------------------- edge cases
+EDGE = [
+    ("empty_seqs", [0, 37, 0, 200, 0], [5, 0, 0, 300, 0]),
+    ("single_tokens", [1, 1, 1, 2], [1, 3, 1, 1]),
+    ("ragged_tails", [129, 63, 65, 191, 257], [129, 63, 65, 191, 257]),
+    ("q_longer_than_k", [824, 300, 40], [724, 33, 1]),
+    ("k_longer_than_q", [200, 5, 77], [300, 500, 130]),
+]
+
+
+@pytest.mark.parametrize("name,lq,lk", EDGE, ids=[e[0] for e in EDGE])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_edge_cases(fa, name, lq, lk, dtype, head_dim):
+    wl = workload_custom(f"{name}_{dtype}_d{head_dim}", lq, lk, 3, head_dim, dtype, seed=len(name) + head_dim)
+    for causal in (False, True):
+        full_parity(fa, wl, causal)
+
+
+def test_many_short_sequences(fa):
+    rng = np.random.default_rng(7)
+    lens = [int(x) for x in rng.integers(0, 40, size=300)]
+    wl = workload_custom("short300", lens, lens, 2, 128, "bf16", seed=77)
+    for causal in (False, True):
+        full_parity(fa, wl, causal)
+
+
+def test_single_long_sequence_fp32(fa):
+    wl = workload_custom("long_fp32", [2000], [2300], 2, 128, "f32", seed=78)
+    for causal in (False, True):
+        full_parity(fa, wl, causal)
+
+
+def test_zero_queries_give_mean_of_visible_values(fa):
+    """Q = 0: every visible key scores alike, so out is the mean of the visible V rows."""
+    wl = workload_custom("q_zero", [300, 129], [280, 129], 2, 128, "bf16", seed=79)
+    data = draw_qkv(wl)
+    data["q"][:] = 0
+    data["q_bits"][:] = 0
+    t = to_device(data, wl)
+    for causal in (False, True):
+        say(f"case q_zero causal={causal}")
+        o, l = host(*run_gpu(wl, t, causal))
+        ref_o, ref_l = attention_fwd(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
+        compare(o, l, ref_o, ref_l, TOL["bf16"], "q_zero")
+
+
+# ---------------------------------------------------------------- buffers, determinism, mapped entry
+def test_poisoned_and_guarded_buffers(fa):
+    """Rows past cu_q[-1] and guard bands around out/lse stay untouched."""
+    wl = workload_custom("guards", [100, 250], [100, 250], 2, 128, "bf16", seed=80)
+    data = draw_qkv(wl)
+    t = to_device(data, wl)
+    extra, guard = 17, 64
+    H, D, Tq = wl.heads, wl.head_dim, wl.total_q + extra
+    q = torch.zeros((Tq, H, D), dtype=torch.bfloat16, device="cuda")
+    q[:wl.total_q] = t["q"]
+    big_o = torch.full((Tq + 2 * guard, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    big_l = torch.full((H * Tq + 2 * guard * 64,), float("nan"), dtype=torch.float32, device="cuda")
+    out = big_o[guard:guard + Tq]
+    lse = big_l[guard * 64:guard * 64 + H * Tq].view(H, Tq)
+    for causal in (False, True):
+        say(f"case guards causal={causal}")
+        fa.fa_varlen_fwd(q, t["k"], t["v"], t["cu_q"], t["cu_k"], wl.max_seqlen_q, wl.max_seqlen_k, wl.scale,
+                         causal, out=out, lse=lse)
+        torch.cuda.synchronize()
+        bo = big_o.float().cpu().numpy()
+        bl = big_l.cpu().numpy()
+        assert np.isnan(bo[:guard]).all() and np.isnan(bo[guard + Tq:]).all()
+        assert np.isnan(bl[:guard * 64]).all() and np.isnan(bl[guard * 64 + H * Tq:]).all()
+        o = bo[guard:guard + Tq]
+        l = bl[guard * 64:guard * 64 + H * Tq].reshape(H, Tq)
+        assert np.isnan(o[wl.total_q:]).all() and np.isnan(l[:, wl.total_q:]).all()
+        ref_o, ref_l = attention_fwd(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
+        compare(o[:wl.total_q], l[:, :wl.total_q], ref_o, ref_l, TOL["bf16"], "guards")
+
+
+def test_deterministic_and_mapped_identical(fa):
+    wl = workload_ragged_qk()
+    data = draw_qkv(wl)
+    t = to_device(data, wl)
+    bm = fa.fa_varlen_block_sizes(wl.head_dim, 1)[0]
+    blk = fa.fa_varlen_tile_map(t["cu_q"], bm)
+    for causal in (False, True):
+        say(f"case determinism causal={causal}")
+        o1, l1 = host(*run_gpu(wl, t, causal))
+        o2, l2 = host(*run_gpu(wl, t, causal))
+        o3, l3 = fa.fa_varlen_fwd_mapped(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], wl.max_seqlen_q,
+                                         wl.max_seqlen_k, blk, wl.scale, causal)
+        torch.cuda.synchronize()
+        o3, l3 = host(o3, l3)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+
+
+def test_check_cu_seqlens_flags(fa):
+    def flags(cq, ck, tq, tk, mq, mk):
+        a = torch.tensor(cq, dtype=torch.int32, device="cuda")
+        b = torch.tensor(ck, dtype=torch.int32, device="cuda")
+        return int(fa.fa_varlen_check_cu_seqlens(a, b, tq, tk, mq, mk).item())
+    assert flags([0, 128, 300], [0, 128, 300], 300, 300, 172, 172) == 0
+    assert flags([1, 128, 300], [0, 128, 300], 300, 300, 300, 300) == 1
+    assert flags([0, 128, 100], [0, 128, 300], 300, 300, 300, 300) == 2
+    assert flags([0, 128, 301], [0, 128, 300], 300, 300, 300, 300) == 4
+    assert flags([0, 128, 300], [0, 128, 300], 300, 300, 171, 172) == 8
+    assert flags([0, 128, 300], [0, 200, 100], 300, 300, 300, 300) == 32
+    assert flags([0], [0], 0, 0, 0, 0) == 0

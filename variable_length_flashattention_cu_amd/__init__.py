@@ -1,0 +1,229 @@
+"""Python binding of libfa_varlen.so (exact varlen attention forward, MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/fa_varlen.h``.  PyTorch supplies device
+memory and the stream; no CPU fallback exists -- when the library is not
+built every entry point raises :class:`FaVarlenError`.
+
+Functions carry the names of the C entry points:
+  fa_varlen_fwd, fa_varlen_fwd_mapped, fa_varlen_tile_map,
+  fa_varlen_block_sizes, fa_varlen_check_cu_seqlens, fa_status_string.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "FaVarlenError",
+    "FA_DTYPE_F32",
+    "FA_DTYPE_BF16",
+    "library_path",
+    "load_library",
+    "fa_status_string",
+    "fa_varlen_block_sizes",
+    "fa_varlen_tile_map",
+    "fa_varlen_fwd",
+    "fa_varlen_fwd_mapped",
+    "fa_varlen_check_cu_seqlens",
+]
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_DTYPE", 3: "FA_ERR_SHAPE", 4: "FA_ERR_HEAD_DIM",
+    5: "FA_ERR_ALIGN", 6: "FA_ERR_ARG", 7: "FA_ERR_HIP", 8: "FA_ERR_TOO_LARGE",
+}
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FaVarlenError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({_status_text(status)})")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG_DIR, "libfa_varlen.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree HIP library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise FaVarlenError(-1, f"HIP library not built: {path} is missing; run "
+                                "`python -m variable_length_flashattention_cu_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_varlen_block_sizes.argtypes = [i32, i32, i32p, i32p]
+    lib.fa_varlen_block_sizes.restype = ctypes.c_int
+    lib.fa_varlen_tile_map.argtypes = [vp, i32, i32, vp, vp]
+    lib.fa_varlen_tile_map.restype = ctypes.c_int
+    fwd_args = [vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, i32, i32, i32, i32, i32, i32]
+    lib.fa_varlen_fwd.argtypes = fwd_args + [vp]
+    lib.fa_varlen_fwd.restype = ctypes.c_int
+    lib.fa_varlen_fwd_mapped.argtypes = fwd_args + [vp, vp]
+    lib.fa_varlen_fwd_mapped.restype = ctypes.c_int
+    lib.fa_varlen_check_cu_seqlens.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.fa_varlen_check_cu_seqlens.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return load_library().fa_status_string(int(status)).decode()
+    except Exception:  # library missing: the message names the problem already
+        return "library unavailable"
+
+
+def _check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FaVarlenError(status, where)
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_varlen_block_sizes(head_dim: int, dtype: int) -> Tuple[int, int]:
+    bm, bn = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load_library().fa_varlen_block_sizes(int(head_dim), int(dtype), ctypes.byref(bm), ctypes.byref(bn)),
+           "fa_varlen_block_sizes")
+    return bm.value, bn.value
+
+
+# --------------------------------------------------------------------------
+# torch-facing helpers (torch is only used for memory and streams)
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev_i32(t, name: str):
+    torch = _torch()
+    if not (t.is_cuda and t.dtype == torch.int32 and t.dim() == 1 and t.is_contiguous()):
+        raise TypeError(f"{name} must be a contiguous int32 CUDA tensor of shape [batch+1]")
+    return t
+
+
+def fa_varlen_tile_map(cu_seqlens_q, block_m: int, blk_start=None, stream=None):
+    """int32 [batch+1] work-item map of the ragged batch (device tensor)."""
+    torch = _torch()
+    cu = _dev_i32(cu_seqlens_q, "cu_seqlens_q")
+    batch = cu.numel() - 1
+    if blk_start is None:
+        blk_start = torch.empty(batch + 1, dtype=torch.int32, device=cu.device)
+    _dev_i32(blk_start, "blk_start")
+    if blk_start.numel() != batch + 1:
+        raise ValueError("blk_start must have batch+1 entries")
+    _check(load_library().fa_varlen_tile_map(cu.data_ptr(), batch, int(block_m), blk_start.data_ptr(),
+                                             _stream_handle(stream)), "fa_varlen_tile_map")
+    return blk_start
+
+
+def _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse):
+    torch = _torch()
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("expected q [total_q, H, D], k and v [total_k, H, D]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must be CUDA tensors of one dtype")
+    dt = _dtype_code(q)
+    cu_q = _dev_i32(cu_seqlens_q, "cu_seqlens_q")
+    cu_k = _dev_i32(cu_seqlens_k, "cu_seqlens_k")
+    if cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    total_q, H, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [H, total_q]")
+    return q, k, v, cu_q, cu_k, float(softmax_scale), out, lse, dt
+
+
+def fa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                  softmax_scale: Optional[float] = None, causal: bool = False, out=None, lse=None,
+                  stream=None):
+    """Exact attention forward over packed variable-length sequences.
+
+    q [total_q, H, D], k/v [total_k, H, D] (bf16 or fp32, CUDA);
+    cu_seqlens_* int32 [batch+1] on the device.  Returns (out, lse) with
+    out shaped like q and lse float32 [H, total_q].
+    """
+    q, k, v, cu_q, cu_k, scale, out, lse, dt = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale,
+                                                        out, lse)
+    total_q, H, D = q.shape
+    st = load_library().fa_varlen_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), int(max_seqlen_q),
+        int(max_seqlen_k), scale, int(bool(causal)), out.data_ptr(), lse.data_ptr(), cu_q.numel() - 1,
+        total_q, k.shape[0], H, D, dt, _stream_handle(stream))
+    _check(st, "fa_varlen_fwd")
+    return out, lse
+
+
+def fa_varlen_fwd_mapped(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                         blk_start, softmax_scale: Optional[float] = None, causal: bool = False, out=None,
+                         lse=None, stream=None):
+    """fa_varlen_fwd with a work-item map built by fa_varlen_tile_map."""
+    q, k, v, cu_q, cu_k, scale, out, lse, dt = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale,
+                                                        out, lse)
+    _dev_i32(blk_start, "blk_start")
+    total_q, H, D = q.shape
+    st = load_library().fa_varlen_fwd_mapped(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), int(max_seqlen_q),
+        int(max_seqlen_k), scale, int(bool(causal)), out.data_ptr(), lse.data_ptr(), cu_q.numel() - 1,
+        total_q, k.shape[0], H, D, dt, blk_start.data_ptr(), _stream_handle(stream))
+    _check(st, "fa_varlen_fwd_mapped")
+    return out, lse
+
+
+def fa_varlen_check_cu_seqlens(cu_seqlens_q, cu_seqlens_k, total_q: int, total_k: int, max_seqlen_q: int,
+                               max_seqlen_k: int, flags=None, stream=None):
+    """Device check of the offset preconditions; returns an int32 [1] flag tensor."""
+    torch = _torch()
+    cu_q = _dev_i32(cu_seqlens_q, "cu_seqlens_q")
+    cu_k = _dev_i32(cu_seqlens_k, "cu_seqlens_k")
+    if flags is None:
+        flags = torch.empty(1, dtype=torch.int32, device=cu_q.device)
+    _check(load_library().fa_varlen_check_cu_seqlens(
+        cu_q.data_ptr(), cu_k.data_ptr(), cu_q.numel() - 1, int(total_q), int(total_k), int(max_seqlen_q),
+        int(max_seqlen_k), flags.data_ptr(), _stream_handle(stream)), "fa_varlen_check_cu_seqlens")
+    return flags

@@ -1,0 +1,70 @@
+"""Build libfa_varlen.so in place with hipcc for gfx950.
+
+    python -m variable_length_flashattention_cu_amd.build [--asm DIR]
+
+The library is written next to this file (the package directory), so it
+travels with the source tree.  ``--asm DIR`` also writes the device assembly
+of the kernels to DIR for inspection.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libfa_varlen.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+
+SOURCES = [os.path.join(CSRC, "fa_varlen_kernels.hip"), os.path.join(CSRC, "fa_varlen_api.cpp")]
+ARCH = "gfx950"
+# Packed fp32 VALU forms are kept out of the generated code.
+NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def common_flags():
+    return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-I", INCLUDE, "-I", CSRC,
+            "-Wall", "-Wno-unused-function"] + NO_PACKED_FP32
+
+
+def build(verbose: bool = False, asm_dir: str | None = None) -> str:
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc()] + common_flags() + ["-shared", "-o", tmp] + SOURCES
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    os.replace(tmp, LIB_PATH)
+    if asm_dir:
+        os.makedirs(asm_dir, exist_ok=True)
+        asm = os.path.join(asm_dir, "fa_varlen_kernels.s")
+        cmd = [hipcc()] + common_flags() + ["--cuda-device-only", "-S", "-o", asm, SOURCES[0]]
+        subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return LIB_PATH
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", default=None, help="also write device assembly to this directory")
+    ap.add_argument("-q", "--quiet", action="store_true")
+    args = ap.parse_args()
+    path = build(verbose=not args.quiet, asm_dir=args.asm)
+    print(path)
+
+
+if __name__ == "__main__":
+    main()

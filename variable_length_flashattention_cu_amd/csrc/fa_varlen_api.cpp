@@ -1,0 +1,172 @@
+// fa_varlen_api.cpp -- the C ABI declared in include/fa_varlen.h: argument
+// validation, launch sizing and the two kernel launches.  Every check runs on
+// the host before any HIP call, so a validation error launches nothing.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_varlen.h"
+#include "fa_varlen_launch.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634074;
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+struct Plan {
+  fa::TileConfig tc;
+  int64_t tmax;
+  int64_t grid;
+};
+
+// Validation shared by fa_varlen_fwd and fa_varlen_fwd_mapped.
+int validate(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+             int32_t max_q, int32_t max_k, float scale, int32_t causal, const void* out, const float* lse,
+             int32_t batch, int32_t total_q, int32_t total_k, int32_t heads, int32_t head_dim, int32_t dtype,
+             Plan* plan) {
+  if (!q || !k || !v || !cu_q || !cu_k || !out || !lse) return FA_ERR_NULL;
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  const fa::TileConfig tc = fa::tile_config(dtype, head_dim);
+  if (tc.block_m == 0) return FA_ERR_HEAD_DIM;
+  if (batch < 0 || total_q < 0 || total_k < 0 || heads < 1 || max_q < 0 || max_k < 0) return FA_ERR_SHAPE;
+  if (max_q > total_q || max_k > total_k) return FA_ERR_SHAPE;
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(cu_q, 4) || !aligned(cu_k, 4)) return FA_ERR_ALIGN;
+  // Upper bound on the number of work items: sum_b ceil(Lq_b / BM) is at most
+  // batch * ceil(max_seqlen_q / BM) and at most ceil(total_q / BM) + batch - 1.
+  const int64_t bm = tc.block_m;
+  const int64_t by_max = (int64_t)batch * ((max_q + bm - 1) / bm);
+  const int64_t by_total = (total_q + bm - 1) / bm + (batch > 0 ? batch - 1 : 0);
+  const int64_t tmax = by_max < by_total ? by_max : by_total;
+  const int64_t work = tmax * heads;
+  const int64_t grid = (work + 7) / 8 * 8;
+  if (grid > INT32_MAX || tmax > INT32_MAX) return FA_ERR_TOO_LARGE;
+  plan->tc = tc;
+  plan->tmax = tmax;
+  plan->grid = grid;
+  return FA_OK;
+}
+
+fa::FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                      float scale, void* out, float* lse, int32_t batch, int32_t total_q, int32_t heads,
+                      int32_t head_dim, const int32_t* blk_start, const Plan& plan) {
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.blk_start = blk_start;
+  a.row_stride = (int64_t)heads * head_dim;
+  a.scale_log2 = (float)((double)scale * kLog2e);
+  a.batch = batch;
+  a.tmax = (int32_t)plan.tmax;
+  a.n_work = (int32_t)(plan.tmax * heads);
+  a.total_q = total_q;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_DTYPE: return "unsupported dtype (expected FA_DTYPE_F32 or FA_DTYPE_BF16)";
+    case FA_ERR_SHAPE: return "invalid sizes (negative, zero heads, or max_seqlen above the row count)";
+    case FA_ERR_HEAD_DIM: return "unsupported head_dim (64 and 128 are supported)";
+    case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse and offsets 4 bytes)";
+    case FA_ERR_ARG: return "invalid argument (softmax_scale must be finite and > 0, causal 0 or 1, block_m 1..4096)";
+    case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_TOO_LARGE: return "problem too large for one launch";
+    default: return "unknown status";
+  }
+}
+
+int fa_varlen_block_sizes(int32_t head_dim, int32_t dtype, int32_t* block_m, int32_t* block_n) {
+  if (!block_m || !block_n) return FA_ERR_NULL;
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  const fa::TileConfig tc = fa::tile_config(dtype, head_dim);
+  if (tc.block_m == 0) return FA_ERR_HEAD_DIM;
+  *block_m = tc.block_m;
+  *block_n = tc.block_n;
+  return FA_OK;
+}
+
+int fa_varlen_tile_map(const int32_t* cu_seqlens_q, int32_t batch, int32_t block_m, int32_t* blk_start,
+                       void* stream) {
+  if (!cu_seqlens_q || !blk_start) return FA_ERR_NULL;
+  if (batch < 0) return FA_ERR_SHAPE;
+  if (block_m < 1 || block_m > 4096) return FA_ERR_ARG;
+  if (!aligned(cu_seqlens_q, 4) || !aligned(blk_start, 4)) return FA_ERR_ALIGN;
+  if (fa::launch_tile_map(cu_seqlens_q, batch, block_m, blk_start, (hipStream_t)stream) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int fa_varlen_fwd_mapped(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                         float softmax_scale, int32_t causal, void* out, float* lse, int32_t batch,
+                         int32_t total_q, int32_t total_k, int32_t num_heads, int32_t head_dim, int32_t dtype,
+                         const int32_t* blk_start, void* stream) {
+  Plan plan;
+  int st = validate(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+                    out, lse, batch, total_q, total_k, num_heads, head_dim, dtype, &plan);
+  if (st != FA_OK) return st;
+  if (!blk_start) return FA_ERR_NULL;
+  if (!aligned(blk_start, 4)) return FA_ERR_ALIGN;
+  if (plan.grid == 0) return FA_OK;  // no query rows: nothing to compute
+  const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse, batch, total_q,
+                                  num_heads, head_dim, blk_start, plan);
+  if (fa::launch_fwd(dtype, head_dim, causal != 0, (int)plan.grid, a, (hipStream_t)stream) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int fa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                  int32_t causal, void* out, float* lse, int32_t batch, int32_t total_q, int32_t total_k,
+                  int32_t num_heads, int32_t head_dim, int32_t dtype, void* stream) {
+  Plan plan;
+  int st = validate(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+                    out, lse, batch, total_q, total_k, num_heads, head_dim, dtype, &plan);
+  if (st != FA_OK) return st;
+  if (plan.grid == 0) return FA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* blk_start = nullptr;
+  if (hipMallocAsync((void**)&blk_start, sizeof(int32_t) * ((size_t)batch + 1), s) != hipSuccess)
+    return FA_ERR_HIP;
+  int rc = FA_OK;
+  if (fa::launch_tile_map(cu_seqlens_q, batch, plan.tc.block_m, blk_start, s) != hipSuccess) {
+    rc = FA_ERR_HIP;
+  } else {
+    const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse, batch,
+                                    total_q, num_heads, head_dim, blk_start, plan);
+    if (fa::launch_fwd(dtype, head_dim, causal != 0, (int)plan.grid, a, s) != hipSuccess) rc = FA_ERR_HIP;
+  }
+  if (hipFreeAsync(blk_start, s) != hipSuccess) rc = FA_ERR_HIP;
+  return rc;
+}
+
+int fa_varlen_check_cu_seqlens(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                               int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t* flags, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k || !flags) return FA_ERR_NULL;
+  if (batch < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return FA_ERR_SHAPE;
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(flags, 4)) return FA_ERR_ALIGN;
+  if (fa::launch_check_cu(cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, flags,
+                          (hipStream_t)stream) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
+}  // extern "C"

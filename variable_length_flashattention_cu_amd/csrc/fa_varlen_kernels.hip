@@ -1,0 +1,678 @@
+// fa_varlen_kernels.hip -- gfx950 kernels for exact attention forward over
+// packed variable-length sequences.
+//
+// Three kernels:
+//   * tile_map_kernel     -- the work-item map: exclusive scan of per-sequence
+//                            query-block counts (the sequence-dimension split,
+//                            iplexlaw.co.kr "FlashAttention-2 GPU work
+//                            partitioning", section "Tres mejoras en la
+//                            utilización de la GPU").
+//   * fwd_bf16_kernel     -- bf16 in/out, bf16 MFMA for both contractions,
+//                            fp32 online softmax.
+//   * fwd_f32_kernel      -- fp32 in/out, fp32 MFMA, same online softmax.
+//   * check_cu_kernel     -- optional device validation of the offsets.
+//
+// Forward-kernel organisation (both dtypes)
+// -----------------------------------------
+// One workgroup owns one (sequence b, query block m, head h) work item: BM
+// query rows split across NW wavefronts, 32*QB rows per wavefront (split-Q:
+// the waves share the K/V tiles and never exchange partial results, as the
+// pages describe for FlashAttention-2's forward pass, zepes.com "Comprendiendo
+// Flash-Atención y Flash-Atención-2", section "FlashAttention-2").  K/V tiles
+// of BN keys stream through double-buffered LDS; the score tile never leaves
+// registers (slavadubrov.com "O que FlashAttention muda na inferência",
+// section "Separar o armazenamento do cálculo").
+//
+// Scores are computed transposed, S^T = K Q^T, with the 32x32 MFMA: in the
+// 32x32 accumulator layout a lane owns one column, so every lane owns one query
+// row and holds 16 of the 32 keys of a key block (the other 16 sit in lane
+// l^32).  Consequences:
+//   * row max / row sum need one cross-lane exchange (lane l <-> l^32);
+//   * rescaling the output by the online-softmax factor is a per-lane scalar
+//     multiply, because O is also accumulated transposed (O^T = V^T P^T) and
+//     each lane again owns one query row;
+//   * the probabilities P^T are already in the B-operand layout of the second
+//     MFMA: no shuffle or LDS round trip between the two contractions.
+// The second contraction needs V^T as its A operand (8 consecutive keys per
+// lane), so V tiles are transposed in registers (v_perm) on their way into
+// LDS.
+//
+// Online softmax per query row (iplexlaw.co.kr, section "Bloques pequeños,
+// normalización global"): with t = scale*log2(e)*s,
+//   m' = max(m, max_j t_j), alpha = 2^(m - m'), l' = alpha l + sum_j 2^(t_j - m'),
+//   O' = alpha O + sum_j 2^(t_j - m') v_j;  out = O / l,  lse = (m + log2 l) ln 2.
+// A row that has seen no visible key keeps m = -inf and is guarded so that no
+// -inf - -inf appears; such rows end with out = 0, lse = -inf.
+//
+// Masks (reading: bottom-right causal alignment, key j visible to query i iff
+// j <= i + Lk - Lq; ragged tails from the offsets, friki.work "Mecanismo
+// cu_seqlens en FlashAttention", section "Lógica de cálculo de longitud") are
+// applied only to key tiles that cross the diagonal or the end of the
+// sequence; tiles entirely above the diagonal are never visited.
+//
+// Scheduling: workgroup ids are remapped so that each of the 8 XCDs receives
+// a contiguous range of work (all query blocks of a head land on one XCD and
+// share its L2 for K/V), and inside a head the items run last-first so that
+// the longest causal rows start early.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_varlen_launch.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// value of lane l^32 (same query row, other half of the keys)
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// ---------------------------------------------------------------------------
+// work decoding shared by both forward kernels
+// ---------------------------------------------------------------------------
+struct WorkItem {
+  int b, m, h;
+  int q_start, Lq, k_start, Lk;
+};
+
+__device__ __forceinline__ bool decode_work(const FwdArgs& a, WorkItem& w) {
+  // hardware dispatch sends workgroup i to XCD i % 8; give each XCD a
+  // contiguous slice of work ids (gridDim.x is a multiple of 8).
+  const uint32_t per_xcd = gridDim.x >> 3;
+  const uint32_t work = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+  if (work >= (uint32_t)a.n_work) return false;
+  w.h = (int)(work / (uint32_t)a.tmax);
+  const int tr = (int)(work % (uint32_t)a.tmax);
+  const int T = a.blk_start[a.batch];
+  if (tr >= T) return false;
+  const int t = T - 1 - tr;
+  int lo = 0, hi = a.batch;  // invariant: blk_start[lo] <= t < blk_start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.blk_start[mid] <= t) lo = mid; else hi = mid;
+  }
+  w.b = lo;
+  w.m = t - a.blk_start[lo];
+  w.q_start = a.cu_q[lo];
+  w.Lq = a.cu_q[lo + 1] - w.q_start;
+  w.k_start = a.cu_k[lo];
+  w.Lk = a.cu_k[lo + 1] - w.k_start;
+  return true;
+}
+
+// Key-tile range of a work item.  Tiles [0, n_full) need no mask, tiles
+// [n_full, n_end) need the causal and/or tail mask, tiles >= n_end are
+// invisible to every row of the item.
+template <int BM, int BN, bool CAUSAL>
+__device__ __forceinline__ void key_tiles(const WorkItem& w, int& n_full, int& n_end) {
+  const int q0 = w.m * BM;
+  const int rows = min(BM, w.Lq - q0);
+  int j_hi = w.Lk, j_full = w.Lk;
+  if (CAUSAL) {
+    const int shift = w.Lk - w.Lq;
+    j_hi = min(w.Lk, q0 + rows + shift);   // keys < j_hi seen by the last row
+    j_full = min(w.Lk, q0 + shift + 1);    // keys < j_full seen by every row
+  }
+  n_end = j_hi > 0 ? (j_hi + BN - 1) / BN : 0;
+  n_full = j_full > 0 ? j_full / BN : 0;
+}
+
+// ---------------------------------------------------------------------------
+// tile map
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict__ cu_q, int batch,
+                                                       int block_m, int32_t* __restrict__ blk_start) {
+  __shared__ int wave_tot[4];
+  __shared__ int carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid == 0) { blk_start[0] = 0; carry_s = 0; }
+  __syncthreads();
+  for (int base = 0; base < batch; base += 256) {
+    const int b = base + tid;
+    int n = 0;
+    if (b < batch) {
+      const int L = cu_q[b + 1] - cu_q[b];
+      n = L > 0 ? (L - 1) / block_m + 1 : 0;
+    }
+    int x = n;  // inclusive scan inside the wavefront
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_tot[wid] = x;
+    __syncthreads();
+    int before = carry_s;
+    for (int i = 0; i < wid; ++i) before += wave_tot[i];
+    const int incl = before + x;
+    if (b < batch) blk_start[b + 1] = incl;
+    __syncthreads();
+    if (tid == 255) carry_s = incl;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cu_seqlens validation (optional, debugging aid)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void check_cu_kernel(const int32_t* __restrict__ cu_q,
+                                                       const int32_t* __restrict__ cu_k, int batch,
+                                                       int total_q, int total_k, int max_q, int max_k,
+                                                       int32_t* __restrict__ flags) {
+  __shared__ int acc;
+  if (threadIdx.x == 0) acc = 0;
+  __syncthreads();
+  int f = 0;
+  if (threadIdx.x == 0) {
+    if (cu_q[0] != 0) f |= 1;
+    if (cu_k[0] != 0) f |= 16;
+    if (cu_q[batch] > total_q) f |= 4;
+    if (cu_k[batch] > total_k) f |= 64;
+  }
+  for (int b = threadIdx.x; b < batch; b += 256) {
+    const int lq = cu_q[b + 1] - cu_q[b], lk = cu_k[b + 1] - cu_k[b];
+    if (lq < 0) f |= 2;
+    if (lk < 0) f |= 32;
+    if (lq > max_q) f |= 8;
+    if (lk > max_k) f |= 128;
+  }
+  if (f) atomicOr(&acc, f);
+  __syncthreads();
+  if (threadIdx.x == 0) flags[0] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 forward
+// ---------------------------------------------------------------------------
+// LDS layouts (16-byte chunks are XOR-swizzled so that the MFMA operand reads
+// hit distinct banks within each group of 8 and of 16 lanes):
+//   Ks[key][d]   key-major, one row of D bf16 per key
+//   Vt[d][key]   dimension-major (V transposed), one row of BN bf16 per d
+//
+// A-operand row permutation for S^T = K Q^T: accumulator row R of the 32x32
+// layout lives in register 4*(R/8) + (R%4) of lane group (R/4)%2.  Loading key
+// pi(R) = 16*((R/4)%2) + 4*(R/8) + R%4 into A row R makes register r of lane
+// group g hold key 16g + r, so the 8 probabilities a lane feeds to one PV MFMA
+// are 8 consecutive keys: a single 16-byte read of Vt.
+__device__ __forceinline__ int key_of_arow(int R) { return ((R >> 2) & 1) * 16 + (R >> 3) * 4 + (R & 3); }
+
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  if constexpr (D == 128) return (row & 3) | ((row >> 2) & 4) | ((row << 1) & 8);
+  else return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 2) & 4);
+}
+template <int BN>
+__device__ __forceinline__ int v_swz(int d) {
+  if constexpr (BN == 128) return d & 15;
+  else return ((d >> 1) & 3) | (((d ^ (d >> 3)) & 1) << 2);
+}
+
+template <int D, int BN, int NW>
+struct Bf16Tile {
+  static constexpr int THREADS = NW * 64;
+  static constexpr int K_CHUNKS = BN * D / 8;             // 16-byte chunks per K tile
+  static constexpr int K_PER_THREAD = K_CHUNKS / THREADS;
+  static constexpr int V_UNITS = (BN / 4) * (D / 8);      // 4 keys x 8 dims per unit
+  static constexpr int V_PER_THREAD = V_UNITS / THREADS;
+  static_assert(K_CHUNKS % THREADS == 0 && V_UNITS % THREADS == 0, "tile/threads mismatch");
+  static_assert((D / 8) % 4 == 0, "V unit mapping needs D/8 divisible by 4");
+
+  u32x4 kreg[K_PER_THREAD];
+  u32x4 vreg[V_PER_THREAD][4];
+
+  // global -> registers; rows at or beyond Lk read as zero
+  __device__ __forceinline__ void load(const __bf16* __restrict__ kbase, const __bf16* __restrict__ vbase,
+                                       int64_t row_stride, int key0, int Lk, int tid) {
+#pragma unroll
+    for (int i = 0; i < K_PER_THREAD; ++i) {
+      const int c = tid + i * THREADS;
+      const int row = c / (D / 8), ch = c % (D / 8);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key0 + row < Lk) x = *(const u32x4*)(kbase + (int64_t)(key0 + row) * row_stride + ch * 8);
+      kreg[i] = x;
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_THREAD; ++i) {
+      const int w = tid + i * THREADS;
+      const int dc = ((w >> 2) / (BN / 4)) * 4 + (w & 3);
+      const int u = (w >> 2) % (BN / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + 4 * u + r;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (key < Lk) x = *(const u32x4*)(vbase + (int64_t)key * row_stride + dc * 8);
+        vreg[i][r] = x;
+      }
+    }
+  }
+
+  // registers -> LDS (K as is, V transposed)
+  __device__ __forceinline__ void store(__bf16* Ks, __bf16* Vt, int tid) const {
+#pragma unroll
+    for (int i = 0; i < K_PER_THREAD; ++i) {
+      const int c = tid + i * THREADS;
+      const int row = c / (D / 8), ch = c % (D / 8);
+      *(u32x4*)(Ks + row * D + 8 * (ch ^ k_swz<D>(row))) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_THREAD; ++i) {
+      const int w = tid + i * THREADS;
+      const int dc = ((w >> 2) / (BN / 4)) * 4 + (w & 3);
+      const int u = (w >> 2) % (BN / 4);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        // dims 2*e2 and 2*e2+1 of the chunk, for keys 4u..4u+3
+        const uint32_t r0 = vreg[i][0][e2], r1 = vreg[i][1][e2];
+        const uint32_t r2 = vreg[i][2][e2], r3 = vreg[i][3][e2];
+        u32x2 lo, hi;
+        lo[0] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // (key0, key1) of dim 2*e2
+        lo[1] = __builtin_amdgcn_perm(r3, r2, 0x05040100u);  // (key2, key3)
+        hi[0] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // dim 2*e2+1
+        hi[1] = __builtin_amdgcn_perm(r3, r2, 0x07060302u);
+        const int d0 = dc * 8 + 2 * e2, d1 = d0 + 1;
+        *(u32x2*)(Vt + d0 * BN + 8 * ((u >> 1) ^ v_swz<BN>(d0)) + 4 * (u & 1)) = lo;
+        *(u32x2*)(Vt + d1 * BN + 8 * ((u >> 1) ^ v_swz<BN>(d1)) + 4 * (u & 1)) = hi;
+      }
+    }
+  }
+};
+
+template <int D, int BN, int NW, int QB, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int BM = 32 * QB * NW;
+  constexpr int KSTEPS = D / 16;  // MFMA k-steps for Q K^T
+  constexpr int KB = BN / 32;     // 32-key blocks per tile
+  constexpr int DB = D / 32;      // 32-dim blocks of the output
+  using Tile = Bf16Tile<D, BN, NW>;
+
+  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * BN];
+
+  WorkItem w;
+  if (!decode_work(a, w)) return;
+  int n_full, n_end;
+  key_tiles<BM, BN, CAUSAL>(w, n_full, n_end);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int q0 = w.m * BM;
+  const int wrow0 = q0 + wave * 32 * QB;  // first query row of this wave (in sequence)
+  const int shift = w.Lk - w.Lq;
+
+  const __bf16* __restrict__ qp = (const __bf16*)a.q;
+  const __bf16* __restrict__ kbase = (const __bf16*)a.k + (int64_t)w.k_start * a.row_stride + (int64_t)w.h * D;
+  const __bf16* __restrict__ vbase = (const __bf16*)a.v + (int64_t)w.k_start * a.row_stride + (int64_t)w.h * D;
+
+  // Q^T as the B operand: lane (query l32, half g) holds dims 16ks+8g .. +7
+  bf16x8 qreg[QB][KSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wrow0 + qb * 32 + l32;
+    const __bf16* src = qp + (int64_t)(w.q_start + row) * a.row_stride + (int64_t)w.h * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (row < w.Lq) x = *(const u32x4*)(src + 16 * ks);
+      qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  f32x16 o[QB][DB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
+  }
+
+  Tile tile;
+  if (n_end > 0) {
+    tile.load(kbase, vbase, a.row_stride, 0, w.Lk, tid);
+    tile.store(lds_k[0], lds_v[0], tid);
+  }
+  __syncthreads();
+
+  // A-operand addressing constants
+  const int arow = key_of_arow(l32);  // key row this lane feeds into A for S^T
+
+  for (int n = 0; n < n_end; ++n) {
+    const int buf = n & 1;
+    const int key0 = n * BN;
+    if (n + 1 < n_end) tile.load(kbase, vbase, a.row_stride, key0 + BN, w.Lk, tid);
+
+    // a wave skips the tile when all its rows lie past the end of the sequence
+    // or (causal) all its rows sit above the tile's first key
+    const bool wave_active = (wrow0 < w.Lq) && (!CAUSAL || (key0 <= wrow0 + 32 * QB - 1 + shift));
+    if (wave_active) {
+      const __bf16* Ks = lds_k[buf];
+      const __bf16* Vt = lds_v[buf];
+      // ---- S^T = K Q^T
+      f32x16 s[QB][KB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int krow = kb * 32 + arow;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const int ch = 2 * ks + g;
+          const bf16x8 av = *(const bf16x8*)(Ks + krow * D + 8 * (ch ^ k_swz<D>(krow)));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[qb][ks], s[qb][kb], 0, 0, 0);
+        }
+      }
+      // ---- masks (diagonal / tail tiles only)
+      if (n >= n_full) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int i = wrow0 + qb * 32 + l32;
+          const int lim = CAUSAL ? min(w.Lk - 1, i + shift) : (w.Lk - 1);  // last visible key
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = key0 + kb * 32 + 16 * g + r;
+              if (key > lim) s[qb][kb][r] = kNegInf;
+            }
+        }
+      }
+      // ---- online softmax (log2 domain)
+      bf16x8 p[QB][KB][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float m_new = fmaxf(m_run[qb], mx * a.scale_log2);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[qb] - m_use);
+        m_run[qb] = m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float pe = fast_exp2(__builtin_fmaf(s[qb][kb][8 * t + e], a.scale_log2, -m_use));
+              lsum += pe;
+              p[qb][kb][t][e] = (__bf16)pe;
+            }
+        l_run[qb] = l_run[qb] * alpha + lsum;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+      }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 32 + l32;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int cs = kb * 4 + 2 * g + t;  // 16-byte chunk of keys 32kb+16g+8t..+7
+            const bf16x8 av = *(const bf16x8*)(Vt + d * BN + 8 * (cs ^ v_swz<BN>(d)));
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[qb][kb][t], o[qb][db], 0, 0, 0);
+          }
+      }
+    }
+
+    if (n + 1 < n_end) tile.store(lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, write out (bf16) and lse
+  __bf16* __restrict__ op = (__bf16*)a.out;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int i = wrow0 + qb * 32 + l32;
+    const float l = l_run[qb] + swap_halves(l_run[qb]);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (i < w.Lq) {
+      __bf16* dst = op + (int64_t)(w.q_start + i) * a.row_stride + (int64_t)w.h * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          bf16x4 v4;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[qb][db][4 * s4 + c] * inv);
+          *(bf16x4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
+        }
+      if (g == 0)
+        a.lse[(int64_t)w.h * a.total_q + w.q_start + i] = l > 0.f ? (m_run[qb] + fast_log2(l)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 forward (fp32 MFMA 32x32x2; no reduced precision anywhere)
+// ---------------------------------------------------------------------------
+// A/B operands of the fp32 MFMA are single elements per lane, so neither K
+// nor V needs a transpose: rows are padded by 4 floats against bank conflicts.
+// Register r of lane group g in the 32x32 accumulator holds key
+// 8*(r/4) + 4g + r%4 of the 32-key block (natural key order in A).
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdArgs a) {
+  constexpr int BN = 32;
+  constexpr int BM = 32 * NW;
+  constexpr int LD = D + 4;
+  constexpr int DB = D / 32;
+  constexpr int THREADS = NW * 64;
+  constexpr int CHUNKS = BN * D / 4;  // float4 chunks per tile
+  constexpr int PER_THREAD = CHUNKS / THREADS;
+  static_assert(CHUNKS % THREADS == 0, "tile/threads mismatch");
+
+  __shared__ __attribute__((aligned(16))) float lds_k[2][BN * LD];
+  __shared__ __attribute__((aligned(16))) float lds_v[2][BN * LD];
+
+  WorkItem w;
+  if (!decode_work(a, w)) return;
+  int n_full, n_end;
+  key_tiles<BM, BN, CAUSAL>(w, n_full, n_end);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int wrow0 = w.m * BM + wave * 32;
+  const int shift = w.Lk - w.Lq;
+  const int i = wrow0 + l32;
+
+  const float* __restrict__ kbase = (const float*)a.k + (int64_t)w.k_start * a.row_stride + (int64_t)w.h * D;
+  const float* __restrict__ vbase = (const float*)a.v + (int64_t)w.k_start * a.row_stride + (int64_t)w.h * D;
+
+  float qreg[D / 2];
+  {
+    const float* src = (const float*)a.q + (int64_t)(w.q_start + i) * a.row_stride + (int64_t)w.h * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) qreg[ks] = (i < w.Lq) ? src[2 * ks + g] : 0.f;
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+
+  f32x4 kreg[PER_THREAD], vreg[PER_THREAD];
+  auto load = [&](int key0) {
+#pragma unroll
+    for (int it = 0; it < PER_THREAD; ++it) {
+      const int c = tid + it * THREADS;
+      const int row = c / (D / 4), ch = c % (D / 4);
+      f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
+      if (key0 + row < w.Lk) {
+        kx = *(const f32x4*)(kbase + (int64_t)(key0 + row) * a.row_stride + 4 * ch);
+        vx = *(const f32x4*)(vbase + (int64_t)(key0 + row) * a.row_stride + 4 * ch);
+      }
+      kreg[it] = kx;
+      vreg[it] = vx;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < PER_THREAD; ++it) {
+      const int c = tid + it * THREADS;
+      const int row = c / (D / 4), ch = c % (D / 4);
+      *(f32x4*)(&lds_k[buf][row * LD + 4 * ch]) = kreg[it];
+      *(f32x4*)(&lds_v[buf][row * LD + 4 * ch]) = vreg[it];
+    }
+  };
+
+  if (n_end > 0) { load(0); store(0); }
+  __syncthreads();
+
+  for (int n = 0; n < n_end; ++n) {
+    const int buf = n & 1;
+    const int key0 = n * BN;
+    if (n + 1 < n_end) load(key0 + BN);
+    const bool wave_active = (wrow0 < w.Lq) && (!CAUSAL || (key0 <= wrow0 + 31 + shift));
+    if (wave_active) {
+      const float* Ks = lds_k[buf];
+      const float* Vs = lds_v[buf];
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 2; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[l32 * LD + 2 * ks + g], qreg[ks], s, 0, 0, 0);
+      if (n >= n_full) {
+        const int lim = CAUSAL ? min(w.Lk - 1, i + shift) : (w.Lk - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key > lim) s[r] = kNegInf;
+        }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -m_use));
+        lsum += s[r];
+      }
+      l_run = l_run * alpha + lsum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int key = 8 * (u >> 2) + 4 * g + (u & 3);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * LD + db * 32 + l32], s[u], o[db], 0, 0, 0);
+        }
+      }
+    }
+    if (n + 1 < n_end) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l = l_run + swap_halves(l_run);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (i < w.Lq) {
+    float* dst = (float*)a.out + (int64_t)(w.q_start + i) * a.row_stride + (int64_t)w.h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        f32x4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = o[db][4 * s4 + c] * inv;
+        *(f32x4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
+      }
+    if (g == 0) a.lse[(int64_t)w.h * a.total_q + w.q_start + i] = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch helpers
+// ---------------------------------------------------------------------------
+template <typename K>
+hipError_t launch(K kernel, int grid, int block, hipStream_t stream, const FwdArgs& a) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile configuration per (dtype, head_dim): must agree with the kernels above.
+TileConfig tile_config(int dtype, int head_dim) {
+  TileConfig c{0, 0, 0};
+  if (dtype == 1) {  // bf16
+    if (head_dim == 128) c = TileConfig{128, 64, 256};
+    else if (head_dim == 64) c = TileConfig{128, 128, 256};
+  } else if (dtype == 0) {  // f32
+    if (head_dim == 128 || head_dim == 64) c = TileConfig{128, 32, 256};
+  }
+  return c;
+}
+
+hipError_t launch_tile_map(const int32_t* cu_q, int batch, int block_m, int32_t* blk_start, hipStream_t stream) {
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(256), 0, stream, cu_q, batch, block_m, blk_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, int total_q, int total_k,
+                           int max_q, int max_k, int32_t* flags, hipStream_t stream) {
+  hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, stream, cu_q, cu_k, batch, total_q, total_k,
+                     max_q, max_k, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream) {
+  if (dtype == 1) {
+    if (head_dim == 128)
+      return causal ? launch(fwd_bf16_kernel<128, 64, 4, 1, true>, grid, 256, stream, a)
+                    : launch(fwd_bf16_kernel<128, 64, 4, 1, false>, grid, 256, stream, a);
+    if (head_dim == 64)
+      return causal ? launch(fwd_bf16_kernel<64, 128, 4, 1, true>, grid, 256, stream, a)
+                    : launch(fwd_bf16_kernel<64, 128, 4, 1, false>, grid, 256, stream, a);
+  } else if (dtype == 0) {
+    if (head_dim == 128)
+      return causal ? launch(fwd_f32_kernel<128, 4, true>, grid, 256, stream, a)
+                    : launch(fwd_f32_kernel<128, 4, false>, grid, 256, stream, a);
+    if (head_dim == 64)
+      return causal ? launch(fwd_f32_kernel<64, 4, true>, grid, 256, stream, a)
+                    : launch(fwd_f32_kernel<64, 4, false>, grid, 256, stream, a);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa
