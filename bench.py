@@ -1,0 +1,372 @@
+#!/usr/bin/env python3
+"""Benchmark of exact varlen attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch: the work-item map and
+the attention kernel, i.e. one fa_varlen_fwd call through the C ABI, with
+Q/K/V, the offsets and the outputs already resident in HBM.  The headline
+workload is the heavily ragged causal batch (65,536 tokens in sequences of
+log-uniform length 64..8192, 32 heads of dimension 128, bf16, seed 4).
+
+Prints ONE JSON line with: the throughput in TFLOP/s of algorithmic work
+(4 * head_dim flops per visible (query, key) pair per head -- two for the
+score, two for the probability-weighted value; masked pairs and the softmax
+are not counted); the attention kernel's own roofline fraction, timed with
+HIP events on the stream it is launched on; the oracle's rate on the host
+cores on a bounded sample (``cpu_baseline``); and secondary rows for the
+16k-token sequence-length sweep (head dim 64 and 128, causal and not) and
+the dense 8x2048 batch.
+
+Counter mode (``--pmc-pass``) runs a short fixed sequence for rocprofv3 --pmc:
+a plain device copy of known size (to calibrate FETCH_SIZE / WRITE_SIZE)
+followed by attention launches; ``--parse-pmc DIR`` turns the two counter
+runs into per-launch HBM bytes stored under profiles/.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import sqlite3
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, Workload, draw_qkv, workload_dense,  # noqa: E402
+                      workload_ragged64k, workload_sweep)
+
+METRIC = "varlen attention fwd TFLOP/s and % of bf16 MFMA peak, d=64/128, causal"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "variable_length_flashattention_cu_amd", "csrc", "fa_varlen_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_ragged64k_causal_d128.json")
+COPY_BYTES = 1 << 30        # calibration copy: 1 GiB read + 1 GiB written
+
+
+def visible_pairs(wl: Workload, causal: bool) -> int:
+    """Visible (query, key) pairs per head; bottom-right causal alignment."""
+    total = 0
+    for Lq, Lk in zip(wl.lengths_q, wl.lengths_k):
+        if not causal:
+            total += Lq * Lk
+            continue
+        # row i sees clip(i + Lk - Lq + 1, 0, Lk) keys
+        s = Lk - Lq + 1
+        i = np.arange(Lq, dtype=np.int64)
+        total += int(np.clip(i + s, 0, Lk).sum())
+    return total
+
+
+def algorithmic_flops(wl: Workload, causal: bool) -> float:
+    return 4.0 * wl.head_dim * wl.heads * visible_pairs(wl, causal)
+
+
+def algorithmic_bytes(wl: Workload) -> float:
+    es = 2 if wl.dtype == "bf16" else 4
+    hd = wl.heads * wl.head_dim
+    return float((wl.total_q + 2 * wl.total_k) * hd * es + wl.total_q * hd * es + 4 * wl.total_q * wl.heads)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def to_device(wl: Workload, data: dict):
+    import torch
+    t = {n: torch.from_numpy(data[n + "_bits"].view(np.int16)).to("cuda").view(torch.bfloat16) for n in "qkv"}
+    t["cu_q"] = torch.tensor(wl.cu_q, dtype=torch.int32, device="cuda")
+    t["cu_k"] = torch.tensor(wl.cu_k, dtype=torch.int32, device="cuda")
+    H, Tq = wl.heads, wl.total_q
+    t["out"] = torch.empty_like(t["q"])
+    t["lse"] = torch.empty((H, Tq), dtype=torch.float32, device="cuda")
+    return t
+
+
+class Runner:
+    """Calls the C ABI with preallocated buffers on torch's current stream."""
+
+    def __init__(self, wl: Workload, t: dict, causal: bool):
+        import torch
+        import variable_length_flashattention_cu_amd as fa
+        self.fa, self.wl, self.t, self.causal = fa, wl, t, causal
+        self.lib = fa.load_library()
+        self.stream = torch.cuda.current_stream().cuda_stream
+        dt = fa.FA_DTYPE_BF16
+        self.bm = fa.fa_varlen_block_sizes(wl.head_dim, dt)[0]
+        self.blk = fa.fa_varlen_tile_map(t["cu_q"], self.bm)
+        self.common = (t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["cu_q"].data_ptr(),
+                       t["cu_k"].data_ptr(), wl.max_seqlen_q, wl.max_seqlen_k, wl.scale, int(causal),
+                       t["out"].data_ptr(), t["lse"].data_ptr(), wl.batch, wl.total_q, wl.total_k, wl.heads,
+                       wl.head_dim, dt)
+
+    def step(self):
+        st = self.lib.fa_varlen_fwd(*self.common, self.stream)
+        if st:
+            raise RuntimeError(f"fa_varlen_fwd failed: {self.fa.fa_status_string(st)}")
+
+    def kernel_only(self):
+        st = self.lib.fa_varlen_fwd_mapped(*self.common, self.blk.data_ptr(), self.stream)
+        if st:
+            raise RuntimeError(f"fa_varlen_fwd_mapped failed: {self.fa.fa_status_string(st)}")
+
+
+def time_events(fn, iters: int) -> float:
+    """Average milliseconds per call, HIP events on torch's current stream."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(iters):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def measure_secondary(wl: Workload, iters: int = 20) -> list:
+    """Both mask modes of one workload (inputs drawn once)."""
+    data = draw_qkv(wl)
+    t = to_device(wl, data)
+    del data
+    rows = []
+    for causal in (False, True):
+        r = Runner(wl, t, causal)
+        for _ in range(3):
+            r.step()
+        ms = time_events(r.step, iters)
+        kms = time_events(r.kernel_only, iters)
+        fl = algorithmic_flops(wl, causal)
+        rows.append({"workload": wl.name, "seq_len": wl.max_seqlen_q, "head_dim": wl.head_dim,
+                     "heads": wl.heads, "causal": causal, "ms_per_step": round(ms, 4),
+                     "tflops": round(fl / ms / 1e9, 1), "kernel_ms": round(kms, 4),
+                     "kernel_tflops": round(fl / kms / 1e9, 1),
+                     "kernel_frac_bf16_peak": round(fl / kms / 1e9 / PEAK_BF16_TFLOPS, 4)})
+        del r
+    del t
+    return rows
+
+
+def cpu_baseline(wl: Workload, causal: bool, data: dict, heads=(0,)) -> dict:
+    """The oracle (float64 numpy) on a bounded sample: one head, every sequence."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention_fwd
+    sub = {n: np.ascontiguousarray(data[n][:, list(heads), :]) for n in "qkv"}
+    t0 = time.perf_counter()
+    attention_fwd(sub["q"], sub["k"], sub["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
+    dt = time.perf_counter() - t0
+    fl = 4.0 * wl.head_dim * len(heads) * visible_pairs(wl, causal)
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = max([p.get("num_threads", 1) for p in blas] or [1])
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{wl.name}: head {list(heads)} of {wl.heads}, all {wl.batch} sequences "
+                      f"({fl / 1e9:.1f} GFLOP algorithmic, {dt:.1f} s, float64 numpy, "
+                      f"{blas[0].get('internal_api', '?') if blas else '?'} BLAS)"}
+
+
+def stored_traffic() -> dict | None:
+    """Per-launch HBM bytes from the committed counter runs, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec
+
+
+# ---------------------------------------------------------------------------
+# counter runs
+# ---------------------------------------------------------------------------
+def pmc_pass(steps: int) -> None:
+    """Fixed launch sequence for rocprofv3 --pmc: one calibration copy, then attention."""
+    import torch
+    wl = workload_ragged64k()
+    data = draw_qkv(wl)
+    t = to_device(wl, data)
+    del data
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)  # elementwise copy kernel: COPY_BYTES read, COPY_BYTES written
+    torch.cuda.synchronize()
+    del src, dst
+    r = Runner(wl, t, True)
+    for _ in range(steps):
+        r.kernel_only()
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_pass": "done", "launches": steps}), flush=True)
+
+
+def _counter_per_dispatch(run_dir: str, counter: str) -> dict:
+    """{(kernel_name, dispatch_id): value} from a rocprofv3 run (rocpd database or CSV)."""
+    out: dict = {}
+    dbs = glob.glob(os.path.join(run_dir, "**", "*results.db"), recursive=True)
+    for db in dbs:
+        con = sqlite3.connect(db)
+        q = ("select kernel_name, dispatch_id, sum(value) from counters_collection "
+             "where counter_name = ? group by kernel_name, dispatch_id")
+        for name, disp, val in con.execute(q, (counter,)):
+            out[(name, (db, disp))] = float(val)
+        con.close()
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter:
+                    key = (row["Kernel_Name"], (path, row["Dispatch_Id"]))
+                    out[key] = out.get(key, 0.0) + float(row["Counter_Value"])
+    return out
+
+
+def parse_pmc(fetch_dir: str, write_dir: str) -> dict:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> calibrated bytes per attention launch.
+
+    Each counter is scaled by COPY_BYTES divided by what the same counter reads
+    for the calibration copy (an elementwise kernel reading and writing
+    COPY_BYTES), in the same process."""
+    out = {"kernel_sha": kernel_sha(), "workload": workload_ragged64k().name, "copy_bytes": COPY_BYTES,
+           "command": "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE -- python bench.py --pmc-pass --steps 3"}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per_disp = _counter_per_dispatch(d, counter)
+        copy_vals = [v for (k, _), v in per_disp.items() if "elementwise" in k.lower()]
+        fwd_vals = [v for (k, _), v in per_disp.items() if "fwd_bf16_kernel" in k]
+        if not copy_vals or not fwd_vals:
+            raise RuntimeError(f"{counter}: calibration copy or attention dispatches not found in {d}")
+        copy_kib = max(copy_vals)
+        factor = (COPY_BYTES / 1024.0) / copy_kib
+        fwd_kib = float(np.mean(fwd_vals))
+        out[counter] = {"raw_kib_per_launch": round(fwd_kib, 1), "copy_raw_kib": round(copy_kib, 1),
+                        "scale_factor": round(factor, 4), "bytes_per_launch": round(fwd_kib * 1024.0 * factor),
+                        "launches": len(fwd_vals)}
+    out["traffic_bytes"] = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    out["algorithmic_bytes"] = round(algorithmic_bytes(workload_ragged64k()))
+    return out
+
+
+def summarize_trace(db_path: str) -> str:
+    """Per-kernel call count / total / average duration from a --kernel-trace run."""
+    con = sqlite3.connect(db_path)
+    rows = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels").fetchall()
+    con.close()
+    # the top_kernels view reports microseconds
+    lines = [f"{'calls':>6} {'total_ms':>10} {'avg_us':>10} {'pct':>6}  kernel"]
+    for name, calls, tot, avg, pct in rows:
+        lines.append(f"{calls:>6} {tot / 1e3:>10.3f} {avg:>10.2f} {pct:>6.2f}  {name}")
+    return "\n".join(lines)
+
+
+# ---------------------------------------------------------------------------
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the sweep and dense rows")
+    ap.add_argument("--pmc-pass", action="store_true", help="launch sequence for a rocprofv3 --pmc run")
+    ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="RESULTS_DB", help="print kernel stats of a rocprofv3 trace")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the forward pass is not sharded across GPUs in this build", file=sys.stderr)
+        return 2
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.parse_pmc:
+        rec = parse_pmc(*args.parse_pmc)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.pmc_pass:
+        pmc_pass(max(1, args.steps))
+        return 0
+
+    wl = workload_ragged64k()
+    causal = True
+    print(f"# bench: {wl.name} batch={wl.batch} tokens={wl.total_q} heads={wl.heads} d={wl.head_dim} "
+          f"causal={causal}", file=sys.stderr, flush=True)
+    data = draw_qkv(wl)
+    t = to_device(wl, data)
+    r = Runner(wl, t, causal)
+    for _ in range(args.warmup):
+        r.step()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ms = time_events(r.step, args.steps)
+    wall = (time.perf_counter() - w0) * 1e3 / args.steps
+    kms = time_events(r.kernel_only, max(args.steps, 10))
+    fl = algorithmic_flops(wl, causal)
+    value = fl / ms / 1e9
+    achieved = fl / kms / 1e9
+    print(f"# step {ms:.3f} ms ({value:.1f} TFLOP/s), attention kernel {kms:.3f} ms ({achieved:.1f} TFLOP/s)",
+          file=sys.stderr, flush=True)
+
+    traffic = stored_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "total_tokens": wl.total_q, "batch": wl.batch,
+                   "seq_len_range": [min(wl.lengths_q), max(wl.lengths_q)], "heads": wl.heads,
+                   "head_dim": wl.head_dim, "causal": causal, "seed": wl.seed,
+                   "gflop_per_step": round(fl / 1e9, 2), "wall_ms_per_step": round(wall, 4)},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": round(traffic["traffic_bytes"]) if traffic else None,
+                     "kernel": "fwd_bf16_kernel<128,64,...,causal>", "kernel_ms": round(kms, 4),
+                     "algorithmic_bytes": round(algorithmic_bytes(wl))},
+    }
+    del r, t
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        rows = []
+        for d in SWEEP_HEAD_DIMS:
+            for L in SWEEP_SEQLENS:
+                rows += measure_secondary(workload_sweep(L, d))
+                for row in rows[-2:]:
+                    print(f"# {row}", file=sys.stderr, flush=True)
+                torch.cuda.empty_cache()
+        line["sweep_16k_tokens"] = rows
+        line["dense_8x2048"] = measure_secondary(workload_dense())
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, causal, data)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
