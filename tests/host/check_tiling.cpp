@@ -1,0 +1,259 @@
+// check_tiling.cpp -- host-side bounds and consistency check of the forward
+// kernels' index arithmetic (fa_varlen_tiling.h), built with g++ by
+// tests/test_host_tiling.py.  For every thread of a workgroup it enumerates:
+//   * the byte offsets of the K/V/Q buffer loads against the resource extents,
+//     under a conservative model of the hardware range check (a load whose
+//     offset is below the extent is taken to touch all of its 16 bytes): every
+//     such access must lie inside a valid token row's slice of the current
+//     head, and every valid element must be loaded exactly once;
+//   * the LDS indices written by the K/V staging and read as MFMA operands:
+//     inside the buffers, aligned, every tile element written exactly once,
+//     and each operand read returning the keys/dimensions the MFMA expects;
+//   * the output-store offsets of the epilogue.
+// Prints a line per configuration and exits non-zero on any violation.
+#include <cstdio>
+#include <cstdlib>
+#include <set>
+#include <vector>
+
+#include "fa_varlen_tiling.h"
+
+using namespace fa::tiling;
+
+static int g_fail = 0;
+#define CHECK(cond, ...)                                 \
+  do {                                                   \
+    if (!(cond)) {                                       \
+      if (g_fail < 30) {                                 \
+        std::fprintf(stderr, "FAIL %s:%d: ", __FILE__, __LINE__); \
+        std::fprintf(stderr, __VA_ARGS__);               \
+        std::fprintf(stderr, "\n");                      \
+      }                                                  \
+      ++g_fail;                                          \
+    }                                                    \
+  } while (0)
+
+// A packed tensor [T, H, D] of elements; a resource starting at the head-h
+// slice of row `row0` with extent `bytes`; a 16-byte load at byte `off`.
+struct Access {
+  long T, H, D, h, row0, rows;  // rows: valid rows from row0
+  unsigned bytes;
+};
+
+// Returns the first element index of the load if it may touch memory, or -1.
+static long touch(const Access& a, unsigned off, int esize, int nbytes) {
+  if (off >= a.bytes) return -1;  // out of range: the hardware returns zeros
+  CHECK(off % esize == 0, "unaligned offset %u", off);
+  const long rs = a.H * a.D;
+  const long first = (a.row0 * rs + a.h * a.D) + off / esize;
+  const long last = first + nbytes / esize - 1;
+  const long row = first / rs, col = first % rs;
+  CHECK(row == last / rs, "load crosses a row: first %ld last %ld", first, last);
+  CHECK(row >= a.row0 && row < a.row0 + a.rows, "row %ld outside valid rows [%ld, %ld)", row, a.row0,
+        a.row0 + a.rows);
+  CHECK(row < a.T, "row %ld past tensor rows %ld", row, a.T);
+  CHECK(col >= a.h * a.D && col + nbytes / esize <= (a.h + 1) * a.D, "cols [%ld,%ld) outside head %ld slice",
+        col, col + nbytes / esize, a.h);
+  return first;
+}
+
+template <int D, int BN, int NW>
+static void check_bf16(long H) {
+  using G = Bf16Geom<D, BN, NW>;
+  const long rs = H * D;
+  // --- K/V tile loads: a sequence that ends at the very end of the tensor
+  for (long h : {0L, H - 1}) {
+    for (int Lk : {1, 5, 31, 63, 64, 65, 100, 128, 129, 200, 333}) {
+      const long k_start = 7, T = k_start + Lk;
+      for (int key0 = 0; key0 < Lk; key0 += BN) {
+        const int rows = (Lk - key0) < BN ? (Lk - key0) : BN;
+        Access a{T, H, D, h, k_start + key0, rows, head_rows_bytes(rows, rs, D, 2)};
+        std::vector<int> kseen(BN * D, 0), vseen(BN * D, 0);
+        for (int tid = 0; tid < G::THREADS; ++tid) {
+          for (int i = 0; i < G::K_PER_THREAD; ++i) {
+            const int c = tid + i * G::THREADS;
+            const int row = G::k_row(c), ch = G::k_chunk(c);
+            const bool inside = row < BN && ch * 8 + 8 <= D;
+            CHECK(inside, "K chunk %d maps outside the tile", c);
+            const long e = touch(a, (unsigned)((row * rs + ch * 8) * 2), 2, 16);
+            if (e >= 0 && inside)
+              for (int j = 0; j < 8; ++j) kseen[row * D + ch * 8 + j]++;
+          }
+          for (int i = 0; i < G::V_PER_THREAD; ++i) {
+            const int w = tid + i * G::THREADS;
+            if (!G::v_owned(w)) continue;
+            const int u = G::v_group(w), dc = G::v_dchunk(w);
+            const bool inside = 4 * u + 3 < BN && dc * 8 + 8 <= D;
+            CHECK(inside, "V unit %d maps outside the tile", w);
+            for (int r = 0; r < 4; ++r) {
+              const long e = touch(a, (unsigned)(((4 * u + r) * rs + dc * 8) * 2), 2, 16);
+              if (e >= 0 && inside)
+                for (int j = 0; j < 8; ++j) vseen[(4 * u + r) * D + dc * 8 + j]++;
+            }
+          }
+        }
+        for (int r = 0; r < BN; ++r)
+          for (int d = 0; d < D; ++d) {
+            const int want = r < rows ? 1 : 0;
+            CHECK(kseen[r * D + d] == want, "K element (%d,%d) loaded %d times", r, d, kseen[r * D + d]);
+            CHECK(vseen[r * D + d] == want, "V element (%d,%d) loaded %d times", r, d, vseen[r * D + d]);
+          }
+      }
+    }
+  }
+  // --- Q loads of one wave (32 rows), rows past the sequence end give zeros
+  for (long h : {0L, H - 1})
+    for (int qrows : {0, 1, 17, 31, 32}) {
+      const long T = 3 + qrows;
+      Access a{T, H, D, h, 3, qrows, head_rows_bytes(qrows, rs, D, 2)};
+      int loaded = 0;
+      for (int lane = 0; lane < 64; ++lane)
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const int l32 = lane & 31, g = lane >> 5;
+          if (touch(a, (unsigned)((l32 * rs + 16 * ks + 8 * g) * 2), 2, 16) >= 0) ++loaded;
+        }
+      CHECK(loaded == qrows * D / 8, "Q: %d chunks loaded for %d rows", loaded, qrows);
+    }
+  // --- LDS staging writes: exact cover, in range, aligned
+  {
+    std::vector<int> kcnt(G::LDS_K, 0), vcnt(G::LDS_V, 0);
+    std::vector<long> vkey(G::LDS_V, -1);
+    for (int tid = 0; tid < G::THREADS; ++tid) {
+      for (int i = 0; i < G::K_PER_THREAD; ++i) {
+        const int c = tid + i * G::THREADS;
+        const int idx = G::ks_index(G::k_row(c), G::k_chunk(c));
+        CHECK(idx >= 0 && idx + 8 <= G::LDS_K && idx % 8 == 0, "K LDS index %d", idx);
+        for (int j = 0; j < 8; ++j) kcnt[idx + j]++;
+      }
+      for (int i = 0; i < G::V_PER_THREAD; ++i) {
+        const int w = tid + i * G::THREADS;
+        if (!G::v_owned(w)) continue;
+        const int u = G::v_group(w), dc = G::v_dchunk(w);
+        for (int e = 0; e < 8; ++e) {
+          const int d = dc * 8 + e, idx = G::vt_index(d, 4 * u);
+          CHECK(idx >= 0 && idx + 4 <= G::LDS_V && idx % 4 == 0, "V LDS index %d", idx);
+          for (int j = 0; j < 4; ++j) {
+            CHECK(G::vt_index(d, 4 * u + j) == idx + j, "V keys of a unit not contiguous");
+            vcnt[idx + j]++;
+            vkey[idx + j] = (long)d * 100000 + 4 * u + j;
+          }
+        }
+      }
+    }
+    for (int i = 0; i < G::LDS_K; ++i) CHECK(kcnt[i] == 1, "K LDS element %d written %d times", i, kcnt[i]);
+    for (int i = 0; i < G::LDS_V; ++i) CHECK(vcnt[i] == 1, "V LDS element %d written %d times", i, vcnt[i]);
+    // --- MFMA operand reads: the elements each lane feeds
+    std::set<int> perm;
+    for (int R = 0; R < 32; ++R) perm.insert(key_of_arow(R));
+    CHECK((int)perm.size() == 32 && *perm.begin() == 0 && *perm.rbegin() == 31, "key_of_arow not a permutation");
+    for (int R = 0; R < 32; ++R) {  // accumulator row R: register 4*(R/8)+R%4 of half (R/4)%2 holds key 16g+r
+      const int g = (R >> 2) & 1, r = 4 * (R >> 3) + (R & 3);
+      CHECK(key_of_arow(R) == 16 * g + r, "A-row permutation breaks the register/key correspondence");
+    }
+    for (int lane = 0; lane < 64; ++lane) {
+      const int l32 = lane & 31, g = lane >> 5;
+      for (int kb = 0; kb < BN / 32; ++kb)
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const int krow = kb * 32 + key_of_arow(l32), ch = 2 * ks + g;
+          const int idx = ks_index<D>(krow, ch);
+          CHECK(idx >= 0 && idx + 8 <= G::LDS_K && (idx * 2) % 16 == 0, "K operand read %d", idx);
+        }
+      for (int d0 = 0; d0 < D; d0 += 32)
+        for (int kb = 0; kb < BN / 32; ++kb)
+          for (int t = 0; t < 2; ++t) {
+            const int d = d0 + l32, key = kb * 32 + 16 * g + 8 * t;
+            const int idx = vt_index<BN>(d, key);
+            CHECK(idx >= 0 && idx + 8 <= G::LDS_V && (idx * 2) % 16 == 0, "V operand read %d", idx);
+            for (int e = 0; e < 8; ++e)
+              CHECK(vkey[idx + e] == (long)d * 100000 + key + e, "V operand element (%d,%d) holds the wrong key", d,
+                    key + e);
+          }
+    }
+  }
+  // --- bank behaviour of the operand reads (information): lanes of a 16-lane
+  // group reading 16-byte chunks should cover 16 distinct 4-bank groups
+  int kconf = 0, vconf = 0;
+  for (int base = 0; base < 64; base += 16) {
+    for (int kb = 0; kb < BN / 32; ++kb)
+      for (int ks = 0; ks < D / 16; ++ks) {
+        std::set<int> banks;
+        for (int lane = base; lane < base + 16; ++lane) {
+          const int l32 = lane & 31, g = lane >> 5;
+          banks.insert((ks_index<D>(kb * 32 + key_of_arow(l32), 2 * ks + g) / 8) % 16);
+        }
+        kconf += 16 - (int)banks.size();
+      }
+    for (int kb = 0; kb < BN / 32; ++kb)
+      for (int t = 0; t < 2; ++t) {
+        std::set<int> banks;
+        for (int lane = base; lane < base + 16; ++lane) {
+          const int l32 = lane & 31, g = lane >> 5;
+          banks.insert((vt_index<BN>(l32, kb * 32 + 16 * g + 8 * t) / 8) % 16);
+        }
+        vconf += 16 - (int)banks.size();
+      }
+  }
+  // --- epilogue stores: lane (row l32, half g) writes dims db*32 + 8*s4 + 4g + c
+  {
+    std::vector<int> cnt(D, 0);
+    for (int g = 0; g < 2; ++g)
+      for (int db = 0; db < D / 32; ++db)
+        for (int s4 = 0; s4 < 4; ++s4)
+          for (int c = 0; c < 4; ++c) {
+            const int d = db * 32 + 8 * s4 + 4 * g + c;
+            CHECK(d >= 0 && d < D, "output dim %d", d);
+            cnt[d]++;
+          }
+    for (int d = 0; d < D; ++d) CHECK(cnt[d] == 1, "output dim %d written %d times", d, cnt[d]);
+  }
+  std::printf("bf16 D=%d BN=%d NW=%d H=%ld: ok (operand-read bank overlaps: K %d, V %d)\n", D, BN, NW, H, kconf,
+              vconf);
+}
+
+template <int D, int NW>
+static void check_f32() {
+  using G = F32Geom<D, NW>;
+  std::vector<int> cnt(G::LDS_ELEMS, 0);
+  for (int tid = 0; tid < G::THREADS; ++tid)
+    for (int i = 0; i < G::PER_THREAD; ++i) {
+      const int c = tid + i * G::THREADS;
+      const int row = G::row(c), ch = G::chunk(c);
+      CHECK(row < G::BN && 4 * ch + 4 <= D, "fp32 chunk %d outside the tile", c);
+      const int idx = row * G::LD + 4 * ch;
+      CHECK(idx % 4 == 0 && idx + 4 <= G::LDS_ELEMS, "fp32 LDS index %d", idx);
+      for (int j = 0; j < 4; ++j) cnt[idx + j]++;
+    }
+  for (int r = 0; r < G::BN; ++r)
+    for (int d = 0; d < G::LD; ++d) CHECK(cnt[r * G::LD + d] == (d < D ? 1 : 0), "fp32 LDS (%d,%d)", r, d);
+  std::set<int> keys;
+  for (int g = 0; g < 2; ++g)
+    for (int r = 0; r < 16; ++r) keys.insert(G::key_of_reg(r, g));
+  CHECK((int)keys.size() == 32 && *keys.rbegin() == 31, "fp32 register/key map not a permutation");
+  for (int lane = 0; lane < 64; ++lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+    for (int ks = 0; ks < D / 2; ++ks) CHECK(l32 * G::LD + 2 * ks + g < G::LDS_ELEMS, "fp32 K read");
+    for (int u = 0; u < 16; ++u)
+      for (int db = 0; db < D / 32; ++db)
+        CHECK(G::key_of_reg(u, g) * G::LD + db * 32 + l32 < G::LDS_ELEMS, "fp32 V read");
+  }
+  std::printf("f32 D=%d NW=%d: ok\n", D, NW);
+}
+
+int main() {
+  // configurations the library instantiates (and neighbours it may use)
+  for (long H : {1L, 3L, 16L}) {
+    check_bf16<128, 64, 8>(H);
+    check_bf16<128, 64, 4>(H);
+    check_bf16<64, 64, 4>(H);
+    check_bf16<64, 64, 8>(H);
+    check_bf16<64, 128, 4>(H);
+  }
+  check_f32<64, 4>();
+  check_f32<128, 4>();
+  if (g_fail) {
+    std::fprintf(stderr, "%d violations\n", g_fail);
+    return 1;
+  }
+  std::printf("all tiling checks passed\n");
+  return 0;
+}

@@ -33,6 +33,8 @@ int validate(const void* q, const void* k, const void* v, const int32_t* cu_q, c
   if (tc.block_m == 0) return FA_ERR_HEAD_DIM;
   if (batch < 0 || total_q < 0 || total_k < 0 || heads < 1 || max_q < 0 || max_k < 0) return FA_ERR_SHAPE;
   if (max_q > total_q || max_k > total_k) return FA_ERR_SHAPE;
+  // In-tile byte offsets are 32-bit: bound the token row size.
+  if ((int64_t)heads * head_dim > (int64_t{1} << 22)) return FA_ERR_TOO_LARGE;
   if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_ALIGN;

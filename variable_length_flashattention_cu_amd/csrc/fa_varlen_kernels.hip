@@ -41,6 +41,11 @@
 // normalización global"): with t = scale*log2(e)*s,
 //   m' = max(m, max_j t_j), alpha = 2^(m - m'), l' = alpha l + sum_j 2^(t_j - m'),
 //   O' = alpha O + sum_j 2^(t_j - m') v_j;  out = O / l,  lse = (m + log2 l) ln 2.
+// The reference m need not be the exact running max: any m >= the max seen so
+// far (up to a bounded slack) gives the same out and lse, because l and O are
+// accumulated against the same m.  The kernel therefore raises m (and pays
+// the rescale of O) only when some row of the wavefront outgrows it by more
+// than 2^8, which after the first tiles is rare.
 // A row that has seen no visible key keeps m = -inf and is guarded so that no
 // -inf - -inf appears; such rows end with out = 0, lse = -inf.
 //
@@ -58,7 +63,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_varlen_launch.h"
+#include "fa_varlen_tiling.h"
 
 namespace fa {
 namespace {
@@ -76,8 +84,42 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// value of lane l^32 (same query row, other half of the keys)
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Lanes l and l^32 hold the two halves of one query row.  v_permlane32_swap
+// exchanges the halves of a register pair; one result holds the lane's own
+// value and the other its partner's, so symmetric reductions need no select.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The running max used as the softmax reference is only raised when a row's
+// new maximum exceeds it by more than this many log2 units (wave-uniform
+// decision).  Probabilities are then at most 2^kRescaleSlack; l and O share
+// the same stale reference, so the result is unchanged.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Raw buffer resource over [base, base + bytes).  Loads at byte offsets at or
+// past `bytes` return zeros from the hardware range check, which is how rows
+// past the end of a sequence are zero-filled without branches.  Dword 3 selects
+// the 32-bit data format that untyped buffer loads need on CDNA.
+// Callers pass wave-uniform values; readfirstlane tells the compiler so, and
+// keeps the resource in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* p = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_offset, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // work decoding shared by both forward kernels
@@ -201,76 +243,70 @@ __global__ __launch_bounds__(256) void check_cu_kernel(const int32_t* __restrict
 //   Ks[key][d]   key-major, one row of D bf16 per key
 //   Vt[d][key]   dimension-major (V transposed), one row of BN bf16 per d
 //
-// A-operand row permutation for S^T = K Q^T: accumulator row R of the 32x32
-// layout lives in register 4*(R/8) + (R%4) of lane group (R/4)%2.  Loading key
-// pi(R) = 16*((R/4)%2) + 4*(R/8) + R%4 into A row R makes register r of lane
-// group g hold key 16g + r, so the 8 probabilities a lane feeds to one PV MFMA
-// are 8 consecutive keys: a single 16-byte read of Vt.
-__device__ __forceinline__ int key_of_arow(int R) { return ((R >> 2) & 1) * 16 + (R >> 3) * 4 + (R & 3); }
-
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-  if constexpr (D == 128) return (row & 3) | ((row >> 2) & 4) | ((row << 1) & 8);
-  else return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 2) & 4);
-}
-template <int BN>
-__device__ __forceinline__ int v_swz(int d) {
-  if constexpr (BN == 128) return d & 15;
-  else return ((d >> 1) & 3) | (((d ^ (d >> 3)) & 1) << 2);
-}
+// Index arithmetic (swizzles, chunk/unit mappings, LDS indices, byte extents)
+// lives in fa_varlen_tiling.h, shared with the host-side bounds checker.
+using tiling::head_rows_bytes;
+using tiling::key_of_arow;
+using tiling::k_swz;
+using tiling::v_swz;
 
 template <int D, int BN, int NW>
-struct Bf16Tile {
-  static constexpr int THREADS = NW * 64;
-  static constexpr int K_CHUNKS = BN * D / 8;             // 16-byte chunks per K tile
-  static constexpr int K_PER_THREAD = K_CHUNKS / THREADS;
-  static constexpr int V_UNITS = (BN / 4) * (D / 8);      // 4 keys x 8 dims per unit
-  static constexpr int V_PER_THREAD = V_UNITS / THREADS;
-  static_assert(K_CHUNKS % THREADS == 0 && V_UNITS % THREADS == 0, "tile/threads mismatch");
-  static_assert((D / 8) % 4 == 0, "V unit mapping needs D/8 divisible by 4");
+struct Bf16Tile : tiling::Bf16Geom<D, BN, NW> {
+  using G = tiling::Bf16Geom<D, BN, NW>;
+  using G::K_PER_THREAD;
+  using G::THREADS;
+  using G::V_PER_THREAD;
 
   u32x4 kreg[K_PER_THREAD];
   u32x4 vreg[V_PER_THREAD][4];
 
-  // global -> registers; rows at or beyond Lk read as zero
-  __device__ __forceinline__ void load(const __bf16* __restrict__ kbase, const __bf16* __restrict__ vbase,
-                                       int64_t row_stride, int key0, int Lk, int tid) {
+  // global -> registers; rows at or beyond Lk read as zero.  The resources
+  // start at the tile's first key (head slice) and end exactly at the end of
+  // the last valid row's head slice, so offsets stay below BN * row_stride * 2
+  // bytes (the host bounds heads * head_dim) and never reach past a tensor.
+  __device__ __forceinline__ void load_k(const __bf16* __restrict__ kbase, int64_t row_stride, int key0, int Lk,
+                                         int tid) {
+    const int rows = max(0, min(BN, Lk - key0));
+    const __amdgpu_buffer_rsrc_t rk =
+        buffer_rsrc(kbase + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
 #pragma unroll
     for (int i = 0; i < K_PER_THREAD; ++i) {
       const int c = tid + i * THREADS;
-      const int row = c / (D / 8), ch = c % (D / 8);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key0 + row < Lk) x = *(const u32x4*)(kbase + (int64_t)(key0 + row) * row_stride + ch * 8);
-      kreg[i] = x;
+      kreg[i] = buffer_load16(rk, ((uint32_t)G::k_row(c) * (uint32_t)row_stride + G::k_chunk(c) * 8) * 2u);
     }
+  }
+  __device__ __forceinline__ void load_v(const __bf16* __restrict__ vbase, int64_t row_stride, int key0, int Lk,
+                                         int tid) {
+    const int rows = max(0, min(BN, Lk - key0));
+    const __amdgpu_buffer_rsrc_t rv =
+        buffer_rsrc(vbase + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
 #pragma unroll
     for (int i = 0; i < V_PER_THREAD; ++i) {
       const int w = tid + i * THREADS;
-      const int dc = ((w >> 2) / (BN / 4)) * 4 + (w & 3);
-      const int u = (w >> 2) % (BN / 4);
+      const int u = G::v_group(w), dc = G::v_dchunk(w);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 4 * u + r;
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < Lk) x = *(const u32x4*)(vbase + (int64_t)key * row_stride + dc * 8);
+        if (G::v_owned(w)) x = buffer_load16(rv, ((uint32_t)(4 * u + r) * (uint32_t)row_stride + dc * 8) * 2u);
         vreg[i][r] = x;
       }
     }
   }
 
-  // registers -> LDS (K as is, V transposed)
-  __device__ __forceinline__ void store(__bf16* Ks, __bf16* Vt, int tid) const {
+  // registers -> LDS: K as is, V transposed
+  __device__ __forceinline__ void store_k(__bf16* Ks, int tid) const {
 #pragma unroll
     for (int i = 0; i < K_PER_THREAD; ++i) {
       const int c = tid + i * THREADS;
-      const int row = c / (D / 8), ch = c % (D / 8);
-      *(u32x4*)(Ks + row * D + 8 * (ch ^ k_swz<D>(row))) = kreg[i];
+      *(u32x4*)(Ks + G::ks_index(G::k_row(c), G::k_chunk(c))) = kreg[i];
     }
+  }
+  __device__ __forceinline__ void store_v(__bf16* Vt, int tid) const {
 #pragma unroll
     for (int i = 0; i < V_PER_THREAD; ++i) {
       const int w = tid + i * THREADS;
-      const int dc = ((w >> 2) / (BN / 4)) * 4 + (w & 3);
-      const int u = (w >> 2) % (BN / 4);
+      if (!G::v_owned(w)) continue;
+      const int u = G::v_group(w), dc = G::v_dchunk(w);
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         // dims 2*e2 and 2*e2+1 of the chunk, for keys 4u..4u+3
@@ -281,21 +317,136 @@ struct Bf16Tile {
         lo[1] = __builtin_amdgcn_perm(r3, r2, 0x05040100u);  // (key2, key3)
         hi[0] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // dim 2*e2+1
         hi[1] = __builtin_amdgcn_perm(r3, r2, 0x07060302u);
-        const int d0 = dc * 8 + 2 * e2, d1 = d0 + 1;
-        *(u32x2*)(Vt + d0 * BN + 8 * ((u >> 1) ^ v_swz<BN>(d0)) + 4 * (u & 1)) = lo;
-        *(u32x2*)(Vt + d1 * BN + 8 * ((u >> 1) ^ v_swz<BN>(d1)) + 4 * (u & 1)) = hi;
+        const int d0 = dc * 8 + 2 * e2;
+        *(u32x2*)(Vt + G::vt_index(d0, 4 * u)) = lo;
+        *(u32x2*)(Vt + G::vt_index(d0 + 1, 4 * u)) = hi;
       }
     }
   }
 };
 
+// Per-wave state and the three tile-level steps of the bf16 forward pass.
+template <int D, int BN, int QB>
+struct Bf16Wave {
+  static constexpr int KSTEPS = D / 16;  // MFMA k-steps for Q K^T
+  static constexpr int KB = BN / 32;     // 32-key blocks per tile
+  static constexpr int DB = D / 32;      // 32-dim blocks of the output
+
+  bf16x8 qreg[QB][KSTEPS];  // Q^T as the B operand
+  f32x16 o[QB][DB];         // O^T accumulators
+  float m_run[QB], l_run[QB];
+
+  // S^T = K Q^T for one key tile (K from LDS, swizzled rows)
+  __device__ __forceinline__ void qk(const __bf16* Ks, f32x16 (&s)[QB][KB], int arow, int g) const {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int krow = kb * 32 + arow;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int ch = 2 * ks + g;
+        const bf16x8 av = *(const bf16x8*)(Ks + tiling::ks_index<D>(krow, ch));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const f32x16 c = ks == 0 ? f32x16{} : s[qb][kb];
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[qb][ks], c, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // -inf for keys past the end of the sequence or (causal) above the diagonal
+  template <bool CAUSAL>
+  __device__ __forceinline__ static void mask(f32x16 (&s)[QB][KB], int key0, int row0, int l32, int g, int Lk,
+                                              int shift) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int i = row0 + qb * 32 + l32;
+      const int lim = CAUSAL ? min(Lk - 1, i + shift) : (Lk - 1);  // last visible key
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + kb * 32 + 16 * g + r > lim) s[qb][kb][r] = kNegInf;
+    }
+  }
+
+  // Online softmax of one tile: probabilities (bf16, in the PV B-operand
+  // layout), running l; returns whether O must be rescaled by alpha[qb].
+  // The returned flag is formed from the tile's row sums, so the (rarely
+  // taken) rescale branch cannot be placed ahead of the exponentials: they
+  // stay in one basic block with the MFMAs of the next score tile.
+  __device__ __forceinline__ bool softmax(const f32x16 (&s)[QB][KB], bf16x8 (&p)[QB][KB][2], float (&alpha)[QB],
+                                          float scale_log2) {
+    bool any_rescale = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+      const float m_tile = pair_max(mx) * scale_log2;
+      const bool need = wave_any(m_tile > m_run[qb] + kRescaleSlack);
+      const float m_new = need ? fmaxf(m_run[qb], m_tile) : m_run[qb];
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      alpha[qb] = fast_exp2(m_run[qb] - m_use);  // 1 when the reference is kept; branch-free
+      m_run[qb] = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pe = fast_exp2(__builtin_fmaf(s[qb][kb][8 * t + e], scale_log2, -m_use));
+            lsum += pe;
+            p[qb][kb][t][e] = (__bf16)pe;
+          }
+      l_run[qb] = l_run[qb] * alpha[qb] + lsum;
+      any_rescale |= wave_any(alpha[qb] != 1.f && !(lsum < 0.f));  // lsum >= 0: ties the flag to the exps
+    }
+    return any_rescale;
+  }
+
+  __device__ __forceinline__ void rescale(const float (&alpha)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
+  }
+
+  // O^T += V^T P^T for one key tile (V^T from LDS)
+  __device__ __forceinline__ void pv(const __bf16* Vt, const bf16x8 (&p)[QB][KB][2], int l32, int g) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + l32;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          // keys 32kb+16g+8t .. +7 of dimension d: one 16-byte chunk
+          const bf16x8 av = *(const bf16x8*)(Vt + tiling::vt_index<BN>(d, kb * 32 + 16 * g + 8 * t));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[qb][kb][t], o[qb][db], 0, 0, 0);
+        }
+    }
+  }
+};
+
+// Software pipeline (per wavefront): while the MFMAs of S(n+1) = K(n+1) Q^T
+// run, the VALU computes the softmax of tile n; then O += V(n)^T P(n).  K
+// therefore runs one tile ahead of V through the double buffers: at step n the
+// buffers hold K(n+1) and V(n) for reading while K(n+2) and V(n+1) are being
+// written into the slots that K(n) and V(n-1) left free.
 template <int D, int BN, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = 32 * QB * NW;
-  constexpr int KSTEPS = D / 16;  // MFMA k-steps for Q K^T
-  constexpr int KB = BN / 32;     // 32-key blocks per tile
-  constexpr int DB = D / 32;      // 32-dim blocks of the output
   using Tile = Bf16Tile<D, BN, NW>;
+  using Wave = Bf16Wave<D, BN, QB>;
+  constexpr int KB = Wave::KB;
 
   __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * D];
   __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * BN];
@@ -306,148 +457,101 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   key_tiles<BM, BN, CAUSAL>(w, n_full, n_end);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int q0 = w.m * BM;
-  const int wrow0 = q0 + wave * 32 * QB;  // first query row of this wave (in sequence)
+  const int wrow0 = w.m * BM + wave * 32 * QB;  // first query row of this wave (in sequence)
   const int shift = w.Lk - w.Lq;
+  const int64_t rs = a.row_stride;
 
-  const __bf16* __restrict__ qp = (const __bf16*)a.q;
-  const __bf16* __restrict__ kbase = (const __bf16*)a.k + (int64_t)w.k_start * a.row_stride + (int64_t)w.h * D;
-  const __bf16* __restrict__ vbase = (const __bf16*)a.v + (int64_t)w.k_start * a.row_stride + (int64_t)w.h * D;
+  const __bf16* __restrict__ kbase = (const __bf16*)a.k + (int64_t)w.k_start * rs + (int64_t)w.h * D;
+  const __bf16* __restrict__ vbase = (const __bf16*)a.v + (int64_t)w.k_start * rs + (int64_t)w.h * D;
 
-  // Q^T as the B operand: lane (query l32, half g) holds dims 16ks+8g .. +7
-  bf16x8 qreg[QB][KSTEPS];
+  Wave wv;
+  {  // Q rows past the end of the sequence load as zeros
+    const int qrows = max(0, min(32 * QB, w.Lq - wrow0));
+    const __amdgpu_buffer_rsrc_t rq =
+        buffer_rsrc((const __bf16*)a.q + (int64_t)(w.q_start + wrow0) * rs + (int64_t)w.h * D,
+                    head_rows_bytes(qrows, rs, D, 2));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < Wave::KSTEPS; ++ks) {
+        const uint32_t off = ((uint32_t)(qb * 32 + l32) * (uint32_t)rs + 16 * ks + 8 * g) * 2u;
+        wv.qreg[qb][ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, off));
+      }
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = wrow0 + qb * 32 + l32;
-    const __bf16* src = qp + (int64_t)(w.q_start + row) * a.row_stride + (int64_t)w.h * D + 8 * g;
+    wv.m_run[qb] = kNegInf;
+    wv.l_run[qb] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < w.Lq) x = *(const u32x4*)(src + 16 * ks);
-      qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
+    for (int db = 0; db < Wave::DB; ++db) wv.o[qb][db] = f32x16{};
+  }
+
+  // Tiles this wave needs: all n < n_wave (rows past the sequence end need
+  // none; causal rows need keys up to their diagonal).
+  int n_wave = 0;
+  if (wrow0 < w.Lq) {
+    if (CAUSAL) {
+      const int last_key = wrow0 + 32 * QB - 1 + shift;
+      n_wave = last_key < 0 ? 0 : min(n_end, last_key / BN + 1);
+    } else {
+      n_wave = n_end;
     }
   }
 
-  f32x16 o[QB][DB];
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = kNegInf;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
-  }
-
+  const int arow = key_of_arow(l32);
   Tile tile;
   if (n_end > 0) {
-    tile.load(kbase, vbase, a.row_stride, 0, w.Lk, tid);
-    tile.store(lds_k[0], lds_v[0], tid);
+    tile.load_k(kbase, rs, 0, w.Lk, tid);
+    tile.load_v(vbase, rs, 0, w.Lk, tid);
+    tile.store_k(lds_k[0], tid);
+    tile.store_v(lds_v[0], tid);
+    if (n_end > 1) {
+      tile.load_k(kbase, rs, BN, w.Lk, tid);
+      tile.store_k(lds_k[1], tid);
+    }
   }
   __syncthreads();
 
-  // A-operand addressing constants
-  const int arow = key_of_arow(l32);  // key row this lane feeds into A for S^T
+  f32x16 s0[QB][KB], s1[QB][KB];
+  if (n_wave > 0) wv.qk(lds_k[0], s0, arow, g);
 
-  for (int n = 0; n < n_end; ++n) {
-    const int buf = n & 1;
-    const int key0 = n * BN;
-    if (n + 1 < n_end) tile.load(kbase, vbase, a.row_stride, key0 + BN, w.Lk, tid);
-
-    // a wave skips the tile when all its rows lie past the end of the sequence
-    // or (causal) all its rows sit above the tile's first key
-    const bool wave_active = (wrow0 < w.Lq) && (!CAUSAL || (key0 <= wrow0 + 32 * QB - 1 + shift));
-    if (wave_active) {
-      const __bf16* Ks = lds_k[buf];
-      const __bf16* Vt = lds_v[buf];
-      // ---- S^T = K Q^T
-      f32x16 s[QB][KB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int krow = kb * 32 + arow;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const int ch = 2 * ks + g;
-          const bf16x8 av = *(const bf16x8*)(Ks + krow * D + 8 * (ch ^ k_swz<D>(krow)));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[qb][ks], s[qb][kb], 0, 0, 0);
-        }
-      }
-      // ---- masks (diagonal / tail tiles only)
-      if (n >= n_full) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int i = wrow0 + qb * 32 + l32;
-          const int lim = CAUSAL ? min(w.Lk - 1, i + shift) : (w.Lk - 1);  // last visible key
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = key0 + kb * 32 + 16 * g + r;
-              if (key > lim) s[qb][kb][r] = kNegInf;
-            }
-        }
-      }
-      // ---- online softmax (log2 domain)
+  // One pipeline step for tile n (scores in s_cur).  With NEXT, the MFMAs of
+  // S(n+1) are issued into s_next in the same basic block as the softmax of
+  // tile n so that the scheduler can interleave them; a wave whose rows stop
+  // before tile n+1 computes that S once without using it.
+  auto step = [&](auto next_tag, int n, f32x16 (&s_cur)[QB][KB], f32x16 (&s_next)[QB][KB]) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    const bool more_k = n + 2 < n_end;
+    const bool more_v = n + 1 < n_end;
+    if (more_k) tile.load_k(kbase, rs, (n + 2) * BN, w.Lk, tid);
+    if (more_v) tile.load_v(vbase, rs, (n + 1) * BN, w.Lk, tid);
+    if (n < n_wave) {
+      if (n >= n_full) Wave::template mask<CAUSAL>(s_cur, n * BN, wrow0, l32, g, w.Lk, shift);
       bf16x8 p[QB][KB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float m_new = fmaxf(m_run[qb], mx * a.scale_log2);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[qb] - m_use);
-        m_run[qb] = m_new;
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float pe = fast_exp2(__builtin_fmaf(s[qb][kb][8 * t + e], a.scale_log2, -m_use));
-              lsum += pe;
-              p[qb][kb][t][e] = (__bf16)pe;
-            }
-        l_run[qb] = l_run[qb] * alpha + lsum;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-      }
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = db * 32 + l32;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int cs = kb * 4 + 2 * g + t;  // 16-byte chunk of keys 32kb+16g+8t..+7
-            const bf16x8 av = *(const bf16x8*)(Vt + d * BN + 8 * (cs ^ v_swz<BN>(d)));
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[qb][kb][t], o[qb][db], 0, 0, 0);
-          }
-      }
+      float alpha[QB];
+      if constexpr (NEXT) wv.qk(lds_k[(n + 1) & 1], s_next, arow, g);
+      const bool rescale = wv.softmax(s_cur, p, alpha, a.scale_log2);
+      if (rescale) wv.rescale(alpha);
+      wv.pv(lds_v[n & 1], p, l32, g);
     }
-
-    if (n + 1 < n_end) tile.store(lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
+    if (more_k) tile.store_k(lds_k[n & 1], tid);
+    if (more_v) tile.store_v(lds_v[(n + 1) & 1], tid);
     __syncthreads();
+  };
+  using Full = std::true_type;
+  using Last = std::false_type;
+  int n = 0;
+  for (; n + 2 < n_end; n += 2) {
+    step(Full{}, n, s0, s1);
+    step(Full{}, n + 1, s1, s0);
+  }
+  if (n + 1 < n_end) {
+    step(Full{}, n, s0, s1);
+    step(Last{}, n + 1, s1, s0);
+  } else if (n < n_end) {
+    step(Last{}, n, s0, s1);
   }
 
   // ---- epilogue: normalise, write out (bf16) and lse
@@ -455,21 +559,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int i = wrow0 + qb * 32 + l32;
-    const float l = l_run[qb] + swap_halves(l_run[qb]);
+    const float l = pair_sum(wv.l_run[qb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (i < w.Lq) {
-      __bf16* dst = op + (int64_t)(w.q_start + i) * a.row_stride + (int64_t)w.h * D;
+      __bf16* dst = op + (int64_t)(w.q_start + i) * rs + (int64_t)w.h * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < Wave::DB; ++db)
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           bf16x4 v4;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[qb][db][4 * s4 + c] * inv);
+          for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(wv.o[qb][db][4 * s4 + c] * inv);
           *(bf16x4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
         }
       if (g == 0)
-        a.lse[(int64_t)w.h * a.total_q + w.q_start + i] = l > 0.f ? (m_run[qb] + fast_log2(l)) * kLn2 : kNegInf;
+        a.lse[(int64_t)w.h * a.total_q + w.q_start + i] =
+            l > 0.f ? (wv.m_run[qb] + fast_log2(l)) * kLn2 : kNegInf;
     }
   }
 }
@@ -577,22 +682,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdArgs a) {
       float mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
+      const float m_tile = pair_max(mx) * a.scale_log2;
+      if (wave_any(m_tile > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
       float lsum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[r] = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -m_use));
         lsum += s[r];
       }
-      l_run = l_run * alpha + lsum;
+      l_run += lsum;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int key = 8 * (u >> 2) + 4 * g + (u & 3);
@@ -604,7 +714,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  const float l = l_run + swap_halves(l_run);
+  const float l = pair_sum(l_run);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (i < w.Lq) {
     float* dst = (float*)a.out + (int64_t)(w.q_start + i) * a.row_stride + (int64_t)w.h * D;
@@ -636,8 +746,8 @@ hipError_t launch(K kernel, int grid, int block, hipStream_t stream, const FwdAr
 TileConfig tile_config(int dtype, int head_dim) {
   TileConfig c{0, 0, 0};
   if (dtype == 1) {  // bf16
-    if (head_dim == 128) c = TileConfig{128, 64, 256};
-    else if (head_dim == 64) c = TileConfig{128, 128, 256};
+    if (head_dim == 128) c = TileConfig{256, 64, 512};
+    else if (head_dim == 64) c = TileConfig{128, 64, 256};
   } else if (dtype == 0) {  // f32
     if (head_dim == 128 || head_dim == 64) c = TileConfig{128, 32, 256};
   }
@@ -659,11 +769,11 @@ hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, 
 hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream) {
   if (dtype == 1) {
     if (head_dim == 128)
-      return causal ? launch(fwd_bf16_kernel<128, 64, 4, 1, true>, grid, 256, stream, a)
-                    : launch(fwd_bf16_kernel<128, 64, 4, 1, false>, grid, 256, stream, a);
+      return causal ? launch(fwd_bf16_kernel<128, 64, 8, 1, true>, grid, 512, stream, a)
+                    : launch(fwd_bf16_kernel<128, 64, 8, 1, false>, grid, 512, stream, a);
     if (head_dim == 64)
-      return causal ? launch(fwd_bf16_kernel<64, 128, 4, 1, true>, grid, 256, stream, a)
-                    : launch(fwd_bf16_kernel<64, 128, 4, 1, false>, grid, 256, stream, a);
+      return causal ? launch(fwd_bf16_kernel<64, 64, 4, 1, true>, grid, 256, stream, a)
+                    : launch(fwd_bf16_kernel<64, 64, 4, 1, false>, grid, 256, stream, a);
   } else if (dtype == 0) {
     if (head_dim == 128)
       return causal ? launch(fwd_f32_kernel<128, 4, true>, grid, 256, stream, a)
