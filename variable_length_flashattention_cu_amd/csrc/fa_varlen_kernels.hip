@@ -325,6 +325,99 @@ struct Bf16Tile : tiling::Bf16Geom<D, BN, NW> {
   }
 };
 
+// Staging for a kernel in which a thread stages either K tiles or V tiles:
+// one register set serves both roles.
+template <int D, int BN, int NW>
+struct Bf16GroupStage : tiling::Bf16Geom<D, BN, NW> {
+  using G = tiling::Bf16Geom<D, BN, NW>;
+  using G::K_PER_THREAD;
+  using G::THREADS;
+  using G::V_PER_THREAD;
+
+  // one register set serves either role: a thread stages K or V, not both
+  static constexpr int NREG = K_PER_THREAD > 4 * V_PER_THREAD ? K_PER_THREAD : 4 * V_PER_THREAD;
+  u32x4 reg[NREG];
+
+  // global -> registers; rows at or beyond Lk read as zero.  The resources
+  // start at the tile's first key (head slice) and end exactly at the end of
+  // the last valid row's head slice, so offsets stay below BN * row_stride * 2
+  // bytes (the host bounds heads * head_dim) and never reach past a tensor.
+  __device__ __forceinline__ void load_k(const __bf16* __restrict__ kbase, int64_t row_stride, int key0, int Lk,
+                                         int tid) {
+    const int rows = max(0, min(BN, Lk - key0));
+    const __amdgpu_buffer_rsrc_t rk =
+        buffer_rsrc(kbase + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
+#pragma unroll
+    for (int i = 0; i < K_PER_THREAD; ++i) {
+      const int c = tid + i * THREADS;
+      reg[i] = buffer_load16(rk, ((uint32_t)G::k_row(c) * (uint32_t)row_stride + G::k_chunk(c) * 8) * 2u);
+    }
+  }
+  __device__ __forceinline__ void load_v(const __bf16* __restrict__ vbase, int64_t row_stride, int key0, int Lk,
+                                         int tid) {
+    const int rows = max(0, min(BN, Lk - key0));
+    const __amdgpu_buffer_rsrc_t rv =
+        buffer_rsrc(vbase + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
+#pragma unroll
+    for (int i = 0; i < V_PER_THREAD; ++i) {
+      const int w = tid + i * THREADS;
+      const int u = G::v_group(w), dc = G::v_dchunk(w);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (G::v_owned(w)) x = buffer_load16(rv, ((uint32_t)(4 * u + r) * (uint32_t)row_stride + dc * 8) * 2u);
+        reg[4 * i + r] = x;
+      }
+    }
+  }
+
+  // registers -> LDS: K as is, V transposed
+  __device__ __forceinline__ void store_k(__bf16* Ks, int tid) const {
+#pragma unroll
+    for (int i = 0; i < K_PER_THREAD; ++i) {
+      const int c = tid + i * THREADS;
+      *(u32x4*)(Ks + G::ks_index(G::k_row(c), G::k_chunk(c))) = reg[i];
+    }
+  }
+  __device__ __forceinline__ void store_v(__bf16* Vt, int tid) const {
+#pragma unroll
+    for (int i = 0; i < V_PER_THREAD; ++i) {
+      const int w = tid + i * THREADS;
+      if (!G::v_owned(w)) continue;
+      const int u = G::v_group(w), dc = G::v_dchunk(w);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        // dims 2*e2 and 2*e2+1 of the chunk, for keys 4u..4u+3
+        const uint32_t r0 = reg[4 * i][e2], r1 = reg[4 * i + 1][e2];
+        const uint32_t r2 = reg[4 * i + 2][e2], r3 = reg[4 * i + 3][e2];
+        u32x2 lo, hi;
+        lo[0] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // (key0, key1) of dim 2*e2
+        lo[1] = __builtin_amdgcn_perm(r3, r2, 0x05040100u);  // (key2, key3)
+        hi[0] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // dim 2*e2+1
+        hi[1] = __builtin_amdgcn_perm(r3, r2, 0x07060302u);
+        const int d0 = dc * 8 + 2 * e2;
+        *(u32x2*)(Vt + G::vt_index(d0, 4 * u)) = lo;
+        *(u32x2*)(Vt + G::vt_index(d0 + 1, 4 * u)) = hi;
+      }
+    }
+  }
+};
+
+// Scheduling order of a block of NM MFMAs fed by NR LDS operand reads: the
+// first PRE reads, then one MFMA and one read alternately, then the
+// remaining MFMAs, so that PRE reads are in flight ahead of their use.
+template <int NM, int NR>
+__device__ __forceinline__ void operand_pipeline() {
+  constexpr int PRE = NR < 8 ? NR : 8;
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < NR - PRE; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR + PRE, 0);
+}
+
 // Per-wave state and the three tile-level steps of the bf16 forward pass.
 template <int D, int BN, int QB>
 struct Bf16Wave {
@@ -352,6 +445,25 @@ struct Bf16Wave {
         }
       }
     }
+  }
+
+  // The same product with the two 32-key blocks interleaved (independent
+  // accumulation chains) and the LDS operand reads issued ahead of their use.
+  __device__ __forceinline__ void qk_ordered(const __bf16* Ks, f32x16 (&s)[QB][KB], int arow, int g) const {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int krow = kb * 32 + arow;
+        const bf16x8 av = *(const bf16x8*)(Ks + tiling::ks_index<D>(krow, 2 * ks + g));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const f32x16 c = ks == 0 ? f32x16{} : s[qb][kb];
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[qb][ks], c, 0, 0, 0);
+        }
+      }
+    }
+    operand_pipeline<KSTEPS * KB * QB, KSTEPS * KB>();
   }
 
   // -inf for keys past the end of the sequence or (causal) above the diagonal
@@ -433,6 +545,23 @@ struct Bf16Wave {
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[qb][kb][t], o[qb][db], 0, 0, 0);
         }
     }
+  }
+
+  // The same product with the output blocks innermost (independent
+  // accumulation chains) and the LDS operand reads issued ahead of their use.
+  __device__ __forceinline__ void pv_ordered(const __bf16* Vt, const bf16x8 (&p)[QB][KB][2], int l32, int g) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 av = *(const bf16x8*)(Vt + tiling::vt_index<BN>(db * 32 + l32, kb * 32 + 16 * g + 8 * t));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[qb][kb][t], o[qb][db], 0, 0, 0);
+        }
+    operand_pipeline<DB * KB * 2 * QB, DB * KB * 2>();
   }
 };
 
@@ -576,6 +705,153 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         a.lse[(int64_t)w.h * a.total_q + w.q_start + i] =
             l > 0.f ? (wv.m_run[qb] + fast_log2(l)) * kLn2 : kNegInf;
     }
+  }
+}
+
+// Ping-pong schedule.  The workgroup's 8 wavefronts form two groups of 4
+// (waves 0-3 and 4-7); wave w runs on SIMD w % 4, so every SIMD holds one wave
+// of each group.  Every wave runs the same loop of a matrix phase M(n) and a
+// vector phase V(n), each closed by a workgroup barrier, but group 1 runs one
+// phase behind group 0 (it passes one extra barrier first, group 0 one extra
+// barrier last).  Between two barriers one wave of each SIMD therefore issues
+// MFMAs while the other runs the softmax, and the matrix cores and the vector
+// ALU work at the same time:
+//
+//   slot        2n                          2n+1
+//   group 0     M(n): S(n) = K(n) Q^T,      V(n): softmax S(n) -> P(n),
+//                     O += V(n-1)^T P(n-1)        stage V(n) into LDS
+//   group 1     V(n-1): softmax S(n-1),     M(n)
+//                     stage K(n+1) into LDS
+//
+// K(n) and V(n-1) are read in slots 2n and 2n+1.  K(n+1) is written in slot
+// 2n into the buffer that K(n-1) left after slot 2n-1, and V(n) in slot 2n+1
+// into the buffer that V(n-2) left after slot 2n-1.  Each group loads the
+// next tile it stages from global memory right after storing the current one,
+// a slot pair ahead of its use.
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void fwd_bf16_pingpong_kernel(FwdArgs a) {
+  constexpr int NW = 8;
+  constexpr int BM = 32 * NW;
+  using Stage = Bf16GroupStage<D, BN, 4>;  // staging by one group of 4 waves
+  using Wave = Bf16Wave<D, BN, 1>;
+  constexpr int KB = Wave::KB;
+
+  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * BN];
+
+  WorkItem w;
+  if (!decode_work(a, w)) return;
+  int n_full, n_end;
+  key_tiles<BM, BN, CAUSAL>(w, n_full, n_end);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int gtid = tid & 255;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int wrow0 = w.m * BM + wave * 32;  // first query row of this wave (in sequence)
+  const int shift = w.Lk - w.Lq;
+  const int64_t rs = a.row_stride;
+
+  const __bf16* __restrict__ kbase = (const __bf16*)a.k + (int64_t)w.k_start * rs + (int64_t)w.h * D;
+  const __bf16* __restrict__ vbase = (const __bf16*)a.v + (int64_t)w.k_start * rs + (int64_t)w.h * D;
+
+  Wave wv;
+  {  // Q rows past the end of the sequence load as zeros
+    const int qrows = max(0, min(32, w.Lq - wrow0));
+    const __amdgpu_buffer_rsrc_t rq =
+        buffer_rsrc((const __bf16*)a.q + (int64_t)(w.q_start + wrow0) * rs + (int64_t)w.h * D,
+                    head_rows_bytes(qrows, rs, D, 2));
+#pragma unroll
+    for (int ks = 0; ks < Wave::KSTEPS; ++ks) {
+      const uint32_t off = ((uint32_t)l32 * (uint32_t)rs + 16 * ks + 8 * g) * 2u;
+      wv.qreg[0][ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, off));
+    }
+  }
+  wv.m_run[0] = kNegInf;
+  wv.l_run[0] = 0.f;
+#pragma unroll
+  for (int db = 0; db < Wave::DB; ++db) wv.o[0][db] = f32x16{};
+
+  // Tiles this wave needs: all n < n_wave (rows past the sequence end need
+  // none; causal rows need keys up to their diagonal).
+  int n_wave = 0;
+  if (wrow0 < w.Lq) {
+    if (CAUSAL) {
+      const int last_key = wrow0 + 31 + shift;
+      n_wave = last_key < 0 ? 0 : min(n_end, last_key / BN + 1);
+    } else {
+      n_wave = n_end;
+    }
+  }
+
+  const int arow = key_of_arow(l32);
+  Stage st;
+  if (n_end > 0) {
+    if (grp == 1) {
+      st.load_k(kbase, rs, 0, w.Lk, gtid);
+      st.store_k(lds_k[0], gtid);
+      if (n_end > 1) st.load_k(kbase, rs, BN, w.Lk, gtid);
+    } else {
+      st.load_v(vbase, rs, 0, w.Lk, gtid);
+    }
+  }
+  __syncthreads();
+  if (grp == 1) {  // group 1's idle first slot: stage K(1)
+    if (n_end > 1) {
+      st.store_k(lds_k[1], gtid);
+      if (n_end > 2) st.load_k(kbase, rs, 2 * BN, w.Lk, gtid);
+    }
+    __syncthreads();
+  }
+
+  f32x16 s[1][KB];
+  bf16x8 p[1][KB][2];
+  for (int n = 0; n <= n_end; ++n) {
+    // matrix phase: S(n) = K(n) Q^T and O += V(n-1)^T P(n-1)
+    if (n < n_wave) wv.qk_ordered(lds_k[n & 1], s, arow, g);
+    if (n >= 1 && n - 1 < n_wave) wv.pv_ordered(lds_v[(n - 1) & 1], p, l32, g);
+    __syncthreads();
+    // vector phase: masks, online softmax and the rare rescale of O for tile
+    // n; group 0 stages V(n), group 1 stages K(n+2)
+    if (n < n_wave) {
+      if (n >= n_full) Wave::template mask<CAUSAL>(s, n * BN, wrow0, l32, g, w.Lk, shift);
+      float alpha[1];
+      if (wv.softmax(s, p, alpha, a.scale_log2)) wv.rescale(alpha);
+    }
+    if (grp == 0) {
+      if (n < n_end) {
+        st.store_v(lds_v[n & 1], gtid);
+        if (n + 1 < n_end) st.load_v(vbase, rs, (n + 1) * BN, w.Lk, gtid);
+      }
+    } else {
+      if (n + 2 < n_end) {
+        st.store_k(lds_k[n & 1], gtid);
+        if (n + 3 < n_end) st.load_k(kbase, rs, (n + 3) * BN, w.Lk, gtid);
+      }
+    }
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();  // group 0's idle last slot
+
+  // ---- epilogue: normalise, write out (bf16) and lse
+  __bf16* __restrict__ op = (__bf16*)a.out;
+  const int i = wrow0 + l32;
+  const float l = pair_sum(wv.l_run[0]);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (i < w.Lq) {
+    __bf16* dst = op + (int64_t)(w.q_start + i) * rs + (int64_t)w.h * D;
+#pragma unroll
+    for (int db = 0; db < Wave::DB; ++db)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        bf16x4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(wv.o[0][db][4 * s4 + c] * inv);
+        *(bf16x4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
+      }
+    if (g == 0)
+      a.lse[(int64_t)w.h * a.total_q + w.q_start + i] = l > 0.f ? (wv.m_run[0] + fast_log2(l)) * kLn2 : kNegInf;
   }
 }
 
@@ -769,8 +1045,8 @@ hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, 
 hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream) {
   if (dtype == 1) {
     if (head_dim == 128)
-      return causal ? launch(fwd_bf16_kernel<128, 64, 8, 1, true>, grid, 512, stream, a)
-                    : launch(fwd_bf16_kernel<128, 64, 8, 1, false>, grid, 512, stream, a);
+      return causal ? launch(fwd_bf16_pingpong_kernel<128, 64, true>, grid, 512, stream, a)
+                    : launch(fwd_bf16_pingpong_kernel<128, 64, false>, grid, 512, stream, a);
     if (head_dim == 64)
       return causal ? launch(fwd_bf16_kernel<64, 64, 4, 1, true>, grid, 256, stream, a)
                     : launch(fwd_bf16_kernel<64, 64, 4, 1, false>, grid, 256, stream, a);
