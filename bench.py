@@ -239,7 +239,7 @@ def parse_pmc(fetch_dir: str, write_dir: str) -> dict:
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per_disp = _counter_per_dispatch(d, counter)
         copy_vals = [v for (k, _), v in per_disp.items() if "elementwise" in k.lower()]
-        fwd_vals = [v for (k, _), v in per_disp.items() if "fwd_bf16_kernel" in k]
+        fwd_vals = [v for (k, _), v in per_disp.items() if "fwd_bf16" in k]
         if not copy_vals or not fwd_vals:
             raise RuntimeError(f"{counter}: calibration copy or attention dispatches not found in {d}")
         copy_kib = max(copy_vals)
@@ -344,7 +344,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": round(traffic["traffic_bytes"]) if traffic else None,
-                     "kernel": "fwd_bf16_kernel<128,64,...,causal>", "kernel_ms": round(kms, 4),
+                     "kernel": "fwd_bf16_pingpong_kernel<128, 64, causal>", "kernel_ms": round(kms, 4),
                      "algorithmic_bytes": round(algorithmic_bytes(wl))},
     }
     del r, t
