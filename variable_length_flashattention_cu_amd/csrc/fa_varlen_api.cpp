@@ -13,6 +13,10 @@
 namespace {
 
 constexpr double kLog2e = 1.4426950408889634074;
+// Compute units of an MI355X; with at most kPairLimit workgroups per CU the
+// causal forward pairs query blocks (see run_work in the kernels).
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kPairLimit = 8;
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -55,8 +59,8 @@ int validate(const void* q, const void* k, const void* v, const int32_t* cu_q, c
 }
 
 fa::FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
-                      float scale, void* out, float* lse, int32_t batch, int32_t total_q, int32_t heads,
-                      int32_t head_dim, const int32_t* blk_start, const Plan& plan) {
+                      float scale, int32_t causal, void* out, float* lse, int32_t batch, int32_t total_q,
+                      int32_t heads, int32_t head_dim, const int32_t* blk_start, const Plan& plan) {
   fa::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -72,6 +76,7 @@ fa::FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t
   a.tmax = (int32_t)plan.tmax;
   a.n_work = (int32_t)(plan.tmax * heads);
   a.total_q = total_q;
+  a.pair_blocks = (causal && plan.tmax * heads <= kPairLimit * kComputeUnits) ? 1 : 0;
   return a;
 }
 
@@ -127,8 +132,8 @@ int fa_varlen_fwd_mapped(const void* q, const void* k, const void* v, const int3
   if (!blk_start) return FA_ERR_NULL;
   if (!aligned(blk_start, 4)) return FA_ERR_ALIGN;
   if (plan.grid == 0) return FA_OK;  // no query rows: nothing to compute
-  const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse, batch, total_q,
-                                  num_heads, head_dim, blk_start, plan);
+  const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, causal, out, lse, batch,
+                                  total_q, num_heads, head_dim, blk_start, plan);
   if (fa::launch_fwd(dtype, head_dim, causal != 0, (int)plan.grid, a, (hipStream_t)stream) != hipSuccess)
     return FA_ERR_HIP;
   return FA_OK;
@@ -151,7 +156,7 @@ int fa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu
   if (fa::launch_tile_map(cu_seqlens_q, batch, plan.tc.block_m, blk_start, s) != hipSuccess) {
     rc = FA_ERR_HIP;
   } else {
-    const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse, batch,
+    const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, causal, out, lse, batch,
                                     total_q, num_heads, head_dim, blk_start, plan);
     if (fa::launch_fwd(dtype, head_dim, causal != 0, (int)plan.grid, a, s) != hipSuccess) rc = FA_ERR_HIP;
   }

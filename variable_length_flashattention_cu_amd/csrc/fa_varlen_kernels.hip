@@ -571,17 +571,13 @@ struct Bf16Wave {
 // buffers hold K(n+1) and V(n) for reading while K(n+2) and V(n+1) are being
 // written into the slots that K(n) and V(n-1) left free.
 template <int D, int BN, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_bf16_item(const FwdArgs& a, const WorkItem& w, __bf16 (&lds_k)[2][BN * D],
+                                              __bf16 (&lds_v)[2][D * BN]) {
   constexpr int BM = 32 * QB * NW;
   using Tile = Bf16Tile<D, BN, NW>;
   using Wave = Bf16Wave<D, BN, QB>;
   constexpr int KB = Wave::KB;
 
-  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * BN];
-
-  WorkItem w;
-  if (!decode_work(a, w)) return;
   int n_full, n_end;
   key_tiles<BM, BN, CAUSAL>(w, n_full, n_end);
 
@@ -729,18 +725,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
 // next tile it stages from global memory right after storing the current one,
 // a slot pair ahead of its use.
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void fwd_bf16_pingpong_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_bf16_pingpong_item(const FwdArgs& a, const WorkItem& w,
+                                                       __bf16 (&lds_k)[2][BN * D], __bf16 (&lds_v)[2][D * BN]) {
   constexpr int NW = 8;
   constexpr int BM = 32 * NW;
   using Stage = Bf16GroupStage<D, BN, 4>;  // staging by one group of 4 waves
   using Wave = Bf16Wave<D, BN, 1>;
   constexpr int KB = Wave::KB;
 
-  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * BN];
-
-  WorkItem w;
-  if (!decode_work(a, w)) return;
   int n_full, n_end;
   key_tiles<BM, BN, CAUSAL>(w, n_full, n_end);
 
@@ -853,6 +845,53 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_pingpong_kernel(FwdArgs a) {
     if (g == 0)
       a.lse[(int64_t)w.h * a.total_q + w.q_start + i] = l > 0.f ? (wv.m_run[0] + fast_log2(l)) * kLn2 : kNegInf;
   }
+}
+
+// Work items of one workgroup.  Under a causal mask, query block m of a
+// sequence with M blocks reads about (m+1)/M of its keys, so blocks m and
+// M-1-m together always carry one full pass.  When the host asks for it
+// (a.pair_blocks: causal, and only a few workgroups per CU, where the last
+// few long workgroups would otherwise decide the run time), the workgroup of
+// block m < M/2 of a sequence with at least kPairMinBlocks blocks processes
+// both and the workgroups of the upper half exit.  Shorter sequences keep one
+// block per workgroup: their blocks are short and pairing would only halve
+// the parallelism.
+constexpr int kPairMinBlocks = 6;
+
+template <int BM, bool CAUSAL, typename Item>
+__device__ __forceinline__ void run_work(const FwdArgs& a, WorkItem& w, Item&& item) {
+  const int M = (w.Lq + BM - 1) / BM;
+  if (CAUSAL && a.pair_blocks && M >= kPairMinBlocks) {
+    if (2 * w.m >= M) return;
+    item(w);
+    if (M - 1 - w.m != w.m) {
+      __syncthreads();  // the second item reuses the LDS buffers
+      w.m = M - 1 - w.m;
+      item(w);
+    }
+  } else {
+    item(w);
+  }
+}
+
+template <int D, int BN, int NW, int QB, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * BN];
+  WorkItem w;
+  if (!decode_work(a, w)) return;
+  run_work<32 * QB * NW, CAUSAL>(a, w, [&](const WorkItem& wi) {
+    fwd_bf16_item<D, BN, NW, QB, CAUSAL>(a, wi, lds_k, lds_v);
+  });
+}
+
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void fwd_bf16_pingpong_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * BN];
+  WorkItem w;
+  if (!decode_work(a, w)) return;
+  run_work<256, CAUSAL>(a, w, [&](const WorkItem& wi) { fwd_bf16_pingpong_item<D, BN, CAUSAL>(a, wi, lds_k, lds_v); });
 }
 
 // ---------------------------------------------------------------------------

@@ -24,6 +24,7 @@ struct FwdArgs {
   int32_t tmax;        // upper bound on work items per head
   int32_t n_work;      // heads * tmax
   int32_t total_q;     // row count of q / columns of lse
+  int32_t pair_blocks; // causal: one workgroup takes query blocks m and M-1-m
 };
 
 struct TileConfig {
