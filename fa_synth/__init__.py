@@ -17,8 +17,10 @@ Workload shapes follow the FlashAttention pages:
 
 Draw recipe: numpy ``default_rng(seed)`` (PCG64); for the ragged 64k batch the
 sequence lengths are drawn first; then Q, K and V are drawn in that order as
-i.i.d. N(0, 1) float32 arrays of shape [tokens, heads, head_dim]; bf16
-workloads round each draw to bf16 with round-to-nearest-even.
+i.i.d. N(0, 1) float32 arrays of shape [tokens, heads, head_dim] (K and V with
+the workload's key/value head count, which may be a divisor of the query head
+count: several query heads sharing one key/value head); bf16 and fp16
+workloads round each draw to that type with round-to-nearest-even.
 """
 from __future__ import annotations
 
@@ -32,6 +34,8 @@ __all__ = [
     "Workload",
     "bf16_rne_bits",
     "bf16_bits_to_f32",
+    "f16_rne_bits",
+    "f16_bits_to_f32",
     "cu_from_lengths",
     "loguniform_lengths",
     "workload_tiny",
@@ -40,6 +44,7 @@ __all__ = [
     "workload_sweep",
     "workload_ragged64k",
     "workload_custom",
+    "workload_ragged64k_gqa",
     "all_parity_workloads",
     "draw_qkv",
     "SWEEP_SEQLENS",
@@ -70,6 +75,17 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact float32 values of bf16 bit patterns."""
     b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32)
+
+
+def f16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE fp16 (round to nearest, ties to even);
+    uint16 bit patterns.  numpy's float32 -> float16 cast rounds this way."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 values of fp16 bit patterns."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -111,10 +127,15 @@ class Workload:
     cu_k: Tuple[int, ...]
     heads: int
     head_dim: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     seed: int
     causal_modes: Tuple[bool, ...]
     lengths_from_rng: bool = False  # ragged 64k: lengths come from the same generator
+    heads_k: int = 0  # key/value heads (0: same as heads); must divide heads
+
+    @property
+    def kv_heads(self) -> int:
+        return self.heads_k or self.heads
 
     @property
     def batch(self) -> int:
@@ -155,6 +176,7 @@ class Workload:
             "total_q": self.total_q,
             "total_k": self.total_k,
             "heads": self.heads,
+            "kv_heads": self.kv_heads,
             "head_dim": self.head_dim,
             "dtype": self.dtype,
             "seed": self.seed,
@@ -202,11 +224,20 @@ def workload_ragged64k(seed: int = 4, total: int = 65536) -> Workload:
 
 def workload_custom(name: str, lengths_q: Sequence[int], lengths_k: Optional[Sequence[int]],
                     heads: int, head_dim: int, dtype: str, seed: int,
-                    causal_modes: Tuple[bool, ...] = (False, True)) -> Workload:
-    """Any ragged shape (used for edge cases: empty sequences, tails, Lq != Lk)."""
+                    causal_modes: Tuple[bool, ...] = (False, True), heads_k: int = 0) -> Workload:
+    """Any ragged shape (used for edge cases: empty sequences, tails, Lq != Lk),
+    optionally with fewer key/value heads than query heads."""
+    if heads_k and heads % heads_k:
+        raise ValueError("heads_k must divide heads")
     cu_q = tuple(int(x) for x in cu_from_lengths(lengths_q))
     cu_k = cu_q if lengths_k is None else tuple(int(x) for x in cu_from_lengths(lengths_k))
-    return Workload(name, cu_q, cu_k, heads, head_dim, dtype, seed, causal_modes)
+    return Workload(name, cu_q, cu_k, heads, head_dim, dtype, seed, causal_modes, heads_k=heads_k)
+
+
+def workload_ragged64k_gqa(seed: int = 4, total: int = 65536, heads_k: int = 8) -> Workload:
+    """The ragged 64k batch with 32 query heads sharing ``heads_k`` key/value heads."""
+    base = workload_ragged64k(seed, total)
+    return dataclasses.replace(base, name=f"ragged64k_h32_kv{heads_k}_d128_causal_seed{seed}", heads_k=heads_k)
 
 
 def all_parity_workloads() -> List[Workload]:
@@ -222,8 +253,9 @@ def draw_qkv(wl: Workload, heads: Optional[Sequence[int]] = None) -> dict:
     Returns float32 arrays ``q``, ``k``, ``v`` (values exactly representable
     in bf16 when the workload is bf16) and, for bf16, the uint16 bit arrays
     ``q_bits``, ``k_bits``, ``v_bits`` that are handed to the device.
-    ``heads`` optionally keeps a subset of heads (the full tensors are still
-    drawn so that the values do not depend on the subset).
+    ``heads`` optionally keeps a subset of query heads (the full tensors are
+    still drawn so that the values do not depend on the subset); K and V are
+    always returned whole.
     """
     rng = np.random.default_rng(wl.seed)
     if wl.lengths_from_rng:
@@ -231,21 +263,23 @@ def draw_qkv(wl: Workload, heads: Optional[Sequence[int]] = None) -> dict:
         if tuple(cu_from_lengths(lengths)) != tuple(wl.cu_q):
             raise RuntimeError("length draw does not reproduce the workload")
     shape_q = (wl.total_q, wl.heads, wl.head_dim)
-    shape_k = (wl.total_k, wl.heads, wl.head_dim)
+    shape_k = (wl.total_k, wl.kv_heads, wl.head_dim)
+    rounders = {"bf16": (bf16_rne_bits, bf16_bits_to_f32), "f16": (f16_rne_bits, f16_bits_to_f32)}
     out = {}
     for name, shape in (("q", shape_q), ("k", shape_k), ("v", shape_k)):
         x = rng.standard_normal(shape, dtype=np.float32)
-        if wl.dtype == "bf16":
-            bits = bf16_rne_bits(x)
+        if wl.dtype in rounders:
+            to_bits, to_f32 = rounders[wl.dtype]
+            bits = to_bits(x)
             del x
-            x = bf16_bits_to_f32(bits).reshape(shape)
+            x = to_f32(bits).reshape(shape)
             bits = bits.reshape(shape)
-            if heads is not None:
+            if heads is not None and name == "q":
                 bits = np.ascontiguousarray(bits[:, list(heads), :])
             out[name + "_bits"] = bits
         elif wl.dtype != "f32":
             raise ValueError(wl.dtype)
-        if heads is not None:
+        if heads is not None and name == "q":
             x = np.ascontiguousarray(x[:, list(heads), :])
         out[name] = x
     return out

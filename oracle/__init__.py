@@ -19,7 +19,7 @@ on the pages, closed forms, invariants, brute force and a library routine.
 """
 from .cu_seqlens import lengths_from_cu, check_cu_seqlens, row_offset
 from .tile_map import tile_map, tile_items
-from .attention import attention_fwd, attention_rows, visible_mask, flops_visible_pairs
+from .attention import attention_fwd, attention_rows, visible_mask, flops_visible_pairs, kv_head_of
 from .online_softmax import online_softmax_attention, blockwise_normalised_attention
 
 __all__ = [
@@ -32,6 +32,7 @@ __all__ = [
     "attention_rows",
     "visible_mask",
     "flops_visible_pairs",
+    "kv_head_of",
     "online_softmax_attention",
     "blockwise_normalised_attention",
 ]

@@ -20,6 +20,11 @@ floating-point order:
     cálculo de longitud").  No query ever sees a key of another sequence.
   * A causal mask may be combined with variable lengths (same page, section
     "Integración con máscaras causales y caché paginada").
+  * Several query heads may share one key/value head (multi-query and
+    grouped-query attention, zepes.com "Comprendiendo Flash-Atención y
+    Flash-Atención-2", section "FlashAttention-2"): with H query heads and Hk
+    key/value heads (Hk dividing H), query head h attends with key/value head
+    h // (H / Hk).  Hk == H is ordinary multi-head attention.
 
 Readings where the pages are silent:
   * Causal alignment is bottom-right: query i (0-based within its sequence)
@@ -31,7 +36,7 @@ Readings where the pages are silent:
   * Inputs are used at the exact values the device receives (bf16 values are
     upcast without change); all arithmetic here is float64.
 
-Layouts: q [Tq, H, D], k and v [Tk, H, D]; out [Tq, H, D]; lse [H, Tq].
+Layouts: q [Tq, H, D], k and v [Tk, Hk, D]; out [Tq, H, D]; lse [H, Tq].
 Rows at or beyond cu_q[-1] belong to no sequence and are returned as NaN.
 """
 from __future__ import annotations
@@ -74,19 +79,31 @@ def _softmax_rows(S: np.ndarray, vis: np.ndarray, Vb: np.ndarray):
     return out, lse
 
 
+def kv_head_of(H: int, Hk: int) -> int:
+    """Query heads per key/value head (the group size); Hk must divide H."""
+    if Hk < 1 or H % Hk:
+        raise ValueError(f"key/value heads ({Hk}) must divide query heads ({H})")
+    return H // Hk
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("expected q [Tq,H,D], k and v [Tk,Hk,D] with equal D")
+    return kv_head_of(q.shape[1], k.shape[1])
+
+
 def attention_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, scale: float,
                   causal: bool, heads: Optional[Sequence[int]] = None, row_chunk: int = 1024):
     """Exact varlen attention forward in float64.
 
-    ``heads`` restricts the computation to a subset of heads (others stay
-    NaN).  Rows are processed in chunks of at most ``row_chunk`` queries,
-    which is still the row-wise definition.
+    ``heads`` restricts the computation to a subset of query heads (others
+    stay NaN).  Rows are processed in chunks of at most ``row_chunk``
+    queries, which is still the row-wise definition.
     """
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
-    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:]:
-        raise ValueError("expected q [Tq,H,D], k and v [Tk,H,D] with equal H and D")
+    group = _check_shapes(q, k, v)
     Tq, H, D = q.shape
     Tk = k.shape[0]
     cq = check_cu_seqlens(cu_q, Tq)
@@ -102,8 +119,8 @@ def attention_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, scale
         if Lq == 0:
             continue
         for h in hs:
-            Kb = k[k0:k0 + Lk, h, :].astype(np.float64)
-            Vb = v[k0:k0 + Lk, h, :].astype(np.float64)
+            Kb = k[k0:k0 + Lk, h // group, :].astype(np.float64)
+            Vb = v[k0:k0 + Lk, h // group, :].astype(np.float64)
             for r0 in range(0, Lq, row_chunk):
                 r1 = min(Lq, r0 + row_chunk)
                 Qb = q[q0 + r0:q0 + r1, h, :].astype(np.float64)
@@ -124,6 +141,7 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, scal
     """
     rows = np.asarray(list(rows), dtype=np.int64)
     heads = list(heads)
+    group = _check_shapes(q, k, v)
     Tq, H, D = q.shape
     cq = check_cu_seqlens(cu_q, Tq)
     ck = check_cu_seqlens(cu_k, k.shape[0])
@@ -140,8 +158,8 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, scal
         local = rows[sel] - q0
         vis = visible_mask(Lq, Lk, causal, local)
         for hi, h in enumerate(heads):
-            Kb = k[k0:k0 + Lk, h, :].astype(np.float64)
-            Vb = v[k0:k0 + Lk, h, :].astype(np.float64)
+            Kb = k[k0:k0 + Lk, h // group, :].astype(np.float64)
+            Vb = v[k0:k0 + Lk, h // group, :].astype(np.float64)
             Qb = q[rows[sel], h, :].astype(np.float64)
             S = scale * (Qb @ Kb.T)
             o, s = _softmax_rows(S, vis, Vb)

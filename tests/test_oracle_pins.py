@@ -450,3 +450,64 @@ def test_planted_internal_mistakes_fail_a_pin(patch, monkeypatch):
         monkeypatch.setattr(oatt, "_softmax_rows", _softmax_no_max_guard)
     results = {p.__name__: p(oatt.attention_fwd) for p in PINS}
     assert not all(results.values()), f"planted mistake {patch} passed every pin"
+
+
+# ---------------------------------------------------------------- shared key/value heads
+def _gqa_case(rng, H=8, Hk=2, D=16):
+    cu_q, cu_k = cu_from_lengths([13, 0, 29, 7]), cu_from_lengths([11, 4, 29, 20])
+    q = rng.standard_normal((int(cu_q[-1]), H, D))
+    k = rng.standard_normal((int(cu_k[-1]), Hk, D))
+    v = rng.standard_normal((int(cu_k[-1]), Hk, D))
+    return q, k, v, cu_q, cu_k
+
+
+def pin_gqa_repeat(attn, H=8, Hk=2):
+    """Query head h shares key/value head h // (H/Hk): the result equals plain
+    multi-head attention on K/V whose heads are repeated H/Hk times each
+    (numpy's repeat builds the shared heads independently of the oracle)."""
+    rng = np.random.default_rng(40 + Hk)
+    q, k, v, cq, ck = _gqa_case(rng, H, Hk)
+    ok = True
+    for causal in (False, True):
+        o, l = attn(q, k, v, cq, ck, 0.3, causal)
+        kr, vr = np.repeat(k, H // Hk, axis=1), np.repeat(v, H // Hk, axis=1)
+        ro, rl = attention_fwd(q, kr, vr, cq, ck, 0.3, causal)
+        n = int(cq[-1])
+        ok &= np.array_equal(o[:n], ro[:n]) and np.array_equal(l[:, :n], rl[:, :n])
+    return bool(ok)
+
+
+@pytest.mark.parametrize("Hk", [1, 2, 4, 8])
+def test_gqa_equals_mha_on_repeated_heads(Hk):
+    assert pin_gqa_repeat(attention_fwd, 8, Hk)
+
+
+def test_gqa_rows_match_full():
+    rng = np.random.default_rng(44)
+    q, k, v, cq, ck = _gqa_case(rng, 8, 2)
+    rows = [0, 5, 12, 13, 30, 41, 48]
+    heads = [0, 3, 4, 7]
+    fo, fl = attention_fwd(q, k, v, cq, ck, 0.3, True)
+    so, sl = attention_rows(q, k, v, cq, ck, 0.3, True, rows, heads)
+    assert np.allclose(so, fo[rows][:, heads], rtol=1e-12, atol=1e-12)
+    assert np.allclose(sl, fl[heads][:, rows], rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_head_count_must_divide():
+    rng = np.random.default_rng(45)
+    q = rng.standard_normal((4, 6, 8))
+    k = rng.standard_normal((4, 4, 8))
+    with pytest.raises(ValueError):
+        attention_fwd(q, k, k, [0, 4], [0, 4], 1.0, False)
+    assert oracle.kv_head_of(32, 8) == 4 and oracle.kv_head_of(5, 1) == 5
+
+
+def test_planted_gqa_interleaved_mapping_fails(monkeypatch):
+    """Pairing query head h with key/value head h % Hk (interleaved instead of
+    contiguous groups) must fail the repeat pin."""
+    def interleaved(q, k, v, cq, ck, s, c):
+        Hk = k.shape[1]
+        kk = np.stack([k[:, h % Hk] for h in range(q.shape[1])], axis=1)
+        vv = np.stack([v[:, h % Hk] for h in range(q.shape[1])], axis=1)
+        return attention_fwd(q, kk, vv, cq, ck, s, c)
+    assert not pin_gqa_repeat(interleaved, 8, 2)
