@@ -71,9 +71,10 @@ def algorithmic_flops(wl: Workload, causal: bool) -> float:
 
 
 def algorithmic_bytes(wl: Workload) -> float:
-    es = 2 if wl.dtype == "bf16" else 4
-    hd = wl.heads * wl.head_dim
-    return float((wl.total_q + 2 * wl.total_k) * hd * es + wl.total_q * hd * es + 4 * wl.total_q * wl.heads)
+    """Q, K, V read once and out, lse written once (K/V with the key/value head count)."""
+    es = 4 if wl.dtype == "f32" else 2
+    hd, hkd = wl.heads * wl.head_dim, wl.kv_heads * wl.head_dim
+    return float(2 * wl.total_q * hd * es + 2 * wl.total_k * hkd * es + 4 * wl.total_q * wl.heads)
 
 
 def kernel_sha() -> str:
@@ -107,7 +108,7 @@ class Runner:
         self.common = (t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["cu_q"].data_ptr(),
                        t["cu_k"].data_ptr(), wl.max_seqlen_q, wl.max_seqlen_k, wl.scale, int(causal),
                        t["out"].data_ptr(), t["lse"].data_ptr(), wl.batch, wl.total_q, wl.total_k, wl.heads,
-                       wl.head_dim, dt)
+                       wl.kv_heads, wl.head_dim, dt)
 
     def step(self):
         st = self.lib.fa_varlen_fwd(*self.common, self.stream)

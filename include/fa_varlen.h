@@ -22,12 +22,19 @@
  *     mejoras en la utilización de la GPU").
  *   * Causal masking may be combined with variable lengths (friki.work,
  *     section "Integración con máscaras causales y caché paginada").
+ *   * Several query heads may share one key/value head (multi-query and
+ *     grouped-query attention, zepes.com "Comprendiendo Flash-Atención y
+ *     Flash-Atención-2", section "FlashAttention-2"); mixed precision
+ *     (FP16/BF16) is the recommended input type (friki.work, section
+ *     "Consejos de optimización").
  *
  * Readings the pages leave open, fixed here:
  *   * causal alignment is bottom-right: query i of a sequence (0-based) sees
  *     key j iff j <= i + Lk - Lq;
  *   * a query row that sees no key gets out = 0 and lse = -inf;
- *   * lse is the natural log of sum_j exp(scale * q_i . k_j) over visible j.
+ *   * lse is the natural log of sum_j exp(scale * q_i . k_j) over visible j;
+ *   * with num_heads_k key/value heads, query head h attends with key/value
+ *     head h / (num_heads / num_heads_k) (contiguous groups).
  *
  * Conventions shared by every entry point
  *   * Device pointers live on the current HIP device (hipSetDevice before the
@@ -54,15 +61,17 @@ extern "C" {
 
 /* Element types of q, k, v and out. */
 typedef enum fa_dtype {
-  FA_DTYPE_F32 = 0,  /* IEEE float32; arithmetic in float32 throughout */
-  FA_DTYPE_BF16 = 1  /* bfloat16 in and out; float32 accumulation */
+  FA_DTYPE_F32 = 0,   /* IEEE float32; arithmetic in float32 throughout */
+  FA_DTYPE_BF16 = 1,  /* bfloat16 in and out; float32 accumulation */
+  FA_DTYPE_F16 = 2    /* IEEE float16 in and out; float32 accumulation */
 } fa_dtype;
 
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,       /* a required pointer is NULL */
   FA_ERR_DTYPE = 2,      /* dtype is not an fa_dtype */
-  FA_ERR_SHAPE = 3,      /* negative size, zero heads, or max_seqlen > rows */
+  FA_ERR_SHAPE = 3,      /* negative size, zero heads, num_heads_k not dividing
+                            num_heads, or max_seqlen > rows */
   FA_ERR_HEAD_DIM = 4,   /* head_dim not supported (64 and 128 are) */
   FA_ERR_ALIGN = 5,      /* a pointer is not aligned as documented */
   FA_ERR_ARG = 6,        /* softmax_scale not finite and > 0, causal not 0/1, bad block_m */
@@ -107,7 +116,7 @@ int fa_varlen_tile_map(const int32_t* cu_seqlens_q, int32_t batch, int32_t block
  * Exact attention forward over packed variable-length sequences.
  *
  *   q             device [total_q, num_heads, head_dim], contiguous, dtype
- *   k, v          device [total_k, num_heads, head_dim], contiguous, dtype
+ *   k, v          device [total_k, num_heads_k, head_dim], contiguous, dtype
  *   cu_seqlens_q  device int32 [batch + 1] query offsets
  *   cu_seqlens_k  device int32 [batch + 1] key/value offsets
  *   max_seqlen_q  >= every query length (sizes the launch; 0..total_q)
@@ -118,9 +127,17 @@ int fa_varlen_tile_map(const int32_t* cu_seqlens_q, int32_t batch, int32_t block
  *                 rows < cu_seqlens_q[batch]; other rows untouched
  *   lse           device float32 [num_heads, total_q], natural-log
  *                 log-sum-exp per (head, query row); same rows as out
- *   batch, total_q, total_k, num_heads, head_dim, dtype   sizes and type
+ *   batch, total_q, total_k, num_heads, num_heads_k, head_dim, dtype
+ *                 sizes and type; num_heads_k (>= 1) divides num_heads, query
+ *                 head h reads key/value head h / (num_heads / num_heads_k);
+ *                 num_heads_k == num_heads is ordinary multi-head attention,
+ *                 num_heads_k == 1 multi-query attention
  *   stream        hipStream_t or NULL
  *
+ * dtype is FA_DTYPE_BF16, FA_DTYPE_F16 or FA_DTYPE_F32 (FA_ERR_DTYPE
+ * otherwise); 16-bit inputs are multiplied on the matrix cores with float32
+ * accumulation, the probabilities are rounded to the input type before the
+ * second product and the output is rounded to nearest even.
  * head_dim must be 64 or 128 (FA_ERR_HEAD_DIM otherwise).  q, k, v and out
  * must be 16-byte aligned, lse and cu_seqlens 4-byte aligned (the offsets
  * are best kept 32-byte aligned, as any hipMalloc'd buffer is).
@@ -134,7 +151,7 @@ int fa_varlen_fwd(const void* q, const void* k, const void* v,
                   float softmax_scale, int32_t causal,
                   void* out, float* lse,
                   int32_t batch, int32_t total_q, int32_t total_k,
-                  int32_t num_heads, int32_t head_dim, int32_t dtype,
+                  int32_t num_heads, int32_t num_heads_k, int32_t head_dim, int32_t dtype,
                   void* stream);
 
 /*
@@ -152,7 +169,7 @@ int fa_varlen_fwd_mapped(const void* q, const void* k, const void* v,
                          float softmax_scale, int32_t causal,
                          void* out, float* lse,
                          int32_t batch, int32_t total_q, int32_t total_k,
-                         int32_t num_heads, int32_t head_dim, int32_t dtype,
+                         int32_t num_heads, int32_t num_heads_k, int32_t head_dim, int32_t dtype,
                          const int32_t* blk_start, void* stream);
 
 /*

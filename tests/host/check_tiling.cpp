@@ -59,7 +59,7 @@ static long touch(const Access& a, unsigned off, int esize, int nbytes) {
 
 template <int D, int BN, int NW>
 static void check_bf16(long H) {
-  using G = Bf16Geom<D, BN, NW>;
+  using G = Geom16<D, BN, NW>;
   const long rs = H * D;
   // --- K/V tile loads: a sequence that ends at the very end of the tensor
   for (long h : {0L, H - 1}) {

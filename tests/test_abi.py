@@ -45,7 +45,7 @@ def test_status_strings():
 
 def test_block_sizes():
     for d in (64, 128):
-        for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16):
+        for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16):
             bm, bn = fa.fa_varlen_block_sizes(d, dt)
             assert bm > 0 and bn > 0 and bm % 32 == 0 and bn % 32 == 0
     with pytest.raises(fa.FaVarlenError) as e:
@@ -66,31 +66,32 @@ A4 = 0x10004
 
 def call_fwd(**over):
     args = dict(q=A16, k=A16, v=A16, cu_q=A16, cu_k=A16, max_q=8, max_k=8, scale=0.125, causal=0, out=A16,
-                lse=A16, batch=1, total_q=8, total_k=8, heads=2, head_dim=64, dtype=1)
+                lse=A16, batch=1, total_q=8, total_k=8, heads=2, heads_k=2, head_dim=64, dtype=1)
     args.update(over)
     lib = fa.load_library()
     return lib.fa_varlen_fwd(args["q"], args["k"], args["v"], args["cu_q"], args["cu_k"], args["max_q"],
                              args["max_k"], args["scale"], args["causal"], args["out"], args["lse"],
-                             args["batch"], args["total_q"], args["total_k"], args["heads"], args["head_dim"],
-                             args["dtype"], None)
+                             args["batch"], args["total_q"], args["total_k"], args["heads"], args["heads_k"],
+                             args["head_dim"], args["dtype"], None)
 
 
 def call_mapped(**over):
     args = dict(q=A16, k=A16, v=A16, cu_q=A16, cu_k=A16, max_q=8, max_k=8, scale=0.125, causal=0, out=A16,
-                lse=A16, batch=1, total_q=8, total_k=8, heads=2, head_dim=64, dtype=1, blk=A16)
+                lse=A16, batch=1, total_q=8, total_k=8, heads=2, heads_k=2, head_dim=64, dtype=1, blk=A16)
     args.update(over)
     lib = fa.load_library()
     return lib.fa_varlen_fwd_mapped(args["q"], args["k"], args["v"], args["cu_q"], args["cu_k"], args["max_q"],
                                     args["max_k"], args["scale"], args["causal"], args["out"], args["lse"],
                                     args["batch"], args["total_q"], args["total_k"], args["heads"],
-                                    args["head_dim"], args["dtype"], args["blk"], None)
+                                    args["heads_k"], args["head_dim"], args["dtype"], args["blk"], None)
 
 
 @pytest.mark.parametrize("call", [call_fwd, call_mapped])
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(cu_q=None), 1), (dict(cu_k=None), 1),
     (dict(out=None), 1), (dict(lse=None), 1),
-    (dict(dtype=2), 2), (dict(dtype=-1), 2),
+    (dict(dtype=3), 2), (dict(dtype=-1), 2),
+    (dict(heads_k=0), 3), (dict(heads_k=3), 3), (dict(heads=4, heads_k=3), 3), (dict(heads_k=-2), 3),
     (dict(head_dim=96), 4), (dict(head_dim=256), 4), (dict(head_dim=0), 4),
     (dict(batch=-1), 3), (dict(total_q=-1), 3), (dict(heads=0), 3), (dict(max_q=9), 3), (dict(max_k=9), 3),
     (dict(max_q=-1), 3),
@@ -101,6 +102,13 @@ def call_mapped(**over):
 ])
 def test_fwd_validation(call, over, code):
     assert call(**over) == code
+
+
+def test_shared_kv_heads_and_f16_pass_validation():
+    # valid groupings and fp16 reach the empty-problem early exit: FA_OK, nothing launched
+    for heads, heads_k in ((8, 1), (8, 2), (8, 4), (8, 8), (6, 3)):
+        for dtype in (0, 1, 2):
+            assert call_fwd(heads=heads, heads_k=heads_k, dtype=dtype, total_q=0, max_q=0) == 0
 
 
 def test_mapped_needs_map():

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, draw_qkv, workload_custom, workload_dense,
-                      workload_ragged64k, workload_ragged_qk, workload_sweep, workload_tiny)
+                      workload_ragged64k, workload_ragged64k_gqa, workload_ragged_qk, workload_sweep, workload_tiny)
 from oracle import attention_fwd, attention_rows, tile_map
 from tests._gpu_util import TOL, compare, host, run_gpu, sample_rows, say, to_device
 
@@ -87,7 +87,7 @@ def sampled_parity(fa, wl, causal, heads, seed):
     data = draw_qkv(wl)
     t = to_device(data, wl)
     o, l = host(*run_gpu(wl, t, causal))
-    bm = fa.fa_varlen_block_sizes(wl.head_dim, 1 if wl.dtype == "bf16" else 0)[0]
+    bm = fa.fa_varlen_block_sizes(wl.head_dim, {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype])[0]
     rows = sample_rows(wl, bm, np.random.default_rng(seed))
     ref_o, ref_l = attention_rows(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal, rows,
                                   heads)
@@ -119,7 +119,8 @@ EDGE = [
 
 
 @pytest.mark.parametrize("name,lq,lk", EDGE, ids=[e[0] for e in EDGE])
-@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 128), ("f16", 64), ("f16", 128), ("f32", 64),
+                                            ("f32", 128)])
 def test_edge_cases(fa, name, lq, lk, dtype, head_dim):
     wl = workload_custom(f"{name}_{dtype}_d{head_dim}", lq, lk, 3, head_dim, dtype, seed=len(name) + head_dim)
     for causal in (False, True):
@@ -214,3 +215,35 @@ def test_check_cu_seqlens_flags(fa):
     assert flags([0, 128, 300], [0, 128, 300], 300, 300, 171, 172) == 8
     assert flags([0, 128, 300], [0, 200, 100], 300, 300, 300, 300) == 32
     assert flags([0], [0], 0, 0, 0, 0) == 0
+
+
+# ---------------------------------------------------------------- fp16 and shared key/value heads
+def test_ragged_qk_f16(fa):
+    base = workload_ragged_qk()
+    wl = workload_custom("ragged_qk_h12_d64_f16", base.lengths_q, base.lengths_k, 12, 64, "f16", seed=5)
+    for causal in (False, True):
+        full_parity(fa, wl, causal)
+
+
+def test_dense_f16_sampled(fa):
+    wl = workload_custom("dense_8x2048_h16_d128_f16", [2048] * 8, None, 16, 128, "f16", seed=6)
+    for causal in (False, True):
+        sampled_parity(fa, wl, causal, [0, 9, 15], seed=6)
+
+
+GQA = [(8, 1), (8, 2), (8, 4), (6, 3), (4, 4)]
+
+
+@pytest.mark.parametrize("heads,heads_k", GQA, ids=[f"h{h}kv{k}" for h, k in GQA])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 128), ("f16", 128), ("f32", 64), ("f32", 128)])
+def test_shared_kv_heads(fa, heads, heads_k, dtype, head_dim):
+    wl = workload_custom(f"gqa_h{heads}_kv{heads_k}_{dtype}_d{head_dim}", [300, 0, 129, 700], [280, 5, 200, 700],
+                         heads, head_dim, dtype, seed=heads * 10 + heads_k, heads_k=heads_k)
+    for causal in (False, True):
+        full_parity(fa, wl, causal)
+
+
+def test_ragged64k_gqa_sampled(fa):
+    """The headline batch with 32 query heads sharing 8 key/value heads."""
+    wl = workload_ragged64k_gqa()
+    sampled_parity(fa, wl, True, [0, 3, 4, 31], seed=41)

@@ -20,6 +20,7 @@ __all__ = [
     "FaVarlenError",
     "FA_DTYPE_F32",
     "FA_DTYPE_BF16",
+    "FA_DTYPE_F16",
     "library_path",
     "load_library",
     "fa_status_string",
@@ -32,6 +33,7 @@ __all__ = [
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_F16 = 2
 
 FA_OK = 0
 STATUS_NAMES = {
@@ -71,7 +73,7 @@ def load_library() -> ctypes.CDLL:
     lib.fa_varlen_block_sizes.restype = ctypes.c_int
     lib.fa_varlen_tile_map.argtypes = [vp, i32, i32, vp, vp]
     lib.fa_varlen_tile_map.restype = ctypes.c_int
-    fwd_args = [vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, i32, i32, i32, i32, i32, i32]
+    fwd_args = [vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32]
     lib.fa_varlen_fwd.argtypes = fwd_args + [vp]
     lib.fa_varlen_fwd.restype = ctypes.c_int
     lib.fa_varlen_fwd_mapped.argtypes = fwd_args + [vp, vp]
@@ -119,7 +121,9 @@ def _dtype_code(t) -> int:
         return FA_DTYPE_F32
     if t.dtype == torch.bfloat16:
         return FA_DTYPE_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return FA_DTYPE_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
 
 
 def _stream_handle(stream) -> Optional[int]:
@@ -156,8 +160,10 @@ def fa_varlen_tile_map(cu_seqlens_q, block_m: int, blk_start=None, stream=None):
 def _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse):
     torch = _torch()
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:]:
-        raise ValueError("expected q [total_q, H, D], k and v [total_k, H, D]")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("expected q [total_q, H, D], k and v [total_k, Hk, D]")
+    if k.shape[1] < 1 or q.shape[1] % k.shape[1]:
+        raise ValueError("the key/value head count must divide the query head count")
     if not (q.is_cuda and k.is_cuda and v.is_cuda) or q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k, v must be CUDA tensors of one dtype")
     dt = _dtype_code(q)
@@ -184,7 +190,8 @@ def fa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_se
                   stream=None):
     """Exact attention forward over packed variable-length sequences.
 
-    q [total_q, H, D], k/v [total_k, H, D] (bf16 or fp32, CUDA);
+    q [total_q, H, D], k/v [total_k, Hk, D] (bf16, fp16 or fp32, CUDA; Hk
+    divides H, query head h uses key/value head h // (H // Hk));
     cu_seqlens_* int32 [batch+1] on the device.  Returns (out, lse) with
     out shaped like q and lse float32 [H, total_q].
     """
@@ -194,7 +201,7 @@ def fa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_se
     st = load_library().fa_varlen_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), int(max_seqlen_q),
         int(max_seqlen_k), scale, int(bool(causal)), out.data_ptr(), lse.data_ptr(), cu_q.numel() - 1,
-        total_q, k.shape[0], H, D, dt, _stream_handle(stream))
+        total_q, k.shape[0], H, k.shape[1], D, dt, _stream_handle(stream))
     _check(st, "fa_varlen_fwd")
     return out, lse
 
@@ -210,7 +217,7 @@ def fa_varlen_fwd_mapped(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
     st = load_library().fa_varlen_fwd_mapped(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), int(max_seqlen_q),
         int(max_seqlen_k), scale, int(bool(causal)), out.data_ptr(), lse.data_ptr(), cu_q.numel() - 1,
-        total_q, k.shape[0], H, D, dt, blk_start.data_ptr(), _stream_handle(stream))
+        total_q, k.shape[0], H, k.shape[1], D, dt, blk_start.data_ptr(), _stream_handle(stream))
     _check(st, "fa_varlen_fwd_mapped")
     return out, lse
 

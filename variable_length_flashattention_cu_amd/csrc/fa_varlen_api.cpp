@@ -27,15 +27,20 @@ struct Plan {
 };
 
 // Validation shared by fa_varlen_fwd and fa_varlen_fwd_mapped.
+bool known_dtype(int32_t dtype) {
+  return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16;
+}
+
 int validate(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
              int32_t max_q, int32_t max_k, float scale, int32_t causal, const void* out, const float* lse,
-             int32_t batch, int32_t total_q, int32_t total_k, int32_t heads, int32_t head_dim, int32_t dtype,
-             Plan* plan) {
+             int32_t batch, int32_t total_q, int32_t total_k, int32_t heads, int32_t heads_k, int32_t head_dim,
+             int32_t dtype, Plan* plan) {
   if (!q || !k || !v || !cu_q || !cu_k || !out || !lse) return FA_ERR_NULL;
-  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!known_dtype(dtype)) return FA_ERR_DTYPE;
   const fa::TileConfig tc = fa::tile_config(dtype, head_dim);
   if (tc.block_m == 0) return FA_ERR_HEAD_DIM;
   if (batch < 0 || total_q < 0 || total_k < 0 || heads < 1 || max_q < 0 || max_k < 0) return FA_ERR_SHAPE;
+  if (heads_k < 1 || heads % heads_k != 0) return FA_ERR_SHAPE;
   if (max_q > total_q || max_k > total_k) return FA_ERR_SHAPE;
   // In-tile byte offsets are 32-bit: bound the token row size.
   if ((int64_t)heads * head_dim > (int64_t{1} << 22)) return FA_ERR_TOO_LARGE;
@@ -60,7 +65,8 @@ int validate(const void* q, const void* k, const void* v, const int32_t* cu_q, c
 
 fa::FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
                       float scale, int32_t causal, void* out, float* lse, int32_t batch, int32_t total_q,
-                      int32_t heads, int32_t head_dim, const int32_t* blk_start, const Plan& plan) {
+                      int32_t heads, int32_t heads_k, int32_t head_dim, const int32_t* blk_start,
+                      const Plan& plan) {
   fa::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -71,6 +77,8 @@ fa::FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t
   a.cu_k = cu_k;
   a.blk_start = blk_start;
   a.row_stride = (int64_t)heads * head_dim;
+  a.kv_row_stride = (int64_t)heads_k * head_dim;
+  a.head_group = heads / heads_k;
   a.scale_log2 = (float)((double)scale * kLog2e);
   a.batch = batch;
   a.tmax = (int32_t)plan.tmax;
@@ -88,8 +96,10 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_DTYPE: return "unsupported dtype (expected FA_DTYPE_F32 or FA_DTYPE_BF16)";
-    case FA_ERR_SHAPE: return "invalid sizes (negative, zero heads, or max_seqlen above the row count)";
+    case FA_ERR_DTYPE: return "unsupported dtype (expected FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16)";
+    case FA_ERR_SHAPE:
+      return "invalid sizes (negative, zero heads, key/value heads not dividing the query heads, or max_seqlen "
+             "above the row count)";
     case FA_ERR_HEAD_DIM: return "unsupported head_dim (64 and 128 are supported)";
     case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse and offsets 4 bytes)";
     case FA_ERR_ARG: return "invalid argument (softmax_scale must be finite and > 0, causal 0 or 1, block_m 1..4096)";
@@ -101,7 +111,7 @@ const char* fa_status_string(int status) {
 
 int fa_varlen_block_sizes(int32_t head_dim, int32_t dtype, int32_t* block_m, int32_t* block_n) {
   if (!block_m || !block_n) return FA_ERR_NULL;
-  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!known_dtype(dtype)) return FA_ERR_DTYPE;
   const fa::TileConfig tc = fa::tile_config(dtype, head_dim);
   if (tc.block_m == 0) return FA_ERR_HEAD_DIM;
   *block_m = tc.block_m;
@@ -123,17 +133,17 @@ int fa_varlen_tile_map(const int32_t* cu_seqlens_q, int32_t batch, int32_t block
 int fa_varlen_fwd_mapped(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                          const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                          float softmax_scale, int32_t causal, void* out, float* lse, int32_t batch,
-                         int32_t total_q, int32_t total_k, int32_t num_heads, int32_t head_dim, int32_t dtype,
-                         const int32_t* blk_start, void* stream) {
+                         int32_t total_q, int32_t total_k, int32_t num_heads, int32_t num_heads_k,
+                         int32_t head_dim, int32_t dtype, const int32_t* blk_start, void* stream) {
   Plan plan;
   int st = validate(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
-                    out, lse, batch, total_q, total_k, num_heads, head_dim, dtype, &plan);
+                    out, lse, batch, total_q, total_k, num_heads, num_heads_k, head_dim, dtype, &plan);
   if (st != FA_OK) return st;
   if (!blk_start) return FA_ERR_NULL;
   if (!aligned(blk_start, 4)) return FA_ERR_ALIGN;
   if (plan.grid == 0) return FA_OK;  // no query rows: nothing to compute
   const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, causal, out, lse, batch,
-                                  total_q, num_heads, head_dim, blk_start, plan);
+                                  total_q, num_heads, num_heads_k, head_dim, blk_start, plan);
   if (fa::launch_fwd(dtype, head_dim, causal != 0, (int)plan.grid, a, (hipStream_t)stream) != hipSuccess)
     return FA_ERR_HIP;
   return FA_OK;
@@ -142,10 +152,10 @@ int fa_varlen_fwd_mapped(const void* q, const void* k, const void* v, const int3
 int fa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                   const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
                   int32_t causal, void* out, float* lse, int32_t batch, int32_t total_q, int32_t total_k,
-                  int32_t num_heads, int32_t head_dim, int32_t dtype, void* stream) {
+                  int32_t num_heads, int32_t num_heads_k, int32_t head_dim, int32_t dtype, void* stream) {
   Plan plan;
   int st = validate(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
-                    out, lse, batch, total_q, total_k, num_heads, head_dim, dtype, &plan);
+                    out, lse, batch, total_q, total_k, num_heads, num_heads_k, head_dim, dtype, &plan);
   if (st != FA_OK) return st;
   if (plan.grid == 0) return FA_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -157,7 +167,7 @@ int fa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu
     rc = FA_ERR_HIP;
   } else {
     const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, causal, out, lse, batch,
-                                    total_q, num_heads, head_dim, blk_start, plan);
+                                    total_q, num_heads, num_heads_k, head_dim, blk_start, plan);
     if (fa::launch_fwd(dtype, head_dim, causal != 0, (int)plan.grid, a, s) != hipSuccess) rc = FA_ERR_HIP;
   }
   if (hipFreeAsync(blk_start, s) != hipSuccess) rc = FA_ERR_HIP;

@@ -1,18 +1,28 @@
 // fa_varlen_kernels.hip -- gfx950 kernels for exact attention forward over
 // packed variable-length sequences.
 //
-// Three kernels:
-//   * tile_map_kernel     -- the work-item map: exclusive scan of per-sequence
-//                            query-block counts (the sequence-dimension split,
-//                            iplexlaw.co.kr "FlashAttention-2 GPU work
-//                            partitioning", section "Tres mejoras en la
-//                            utilización de la GPU").
-//   * fwd_bf16_kernel     -- bf16 in/out, bf16 MFMA for both contractions,
-//                            fp32 online softmax.
-//   * fwd_f32_kernel      -- fp32 in/out, fp32 MFMA, same online softmax.
-//   * check_cu_kernel     -- optional device validation of the offsets.
+// Kernels:
+//   * tile_map_kernel       -- the work-item map: exclusive scan of per-sequence
+//                              query-block counts (the sequence-dimension split,
+//                              iplexlaw.co.kr "FlashAttention-2 GPU work
+//                              partitioning", section "Tres mejoras en la
+//                              utilización de la GPU").
+//   * fwd16_pingpong_kernel -- 16-bit (bf16 or fp16) in/out, head_dim 128: two
+//                              wave groups alternate MFMA and softmax phases.
+//   * fwd16_kernel          -- 16-bit in/out, head_dim 64: one wave group with
+//                              a software pipeline inside each wave.
+//                              Both use 16-bit MFMA for the two contractions
+//                              and an fp32 online softmax.
+//   * fwd_f32_kernel        -- fp32 in/out, fp32 MFMA, same online softmax.
+//   * check_cu_kernel       -- optional device validation of the offsets.
 //
-// Forward-kernel organisation (both dtypes)
+// Several query heads may share one key/value head (multi-query and
+// grouped-query attention, zepes.com "Comprendiendo Flash-Atención y
+// Flash-Atención-2", section "FlashAttention-2"): query head h reads the K/V
+// slices of head h / head_group, in tensors of kv_heads = heads / head_group
+// heads per token row.
+//
+// Forward-kernel organisation (all dtypes)
 // -----------------------------------------
 // One workgroup owns one (sequence b, query block m, head h) work item: BM
 // query rows split across NW wavefronts, 32*QB rows per wavefront (split-Q:
@@ -73,6 +83,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -80,6 +92,28 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
+
+// 16-bit element types of the MFMA path: bf16 and IEEE fp16 share every tile
+// layout (2-byte elements, moved as raw bits through LDS); only the MFMA and
+// the float conversions (round to nearest even) differ.
+template <typename T>
+struct Elem16;
+template <>
+struct Elem16<__bf16> {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+  __device__ __forceinline__ static f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Elem16<_Float16> {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+  __device__ __forceinline__ static f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -251,8 +285,8 @@ using tiling::k_swz;
 using tiling::v_swz;
 
 template <int D, int BN, int NW>
-struct Bf16Tile : tiling::Bf16Geom<D, BN, NW> {
-  using G = tiling::Bf16Geom<D, BN, NW>;
+struct Tile16 : tiling::Geom16<D, BN, NW> {
+  using G = tiling::Geom16<D, BN, NW>;
   using G::K_PER_THREAD;
   using G::THREADS;
   using G::V_PER_THREAD;
@@ -264,7 +298,7 @@ struct Bf16Tile : tiling::Bf16Geom<D, BN, NW> {
   // start at the tile's first key (head slice) and end exactly at the end of
   // the last valid row's head slice, so offsets stay below BN * row_stride * 2
   // bytes (the host bounds heads * head_dim) and never reach past a tensor.
-  __device__ __forceinline__ void load_k(const __bf16* __restrict__ kbase, int64_t row_stride, int key0, int Lk,
+  __device__ __forceinline__ void load_k(const uint16_t* __restrict__ kbase, int64_t row_stride, int key0, int Lk,
                                          int tid) {
     const int rows = max(0, min(BN, Lk - key0));
     const __amdgpu_buffer_rsrc_t rk =
@@ -275,7 +309,7 @@ struct Bf16Tile : tiling::Bf16Geom<D, BN, NW> {
       kreg[i] = buffer_load16(rk, ((uint32_t)G::k_row(c) * (uint32_t)row_stride + G::k_chunk(c) * 8) * 2u);
     }
   }
-  __device__ __forceinline__ void load_v(const __bf16* __restrict__ vbase, int64_t row_stride, int key0, int Lk,
+  __device__ __forceinline__ void load_v(const uint16_t* __restrict__ vbase, int64_t row_stride, int key0, int Lk,
                                          int tid) {
     const int rows = max(0, min(BN, Lk - key0));
     const __amdgpu_buffer_rsrc_t rv =
@@ -294,14 +328,14 @@ struct Bf16Tile : tiling::Bf16Geom<D, BN, NW> {
   }
 
   // registers -> LDS: K as is, V transposed
-  __device__ __forceinline__ void store_k(__bf16* Ks, int tid) const {
+  __device__ __forceinline__ void store_k(uint16_t* Ks, int tid) const {
 #pragma unroll
     for (int i = 0; i < K_PER_THREAD; ++i) {
       const int c = tid + i * THREADS;
       *(u32x4*)(Ks + G::ks_index(G::k_row(c), G::k_chunk(c))) = kreg[i];
     }
   }
-  __device__ __forceinline__ void store_v(__bf16* Vt, int tid) const {
+  __device__ __forceinline__ void store_v(uint16_t* Vt, int tid) const {
 #pragma unroll
     for (int i = 0; i < V_PER_THREAD; ++i) {
       const int w = tid + i * THREADS;
@@ -328,8 +362,8 @@ struct Bf16Tile : tiling::Bf16Geom<D, BN, NW> {
 // Staging for a kernel in which a thread stages either K tiles or V tiles:
 // one register set serves both roles.
 template <int D, int BN, int NW>
-struct Bf16GroupStage : tiling::Bf16Geom<D, BN, NW> {
-  using G = tiling::Bf16Geom<D, BN, NW>;
+struct GroupStage16 : tiling::Geom16<D, BN, NW> {
+  using G = tiling::Geom16<D, BN, NW>;
   using G::K_PER_THREAD;
   using G::THREADS;
   using G::V_PER_THREAD;
@@ -342,7 +376,7 @@ struct Bf16GroupStage : tiling::Bf16Geom<D, BN, NW> {
   // start at the tile's first key (head slice) and end exactly at the end of
   // the last valid row's head slice, so offsets stay below BN * row_stride * 2
   // bytes (the host bounds heads * head_dim) and never reach past a tensor.
-  __device__ __forceinline__ void load_k(const __bf16* __restrict__ kbase, int64_t row_stride, int key0, int Lk,
+  __device__ __forceinline__ void load_k(const uint16_t* __restrict__ kbase, int64_t row_stride, int key0, int Lk,
                                          int tid) {
     const int rows = max(0, min(BN, Lk - key0));
     const __amdgpu_buffer_rsrc_t rk =
@@ -353,7 +387,7 @@ struct Bf16GroupStage : tiling::Bf16Geom<D, BN, NW> {
       reg[i] = buffer_load16(rk, ((uint32_t)G::k_row(c) * (uint32_t)row_stride + G::k_chunk(c) * 8) * 2u);
     }
   }
-  __device__ __forceinline__ void load_v(const __bf16* __restrict__ vbase, int64_t row_stride, int key0, int Lk,
+  __device__ __forceinline__ void load_v(const uint16_t* __restrict__ vbase, int64_t row_stride, int key0, int Lk,
                                          int tid) {
     const int rows = max(0, min(BN, Lk - key0));
     const __amdgpu_buffer_rsrc_t rv =
@@ -372,14 +406,14 @@ struct Bf16GroupStage : tiling::Bf16Geom<D, BN, NW> {
   }
 
   // registers -> LDS: K as is, V transposed
-  __device__ __forceinline__ void store_k(__bf16* Ks, int tid) const {
+  __device__ __forceinline__ void store_k(uint16_t* Ks, int tid) const {
 #pragma unroll
     for (int i = 0; i < K_PER_THREAD; ++i) {
       const int c = tid + i * THREADS;
       *(u32x4*)(Ks + G::ks_index(G::k_row(c), G::k_chunk(c))) = reg[i];
     }
   }
-  __device__ __forceinline__ void store_v(__bf16* Vt, int tid) const {
+  __device__ __forceinline__ void store_v(uint16_t* Vt, int tid) const {
 #pragma unroll
     for (int i = 0; i < V_PER_THREAD; ++i) {
       const int w = tid + i * THREADS;
@@ -418,30 +452,31 @@ __device__ __forceinline__ void operand_pipeline() {
   __builtin_amdgcn_sched_group_barrier(0x008, NM - NR + PRE, 0);
 }
 
-// Per-wave state and the three tile-level steps of the bf16 forward pass.
-template <int D, int BN, int QB>
-struct Bf16Wave {
+// Per-wave state and the three tile-level steps of the 16-bit forward pass.
+template <typename T, int D, int BN, int QB>
+struct Wave16 {
+  typedef typename Elem16<T>::v8 v8;
   static constexpr int KSTEPS = D / 16;  // MFMA k-steps for Q K^T
   static constexpr int KB = BN / 32;     // 32-key blocks per tile
   static constexpr int DB = D / 32;      // 32-dim blocks of the output
 
-  bf16x8 qreg[QB][KSTEPS];  // Q^T as the B operand
+  v8 qreg[QB][KSTEPS];  // Q^T as the B operand
   f32x16 o[QB][DB];         // O^T accumulators
   float m_run[QB], l_run[QB];
 
   // S^T = K Q^T for one key tile (K from LDS, swizzled rows)
-  __device__ __forceinline__ void qk(const __bf16* Ks, f32x16 (&s)[QB][KB], int arow, int g) const {
+  __device__ __forceinline__ void qk(const uint16_t* Ks, f32x16 (&s)[QB][KB], int arow, int g) const {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int krow = kb * 32 + arow;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int ch = 2 * ks + g;
-        const bf16x8 av = *(const bf16x8*)(Ks + tiling::ks_index<D>(krow, ch));
+        const v8 av = *(const v8*)(Ks + tiling::ks_index<D>(krow, ch));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const f32x16 c = ks == 0 ? f32x16{} : s[qb][kb];
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[qb][ks], c, 0, 0, 0);
+          s[qb][kb] = Elem16<T>::mfma(av, qreg[qb][ks], c);
         }
       }
     }
@@ -449,17 +484,17 @@ struct Bf16Wave {
 
   // The same product with the two 32-key blocks interleaved (independent
   // accumulation chains) and the LDS operand reads issued ahead of their use.
-  __device__ __forceinline__ void qk_ordered(const __bf16* Ks, f32x16 (&s)[QB][KB], int arow, int g) const {
+  __device__ __forceinline__ void qk_ordered(const uint16_t* Ks, f32x16 (&s)[QB][KB], int arow, int g) const {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int krow = kb * 32 + arow;
-        const bf16x8 av = *(const bf16x8*)(Ks + tiling::ks_index<D>(krow, 2 * ks + g));
+        const v8 av = *(const v8*)(Ks + tiling::ks_index<D>(krow, 2 * ks + g));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const f32x16 c = ks == 0 ? f32x16{} : s[qb][kb];
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[qb][ks], c, 0, 0, 0);
+          s[qb][kb] = Elem16<T>::mfma(av, qreg[qb][ks], c);
         }
       }
     }
@@ -487,7 +522,7 @@ struct Bf16Wave {
   // The returned flag is formed from the tile's row sums, so the (rarely
   // taken) rescale branch cannot be placed ahead of the exponentials: they
   // stay in one basic block with the MFMAs of the next score tile.
-  __device__ __forceinline__ bool softmax(const f32x16 (&s)[QB][KB], bf16x8 (&p)[QB][KB][2], float (&alpha)[QB],
+  __device__ __forceinline__ bool softmax(const f32x16 (&s)[QB][KB], v8 (&p)[QB][KB][2], float (&alpha)[QB],
                                           float scale_log2) {
     bool any_rescale = false;
 #pragma unroll
@@ -512,7 +547,7 @@ struct Bf16Wave {
           for (int e = 0; e < 8; ++e) {
             const float pe = fast_exp2(__builtin_fmaf(s[qb][kb][8 * t + e], scale_log2, -m_use));
             lsum += pe;
-            p[qb][kb][t][e] = (__bf16)pe;
+            p[qb][kb][t][e] = (T)pe;
           }
       l_run[qb] = l_run[qb] * alpha[qb] + lsum;
       any_rescale |= wave_any(alpha[qb] != 1.f && !(lsum < 0.f));  // lsum >= 0: ties the flag to the exps
@@ -530,7 +565,7 @@ struct Bf16Wave {
   }
 
   // O^T += V^T P^T for one key tile (V^T from LDS)
-  __device__ __forceinline__ void pv(const __bf16* Vt, const bf16x8 (&p)[QB][KB][2], int l32, int g) {
+  __device__ __forceinline__ void pv(const uint16_t* Vt, const v8 (&p)[QB][KB][2], int l32, int g) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d = db * 32 + l32;
@@ -539,27 +574,27 @@ struct Bf16Wave {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           // keys 32kb+16g+8t .. +7 of dimension d: one 16-byte chunk
-          const bf16x8 av = *(const bf16x8*)(Vt + tiling::vt_index<BN>(d, kb * 32 + 16 * g + 8 * t));
+          const v8 av = *(const v8*)(Vt + tiling::vt_index<BN>(d, kb * 32 + 16 * g + 8 * t));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[qb][kb][t], o[qb][db], 0, 0, 0);
+            o[qb][db] = Elem16<T>::mfma(av, p[qb][kb][t], o[qb][db]);
         }
     }
   }
 
   // The same product with the output blocks innermost (independent
   // accumulation chains) and the LDS operand reads issued ahead of their use.
-  __device__ __forceinline__ void pv_ordered(const __bf16* Vt, const bf16x8 (&p)[QB][KB][2], int l32, int g) {
+  __device__ __forceinline__ void pv_ordered(const uint16_t* Vt, const v8 (&p)[QB][KB][2], int l32, int g) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 av = *(const bf16x8*)(Vt + tiling::vt_index<BN>(db * 32 + l32, kb * 32 + 16 * g + 8 * t));
+          const v8 av = *(const v8*)(Vt + tiling::vt_index<BN>(db * 32 + l32, kb * 32 + 16 * g + 8 * t));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[qb][kb][t], o[qb][db], 0, 0, 0);
+            o[qb][db] = Elem16<T>::mfma(av, p[qb][kb][t], o[qb][db]);
         }
     operand_pipeline<DB * KB * 2 * QB, DB * KB * 2>();
   }
@@ -570,12 +605,12 @@ struct Bf16Wave {
 // therefore runs one tile ahead of V through the double buffers: at step n the
 // buffers hold K(n+1) and V(n) for reading while K(n+2) and V(n+1) are being
 // written into the slots that K(n) and V(n-1) left free.
-template <int D, int BN, int NW, int QB, bool CAUSAL>
-__device__ __forceinline__ void fwd_bf16_item(const FwdArgs& a, const WorkItem& w, __bf16 (&lds_k)[2][BN * D],
-                                              __bf16 (&lds_v)[2][D * BN]) {
+template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
+__device__ __forceinline__ void fwd16_item(const FwdArgs& a, const WorkItem& w, uint16_t (&lds_k)[2][BN * D],
+                                           uint16_t (&lds_v)[2][D * BN]) {
   constexpr int BM = 32 * QB * NW;
-  using Tile = Bf16Tile<D, BN, NW>;
-  using Wave = Bf16Wave<D, BN, QB>;
+  using Tile = Tile16<D, BN, NW>;
+  using Wave = Wave16<T, D, BN, QB>;
   constexpr int KB = Wave::KB;
 
   int n_full, n_end;
@@ -588,21 +623,24 @@ __device__ __forceinline__ void fwd_bf16_item(const FwdArgs& a, const WorkItem& 
   const int shift = w.Lk - w.Lq;
   const int64_t rs = a.row_stride;
 
-  const __bf16* __restrict__ kbase = (const __bf16*)a.k + (int64_t)w.k_start * rs + (int64_t)w.h * D;
-  const __bf16* __restrict__ vbase = (const __bf16*)a.v + (int64_t)w.k_start * rs + (int64_t)w.h * D;
+  // key/value head of this query head; K/V rows hold kv_heads * D elements
+  const int64_t rsk = a.kv_row_stride;
+  const int hk = w.h / a.head_group;
+  const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)hk * D;
+  const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)hk * D;
 
   Wave wv;
   {  // Q rows past the end of the sequence load as zeros
     const int qrows = max(0, min(32 * QB, w.Lq - wrow0));
     const __amdgpu_buffer_rsrc_t rq =
-        buffer_rsrc((const __bf16*)a.q + (int64_t)(w.q_start + wrow0) * rs + (int64_t)w.h * D,
+        buffer_rsrc((const uint16_t*)a.q + (int64_t)(w.q_start + wrow0) * rs + (int64_t)w.h * D,
                     head_rows_bytes(qrows, rs, D, 2));
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int ks = 0; ks < Wave::KSTEPS; ++ks) {
         const uint32_t off = ((uint32_t)(qb * 32 + l32) * (uint32_t)rs + 16 * ks + 8 * g) * 2u;
-        wv.qreg[qb][ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, off));
+        wv.qreg[qb][ks] = __builtin_bit_cast(typename Wave::v8, buffer_load16(rq, off));
       }
   }
 #pragma unroll
@@ -628,12 +666,12 @@ __device__ __forceinline__ void fwd_bf16_item(const FwdArgs& a, const WorkItem& 
   const int arow = key_of_arow(l32);
   Tile tile;
   if (n_end > 0) {
-    tile.load_k(kbase, rs, 0, w.Lk, tid);
-    tile.load_v(vbase, rs, 0, w.Lk, tid);
+    tile.load_k(kbase, rsk, 0, w.Lk, tid);
+    tile.load_v(vbase, rsk, 0, w.Lk, tid);
     tile.store_k(lds_k[0], tid);
     tile.store_v(lds_v[0], tid);
     if (n_end > 1) {
-      tile.load_k(kbase, rs, BN, w.Lk, tid);
+      tile.load_k(kbase, rsk, BN, w.Lk, tid);
       tile.store_k(lds_k[1], tid);
     }
   }
@@ -650,11 +688,11 @@ __device__ __forceinline__ void fwd_bf16_item(const FwdArgs& a, const WorkItem& 
     constexpr bool NEXT = decltype(next_tag)::value;
     const bool more_k = n + 2 < n_end;
     const bool more_v = n + 1 < n_end;
-    if (more_k) tile.load_k(kbase, rs, (n + 2) * BN, w.Lk, tid);
-    if (more_v) tile.load_v(vbase, rs, (n + 1) * BN, w.Lk, tid);
+    if (more_k) tile.load_k(kbase, rsk, (n + 2) * BN, w.Lk, tid);
+    if (more_v) tile.load_v(vbase, rsk, (n + 1) * BN, w.Lk, tid);
     if (n < n_wave) {
       if (n >= n_full) Wave::template mask<CAUSAL>(s_cur, n * BN, wrow0, l32, g, w.Lk, shift);
-      bf16x8 p[QB][KB][2];
+      typename Wave::v8 p[QB][KB][2];
       float alpha[QB];
       if constexpr (NEXT) wv.qk(lds_k[(n + 1) & 1], s_next, arow, g);
       const bool rescale = wv.softmax(s_cur, p, alpha, a.scale_log2);
@@ -679,23 +717,23 @@ __device__ __forceinline__ void fwd_bf16_item(const FwdArgs& a, const WorkItem& 
     step(Last{}, n, s0, s1);
   }
 
-  // ---- epilogue: normalise, write out (bf16) and lse
-  __bf16* __restrict__ op = (__bf16*)a.out;
+  // ---- epilogue: normalise, write out (16-bit, round to nearest even) and lse
+  T* __restrict__ op = (T*)a.out;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int i = wrow0 + qb * 32 + l32;
     const float l = pair_sum(wv.l_run[qb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (i < w.Lq) {
-      __bf16* dst = op + (int64_t)(w.q_start + i) * rs + (int64_t)w.h * D;
+      T* dst = op + (int64_t)(w.q_start + i) * rs + (int64_t)w.h * D;
 #pragma unroll
       for (int db = 0; db < Wave::DB; ++db)
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-          bf16x4 v4;
+          typename Elem16<T>::v4 v4;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(wv.o[qb][db][4 * s4 + c] * inv);
-          *(bf16x4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
+          for (int c = 0; c < 4; ++c) v4[c] = (T)(wv.o[qb][db][4 * s4 + c] * inv);
+          *(typename Elem16<T>::v4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
         }
       if (g == 0)
         a.lse[(int64_t)w.h * a.total_q + w.q_start + i] =
@@ -724,13 +762,13 @@ __device__ __forceinline__ void fwd_bf16_item(const FwdArgs& a, const WorkItem& 
 // into the buffer that V(n-2) left after slot 2n-1.  Each group loads the
 // next tile it stages from global memory right after storing the current one,
 // a slot pair ahead of its use.
-template <int D, int BN, bool CAUSAL>
-__device__ __forceinline__ void fwd_bf16_pingpong_item(const FwdArgs& a, const WorkItem& w,
-                                                       __bf16 (&lds_k)[2][BN * D], __bf16 (&lds_v)[2][D * BN]) {
+template <typename T, int D, int BN, bool CAUSAL>
+__device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const WorkItem& w,
+                                                    uint16_t (&lds_k)[2][BN * D], uint16_t (&lds_v)[2][D * BN]) {
   constexpr int NW = 8;
   constexpr int BM = 32 * NW;
-  using Stage = Bf16GroupStage<D, BN, 4>;  // staging by one group of 4 waves
-  using Wave = Bf16Wave<D, BN, 1>;
+  using Stage = GroupStage16<D, BN, 4>;  // staging by one group of 4 waves
+  using Wave = Wave16<T, D, BN, 1>;
   constexpr int KB = Wave::KB;
 
   int n_full, n_end;
@@ -745,19 +783,22 @@ __device__ __forceinline__ void fwd_bf16_pingpong_item(const FwdArgs& a, const W
   const int shift = w.Lk - w.Lq;
   const int64_t rs = a.row_stride;
 
-  const __bf16* __restrict__ kbase = (const __bf16*)a.k + (int64_t)w.k_start * rs + (int64_t)w.h * D;
-  const __bf16* __restrict__ vbase = (const __bf16*)a.v + (int64_t)w.k_start * rs + (int64_t)w.h * D;
+  // key/value head of this query head; K/V rows hold kv_heads * D elements
+  const int64_t rsk = a.kv_row_stride;
+  const int hk = w.h / a.head_group;
+  const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)hk * D;
+  const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)hk * D;
 
   Wave wv;
   {  // Q rows past the end of the sequence load as zeros
     const int qrows = max(0, min(32, w.Lq - wrow0));
     const __amdgpu_buffer_rsrc_t rq =
-        buffer_rsrc((const __bf16*)a.q + (int64_t)(w.q_start + wrow0) * rs + (int64_t)w.h * D,
+        buffer_rsrc((const uint16_t*)a.q + (int64_t)(w.q_start + wrow0) * rs + (int64_t)w.h * D,
                     head_rows_bytes(qrows, rs, D, 2));
 #pragma unroll
     for (int ks = 0; ks < Wave::KSTEPS; ++ks) {
       const uint32_t off = ((uint32_t)l32 * (uint32_t)rs + 16 * ks + 8 * g) * 2u;
-      wv.qreg[0][ks] = __builtin_bit_cast(bf16x8, buffer_load16(rq, off));
+      wv.qreg[0][ks] = __builtin_bit_cast(typename Wave::v8, buffer_load16(rq, off));
     }
   }
   wv.m_run[0] = kNegInf;
@@ -781,24 +822,24 @@ __device__ __forceinline__ void fwd_bf16_pingpong_item(const FwdArgs& a, const W
   Stage st;
   if (n_end > 0) {
     if (grp == 1) {
-      st.load_k(kbase, rs, 0, w.Lk, gtid);
+      st.load_k(kbase, rsk, 0, w.Lk, gtid);
       st.store_k(lds_k[0], gtid);
-      if (n_end > 1) st.load_k(kbase, rs, BN, w.Lk, gtid);
+      if (n_end > 1) st.load_k(kbase, rsk, BN, w.Lk, gtid);
     } else {
-      st.load_v(vbase, rs, 0, w.Lk, gtid);
+      st.load_v(vbase, rsk, 0, w.Lk, gtid);
     }
   }
   __syncthreads();
   if (grp == 1) {  // group 1's idle first slot: stage K(1)
     if (n_end > 1) {
       st.store_k(lds_k[1], gtid);
-      if (n_end > 2) st.load_k(kbase, rs, 2 * BN, w.Lk, gtid);
+      if (n_end > 2) st.load_k(kbase, rsk, 2 * BN, w.Lk, gtid);
     }
     __syncthreads();
   }
 
   f32x16 s[1][KB];
-  bf16x8 p[1][KB][2];
+  typename Wave::v8 p[1][KB][2];
   for (int n = 0; n <= n_end; ++n) {
     // matrix phase: S(n) = K(n) Q^T and O += V(n-1)^T P(n-1)
     if (n < n_wave) wv.qk_ordered(lds_k[n & 1], s, arow, g);
@@ -814,33 +855,33 @@ __device__ __forceinline__ void fwd_bf16_pingpong_item(const FwdArgs& a, const W
     if (grp == 0) {
       if (n < n_end) {
         st.store_v(lds_v[n & 1], gtid);
-        if (n + 1 < n_end) st.load_v(vbase, rs, (n + 1) * BN, w.Lk, gtid);
+        if (n + 1 < n_end) st.load_v(vbase, rsk, (n + 1) * BN, w.Lk, gtid);
       }
     } else {
       if (n + 2 < n_end) {
         st.store_k(lds_k[n & 1], gtid);
-        if (n + 3 < n_end) st.load_k(kbase, rs, (n + 3) * BN, w.Lk, gtid);
+        if (n + 3 < n_end) st.load_k(kbase, rsk, (n + 3) * BN, w.Lk, gtid);
       }
     }
     __syncthreads();
   }
   if (grp == 0) __syncthreads();  // group 0's idle last slot
 
-  // ---- epilogue: normalise, write out (bf16) and lse
-  __bf16* __restrict__ op = (__bf16*)a.out;
+  // ---- epilogue: normalise, write out (16-bit, round to nearest even) and lse
+  T* __restrict__ op = (T*)a.out;
   const int i = wrow0 + l32;
   const float l = pair_sum(wv.l_run[0]);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (i < w.Lq) {
-    __bf16* dst = op + (int64_t)(w.q_start + i) * rs + (int64_t)w.h * D;
+    T* dst = op + (int64_t)(w.q_start + i) * rs + (int64_t)w.h * D;
 #pragma unroll
     for (int db = 0; db < Wave::DB; ++db)
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        bf16x4 v4;
+        typename Elem16<T>::v4 v4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(wv.o[0][db][4 * s4 + c] * inv);
-        *(bf16x4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
+        for (int c = 0; c < 4; ++c) v4[c] = (T)(wv.o[0][db][4 * s4 + c] * inv);
+        *(typename Elem16<T>::v4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
       }
     if (g == 0)
       a.lse[(int64_t)w.h * a.total_q + w.q_start + i] = l > 0.f ? (wv.m_run[0] + fast_log2(l)) * kLn2 : kNegInf;
@@ -874,24 +915,24 @@ __device__ __forceinline__ void run_work(const FwdArgs& a, WorkItem& w, Item&& i
   }
 }
 
-template <int D, int BN, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * BN];
+template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * BN];
   WorkItem w;
   if (!decode_work(a, w)) return;
   run_work<32 * QB * NW, CAUSAL>(a, w, [&](const WorkItem& wi) {
-    fwd_bf16_item<D, BN, NW, QB, CAUSAL>(a, wi, lds_k, lds_v);
+    fwd16_item<T, D, BN, NW, QB, CAUSAL>(a, wi, lds_k, lds_v);
   });
 }
 
-template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void fwd_bf16_pingpong_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * BN];
+template <typename T, int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void fwd16_pingpong_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * BN];
   WorkItem w;
   if (!decode_work(a, w)) return;
-  run_work<256, CAUSAL>(a, w, [&](const WorkItem& wi) { fwd_bf16_pingpong_item<D, BN, CAUSAL>(a, wi, lds_k, lds_v); });
+  run_work<256, CAUSAL>(a, w, [&](const WorkItem& wi) { fwd16_pingpong_item<T, D, BN, CAUSAL>(a, wi, lds_k, lds_v); });
 }
 
 // ---------------------------------------------------------------------------
@@ -927,8 +968,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdArgs a) {
   const int shift = w.Lk - w.Lq;
   const int i = wrow0 + l32;
 
-  const float* __restrict__ kbase = (const float*)a.k + (int64_t)w.k_start * a.row_stride + (int64_t)w.h * D;
-  const float* __restrict__ vbase = (const float*)a.v + (int64_t)w.k_start * a.row_stride + (int64_t)w.h * D;
+  // key/value head of this query head; K/V rows hold kv_heads * D elements
+  const int hk = w.h / a.head_group;
+  const float* __restrict__ kbase = (const float*)a.k + (int64_t)w.k_start * a.kv_row_stride + (int64_t)hk * D;
+  const float* __restrict__ vbase = (const float*)a.v + (int64_t)w.k_start * a.kv_row_stride + (int64_t)hk * D;
 
   float qreg[D / 2];
   {
@@ -952,8 +995,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdArgs a) {
       const int row = c / (D / 4), ch = c % (D / 4);
       f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
       if (key0 + row < w.Lk) {
-        kx = *(const f32x4*)(kbase + (int64_t)(key0 + row) * a.row_stride + 4 * ch);
-        vx = *(const f32x4*)(vbase + (int64_t)(key0 + row) * a.row_stride + 4 * ch);
+        kx = *(const f32x4*)(kbase + (int64_t)(key0 + row) * a.kv_row_stride + 4 * ch);
+        vx = *(const f32x4*)(vbase + (int64_t)(key0 + row) * a.kv_row_stride + 4 * ch);
       }
       kreg[it] = kx;
       vreg[it] = vx;
@@ -1060,7 +1103,7 @@ hipError_t launch(K kernel, int grid, int block, hipStream_t stream, const FwdAr
 // Tile configuration per (dtype, head_dim): must agree with the kernels above.
 TileConfig tile_config(int dtype, int head_dim) {
   TileConfig c{0, 0, 0};
-  if (dtype == 1) {  // bf16
+  if (dtype == 1 || dtype == 2) {  // bf16, fp16
     if (head_dim == 128) c = TileConfig{256, 64, 512};
     else if (head_dim == 64) c = TileConfig{128, 64, 256};
   } else if (dtype == 0) {  // f32
@@ -1081,14 +1124,22 @@ hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, 
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_fwd16(int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream) {
+  if (head_dim == 128)
+    return causal ? launch(fwd16_pingpong_kernel<T, 128, 64, true>, grid, 512, stream, a)
+                  : launch(fwd16_pingpong_kernel<T, 128, 64, false>, grid, 512, stream, a);
+  if (head_dim == 64)
+    return causal ? launch(fwd16_kernel<T, 64, 64, 4, 1, true>, grid, 256, stream, a)
+                  : launch(fwd16_kernel<T, 64, 64, 4, 1, false>, grid, 256, stream, a);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream) {
   if (dtype == 1) {
-    if (head_dim == 128)
-      return causal ? launch(fwd_bf16_pingpong_kernel<128, 64, true>, grid, 512, stream, a)
-                    : launch(fwd_bf16_pingpong_kernel<128, 64, false>, grid, 512, stream, a);
-    if (head_dim == 64)
-      return causal ? launch(fwd_bf16_kernel<64, 64, 4, 1, true>, grid, 256, stream, a)
-                    : launch(fwd_bf16_kernel<64, 64, 4, 1, false>, grid, 256, stream, a);
+    return launch_fwd16<__bf16>(head_dim, causal, grid, a, stream);
+  } else if (dtype == 2) {
+    return launch_fwd16<_Float16>(head_dim, causal, grid, a, stream);
   } else if (dtype == 0) {
     if (head_dim == 128)
       return causal ? launch(fwd_f32_kernel<128, 4, true>, grid, 256, stream, a)

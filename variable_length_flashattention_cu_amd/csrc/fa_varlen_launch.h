@@ -18,13 +18,15 @@ struct FwdArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   const int32_t* blk_start;
-  int64_t row_stride;  // elements between consecutive tokens: heads * head_dim
+  int64_t row_stride;     // elements between consecutive tokens of q/out: heads * head_dim
+  int64_t kv_row_stride;  // elements between consecutive tokens of k/v: kv_heads * head_dim
   float scale_log2;    // softmax_scale * log2(e)
   int32_t batch;
   int32_t tmax;        // upper bound on work items per head
   int32_t n_work;      // heads * tmax
   int32_t total_q;     // row count of q / columns of lse
   int32_t pair_blocks; // causal: one workgroup takes query blocks m and M-1-m
+  int32_t head_group;  // query heads per key/value head (heads / kv_heads)
 };
 
 struct TileConfig {

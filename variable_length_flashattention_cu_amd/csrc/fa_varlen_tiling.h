@@ -24,8 +24,8 @@ FA_HD int key_of_arow(int R) { return ((R >> 2) & 1) * 16 + (R >> 3) * 4 + (R & 
 
 // XOR swizzles of 16-byte chunks so that the MFMA operand reads from LDS hit
 // distinct banks within each group of 8 and of 16 lanes.
-//   K rows (D bf16 per key row): the chunk index is XORed with bits of the row.
-//   V^T rows (BN bf16 per dimension): the chunk index is XORed with bits of d.
+//   K rows (D 16-bit elements per key row): the chunk index is XORed with bits of the row.
+//   V^T rows (BN elements per dimension): the chunk index is XORed with bits of d.
 template <int D>
 FA_HD int k_swz(int row) {
   if constexpr (D == 128) return (row & 3) | ((row >> 2) & 4) | ((row << 1) & 8);
@@ -37,7 +37,7 @@ FA_HD int v_swz(int d) {
   else return ((d >> 1) & 3) | (((d ^ (d >> 3)) & 1) << 2);
 }
 
-// LDS element index of K chunk `ch` of key row `row` (8 consecutive bf16), and
+// LDS element index of K chunk `ch` of key row `row` (8 consecutive elements), and
 // of key `key` of dimension `d` in V^T (keys 8*(key/8) .. +7 are contiguous).
 template <int D>
 FA_HD int ks_index(int row, int ch) { return row * D + 8 * (ch ^ k_swz<D>(row)); }
@@ -51,11 +51,11 @@ FA_HD uint32_t head_rows_bytes(int rows, int64_t row_stride, int head_dim, int e
   return rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * row_stride + head_dim) * esize) : 0u;
 }
 
-// bf16 tiles: K tile [BN keys][D], staged as 16-byte chunks (8 bf16); V tile
+// 16-bit (bf16 or fp16) tiles: K tile [BN keys][D], staged as 16-byte chunks (8 elements); V tile
 // staged as units of 4 consecutive keys x 8 consecutive dims and written to
 // LDS transposed (V^T, [D][BN]).
 template <int D, int BN, int NW>
-struct Bf16Geom {
+struct Geom16 {
   static constexpr int THREADS = NW * 64;
   static constexpr int K_CHUNKS = BN * D / 8;
   static constexpr int K_PER_THREAD = K_CHUNKS / THREADS;
