@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import glob
 import hashlib
 import json
@@ -42,7 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, Workload, draw_qkv, workload_dense,  # noqa: E402
-                      workload_ragged64k, workload_sweep)
+                      workload_ragged64k, workload_ragged64k_gqa, workload_sweep)
 
 METRIC = "varlen attention fwd TFLOP/s and % of bf16 MFMA peak, d=64/128, causal"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
@@ -84,7 +85,8 @@ def kernel_sha() -> str:
 
 def to_device(wl: Workload, data: dict):
     import torch
-    t = {n: torch.from_numpy(data[n + "_bits"].view(np.int16)).to("cuda").view(torch.bfloat16) for n in "qkv"}
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
+    t = {n: torch.from_numpy(data[n + "_bits"].view(np.int16)).to("cuda").view(tdt) for n in "qkv"}
     t["cu_q"] = torch.tensor(wl.cu_q, dtype=torch.int32, device="cuda")
     t["cu_k"] = torch.tensor(wl.cu_k, dtype=torch.int32, device="cuda")
     H, Tq = wl.heads, wl.total_q
@@ -102,7 +104,7 @@ class Runner:
         self.fa, self.wl, self.t, self.causal = fa, wl, t, causal
         self.lib = fa.load_library()
         self.stream = torch.cuda.current_stream().cuda_stream
-        dt = fa.FA_DTYPE_BF16
+        dt = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16}[wl.dtype]
         self.bm = fa.fa_varlen_block_sizes(wl.head_dim, dt)[0]
         self.blk = fa.fa_varlen_tile_map(t["cu_q"], self.bm)
         self.common = (t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["cu_q"].data_ptr(),
@@ -134,13 +136,13 @@ def time_events(fn, iters: int) -> float:
     return start.elapsed_time(end) / iters
 
 
-def measure_secondary(wl: Workload, iters: int = 20) -> list:
-    """Both mask modes of one workload (inputs drawn once)."""
+def measure_secondary(wl: Workload, iters: int = 20, modes=(False, True)) -> list:
+    """The given mask modes of one workload (inputs drawn once)."""
     data = draw_qkv(wl)
     t = to_device(wl, data)
     del data
     rows = []
-    for causal in (False, True):
+    for causal in modes:
         r = Runner(wl, t, causal)
         for _ in range(3):
             r.step()
@@ -148,7 +150,7 @@ def measure_secondary(wl: Workload, iters: int = 20) -> list:
         kms = time_events(r.kernel_only, iters)
         fl = algorithmic_flops(wl, causal)
         rows.append({"workload": wl.name, "seq_len": wl.max_seqlen_q, "head_dim": wl.head_dim,
-                     "heads": wl.heads, "causal": causal, "ms_per_step": round(ms, 4),
+                     "heads": wl.heads, "kv_heads": wl.kv_heads, "dtype": wl.dtype, "causal": causal, "ms_per_step": round(ms, 4),
                      "tflops": round(fl / ms / 1e9, 1), "kernel_ms": round(kms, 4),
                      "kernel_tflops": round(fl / kms / 1e9, 1),
                      "kernel_frac_bf16_peak": round(fl / kms / 1e9 / PEAK_BF16_TFLOPS, 4)})
@@ -240,7 +242,7 @@ def parse_pmc(fetch_dir: str, write_dir: str) -> dict:
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per_disp = _counter_per_dispatch(d, counter)
         copy_vals = [v for (k, _), v in per_disp.items() if "elementwise" in k.lower()]
-        fwd_vals = [v for (k, _), v in per_disp.items() if "fwd_bf16" in k]
+        fwd_vals = [v for (k, _), v in per_disp.items() if "fwd16_pingpong_kernel" in k]
         if not copy_vals or not fwd_vals:
             raise RuntimeError(f"{counter}: calibration copy or attention dispatches not found in {d}")
         copy_kib = max(copy_vals)
@@ -282,7 +284,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
-              "the forward pass is not sharded across GPUs in this build", file=sys.stderr)
+              "the forward pass runs on one GPU and is not sharded across GPUs", file=sys.stderr)
         return 2
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
@@ -345,7 +347,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": round(traffic["traffic_bytes"]) if traffic else None,
-                     "kernel": "fwd_bf16_pingpong_kernel<128, 64, causal>", "kernel_ms": round(kms, 4),
+                     "kernel": "fwd16_pingpong_kernel<__bf16, 128, 64, causal>", "kernel_ms": round(kms, 4),
                      "algorithmic_bytes": round(algorithmic_bytes(wl))},
     }
     del r, t
@@ -362,6 +364,16 @@ def main() -> int:
         line["sweep_16k_tokens"] = rows
         line["dense_8x2048"] = measure_secondary(workload_dense())
         torch.cuda.empty_cache()
+        # the headline length mix with fp16 inputs, 8 shared key/value heads, head_dim 96
+        base = workload_ragged64k()
+        variants = [dataclasses.replace(base, name=base.name.replace("_h32_", "_h32_f16_"), dtype="f16"),
+                    workload_ragged64k_gqa(),
+                    dataclasses.replace(base, name=base.name.replace("_d128_", "_d96_"), head_dim=96)]
+        line["ragged64k_variants"] = []
+        for v in variants:
+            line["ragged64k_variants"] += measure_secondary(v, modes=(True,))
+            print(f"# {line['ragged64k_variants'][-1]}", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, causal, data)

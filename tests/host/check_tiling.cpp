@@ -117,13 +117,16 @@ static void check_bf16(long H) {
   // --- LDS staging writes: exact cover, in range, aligned
   {
     std::vector<int> kcnt(G::LDS_K, 0), vcnt(G::LDS_V, 0);
-    std::vector<long> vkey(G::LDS_V, -1);
+    std::vector<long> kkey(G::LDS_K, -1), vkey(G::LDS_V, -1);
     for (int tid = 0; tid < G::THREADS; ++tid) {
       for (int i = 0; i < G::K_PER_THREAD; ++i) {
         const int c = tid + i * G::THREADS;
         const int idx = G::ks_index(G::k_row(c), G::k_chunk(c));
         CHECK(idx >= 0 && idx + 8 <= G::LDS_K && idx % 8 == 0, "K LDS index %d", idx);
-        for (int j = 0; j < 8; ++j) kcnt[idx + j]++;
+        for (int j = 0; j < 8; ++j) {
+          kcnt[idx + j]++;
+          kkey[idx + j] = (long)G::k_row(c) * 100000 + G::k_chunk(c) * 8 + j;
+        }
       }
       for (int i = 0; i < G::V_PER_THREAD; ++i) {
         const int w = tid + i * G::THREADS;
@@ -140,7 +143,13 @@ static void check_bf16(long H) {
         }
       }
     }
-    for (int i = 0; i < G::LDS_K; ++i) CHECK(kcnt[i] == 1, "K LDS element %d written %d times", i, kcnt[i]);
+    // every K element once; a row slot wider than D (head_dim 96 in 128) leaves its tail unwritten
+    long kwritten = 0;
+    for (int i = 0; i < G::LDS_K; ++i) {
+      CHECK(kcnt[i] <= 1, "K LDS element %d written %d times", i, kcnt[i]);
+      kwritten += kcnt[i];
+    }
+    CHECK(kwritten == (long)BN * D, "K LDS: %ld elements written, want %d", kwritten, BN * D);
     for (int i = 0; i < G::LDS_V; ++i) CHECK(vcnt[i] == 1, "V LDS element %d written %d times", i, vcnt[i]);
     // --- MFMA operand reads: the elements each lane feeds
     std::set<int> perm;
@@ -157,6 +166,9 @@ static void check_bf16(long H) {
           const int krow = kb * 32 + key_of_arow(l32), ch = 2 * ks + g;
           const int idx = ks_index<D>(krow, ch);
           CHECK(idx >= 0 && idx + 8 <= G::LDS_K && (idx * 2) % 16 == 0, "K operand read %d", idx);
+          for (int e = 0; e < 8; ++e)
+            CHECK(kkey[idx + e] == (long)krow * 100000 + ch * 8 + e, "K operand element (%d,%d) is wrong", krow,
+                  ch * 8 + e);
         }
       for (int d0 = 0; d0 < D; d0 += 32)
         for (int kb = 0; kb < BN / 32; ++kb)
@@ -244,11 +256,13 @@ int main() {
   for (long H : {1L, 3L, 16L}) {
     check_bf16<128, 64, 8>(H);
     check_bf16<128, 64, 4>(H);
+    check_bf16<96, 64, 4>(H);
     check_bf16<64, 64, 4>(H);
     check_bf16<64, 64, 8>(H);
     check_bf16<64, 128, 4>(H);
   }
   check_f32<64, 4>();
+  check_f32<96, 4>();
   check_f32<128, 4>();
   if (g_fail) {
     std::fprintf(stderr, "%d violations\n", g_fail);

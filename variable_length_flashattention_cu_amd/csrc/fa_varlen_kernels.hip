@@ -7,8 +7,9 @@
 //                              iplexlaw.co.kr "FlashAttention-2 GPU work
 //                              partitioning", section "Tres mejoras en la
 //                              utilización de la GPU").
-//   * fwd16_pingpong_kernel -- 16-bit (bf16 or fp16) in/out, head_dim 128: two
-//                              wave groups alternate MFMA and softmax phases.
+//   * fwd16_pingpong_kernel -- 16-bit (bf16 or fp16) in/out, head_dim 96 and
+//                              128: two wave groups alternate MFMA and softmax
+//                              phases.
 //   * fwd16_kernel          -- 16-bit in/out, head_dim 64: one wave group with
 //                              a software pipeline inside each wave.
 //                              Both use 16-bit MFMA for the two contractions
@@ -606,7 +607,8 @@ struct Wave16 {
 // buffers hold K(n+1) and V(n) for reading while K(n+2) and V(n+1) are being
 // written into the slots that K(n) and V(n-1) left free.
 template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
-__device__ __forceinline__ void fwd16_item(const FwdArgs& a, const WorkItem& w, uint16_t (&lds_k)[2][BN * D],
+__device__ __forceinline__ void fwd16_item(const FwdArgs& a, const WorkItem& w,
+                                           uint16_t (&lds_k)[2][BN * tiling::k_stride<D>()],
                                            uint16_t (&lds_v)[2][D * BN]) {
   constexpr int BM = 32 * QB * NW;
   using Tile = Tile16<D, BN, NW>;
@@ -764,7 +766,8 @@ __device__ __forceinline__ void fwd16_item(const FwdArgs& a, const WorkItem& w, 
 // a slot pair ahead of its use.
 template <typename T, int D, int BN, bool CAUSAL>
 __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const WorkItem& w,
-                                                    uint16_t (&lds_k)[2][BN * D], uint16_t (&lds_v)[2][D * BN]) {
+                                                    uint16_t (&lds_k)[2][BN * tiling::k_stride<D>()],
+                                                    uint16_t (&lds_v)[2][D * BN]) {
   constexpr int NW = 8;
   constexpr int BM = 32 * NW;
   using Stage = GroupStage16<D, BN, 4>;  // staging by one group of 4 waves
@@ -917,7 +920,7 @@ __device__ __forceinline__ void run_work(const FwdArgs& a, WorkItem& w, Item&& i
 
 template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * tiling::k_stride<D>()];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * BN];
   WorkItem w;
   if (!decode_work(a, w)) return;
@@ -928,7 +931,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(FwdArgs a) {
 
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void fwd16_pingpong_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * tiling::k_stride<D>()];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * BN];
   WorkItem w;
   if (!decode_work(a, w)) return;
@@ -1104,10 +1107,10 @@ hipError_t launch(K kernel, int grid, int block, hipStream_t stream, const FwdAr
 TileConfig tile_config(int dtype, int head_dim) {
   TileConfig c{0, 0, 0};
   if (dtype == 1 || dtype == 2) {  // bf16, fp16
-    if (head_dim == 128) c = TileConfig{256, 64, 512};
+    if (head_dim == 128 || head_dim == 96) c = TileConfig{256, 64, 512};
     else if (head_dim == 64) c = TileConfig{128, 64, 256};
   } else if (dtype == 0) {  // f32
-    if (head_dim == 128 || head_dim == 64) c = TileConfig{128, 32, 256};
+    if (head_dim == 128 || head_dim == 96 || head_dim == 64) c = TileConfig{128, 32, 256};
   }
   return c;
 }
@@ -1129,6 +1132,9 @@ hipError_t launch_fwd16(int head_dim, bool causal, int grid, const FwdArgs& a, h
   if (head_dim == 128)
     return causal ? launch(fwd16_pingpong_kernel<T, 128, 64, true>, grid, 512, stream, a)
                   : launch(fwd16_pingpong_kernel<T, 128, 64, false>, grid, 512, stream, a);
+  if (head_dim == 96)
+    return causal ? launch(fwd16_pingpong_kernel<T, 96, 64, true>, grid, 512, stream, a)
+                  : launch(fwd16_pingpong_kernel<T, 96, 64, false>, grid, 512, stream, a);
   if (head_dim == 64)
     return causal ? launch(fwd16_kernel<T, 64, 64, 4, 1, true>, grid, 256, stream, a)
                   : launch(fwd16_kernel<T, 64, 64, 4, 1, false>, grid, 256, stream, a);
@@ -1144,6 +1150,9 @@ hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdA
     if (head_dim == 128)
       return causal ? launch(fwd_f32_kernel<128, 4, true>, grid, 256, stream, a)
                     : launch(fwd_f32_kernel<128, 4, false>, grid, 256, stream, a);
+    if (head_dim == 96)
+      return causal ? launch(fwd_f32_kernel<96, 4, true>, grid, 256, stream, a)
+                    : launch(fwd_f32_kernel<96, 4, false>, grid, 256, stream, a);
     if (head_dim == 64)
       return causal ? launch(fwd_f32_kernel<64, 4, true>, grid, 256, stream, a)
                     : launch(fwd_f32_kernel<64, 4, false>, grid, 256, stream, a);

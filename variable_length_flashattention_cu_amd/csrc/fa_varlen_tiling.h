@@ -37,10 +37,19 @@ FA_HD int v_swz(int d) {
   else return ((d >> 1) & 3) | (((d ^ (d >> 3)) & 1) << 2);
 }
 
+// Elements per K row in LDS: head_dim 96 rows (12 chunks) are kept in slots of
+// 128 elements so that they use the 16-chunk swizzle of head_dim 128 (the
+// last 4 chunks of a slot stay unused).
+template <int D>
+constexpr int k_stride() { return D == 96 ? 128 : D; }
+
 // LDS element index of K chunk `ch` of key row `row` (8 consecutive elements), and
 // of key `key` of dimension `d` in V^T (keys 8*(key/8) .. +7 are contiguous).
 template <int D>
-FA_HD int ks_index(int row, int ch) { return row * D + 8 * (ch ^ k_swz<D>(row)); }
+FA_HD int ks_index(int row, int ch) {
+  constexpr int KS = k_stride<D>();
+  return row * KS + 8 * (ch ^ k_swz<KS>(row));
+}
 template <int BN>
 FA_HD int vt_index(int d, int key) { return d * BN + 8 * ((key >> 3) ^ v_swz<BN>(d)) + (key & 7); }
 
@@ -62,7 +71,7 @@ struct Geom16 {
   static constexpr int V_UNITS = (BN / 4) * (D / 8);
   static constexpr int V_PER_THREAD = (V_UNITS + THREADS - 1) / THREADS;
   static constexpr bool V_GUARD = (V_UNITS % THREADS) != 0;  // some threads own no unit
-  static constexpr int LDS_K = BN * D;                       // elements per K buffer
+  static constexpr int LDS_K = BN * k_stride<D>();           // elements per K buffer
   static constexpr int LDS_V = D * BN;                       // elements per V^T buffer
   static_assert(K_CHUNKS % THREADS == 0, "K tile/threads mismatch");
   static_assert(!V_GUARD || V_PER_THREAD == 1, "V units must fill the threads evenly or cover a prefix");
