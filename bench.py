@@ -364,11 +364,13 @@ def main() -> int:
         line["sweep_16k_tokens"] = rows
         line["dense_8x2048"] = measure_secondary(workload_dense())
         torch.cuda.empty_cache()
-        # the headline length mix with fp16 inputs, 8 shared key/value heads, head_dim 96
+        # the headline length mix with fp16 inputs, 8 shared key/value heads, head_dim 96 and 256
         base = workload_ragged64k()
         variants = [dataclasses.replace(base, name=base.name.replace("_h32_", "_h32_f16_"), dtype="f16"),
                     workload_ragged64k_gqa(),
-                    dataclasses.replace(base, name=base.name.replace("_d128_", "_d96_"), head_dim=96)]
+                    dataclasses.replace(base, name=base.name.replace("_d128_", "_d96_"), head_dim=96),
+                    dataclasses.replace(base, name=base.name.replace("_h32_d128_", "_h16_d256_"), heads=16,
+                                        head_dim=256)]
         line["ragged64k_variants"] = []
         for v in variants:
             line["ragged64k_variants"] += measure_secondary(v, modes=(True,))

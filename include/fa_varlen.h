@@ -72,7 +72,7 @@ typedef enum fa_status {
   FA_ERR_DTYPE = 2,      /* dtype is not an fa_dtype */
   FA_ERR_SHAPE = 3,      /* negative size, zero heads, num_heads_k not dividing
                             num_heads, or max_seqlen > rows */
-  FA_ERR_HEAD_DIM = 4,   /* head_dim not supported (64, 96 and 128 are) */
+  FA_ERR_HEAD_DIM = 4,   /* head_dim not supported for this dtype (64, 96, 128; 256 for bf16/fp16) */
   FA_ERR_ALIGN = 5,      /* a pointer is not aligned as documented */
   FA_ERR_ARG = 6,        /* softmax_scale not finite and > 0, causal not 0/1, bad block_m */
   FA_ERR_HIP = 7,        /* the HIP runtime reported an error (no device, launch failure) */
@@ -138,8 +138,9 @@ int fa_varlen_tile_map(const int32_t* cu_seqlens_q, int32_t batch, int32_t block
  * otherwise); 16-bit inputs are multiplied on the matrix cores with float32
  * accumulation, the probabilities are rounded to the input type before the
  * second product and the output is rounded to nearest even.
- * head_dim must be 64, 96 or 128 (FA_ERR_HEAD_DIM otherwise).  q, k, v and out
- * must be 16-byte aligned, lse and cu_seqlens 4-byte aligned (the offsets
+ * head_dim must be 64, 96 or 128, or 256 with bf16 or fp16 inputs
+ * (FA_ERR_HEAD_DIM otherwise).  q, k, v and out must be 16-byte aligned,
+ * lse and cu_seqlens 4-byte aligned (the offsets
  * are best kept 32-byte aligned, as any hipMalloc'd buffer is).
  * Scratch: a (batch+1)-entry int32 work-item map is allocated and freed
  * stream-ordered (hipMallocAsync / hipFreeAsync) on `stream`.

@@ -257,6 +257,7 @@ int main() {
     check_bf16<128, 64, 8>(H);
     check_bf16<128, 64, 4>(H);
     check_bf16<96, 64, 4>(H);
+    check_bf16<256, 32, 4>(H);
     check_bf16<64, 64, 4>(H);
     check_bf16<64, 64, 8>(H);
     check_bf16<64, 128, 4>(H);

@@ -48,9 +48,13 @@ def test_block_sizes():
         for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16):
             bm, bn = fa.fa_varlen_block_sizes(d, dt)
             assert bm > 0 and bn > 0 and bm % 32 == 0 and bn % 32 == 0
-    with pytest.raises(fa.FaVarlenError) as e:
-        fa.fa_varlen_block_sizes(80, fa.FA_DTYPE_BF16)
-    assert e.value.status == 4
+    for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16):
+        bm, bn = fa.fa_varlen_block_sizes(256, dt)
+        assert bm > 0 and bn > 0 and bm % 32 == 0 and bn % 32 == 0
+    for d, dt in ((80, fa.FA_DTYPE_BF16), (256, fa.FA_DTYPE_F32), (512, fa.FA_DTYPE_BF16)):
+        with pytest.raises(fa.FaVarlenError) as e:
+            fa.fa_varlen_block_sizes(d, dt)
+        assert e.value.status == 4
     with pytest.raises(fa.FaVarlenError) as e:
         fa.fa_varlen_block_sizes(64, 7)
     assert e.value.status == 2
@@ -92,7 +96,8 @@ def call_mapped(**over):
     (dict(out=None), 1), (dict(lse=None), 1),
     (dict(dtype=3), 2), (dict(dtype=-1), 2),
     (dict(heads_k=0), 3), (dict(heads_k=3), 3), (dict(heads=4, heads_k=3), 3), (dict(heads_k=-2), 3),
-    (dict(head_dim=80), 4), (dict(head_dim=256), 4), (dict(head_dim=0), 4), (dict(head_dim=32), 4),
+    (dict(head_dim=80), 4), (dict(head_dim=256, dtype=0), 4), (dict(head_dim=512), 4), (dict(head_dim=0), 4),
+    (dict(head_dim=32), 4),
     (dict(batch=-1), 3), (dict(total_q=-1), 3), (dict(heads=0), 3), (dict(max_q=9), 3), (dict(max_k=9), 3),
     (dict(max_q=-1), 3),
     (dict(scale=0.0), 6), (dict(scale=-1.0), 6), (dict(scale=math.inf), 6), (dict(scale=math.nan), 6),
@@ -104,11 +109,11 @@ def test_fwd_validation(call, over, code):
     assert call(**over) == code
 
 
-def test_shared_kv_heads_f16_and_d96_pass_validation():
+def test_shared_kv_heads_dtypes_and_head_dims_pass_validation():
     # valid groupings, dtypes and head dims reach the empty-problem early exit: FA_OK, nothing launched
     for heads, heads_k in ((8, 1), (8, 2), (8, 4), (8, 8), (6, 3)):
         for dtype in (0, 1, 2):
-            for head_dim in (64, 96, 128):
+            for head_dim in (64, 96, 128) if dtype == 0 else (64, 96, 128, 256):
                 assert call_fwd(heads=heads, heads_k=heads_k, dtype=dtype, head_dim=head_dim, total_q=0,
                                 max_q=0) == 0
 

@@ -119,8 +119,9 @@ EDGE = [
 
 
 @pytest.mark.parametrize("name,lq,lk", EDGE, ids=[e[0] for e in EDGE])
-@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 96), ("bf16", 128), ("f16", 64), ("f16", 96),
-                                            ("f16", 128), ("f32", 64), ("f32", 96), ("f32", 128)])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 96), ("bf16", 128), ("bf16", 256), ("f16", 64),
+                                            ("f16", 96), ("f16", 128), ("f16", 256), ("f32", 64), ("f32", 96),
+                                            ("f32", 128)])
 def test_edge_cases(fa, name, lq, lk, dtype, head_dim):
     wl = workload_custom(f"{name}_{dtype}_d{head_dim}", lq, lk, 3, head_dim, dtype, seed=len(name) + head_dim)
     for causal in (False, True):
@@ -235,8 +236,8 @@ GQA = [(8, 1), (8, 2), (8, 4), (6, 3), (4, 4)]
 
 
 @pytest.mark.parametrize("heads,heads_k", GQA, ids=[f"h{h}kv{k}" for h, k in GQA])
-@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 96), ("bf16", 128), ("f16", 128), ("f32", 64),
-                                            ("f32", 128)])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 96), ("bf16", 128), ("bf16", 256), ("f16", 128),
+                                            ("f32", 64), ("f32", 128)])
 def test_shared_kv_heads(fa, heads, heads_k, dtype, head_dim):
     wl = workload_custom(f"gqa_h{heads}_kv{heads_k}_{dtype}_d{head_dim}", [300, 0, 129, 700], [280, 5, 200, 700],
                          heads, head_dim, dtype, seed=heads * 10 + heads_k, heads_k=heads_k)
@@ -265,3 +266,20 @@ def test_ragged64k_d96_sampled(fa):
     wl = workload_custom("ragged64k_h32_d96", base.lengths_q, None, 32, 96, "bf16", seed=8)
     for causal in (False, True):
         sampled_parity(fa, wl, causal, [0, 13, 31], seed=8)
+
+
+# ---------------------------------------------------------------- head_dim 256
+def test_ragged_qk_d256(fa):
+    base = workload_ragged_qk()
+    for dtype in ("bf16", "f16"):
+        wl = workload_custom(f"ragged_qk_h12_d256_{dtype}", base.lengths_q, base.lengths_k, 12, 256, dtype, seed=9)
+        for causal in (False, True):
+            full_parity(fa, wl, causal)
+
+
+def test_ragged64k_d256_sampled(fa):
+    """The headline length mix (64k tokens) at head_dim 256 with 16 heads."""
+    base = workload_ragged64k()
+    wl = workload_custom("ragged64k_h16_d256", base.lengths_q, None, 16, 256, "bf16", seed=10)
+    for causal in (False, True):
+        sampled_parity(fa, wl, causal, [0, 7, 15], seed=10)

@@ -100,7 +100,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE:
       return "invalid sizes (negative, zero heads, key/value heads not dividing the query heads, or max_seqlen "
              "above the row count)";
-    case FA_ERR_HEAD_DIM: return "unsupported head_dim (64, 96 and 128 are supported)";
+    case FA_ERR_HEAD_DIM: return "unsupported head_dim (64, 96, 128; 256 with bf16/fp16)";
     case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse and offsets 4 bytes)";
     case FA_ERR_ARG: return "invalid argument (softmax_scale must be finite and > 0, causal 0 or 1, block_m 1..4096)";
     case FA_ERR_HIP: return "HIP runtime error";

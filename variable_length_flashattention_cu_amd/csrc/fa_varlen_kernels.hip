@@ -441,9 +441,9 @@ struct GroupStage16 : tiling::Geom16<D, BN, NW> {
 // Scheduling order of a block of NM MFMAs fed by NR LDS operand reads: the
 // first PRE reads, then one MFMA and one read alternately, then the
 // remaining MFMAs, so that PRE reads are in flight ahead of their use.
-template <int NM, int NR>
+template <int NM, int NR, int AHEAD = 8>
 __device__ __forceinline__ void operand_pipeline() {
-  constexpr int PRE = NR < 8 ? NR : 8;
+  constexpr int PRE = NR < AHEAD ? NR : AHEAD;
   __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);  // LDS reads
 #pragma unroll
   for (int i = 0; i < NR - PRE; ++i) {
@@ -460,6 +460,7 @@ struct Wave16 {
   static constexpr int KSTEPS = D / 16;  // MFMA k-steps for Q K^T
   static constexpr int KB = BN / 32;     // 32-key blocks per tile
   static constexpr int DB = D / 32;      // 32-dim blocks of the output
+  static constexpr int AHEAD = D > 128 ? 4 : 8;  // operand reads in flight (registers at D=256)
 
   v8 qreg[QB][KSTEPS];  // Q^T as the B operand
   f32x16 o[QB][DB];         // O^T accumulators
@@ -499,7 +500,7 @@ struct Wave16 {
         }
       }
     }
-    operand_pipeline<KSTEPS * KB * QB, KSTEPS * KB>();
+    operand_pipeline<KSTEPS * KB * QB, KSTEPS * KB, AHEAD>();
   }
 
   // -inf for keys past the end of the sequence or (causal) above the diagonal
@@ -597,7 +598,7 @@ struct Wave16 {
           for (int qb = 0; qb < QB; ++qb)
             o[qb][db] = Elem16<T>::mfma(av, p[qb][kb][t], o[qb][db]);
         }
-    operand_pipeline<DB * KB * 2 * QB, DB * KB * 2>();
+    operand_pipeline<DB * KB * 2 * QB, DB * KB * 2, AHEAD>();
   }
 };
 
@@ -1108,6 +1109,7 @@ TileConfig tile_config(int dtype, int head_dim) {
   TileConfig c{0, 0, 0};
   if (dtype == 1 || dtype == 2) {  // bf16, fp16
     if (head_dim == 128 || head_dim == 96) c = TileConfig{256, 64, 512};
+    else if (head_dim == 256) c = TileConfig{256, 32, 512};
     else if (head_dim == 64) c = TileConfig{128, 64, 256};
   } else if (dtype == 0) {  // f32
     if (head_dim == 128 || head_dim == 96 || head_dim == 64) c = TileConfig{128, 32, 256};
@@ -1135,6 +1137,9 @@ hipError_t launch_fwd16(int head_dim, bool causal, int grid, const FwdArgs& a, h
   if (head_dim == 96)
     return causal ? launch(fwd16_pingpong_kernel<T, 96, 64, true>, grid, 512, stream, a)
                   : launch(fwd16_pingpong_kernel<T, 96, 64, false>, grid, 512, stream, a);
+  if (head_dim == 256)
+    return causal ? launch(fwd16_pingpong_kernel<T, 256, 32, true>, grid, 512, stream, a)
+                  : launch(fwd16_pingpong_kernel<T, 256, 32, false>, grid, 512, stream, a);
   if (head_dim == 64)
     return causal ? launch(fwd16_kernel<T, 64, 64, 4, 1, true>, grid, 256, stream, a)
                   : launch(fwd16_kernel<T, 64, 64, 4, 1, false>, grid, 256, stream, a);

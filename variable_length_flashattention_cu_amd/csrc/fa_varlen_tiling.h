@@ -26,14 +26,18 @@ FA_HD int key_of_arow(int R) { return ((R >> 2) & 1) * 16 + (R >> 3) * 4 + (R & 
 // distinct banks within each group of 8 and of 16 lanes.
 //   K rows (D 16-bit elements per key row): the chunk index is XORed with bits of the row.
 //   V^T rows (BN elements per dimension): the chunk index is XORed with bits of d.
+//   A row of 256 elements spans the 64 banks twice, so its chunks fall on the
+//   same bank groups as those of a 128-element row and it uses the same swizzle
+//   (which only touches the low 4 bits of the chunk index).
 template <int D>
 FA_HD int k_swz(int row) {
-  if constexpr (D == 128) return (row & 3) | ((row >> 2) & 4) | ((row << 1) & 8);
+  if constexpr (D == 128 || D == 256) return (row & 3) | ((row >> 2) & 4) | ((row << 1) & 8);
   else return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 2) & 4);
 }
 template <int BN>
 FA_HD int v_swz(int d) {
   if constexpr (BN == 128) return d & 15;
+  else if constexpr (BN == 32) return (d >> 2) & 3;
   else return ((d >> 1) & 3) | (((d ^ (d >> 3)) & 1) << 2);
 }
 
