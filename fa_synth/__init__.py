@@ -47,6 +47,7 @@ __all__ = [
     "workload_ragged64k_gqa",
     "all_parity_workloads",
     "draw_qkv",
+    "draw_dout",
     "SWEEP_SEQLENS",
     "SWEEP_HEAD_DIMS",
 ]
@@ -238,6 +239,24 @@ def workload_ragged64k_gqa(seed: int = 4, total: int = 65536, heads_k: int = 8) 
     """The ragged 64k batch with 32 query heads sharing ``heads_k`` key/value heads."""
     base = workload_ragged64k(seed, total)
     return dataclasses.replace(base, name=f"ragged64k_h32_kv{heads_k}_d128_causal_seed{seed}", heads_k=heads_k)
+
+
+def draw_dout(wl: Workload) -> dict:
+    """Output gradient for the backward pass: standard normal [total_q, heads,
+    head_dim] from its own stream (seed + 7919, so Q, K and V are unchanged),
+    rounded to the workload's type like the inputs.  Returns ``dout`` (float32)
+    and, for 16-bit types, ``dout_bits``."""
+    rng = np.random.default_rng(wl.seed + 7919)
+    shape = (wl.total_q, wl.heads, wl.head_dim)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    rounders = {"bf16": (bf16_rne_bits, bf16_bits_to_f32), "f16": (f16_rne_bits, f16_bits_to_f32)}
+    if wl.dtype in rounders:
+        to_bits, to_f32 = rounders[wl.dtype]
+        bits = to_bits(x).reshape(shape)
+        return {"dout": to_f32(bits).reshape(shape), "dout_bits": bits}
+    if wl.dtype != "f32":
+        raise ValueError(wl.dtype)
+    return {"dout": x}
 
 
 def all_parity_workloads() -> List[Workload]:

@@ -10,6 +10,8 @@ Contents
   * :mod:`oracle.cu_seqlens`     -- lengths and row offsets from cumulative offsets
   * :mod:`oracle.tile_map`       -- the flat (sequence, q-block) work-item map
   * :mod:`oracle.attention`      -- materialised fp64 attention (the definition)
+  * :mod:`oracle.attention_grad` -- its gradients dq, dk, dv (chain rule on the
+    materialised matrices)
   * :mod:`oracle.online_softmax` -- fp64 tile-by-tile emulation of the online
     softmax, used only to pin the claim that rescaled running statistics give
     the global softmax
@@ -20,6 +22,7 @@ on the pages, closed forms, invariants, brute force and a library routine.
 from .cu_seqlens import lengths_from_cu, check_cu_seqlens, row_offset
 from .tile_map import tile_map, tile_items
 from .attention import attention_fwd, attention_rows, visible_mask, flops_visible_pairs, kv_head_of
+from .attention_grad import attention_bwd, attention_loss
 from .online_softmax import online_softmax_attention, blockwise_normalised_attention
 
 __all__ = [
@@ -33,6 +36,8 @@ __all__ = [
     "visible_mask",
     "flops_visible_pairs",
     "kv_head_of",
+    "attention_bwd",
+    "attention_loss",
     "online_softmax_attention",
     "blockwise_normalised_attention",
 ]

@@ -83,3 +83,14 @@ def test_gqa_and_f16_workloads():
     import pytest
     with pytest.raises(ValueError):
         workload_custom("bad", [4], None, 6, 64, "bf16", 0, heads_k=4)
+
+
+def test_dout_is_seeded_rounded_and_separate_from_qkv():
+    from fa_synth import bf16_bits_to_f32, draw_dout
+    wl = workload_ragged_qk()
+    a, b = draw_dout(wl), draw_dout(wl)
+    assert np.array_equal(a["dout_bits"], b["dout_bits"])
+    assert np.array_equal(bf16_bits_to_f32(a["dout_bits"]).reshape(a["dout"].shape), a["dout"])
+    qkv = draw_qkv(wl)
+    assert a["dout"].shape == qkv["q"].shape and not np.array_equal(a["dout"], qkv["q"])
+    assert abs(float(a["dout"].std()) - 1.0) < 0.02
