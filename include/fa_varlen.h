@@ -1,6 +1,7 @@
 /*
- * fa_varlen.h -- C ABI of libfa_varlen.so: exact attention forward over packed
- * variable-length sequences on AMD Instinct MI355X (gfx950).
+ * fa_varlen.h -- C ABI of libfa_varlen.so: exact attention over packed
+ * variable-length sequences on AMD Instinct MI355X (gfx950), forward pass
+ * and backward pass.
  *
  * The operation (FlashAttention pages):
  *   * Sequences are packed back to back with no padding and addressed by
@@ -53,6 +54,7 @@
 #ifndef FA_VARLEN_H_
 #define FA_VARLEN_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -76,7 +78,8 @@ typedef enum fa_status {
   FA_ERR_ALIGN = 5,      /* a pointer is not aligned as documented */
   FA_ERR_ARG = 6,        /* softmax_scale not finite and > 0, causal not 0/1, bad block_m */
   FA_ERR_HIP = 7,        /* the HIP runtime reported an error (no device, launch failure) */
-  FA_ERR_TOO_LARGE = 8   /* the launch grid would exceed 2^31 workgroups */
+  FA_ERR_TOO_LARGE = 8,  /* the launch grid would exceed 2^31 workgroups */
+  FA_ERR_WORKSPACE = 9   /* backward workspace NULL or smaller than fa_varlen_bwd_workspace_size */
 } fa_status;
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -172,6 +175,62 @@ int fa_varlen_fwd_mapped(const void* q, const void* k, const void* v,
                          int32_t batch, int32_t total_q, int32_t total_k,
                          int32_t num_heads, int32_t num_heads_k, int32_t head_dim, int32_t dtype,
                          const int32_t* blk_start, void* stream);
+
+/*
+ * Backward pass: gradients of the attention of fa_varlen_fwd with respect to
+ * q, k and v, given the gradient dout of its output.
+ *
+ * What is computed (the derivative of the forward definition): per sequence
+ * and query head, with P the attention probabilities,
+ *   dv = P^T dout,  dP = dout v^T,  dS = P * (dP - rowsum(dout * out)),
+ *   dq = softmax_scale * dS k,  dk = softmax_scale * dS^T q;
+ * a key/value head shared by several query heads receives the sum of their
+ * dk and dv.  How the pass is organised follows the pages (zepes.com,
+ * "Comprendiendo Flash-Atención y Flash-Atención-2", section "FashAttention
+ * v1" (sic)): workers own blocks of key columns, recompute P from the forward
+ * pass's lse instead of storing it, and add their parts of dq with atomic
+ * operations.
+ *
+ *   q, k, v, cu_seqlens_*, max_seqlen_*, softmax_scale, causal, sizes
+ *                 exactly as passed to fa_varlen_fwd
+ *   out, lse      the outputs of that fa_varlen_fwd call (out [total_q,
+ *                 num_heads, head_dim] dtype, lse float32 [num_heads,
+ *                 total_q])
+ *   dout          device [total_q, num_heads, head_dim], dtype
+ *   dq            device [total_q, num_heads, head_dim], dtype; written for
+ *                 rows < cu_seqlens_q[batch] (rows that see no key get 0)
+ *   dk, dv        device [total_k, num_heads_k, head_dim], dtype; written
+ *                 for rows < cu_seqlens_k[batch] (keys no query sees get 0)
+ *   workspace     device scratch of at least workspace_bytes >=
+ *                 fa_varlen_bwd_workspace_size(...) bytes, 16-byte aligned,
+ *                 owned by the caller; its contents on entry do not matter
+ *                 and are undefined afterwards.  Calls that run at the same
+ *                 time need separate workspaces.
+ * dtype must be FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_ERR_DTYPE otherwise) and
+ * head_dim 64 or 128 (FA_ERR_HEAD_DIM otherwise); products use the 16-bit
+ * MFMA with float32 accumulation, P and dS are rounded to dtype before they
+ * enter a product, dq is summed in float32.  Because dq is accumulated with
+ * atomic additions, its low bits may differ from run to run.
+ * NULL, size, alignment and argument checks as for fa_varlen_fwd; dout, dq,
+ * dk and dv need 16 bytes.  A workspace that is NULL or too small gives
+ * FA_ERR_WORKSPACE.
+ */
+int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                  const float* lse, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                  void* dq, void* dk, void* dv, int32_t batch, int32_t total_q, int32_t total_k,
+                  int32_t num_heads, int32_t num_heads_k, int32_t head_dim, int32_t dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace fa_varlen_bwd needs for these sizes: a float32 dq
+ * accumulator [total_q, num_heads, head_dim], the float32 row terms
+ * rowsum(dout * out) [num_heads, total_q] and the key-block map
+ * [batch + 1], each rounded up to 256 bytes.  Host only.
+ * Returns FA_ERR_NULL or FA_ERR_SHAPE on bad arguments.
+ */
+int fa_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t num_heads, int32_t head_dim,
+                                 size_t* bytes);
 
 /*
  * Device-side check of the cu_seqlens preconditions (friki.work, section

@@ -258,6 +258,11 @@ int main() {
     check_bf16<128, 64, 4>(H);
     check_bf16<96, 64, 4>(H);
     check_bf16<256, 32, 4>(H);
+    // backward: 32-row query blocks (row-major and transposed) and the
+    // transposed 128-key K block
+    check_bf16<128, 32, 4>(H);
+    check_bf16<64, 32, 4>(H);
+    check_bf16<128, 128, 4>(H);
     check_bf16<64, 64, 4>(H);
     check_bf16<64, 64, 8>(H);
     check_bf16<64, 128, 4>(H);

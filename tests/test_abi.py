@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["fa_status_string", "fa_varlen_block_sizes", "fa_varlen_tile_map",
-                            "fa_varlen_fwd", "fa_varlen_fwd_mapped", "fa_varlen_check_cu_seqlens"])
+                            "fa_varlen_fwd", "fa_varlen_fwd_mapped", "fa_varlen_check_cu_seqlens",
+                            "fa_varlen_bwd", "fa_varlen_bwd_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         s = fa.fa_status_string(code)
         assert isinstance(s, str) and s
     assert fa.fa_status_string(12345) == "unknown status"
@@ -165,3 +166,54 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
         fa.load_library()
     with pytest.raises(fa.FaVarlenError, match="not built"):
         fa.fa_varlen_block_sizes(64, 1)
+
+
+# ---------------------------------------------------------------- backward
+WS = 1 << 20
+
+
+def call_bwd(**over):
+    args = dict(q=A16, k=A16, v=A16, out=A16, dout=A16, lse=A16, cu_q=A16, cu_k=A16, max_q=8, max_k=8,
+                scale=0.125, causal=0, dq=A16, dk=A16, dv=A16, batch=1, total_q=8, total_k=8, heads=2,
+                heads_k=2, head_dim=64, dtype=1, ws=A16, ws_bytes=WS)
+    args.update(over)
+    lib = fa.load_library()
+    return lib.fa_varlen_bwd(args["q"], args["k"], args["v"], args["out"], args["dout"], args["lse"],
+                             args["cu_q"], args["cu_k"], args["max_q"], args["max_k"], args["scale"],
+                             args["causal"], args["dq"], args["dk"], args["dv"], args["batch"], args["total_q"],
+                             args["total_k"], args["heads"], args["heads_k"], args["head_dim"], args["dtype"],
+                             args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(lse=None), 1), (dict(dout=None), 1), (dict(dq=None), 1),
+    (dict(dk=None), 1), (dict(dv=None), 1), (dict(cu_k=None), 1),
+    (dict(dtype=0), 2), (dict(dtype=3), 2),
+    (dict(head_dim=96), 4), (dict(head_dim=256), 4), (dict(head_dim=80), 4),
+    (dict(heads_k=3), 3), (dict(max_q=9), 3), (dict(batch=-1), 3),
+    (dict(scale=0.0), 6), (dict(causal=2), 6),
+    (dict(dout=A16 + 8), 5), (dict(dq=A16 + 2), 5), (dict(dk=A16 + 4), 5), (dict(dv=A16 + 8), 5),
+    (dict(ws=A16 + 8), 5),
+    (dict(ws=None), 9), (dict(ws_bytes=100), 9), (dict(ws_bytes=0), 9),
+])
+def test_bwd_validation(over, code):
+    assert call_bwd(**over) == code
+
+
+def test_bwd_workspace_size():
+    def size(b, t, h, d):
+        n = ctypes.c_size_t(0)
+        assert fa.load_library().fa_varlen_bwd_workspace_size(b, t, h, d, ctypes.byref(n)) == 0
+        return n.value
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for b, t, h, d in ((1, 8, 2, 64), (2, 300, 2, 64), (23, 65536, 32, 128), (0, 0, 1, 64)):
+        assert size(b, t, h, d) == r(t * h * d * 4) + r(h * t * 4) + r((b + 1) * 4)
+        assert fa.fa_varlen_bwd_workspace_size(b, t, h, d) == size(b, t, h, d)
+    lib = fa.load_library()
+    assert lib.fa_varlen_bwd_workspace_size(1, 8, 2, 64, None) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.fa_varlen_bwd_workspace_size(-1, 8, 2, 64, ctypes.byref(n)) == 3
+    assert lib.fa_varlen_bwd_workspace_size(1, 8, 0, 64, ctypes.byref(n)) == 3
+    # the exact size passes validation; one byte less does not
+    need = size(1, 8, 2, 64)
+    assert call_bwd(ws_bytes=need - 1) == 9

@@ -1,4 +1,5 @@
-"""Python binding of libfa_varlen.so (exact varlen attention forward, MI355X).
+"""Python binding of libfa_varlen.so (exact varlen attention, forward and
+backward, MI355X).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI of ``include/fa_varlen.h``.  PyTorch supplies device
@@ -6,8 +7,9 @@ memory and the stream; no CPU fallback exists -- when the library is not
 built every entry point raises :class:`FaVarlenError`.
 
 Functions carry the names of the C entry points:
-  fa_varlen_fwd, fa_varlen_fwd_mapped, fa_varlen_tile_map,
-  fa_varlen_block_sizes, fa_varlen_check_cu_seqlens, fa_status_string.
+  fa_varlen_fwd, fa_varlen_fwd_mapped, fa_varlen_bwd,
+  fa_varlen_bwd_workspace_size, fa_varlen_tile_map, fa_varlen_block_sizes,
+  fa_varlen_check_cu_seqlens, fa_status_string.
 """
 from __future__ import annotations
 
@@ -28,6 +30,8 @@ __all__ = [
     "fa_varlen_tile_map",
     "fa_varlen_fwd",
     "fa_varlen_fwd_mapped",
+    "fa_varlen_bwd",
+    "fa_varlen_bwd_workspace_size",
     "fa_varlen_check_cu_seqlens",
 ]
 
@@ -38,7 +42,7 @@ FA_DTYPE_F16 = 2
 FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_DTYPE", 3: "FA_ERR_SHAPE", 4: "FA_ERR_HEAD_DIM",
-    5: "FA_ERR_ALIGN", 6: "FA_ERR_ARG", 7: "FA_ERR_HIP", 8: "FA_ERR_TOO_LARGE",
+    5: "FA_ERR_ALIGN", 6: "FA_ERR_ARG", 7: "FA_ERR_HIP", 8: "FA_ERR_TOO_LARGE", 9: "FA_ERR_WORKSPACE",
 }
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +82,11 @@ def load_library() -> ctypes.CDLL:
     lib.fa_varlen_fwd.restype = ctypes.c_int
     lib.fa_varlen_fwd_mapped.argtypes = fwd_args + [vp, vp]
     lib.fa_varlen_fwd_mapped.restype = ctypes.c_int
+    lib.fa_varlen_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp,
+                                  i32, i32, i32, i32, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.fa_varlen_bwd.restype = ctypes.c_int
+    lib.fa_varlen_bwd_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_varlen_bwd_workspace_size.restype = ctypes.c_int
     lib.fa_varlen_check_cu_seqlens.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.fa_varlen_check_cu_seqlens.restype = ctypes.c_int
     _LIB = lib
@@ -220,6 +229,51 @@ def fa_varlen_fwd_mapped(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
         total_q, k.shape[0], H, k.shape[1], D, dt, blk_start.data_ptr(), _stream_handle(stream))
     _check(st, "fa_varlen_fwd_mapped")
     return out, lse
+
+
+def fa_varlen_bwd_workspace_size(batch: int, total_q: int, num_heads: int, head_dim: int) -> int:
+    """Bytes of device workspace fa_varlen_bwd needs."""
+    n = ctypes.c_size_t(0)
+    _check(load_library().fa_varlen_bwd_workspace_size(int(batch), int(total_q), int(num_heads), int(head_dim),
+                                                       ctypes.byref(n)), "fa_varlen_bwd_workspace_size")
+    return n.value
+
+
+def fa_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                  softmax_scale: Optional[float] = None, causal: bool = False, dq=None, dk=None, dv=None,
+                  workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of fa_varlen_fwd given dout, the forward's out and lse.
+
+    bf16 or fp16 inputs, head_dim 64 or 128.  dq is shaped like q, dk and dv
+    like k.  ``workspace`` (a CUDA byte tensor of at least
+    fa_varlen_bwd_workspace_size bytes) is allocated when not given.
+    """
+    torch = _torch()
+    q, k, v, cu_q, cu_k, scale, out, lse, dt = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale,
+                                                        out, lse)
+    dout = dout.contiguous()
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_cuda:
+        raise ValueError("dout must be a CUDA tensor shaped and typed like q")
+    total_q, H, D = q.shape
+    batch = cu_q.numel() - 1
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like its input")
+    need = fa_varlen_bwd_workspace_size(batch, total_q, H, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not workspace.is_cuda:
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    st = load_library().fa_varlen_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        cu_q.data_ptr(), cu_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale, int(bool(causal)),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), batch, total_q, k.shape[0], H, k.shape[1], D, dt,
+        workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
+    _check(st, "fa_varlen_bwd")
+    return dq, dk, dv
 
 
 def fa_varlen_check_cu_seqlens(cu_seqlens_q, cu_seqlens_k, total_q: int, total_k: int, max_seqlen_q: int,

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_varlen.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = [os.path.join(CSRC, "fa_varlen_kernels.hip"), os.path.join(CSRC, "fa_varlen_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fa_varlen_kernels.hip"), os.path.join(CSRC, "fa_varlen_bwd.hip"),
+           os.path.join(CSRC, "fa_varlen_api.cpp")]
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the generated code.
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -51,9 +52,11 @@ def build(verbose: bool = False, asm_dir: str | None = None) -> str:
     os.replace(tmp, LIB_PATH)
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
-        asm = os.path.join(asm_dir, "fa_varlen_kernels.s")
-        cmd = [hipcc()] + common_flags() + ["--cuda-device-only", "-S", "-o", asm, SOURCES[0]]
-        subprocess.run(cmd, check=True, capture_output=True, text=True)
+        for src in SOURCES:
+            if src.endswith(".hip"):
+                asm = os.path.join(asm_dir, os.path.basename(src)[:-4] + ".s")
+                cmd = [hipcc()] + common_flags() + ["--cuda-device-only", "-S", "-o", asm, src]
+                subprocess.run(cmd, check=True, capture_output=True, text=True)
     return LIB_PATH
 
 

@@ -1,6 +1,7 @@
 // fa_varlen_api.cpp -- the C ABI declared in include/fa_varlen.h: argument
-// validation, launch sizing and the two kernel launches.  Every check runs on
-// the host before any HIP call, so a validation error launches nothing.
+// validation, launch sizing and the kernel launches of the forward and
+// backward passes.  Every check runs on the host before any HIP call, so a
+// validation error launches nothing.
 
 #include <hip/hip_runtime_api.h>
 
@@ -88,6 +89,22 @@ fa::FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t
   return a;
 }
 
+// Backward workspace: dq accumulator, row terms, key-block map (256-byte aligned parts).
+struct BwdLayout {
+  size_t dq_acc, drow, blk, total;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+BwdLayout bwd_layout(int64_t batch, int64_t total_q, int64_t heads, int64_t head_dim) {
+  BwdLayout l;
+  l.dq_acc = 0;
+  l.drow = round256((size_t)total_q * heads * head_dim * sizeof(float));
+  l.blk = l.drow + round256((size_t)heads * total_q * sizeof(float));
+  l.total = l.blk + round256(((size_t)batch + 1) * sizeof(int32_t));
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,6 +122,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_ARG: return "invalid argument (softmax_scale must be finite and > 0, causal 0 or 1, block_m 1..4096)";
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_TOO_LARGE: return "problem too large for one launch";
+    case FA_ERR_WORKSPACE: return "backward workspace missing or smaller than fa_varlen_bwd_workspace_size";
     default: return "unknown status";
   }
 }
@@ -172,6 +190,76 @@ int fa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu
   }
   if (hipFreeAsync(blk_start, s) != hipSuccess) rc = FA_ERR_HIP;
   return rc;
+}
+
+int fa_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t num_heads, int32_t head_dim,
+                                 size_t* bytes) {
+  if (!bytes) return FA_ERR_NULL;
+  if (batch < 0 || total_q < 0 || num_heads < 1 || head_dim < 1) return FA_ERR_SHAPE;
+  *bytes = bwd_layout(batch, total_q, num_heads, head_dim).total;
+  return FA_OK;
+}
+
+int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                  int32_t max_seqlen_k, float softmax_scale, int32_t causal, void* dq, void* dk, void* dv,
+                  int32_t batch, int32_t total_q, int32_t total_k, int32_t num_heads, int32_t num_heads_k,
+                  int32_t head_dim, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  Plan plan;  // the forward's checks cover q, k, v, offsets, out, lse, sizes, scale, causal
+  int st = validate(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal, out,
+                    lse, batch, total_q, total_k, num_heads, num_heads_k, head_dim, dtype, &plan);
+  if (st != FA_OK) return st;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_DTYPE;
+  const int bn = fa::bwd_block_n(dtype, head_dim);
+  if (bn == 0) return FA_ERR_HEAD_DIM;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16)) return FA_ERR_ALIGN;
+  const BwdLayout lay = bwd_layout(batch, total_q, num_heads, head_dim);
+  if (!workspace || workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+  // key blocks: sum_b ceil(Lk_b / bn) <= min(batch * ceil(max_k / bn), ceil(total_k / bn) + batch - 1)
+  const int64_t by_max = (int64_t)batch * ((max_seqlen_k + bn - 1) / bn);
+  const int64_t by_total = ((int64_t)total_k + bn - 1) / bn + (batch > 0 ? batch - 1 : 0);
+  const int64_t tmax = by_max < by_total ? by_max : by_total;
+  const int64_t grid = (tmax * num_heads_k + 7) / 8 * 8;
+  if (grid > INT32_MAX) return FA_ERR_TOO_LARGE;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* blk = reinterpret_cast<int32_t*>(ws + lay.blk);
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.blk_start = blk;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dq_acc = reinterpret_cast<float*>(ws + lay.dq_acc);
+  a.drow = reinterpret_cast<float*>(ws + lay.drow);
+  a.row_stride = (int64_t)num_heads * head_dim;
+  a.kv_row_stride = (int64_t)num_heads_k * head_dim;
+  a.scale = softmax_scale;
+  a.scale_log2 = (float)((double)softmax_scale * kLog2e);
+  a.batch = batch;
+  a.tmax = (int32_t)tmax;
+  a.n_work = (int32_t)(tmax * num_heads_k);
+  a.total_q = total_q;
+  a.heads = num_heads;
+  a.head_group = num_heads / num_heads_k;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (fa::launch_bwd_prep(dtype, head_dim, a, s) != hipSuccess) return FA_ERR_HIP;
+  if (grid > 0) {
+    if (fa::launch_tile_map(cu_seqlens_k, batch, bn, blk, s) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_bwd(dtype, head_dim, causal != 0, (int)grid, a, s) != hipSuccess) return FA_ERR_HIP;
+  }
+  if (fa::launch_bwd_dq(dtype, head_dim, a, s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
 }
 
 int fa_varlen_check_cu_seqlens(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,

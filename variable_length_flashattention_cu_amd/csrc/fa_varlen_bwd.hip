@@ -1,0 +1,437 @@
+// fa_varlen_bwd.hip -- gfx950 kernels for the backward pass of exact attention
+// over packed variable-length sequences (16-bit inputs, head_dim 64 and 128).
+//
+// Organisation (zepes.com "Comprendiendo Flash-Atención y Flash-Atención-2",
+// section "FashAttention v1" (sic)): each workgroup owns a block of key columns
+// of one sequence and one key/value head; it recomputes the attention
+// probabilities of its block from the forward pass's log-sum-exp instead of
+// reading a stored score matrix, accumulates dK and dV of its keys in
+// registers, and adds its share of dQ to a float32 accumulator with atomic
+// operations.  With several query heads per key/value head the workgroup walks
+// all of them, so dK and dV of a key/value head are complete when it ends.
+//
+// Per (sequence, query head), with the forward definition S = scale Q K^T,
+// P = softmax(S) over visible keys, O = P V, the chain rule gives
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D_i = rowsum(dO_i * O_i),
+//   dQ = scale dS K,   dK = scale dS^T Q,
+// where P_ij = exp(S_ij - lse_i) is rebuilt from the forward's lse
+// (D_i equals rowsum(P * dP) because O_i = sum_j P_ij v_j).
+//
+// Three launches:
+//   bwd_prep_kernel  D_i for every (row, head) and a zeroed dQ accumulator;
+//   bwd16_kernel     one workgroup per (key block of 128 keys, key/value head):
+//                    dK, dV of the block and atomic dQ contributions;
+//   bwd_dq_kernel    dq = accumulator (already scaled) in the input type.
+//
+// bwd16_kernel layout (4 wavefronts, wave w owns keys 32w..32w+31 of the
+// block; one 32-row query block per step):
+//   * K and V of the wave's keys stay in registers as the B operands of
+//     S = Q K^T and dP = dO V^T (contraction over head_dim); Q and dO rows are
+//     read from LDS in the permuted row order of the forward kernels, so that
+//     register r of lane half g of the 32x32 accumulators holds query row
+//     16g + r and lane l32 the key 32w + l32.
+//   * That is the B-operand layout of dV^T = dO^T P and dK^T = Q^T dS
+//     (contraction over the 32 query rows), whose A operands Q^T and dO^T are
+//     staged transposed in LDS.  dK^T and dV^T accumulate in registers.
+//   * dS goes to LDS row-major; dQ = dS K reads it with K^T (staged once per
+//     item) and each wave adds one 32x32 output tile (or half of one) to the
+//     accumulator.
+//   * Q, dO, lse and D of the next query block are loaded into registers
+//     while the current one is computed and stored into the other LDS buffer.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_varlen_device.h"
+#include "fa_varlen_launch.h"
+#include "fa_varlen_tiling.h"
+
+namespace fa {
+namespace {
+
+constexpr float kLog2eF = 1.4426950408889634074f;
+constexpr int kBwdBN = 128;  // keys per work item (4 waves x 32)
+constexpr int kBwdBM = 32;   // query rows per step
+
+template <typename T>
+__device__ __forceinline__ float half_to_f32(uint32_t bits16);
+template <>
+__device__ __forceinline__ float half_to_f32<__bf16>(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+template <>
+__device__ __forceinline__ float half_to_f32<_Float16>(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+template <typename T>
+__device__ __forceinline__ uint16_t f32_to_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (T)x);
+}
+
+// ---------------------------------------------------------------------------
+// D_i = rowsum(dout * out) and the zeroed dq accumulator
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int CH = D / 8;          // 16-byte chunks per (row, head)
+  constexpr int PAIRS = 256 / CH;    // (row, head) pairs per workgroup
+  static_assert((CH & (CH - 1)) == 0 && CH <= 64, "chunks of a row must form a power-of-two lane group");
+  const int tid = threadIdx.x;
+  const int64_t p = (int64_t)blockIdx.x * PAIRS + tid / CH;  // row * heads + head
+  const int c = tid % CH;
+  const int64_t npairs = (int64_t)a.total_q * a.heads;
+  float dot = 0.f;
+  if (p < npairs) {
+    const u32x4 o = *(const u32x4*)((const uint16_t*)a.out + p * D + 8 * c);
+    const u32x4 g = *(const u32x4*)((const uint16_t*)a.dout + p * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dot += half_to_f32<T>(o[e] & 0xffffu) * half_to_f32<T>(g[e] & 0xffffu);
+      dot += half_to_f32<T>(o[e] >> 16) * half_to_f32<T>(g[e] >> 16);
+    }
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    *(f32x4*)(a.dq_acc + p * D + 8 * c) = z;
+    *(f32x4*)(a.dq_acc + p * D + 8 * c + 4) = z;
+  }
+#pragma unroll
+  for (int off = CH / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+  if (p < npairs && c == 0) {
+    const int64_t row = p / a.heads;
+    const int h = (int)(p % a.heads);
+    a.drow[(int64_t)h * a.total_q + row] = dot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq = accumulator (the scale is applied when the atomics add) in the input type
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int CH = D / 8;
+  constexpr int PAIRS = 256 / CH;
+  const int tid = threadIdx.x;
+  const int64_t p = (int64_t)blockIdx.x * PAIRS + tid / CH;
+  const int c = tid % CH;
+  const int64_t rows = a.cu_q[a.batch];  // rows past the last sequence are not written
+  if (p < rows * a.heads) {
+    const f32x4 x0 = *(const f32x4*)(a.dq_acc + p * D + 8 * c);
+    const f32x4 x1 = *(const f32x4*)(a.dq_acc + p * D + 8 * c + 4);
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      r[e] = (uint32_t)f32_to_bits<T>(x0[2 * e]) | ((uint32_t)f32_to_bits<T>(x0[2 * e + 1]) << 16);
+      r[e + 2] = (uint32_t)f32_to_bits<T>(x1[2 * e]) | ((uint32_t)f32_to_bits<T>(x1[2 * e + 1]) << 16);
+    }
+    *(u32x4*)((uint16_t*)a.dq + p * D + 8 * c) = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// work items: (key block j of sequence b, key/value head hk)
+// ---------------------------------------------------------------------------
+struct ColItem {
+  int b, j, hk;
+  int q_start, Lq, k_start, Lk;
+};
+
+__device__ __forceinline__ bool decode_col(const BwdArgs& a, ColItem& w) {
+  // each XCD (workgroup i runs on XCD i % 8) takes a contiguous slice of items
+  const uint32_t per_xcd = gridDim.x >> 3;
+  const uint32_t work = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+  if (work >= (uint32_t)a.n_work) return false;
+  w.hk = (int)(work / (uint32_t)a.tmax);
+  const int t = (int)(work % (uint32_t)a.tmax);
+  const int T = a.blk_start[a.batch];
+  if (t >= T) return false;
+  int lo = 0, hi = a.batch;  // invariant: blk_start[lo] <= t < blk_start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.blk_start[mid] <= t) lo = mid; else hi = mid;
+  }
+  w.b = lo;
+  w.j = t - a.blk_start[lo];
+  w.q_start = a.cu_q[lo];
+  w.Lq = a.cu_q[lo + 1] - w.q_start;
+  w.k_start = a.cu_k[lo];
+  w.Lk = a.cu_k[lo + 1] - w.k_start;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// the backward workgroup
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
+  constexpr int BN = kBwdBN, BM = kBwdBM, NW = 4;
+  constexpr int KSTEPS = D / 16;  // k-steps over head_dim
+  constexpr int DB = D / 32;      // 32-dim tiles
+  static_assert(D == 64 || D == 128, "backward head_dim");
+  using E = Elem16<T>;
+  typedef typename E::v8 v8;
+  using KT = Tile16<D, BN, NW>;   // K^T of the item (V-style staging)
+  using RT = Tile16<D, BM, NW>;   // a query block: row-major and transposed
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds_kt[D * BN];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][BM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_qt[2][D * BM];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_do[2][BM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_dot[2][D * BM];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ds[BM * BN];
+  __shared__ __attribute__((aligned(16))) float lds_lse[2][BM];
+  __shared__ __attribute__((aligned(16))) float lds_dr[2][BM];
+
+  ColItem w;
+  if (!decode_col(a, w)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int key0 = w.j * BN;
+  const int kcol = key0 + 32 * wave + l32;  // this lane's key (in the sequence)
+  const int shift = w.Lk - w.Lq;
+  const int64_t rs = a.row_stride, rsk = a.kv_row_stride;
+  const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
+  const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
+
+  // K^T of the block for dQ = dS K
+  {
+    KT kt;
+    kt.load_v(kbase, rsk, key0, w.Lk, tid);
+    kt.store_v(lds_kt, tid);
+  }
+  // K and V of the wave's keys: B operands, keys past the sequence read as zero
+  v8 kb[KSTEPS], vb[KSTEPS];
+  {
+    const int rows = max(0, min(32, w.Lk - key0 - 32 * wave));
+    const int64_t off0 = (int64_t)(key0 + 32 * wave) * rsk;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + off0, tiling::head_rows_bytes(rows, rsk, D, 2));
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + off0, tiling::head_rows_bytes(rows, rsk, D, 2));
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const uint32_t off = ((uint32_t)l32 * (uint32_t)rsk + 16 * ks + 8 * g) * 2u;
+      kb[ks] = __builtin_bit_cast(v8, buffer_load16(rk, off));
+      vb[ks] = __builtin_bit_cast(v8, buffer_load16(rv, off));
+    }
+  }
+
+  // query blocks that see a key of this block: rows q with q + shift >= key0
+  const int i_begin = CAUSAL ? max(0, key0 - shift) / BM : 0;
+  const int i_end = (w.Lq + BM - 1) / BM;
+  const int nblk = max(0, i_end - i_begin);
+  const int nsteps = a.head_group * nblk;
+
+  RT tq, tdo;
+  float lse_v = 0.f, dr_v = 0.f;
+  auto load_step = [&](int s) {
+    const int h = w.hk * a.head_group + s / nblk;
+    const int r0 = (i_begin + s % nblk) * BM;
+    const uint16_t* qh = (const uint16_t*)a.q + (int64_t)w.q_start * rs + (int64_t)h * D;
+    const uint16_t* doh = (const uint16_t*)a.dout + (int64_t)w.q_start * rs + (int64_t)h * D;
+    tq.load_k(qh, rs, r0, w.Lq, tid);
+    tq.load_v(qh, rs, r0, w.Lq, tid);
+    tdo.load_k(doh, rs, r0, w.Lq, tid);
+    tdo.load_v(doh, rs, r0, w.Lq, tid);
+    const int q = r0 + (tid & (BM - 1));
+    const int64_t at = (int64_t)h * a.total_q + w.q_start + q;
+    if (tid < BM) lse_v = q < w.Lq ? a.lse[at] : 0.f;
+    else if (tid < 2 * BM) dr_v = q < w.Lq ? a.drow[at] : 0.f;
+  };
+  auto store_step = [&](int buf) {
+    tq.store_k(lds_q[buf], tid);
+    tq.store_v(lds_qt[buf], tid);
+    tdo.store_k(lds_do[buf], tid);
+    tdo.store_v(lds_dot[buf], tid);
+    if (tid < BM) lds_lse[buf][tid] = lse_v * kLog2eF;
+    else if (tid < 2 * BM) lds_dr[buf][tid - BM] = dr_v;
+  };
+
+  f32x16 dkt[DB], dvt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkt[db] = f32x16{};
+    dvt[db] = f32x16{};
+  }
+
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(0);
+  }
+  __syncthreads();
+
+  const int arow = tiling::key_of_arow(l32);
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    const int h = w.hk * a.head_group + s / nblk;
+    const int r0 = (i_begin + s % nblk) * BM;
+    if (s + 1 < nsteps) load_step(s + 1);
+
+    // S = Q K^T and dP = dO V^T (rows permuted: register r of half g = row 16g + r)
+    f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const v8 aq = *(const v8*)(lds_q[buf] + tiling::ks_index<D>(arow, 2 * ks + g));
+      const v8 ad = *(const v8*)(lds_do[buf] + tiling::ks_index<D>(arow, 2 * ks + g));
+      sc = E::mfma(aq, kb[ks], sc);
+      dp = E::mfma(ad, vb[ks], dp);
+    }
+
+    // P and dS of the lane's 16 rows for its key
+    float lse2[16], drr[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 l4 = *(const f32x4*)(&lds_lse[buf][16 * g + 4 * r4]);
+      const f32x4 d4 = *(const f32x4*)(&lds_dr[buf][16 * g + 4 * r4]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        lse2[4 * r4 + c] = l4[c];
+        drr[4 * r4 + c] = d4[c];
+      }
+    }
+    v8 p16[2], ds16[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = r0 + 16 * g + r;
+      const bool vis = q < w.Lq && kcol < w.Lk && (!CAUSAL || kcol <= q + shift);
+      const float pr = vis ? fast_exp2(__builtin_fmaf(sc[r], a.scale_log2, -lse2[r])) : 0.f;
+      const float dsr = pr * (dp[r] - drr[r]);
+      p16[r >> 3][r & 7] = (T)pr;
+      ds16[r >> 3][r & 7] = (T)dsr;
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 rows)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int d = 32 * db + l32;
+        const v8 adt = *(const v8*)(lds_dot[buf] + tiling::vt_index<BM>(d, 16 * g + 8 * t));
+        const v8 aqt = *(const v8*)(lds_qt[buf] + tiling::vt_index<BM>(d, 16 * g + 8 * t));
+        dvt[db] = E::mfma(adt, p16[t], dvt[db]);
+        dkt[db] = E::mfma(aqt, ds16[t], dkt[db]);
+      }
+
+    // dS -> LDS, row-major [row][key].  The 16-bit values are taken from the
+    // packed operand registers as whole words (element-wise access to the
+    // 16-bit vector was miscompiled into one element per half).
+    {
+      const int kk = 32 * wave + l32;
+      const u32x4 w0 = __builtin_bit_cast(u32x4, ds16[0]);
+      const u32x4 w1 = __builtin_bit_cast(u32x4, ds16[1]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t word = r < 8 ? w0[(r & 7) >> 1] : w1[(r & 7) >> 1];
+        lds_ds[tiling::ks_index<BN>(16 * g + r, kk >> 3) + (kk & 7)] = (uint16_t)((r & 1) ? (word >> 16) : word);
+      }
+    }
+    __syncthreads();
+
+    // dQ rows r0..r0+31: wave -> (32-dim tile, key part); scale applied here
+    {
+      constexpr int SPLIT = NW / DB;        // waves per tile (1 at D=128, 2 at D=64)
+      constexpr int KEYS = BN / SPLIT;      // keys per wave
+      const int tile = wave % DB, part = wave / DB;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KEYS / 16; ++kk) {
+        const int k16 = part * KEYS + 16 * kk;
+        const v8 ads = *(const v8*)(lds_ds + tiling::ks_index<BN>(l32, (k16 >> 3) + g));
+        const v8 bkt = *(const v8*)(lds_kt + tiling::vt_index<BN>(32 * tile + l32, k16 + 8 * g));
+        acc = E::mfma(ads, bkt, acc);
+      }
+      // accumulator register r of half g holds row 8*(r/4) + 4g + r%4, column 32*tile + l32
+      float* dqh = a.dq_acc + ((int64_t)(w.q_start + r0)) * rs + (int64_t)h * D + 32 * tile + l32;
+      if (r0 + BM <= w.Lq) {  // wave-uniform: every row of the block is in the sequence
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          unsafeAtomicAdd(dqh + (int64_t)(8 * (r >> 2) + 4 * g + (r & 3)) * rs, acc[r] * a.scale);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = 8 * (r >> 2) + 4 * g + (r & 3);
+          if (r0 + q < w.Lq) unsafeAtomicAdd(dqh + (int64_t)q * rs, acc[r] * a.scale);
+        }
+      }
+    }
+
+    if (s + 1 < nsteps) store_step(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dK = scale dK^T^T, dV, rows of this lane's key
+  if (kcol < w.Lk) {
+    T* dkp = (T*)a.dk + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
+    T* dvp = (T*)a.dv + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        typename E::v4 k4, v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          k4[c] = (T)(dkt[db][4 * s4 + c] * a.scale);
+          v4[c] = (T)dvt[db][4 * s4 + c];
+        }
+        const int d0 = 32 * db + 8 * s4 + 4 * g;
+        *(typename E::v4*)(dkp + d0) = k4;
+        *(typename E::v4*)(dvp + d0) = v4;
+      }
+  }
+}
+
+template <typename F>
+hipError_t launch(F kernel, int grid, int threads, hipStream_t stream, const BwdArgs& a) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_t(int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
+  if (head_dim == 128)
+    return causal ? launch(bwd16_kernel<T, 128, true>, grid, 256, stream, a)
+                  : launch(bwd16_kernel<T, 128, false>, grid, 256, stream, a);
+  if (head_dim == 64)
+    return causal ? launch(bwd16_kernel<T, 64, true>, grid, 256, stream, a)
+                  : launch(bwd16_kernel<T, 64, false>, grid, 256, stream, a);
+  return hipErrorInvalidValue;
+}
+
+int64_t row_pairs_grid(const BwdArgs& a, int head_dim) {
+  const int64_t pairs = (int64_t)a.total_q * a.heads;
+  const int64_t per = 256 / (head_dim / 8);
+  return (pairs + per - 1) / per;
+}
+
+}  // namespace
+
+int bwd_block_n(int dtype, int head_dim) {
+  if ((dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 128)) return kBwdBN;
+  return 0;
+}
+
+hipError_t launch_bwd_prep(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream) {
+  const int grid = (int)row_pairs_grid(a, head_dim);
+  if (grid == 0) return hipSuccess;
+  if (dtype == 1)
+    return head_dim == 128 ? launch(bwd_prep_kernel<__bf16, 128>, grid, 256, stream, a)
+                           : launch(bwd_prep_kernel<__bf16, 64>, grid, 256, stream, a);
+  return head_dim == 128 ? launch(bwd_prep_kernel<_Float16, 128>, grid, 256, stream, a)
+                         : launch(bwd_prep_kernel<_Float16, 64>, grid, 256, stream, a);
+}
+
+hipError_t launch_bwd(int dtype, int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
+  if (dtype == 1) return launch_bwd_t<__bf16>(head_dim, causal, grid, a, stream);
+  if (dtype == 2) return launch_bwd_t<_Float16>(head_dim, causal, grid, a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream) {
+  const int grid = (int)row_pairs_grid(a, head_dim);
+  if (grid == 0) return hipSuccess;
+  if (dtype == 1)
+    return head_dim == 128 ? launch(bwd_dq_kernel<__bf16, 128>, grid, 256, stream, a)
+                           : launch(bwd_dq_kernel<__bf16, 64>, grid, 256, stream, a);
+  return head_dim == 128 ? launch(bwd_dq_kernel<_Float16, 128>, grid, 256, stream, a)
+                         : launch(bwd_dq_kernel<_Float16, 64>, grid, 256, stream, a);
+}
+
+}  // namespace fa

@@ -1,6 +1,6 @@
 // fa_varlen_launch.h -- internal interface between the C ABI (fa_varlen_api.cpp)
-// and the kernels (fa_varlen_kernels.hip).  Not installed; callers use
-// include/fa_varlen.h.
+// and the kernels (fa_varlen_kernels.hip, fa_varlen_bwd.hip).  Not installed;
+// callers use include/fa_varlen.h.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -37,6 +37,45 @@ struct TileConfig {
 
 // {0,0,0} for an unsupported (dtype, head_dim).
 TileConfig tile_config(int dtype, int head_dim);
+
+// Kernel arguments of the backward pass (passed by value).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;        // [heads, total_q], natural log
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* blk_start;  // key-block map: scan of ceil(Lk_b / block_n)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;           // [total_q, heads, head_dim] float32 accumulator
+  float* drow;             // [heads, total_q]: rowsum(dout * out)
+  int64_t row_stride;      // heads * head_dim
+  int64_t kv_row_stride;   // kv_heads * head_dim
+  float scale;             // softmax_scale
+  float scale_log2;        // softmax_scale * log2(e)
+  int32_t batch;
+  int32_t tmax;            // upper bound on key blocks per key/value head
+  int32_t n_work;          // kv_heads * tmax
+  int32_t total_q;
+  int32_t heads;
+  int32_t head_group;      // query heads per key/value head
+};
+
+// Keys per work item of the backward pass for (dtype, head_dim); 0 if the
+// backward pass does not support the pair.
+int bwd_block_n(int dtype, int head_dim);
+
+// rowsum(dout * out) per (head, row) and a zeroed dq accumulator
+hipError_t launch_bwd_prep(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream);
+// dk, dv and the dq accumulator, one workgroup per (key block, key/value head)
+hipError_t launch_bwd(int dtype, int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream);
+// dq = softmax_scale * accumulator, in the input type
+hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream);
 
 hipError_t launch_tile_map(const int32_t* cu_q, int batch, int block_m, int32_t* blk_start, hipStream_t stream);
 hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream);
