@@ -42,7 +42,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, Workload, draw_qkv, workload_dense,  # noqa: E402
+from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, Workload, draw_dout, draw_qkv, workload_dense,  # noqa: E402
                       workload_ragged64k, workload_ragged64k_gqa, workload_sweep)
 
 METRIC = "varlen attention fwd TFLOP/s and % of bf16 MFMA peak, d=64/128, causal"
@@ -157,6 +157,36 @@ def measure_secondary(wl: Workload, iters: int = 20, modes=(False, True)) -> lis
         del r
     del t
     return rows
+
+
+def measure_backward(wl: Workload, causal: bool, iters: int = 10) -> dict:
+    """fa_varlen_bwd (all four launches) after one forward; 10*D flops per
+    visible pair and head (S recomputed, dP, dV, dK, dQ: five products)."""
+    import torch
+    import variable_length_flashattention_cu_amd as fa
+    data = draw_qkv(wl)
+    t = to_device(wl, data)
+    del data
+    g = draw_dout(wl)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
+    dout = torch.from_numpy(g["dout_bits"].view(np.int16)).to("cuda").view(tdt)
+    del g
+    out, lse = fa.fa_varlen_fwd(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], wl.max_seqlen_q, wl.max_seqlen_k,
+                                wl.scale, causal)
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    ws = torch.empty(fa.fa_varlen_bwd_workspace_size(wl.batch, wl.total_q, wl.heads, wl.head_dim),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        fa.fa_varlen_bwd(t["q"], t["k"], t["v"], out, dout, lse, t["cu_q"], t["cu_k"], wl.max_seqlen_q,
+                         wl.max_seqlen_k, wl.scale, causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+    for _ in range(2):
+        step()
+    ms = time_events(step, iters)
+    fl = 2.5 * algorithmic_flops(wl, causal)
+    return {"workload": wl.name, "seq_len": wl.max_seqlen_q, "head_dim": wl.head_dim, "heads": wl.heads,
+            "kv_heads": wl.kv_heads, "dtype": wl.dtype, "causal": causal, "ms_per_call": round(ms, 4),
+            "tflops": round(fl / ms / 1e9, 1), "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
 
 def cpu_baseline(wl: Workload, causal: bool, data: dict, heads=(0,)) -> dict:
@@ -375,6 +405,15 @@ def main() -> int:
         for v in variants:
             line["ragged64k_variants"] += measure_secondary(v, modes=(True,))
             print(f"# {line['ragged64k_variants'][-1]}", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        # backward pass (fa_varlen_bwd, after the forward that gives out and lse)
+        line["backward"] = []
+        for bwl, bc in ((workload_ragged64k(), True), (workload_sweep(4096, 128), False),
+                        (workload_sweep(4096, 128), True), (workload_sweep(4096, 64), True)):
+            line["backward"].append(measure_backward(bwl, bc))
+            print(f"# {line['backward'][-1]}", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
       const int q = r0 + 16 * g + r;
       const bool vis = q < w.Lq && kcol < w.Lk && (!CAUSAL || kcol <= q + shift);
       const float pr = vis ? fast_exp2(__builtin_fmaf(sc[r], a.scale_log2, -lse2[r])) : 0.f;
-      const float dsr = pr * (dp[r] - drr[r]);
+      const float dsr = pr * (dp[r] - drr[r]) * a.scale;  // dS with the softmax scale folded in
       p16[r >> 3][r & 7] = (T)pr;
       ds16[r >> 3][r & 7] = (T)dsr;
     }
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // dQ rows r0..r0+31: wave -> (32-dim tile, key part); scale applied here
+    // dQ rows r0..r0+31: wave -> (32-dim tile, key part)
     {
       constexpr int SPLIT = NW / DB;        // waves per tile (1 at D=128, 2 at D=64)
       constexpr int KEYS = BN / SPLIT;      // keys per wave
@@ -338,18 +338,16 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
         const v8 bkt = *(const v8*)(lds_kt + tiling::vt_index<BN>(32 * tile + l32, k16 + 8 * g));
         acc = E::mfma(ads, bkt, acc);
       }
-      // accumulator register r of half g holds row 8*(r/4) + 4g + r%4, column 32*tile + l32
-      float* dqh = a.dq_acc + ((int64_t)(w.q_start + r0)) * rs + (int64_t)h * D + 32 * tile + l32;
-      if (r0 + BM <= w.Lq) {  // wave-uniform: every row of the block is in the sequence
+      // accumulator register r of half g holds row 8*(r/4) + 4g + r%4, column 32*tile + l32.
+      // Buffer atomics over the rows of this block that lie in the sequence:
+      // the range check drops the additions of rows past its end.
+      const __amdgpu_buffer_rsrc_t racc =
+          buffer_rsrc(a.dq_acc + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D,
+                      tiling::head_rows_bytes(min(BM, w.Lq - r0), rs, D, 4));
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          unsafeAtomicAdd(dqh + (int64_t)(8 * (r >> 2) + 4 * g + (r & 3)) * rs, acc[r] * a.scale);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = 8 * (r >> 2) + 4 * g + (r & 3);
-          if (r0 + q < w.Lq) unsafeAtomicAdd(dqh + (int64_t)q * rs, acc[r] * a.scale);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t off = ((uint32_t)(8 * (r >> 2) + 4 * g + (r & 3)) * (uint32_t)rs + 32 * tile + l32) * 4u;
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], racc, (int)off, 0, 0);
       }
     }
 
@@ -357,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: dK = scale dK^T^T, dV, rows of this lane's key
+  // ---- epilogue: dK (scale already in dS) and dV of this lane's key
   if (kcol < w.Lk) {
     T* dkp = (T*)a.dk + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
     T* dvp = (T*)a.dv + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
@@ -368,7 +366,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
         typename E::v4 k4, v4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          k4[c] = (T)(dkt[db][4 * s4 + c] * a.scale);
+          k4[c] = (T)dkt[db][4 * s4 + c];
           v4[c] = (T)dvt[db][4 * s4 + c];
         }
         const int d0 = 32 * db + 8 * s4 + 4 * g;
