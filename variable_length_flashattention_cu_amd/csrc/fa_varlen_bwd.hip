@@ -160,6 +160,84 @@ __device__ __forceinline__ bool decode_col(const BwdArgs& a, ColItem& w) {
 // ---------------------------------------------------------------------------
 // the backward workgroup
 // ---------------------------------------------------------------------------
+// Direct global -> LDS staging of a row-major tile of ROWS rows x D 16-bit
+// elements in the swizzled K-style layout (tiling::ks_index<D>): each lane's
+// 16 bytes land at LDS chunk position p = 64 * instruction + lane, so the lane
+// loads the logical chunk that the swizzle stores there.  Rows at or past
+// `valid` read as zeros (buffer range check); no registers hold the data.
+template <int D, int ROWS>
+__device__ __forceinline__ void lds_load_rows(uint16_t* dst, const uint16_t* base, int64_t row_stride, int valid,
+                                              int wave, int lane) {
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int PER_WAVE = ROWS * CPR / 256;  // instructions per wave (4 waves)
+  static_assert(ROWS * CPR % 256 == 0, "tile must split into whole wave loads");
+  const __amdgpu_buffer_rsrc_t r =
+      buffer_rsrc(base, tiling::head_rows_bytes(max(0, min(ROWS, valid)), row_stride, D, 2));
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int seg = wave * PER_WAVE + i;
+    const int p = seg * 64 + lane;
+    const int row = p / CPR;
+    const int lc = (p % CPR) ^ tiling::k_swz<D>(row);
+    const uint32_t off = ((uint32_t)row * (uint32_t)row_stride + (uint32_t)lc * 8u) * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + seg * 512), 16, off,
+                                             0, 0, 0);
+  }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i reads 8 bytes at row r0 + i/4, columns c0 + 4(i%4) .. +3 of a
+// row-major swizzled tile, and the hardware hands lane i the four elements
+// X[r0 + e][c0 + i], e = 0..3 (column c0 + i, four consecutive rows).
+template <int D>
+__device__ __forceinline__ s16x4 tr_read4(const uint16_t* tile, int r0, int c0, int i) {
+  const int row = r0 + (i >> 2), col = c0 + 4 * (i & 3);
+  const uint16_t* p = tile + tiling::ks_index<D>(row, col >> 3) + (col & 7);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+// 8 consecutive rows r0 .. r0+7 of column c0 + i as one MFMA operand
+template <typename V8, int D>
+__device__ __forceinline__ V8 tr_read8(const uint16_t* tile, int r0, int c0, int i) {
+  const s16x4 lo = tr_read4<D>(tile, r0, c0, i);
+  const s16x4 hi = tr_read4<D>(tile, r0 + 4, c0, i);
+  const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(V8, v);
+}
+
+// Query block s of a work item (Q, dO, lse, D): loaded into registers while
+// the previous block is computed, then stored into an LDS buffer.  Rows past
+// the sequence read as zeros.  Step s covers query head
+// kv_head * head_group + s / nblk and rows (i_begin + s % nblk) * BM ...
+template <int D, int BM>
+struct BlockStage {
+  Tile16<D, BM, 4> tq, tdo;
+  float lse_v = 0.f, dr_v = 0.f;
+
+  __device__ __forceinline__ void load(const BwdArgs& a, const ColItem& w, int s, int nblk, int i_begin, int tid) {
+    const int h = w.hk * a.head_group + s / nblk;
+    const int r0 = (i_begin + s % nblk) * BM;
+    const int64_t rs = a.row_stride;
+    const uint16_t* qh = (const uint16_t*)a.q + (int64_t)w.q_start * rs + (int64_t)h * D;
+    const uint16_t* doh = (const uint16_t*)a.dout + (int64_t)w.q_start * rs + (int64_t)h * D;
+    tq.load_k(qh, rs, r0, w.Lq, tid);
+    tdo.load_k(doh, rs, r0, w.Lq, tid);
+    const int q = r0 + (tid & (BM - 1));
+    const int64_t at = (int64_t)h * a.total_q + w.q_start + q;
+    if (tid < BM) lse_v = q < w.Lq ? a.lse[at] : 0.f;
+    else if (tid < 2 * BM) dr_v = q < w.Lq ? a.drow[at] : 0.f;
+  }
+  // lse is stored in log2 units
+  __device__ __forceinline__ void store(uint16_t* qs, uint16_t* dos, float* lse, float* dr, int tid) const {
+    tq.store_k(qs, tid);
+    tdo.store_k(dos, tid);
+    if (tid < BM) lse[tid] = lse_v * kLog2eF;
+    else if (tid < 2 * BM) dr[tid - BM] = dr_v;
+  }
+};
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   constexpr int BN = kBwdBN, BM = kBwdBM, NW = 4;
@@ -168,15 +246,12 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   static_assert(D == 64 || D == 128, "backward head_dim");
   using E = Elem16<T>;
   typedef typename E::v8 v8;
-  using KT = Tile16<D, BN, NW>;   // K^T of the item (V-style staging)
-  using RT = Tile16<D, BM, NW>;   // a query block: row-major and transposed
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_kt[D * BN];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][BM * D];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_qt[2][D * BM];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[BN * D];       // K block, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[BN * D];       // V block, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ds[BM * BN];     // dS, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][BM * D];    // query block, row-major
   __shared__ __attribute__((aligned(16))) uint16_t lds_do[2][BM * D];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_dot[2][D * BM];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_ds[BM * BN];
   __shared__ __attribute__((aligned(16))) float lds_lse[2][BM];
   __shared__ __attribute__((aligned(16))) float lds_dr[2][BM];
 
@@ -186,6 +261,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
+  const int li = lane & 15, lg = lane >> 4;  // lane in its 16-lane group, group
   const int key0 = w.j * BN;
   const int kcol = key0 + 32 * wave + l32;  // this lane's key (in the sequence)
   const int shift = w.Lk - w.Lq;
@@ -193,26 +269,11 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
   const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
 
-  // K^T of the block for dQ = dS K
-  {
-    KT kt;
-    kt.load_v(kbase, rsk, key0, w.Lk, tid);
-    kt.store_v(lds_kt, tid);
-  }
-  // K and V of the wave's keys: B operands, keys past the sequence read as zero
-  v8 kb[KSTEPS], vb[KSTEPS];
-  {
-    const int rows = max(0, min(32, w.Lk - key0 - 32 * wave));
-    const int64_t off0 = (int64_t)(key0 + 32 * wave) * rsk;
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + off0, tiling::head_rows_bytes(rows, rsk, D, 2));
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + off0, tiling::head_rows_bytes(rows, rsk, D, 2));
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const uint32_t off = ((uint32_t)l32 * (uint32_t)rsk + 16 * ks + 8 * g) * 2u;
-      kb[ks] = __builtin_bit_cast(v8, buffer_load16(rk, off));
-      vb[ks] = __builtin_bit_cast(v8, buffer_load16(rv, off));
-    }
-  }
+  // the K and V blocks of the item in LDS (B operands of S = Q K^T and
+  // dP = dO V^T, and K for dQ = dS K); keys past the sequence read as zero
+  lds_load_rows<D, BN>(lds_k, kbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
+  lds_load_rows<D, BN>(lds_v, vbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
+  const int krow = 32 * wave + l32;  // this lane's key row in the block
 
   // query blocks that see a key of this block: rows q with q + shift >= key0
   const int i_begin = CAUSAL ? max(0, key0 - shift) / BM : 0;
@@ -220,30 +281,10 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   const int nblk = max(0, i_end - i_begin);
   const int nsteps = a.head_group * nblk;
 
-  RT tq, tdo;
-  float lse_v = 0.f, dr_v = 0.f;
-  auto load_step = [&](int s) {
-    const int h = w.hk * a.head_group + s / nblk;
-    const int r0 = (i_begin + s % nblk) * BM;
-    const uint16_t* qh = (const uint16_t*)a.q + (int64_t)w.q_start * rs + (int64_t)h * D;
-    const uint16_t* doh = (const uint16_t*)a.dout + (int64_t)w.q_start * rs + (int64_t)h * D;
-    tq.load_k(qh, rs, r0, w.Lq, tid);
-    tq.load_v(qh, rs, r0, w.Lq, tid);
-    tdo.load_k(doh, rs, r0, w.Lq, tid);
-    tdo.load_v(doh, rs, r0, w.Lq, tid);
-    const int q = r0 + (tid & (BM - 1));
-    const int64_t at = (int64_t)h * a.total_q + w.q_start + q;
-    if (tid < BM) lse_v = q < w.Lq ? a.lse[at] : 0.f;
-    else if (tid < 2 * BM) dr_v = q < w.Lq ? a.drow[at] : 0.f;
-  };
-  auto store_step = [&](int buf) {
-    tq.store_k(lds_q[buf], tid);
-    tq.store_v(lds_qt[buf], tid);
-    tdo.store_k(lds_do[buf], tid);
-    tdo.store_v(lds_dot[buf], tid);
-    if (tid < BM) lds_lse[buf][tid] = lse_v * kLog2eF;
-    else if (tid < 2 * BM) lds_dr[buf][tid - BM] = dr_v;
-  };
+  // Query block s (Q, dO, lse, D): loaded into registers while the previous
+  // block is computed, then stored into an LDS buffer.  Rows past the
+  // sequence read as zeros.
+  BlockStage<D, BM> stage;
 
   f32x16 dkt[DB], dvt[DB];
 #pragma unroll
@@ -253,8 +294,8 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   }
 
   if (nsteps > 0) {
-    load_step(0);
-    store_step(0);
+    stage.load(a, w, 0, nblk, i_begin, tid);
+    stage.store(lds_q[0], lds_do[0], lds_lse[0], lds_dr[0], tid);
   }
   __syncthreads();
 
@@ -263,19 +304,23 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     const int buf = s & 1;
     const int h = w.hk * a.head_group + s / nblk;
     const int r0 = (i_begin + s % nblk) * BM;
-    if (s + 1 < nsteps) load_step(s + 1);
+    if (s + 1 < nsteps) stage.load(a, w, s + 1, nblk, i_begin, tid);
+    const uint16_t* qs = lds_q[buf];
+    const uint16_t* dos = lds_do[buf];
 
     // S = Q K^T and dP = dO V^T (rows permuted: register r of half g = row 16g + r)
     f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const v8 aq = *(const v8*)(lds_q[buf] + tiling::ks_index<D>(arow, 2 * ks + g));
-      const v8 ad = *(const v8*)(lds_do[buf] + tiling::ks_index<D>(arow, 2 * ks + g));
-      sc = E::mfma(aq, kb[ks], sc);
-      dp = E::mfma(ad, vb[ks], dp);
+      const v8 aq = *(const v8*)(qs + tiling::ks_index<D>(arow, 2 * ks + g));
+      const v8 ad = *(const v8*)(dos + tiling::ks_index<D>(arow, 2 * ks + g));
+      const v8 bk = *(const v8*)(lds_k + tiling::ks_index<D>(krow, 2 * ks + g));
+      const v8 bv = *(const v8*)(lds_v + tiling::ks_index<D>(krow, 2 * ks + g));
+      sc = E::mfma(aq, bk, sc);
+      dp = E::mfma(ad, bv, dp);
     }
 
-    // P and dS of the lane's 16 rows for its key
+    // P and dS (softmax scale folded in) of the lane's 16 rows for its key
     float lse2[16], drr[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -293,19 +338,20 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
       const int q = r0 + 16 * g + r;
       const bool vis = q < w.Lq && kcol < w.Lk && (!CAUSAL || kcol <= q + shift);
       const float pr = vis ? fast_exp2(__builtin_fmaf(sc[r], a.scale_log2, -lse2[r])) : 0.f;
-      const float dsr = pr * (dp[r] - drr[r]) * a.scale;  // dS with the softmax scale folded in
+      const float dsr = pr * (dp[r] - drr[r]) * a.scale;
       p16[r >> 3][r & 7] = (T)pr;
       ds16[r >> 3][r & 7] = (T)dsr;
     }
 
-    // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 rows)
+    // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 rows); the
+    // transposed A operands come from the row-major tiles by transposing reads
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int d = 32 * db + l32;
-        const v8 adt = *(const v8*)(lds_dot[buf] + tiling::vt_index<BM>(d, 16 * g + 8 * t));
-        const v8 aqt = *(const v8*)(lds_qt[buf] + tiling::vt_index<BM>(d, 16 * g + 8 * t));
+        const int c0 = 32 * db + 16 * (lg & 1), rr = 16 * (lg >> 1) + 8 * t;
+        const v8 adt = tr_read8<v8, D>(dos, rr, c0, li);
+        const v8 aqt = tr_read8<v8, D>(qs, rr, c0, li);
         dvt[db] = E::mfma(adt, p16[t], dvt[db]);
         dkt[db] = E::mfma(aqt, ds16[t], dkt[db]);
       }
@@ -325,7 +371,8 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // dQ rows r0..r0+31: wave -> (32-dim tile, key part)
+    // dQ rows r0..r0+31: wave -> (32-dim tile, key part); K^T operand by
+    // transposing reads of the row-major K block
     {
       constexpr int SPLIT = NW / DB;        // waves per tile (1 at D=128, 2 at D=64)
       constexpr int KEYS = BN / SPLIT;      // keys per wave
@@ -335,7 +382,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
       for (int kk = 0; kk < KEYS / 16; ++kk) {
         const int k16 = part * KEYS + 16 * kk;
         const v8 ads = *(const v8*)(lds_ds + tiling::ks_index<BN>(l32, (k16 >> 3) + g));
-        const v8 bkt = *(const v8*)(lds_kt + tiling::vt_index<BN>(32 * tile + l32, k16 + 8 * g));
+        const v8 bkt = tr_read8<v8, D>(lds_k, k16 + 8 * (lg >> 1), 32 * tile + 16 * (lg & 1), li);
         acc = E::mfma(ads, bkt, acc);
       }
       // accumulator register r of half g holds row 8*(r/4) + 4g + r%4, column 32*tile + l32.
@@ -351,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
       }
     }
 
-    if (s + 1 < nsteps) store_step(buf ^ 1);
+    if (s + 1 < nsteps) stage.store(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_lse[buf ^ 1], lds_dr[buf ^ 1], tid);
     __syncthreads();
   }
 
