@@ -207,6 +207,26 @@ __device__ __forceinline__ V8 tr_read8(const uint16_t* tile, int r0, int c0, int
   return __builtin_bit_cast(V8, v);
 }
 
+// Scheduling order of a block of NM MFMAs fed by NR LDS reads (NR a multiple
+// of NM): the first AHEAD reads, then each MFMA followed by the reads of a
+// later one, so that AHEAD reads are in flight ahead of their use.
+template <int I, int NM, int NR, int AHEAD>
+__device__ __forceinline__ void read_ahead_tail() {
+  if constexpr (I < NM) {
+    constexpr int PER = NR / NM;
+    constexpr int LEFT = NR - AHEAD - I * PER;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (LEFT > 0) __builtin_amdgcn_sched_group_barrier(0x100, LEFT < PER ? LEFT : PER, 0);
+    read_ahead_tail<I + 1, NM, NR, AHEAD>();
+  }
+}
+template <int NM, int NR, int AHEAD>
+__device__ __forceinline__ void read_ahead_schedule() {
+  static_assert(NR % NM == 0 && AHEAD <= NR, "reads per MFMA");
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // LDS reads
+  read_ahead_tail<0, NM, NR, AHEAD>();
+}
+
 // Query block s of a work item (Q, dO, lse, D): loaded into registers while
 // the previous block is computed, then stored into an LDS buffer.  Rows past
 // the sequence read as zeros.  Step s covers query head
@@ -248,12 +268,13 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   typedef typename E::v8 v8;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[BN * D];       // K block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[BN * D];       // V block, row-major
   __shared__ __attribute__((aligned(16))) uint16_t lds_ds[BM * BN];     // dS, row-major
   __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][BM * D];    // query block, row-major
   __shared__ __attribute__((aligned(16))) uint16_t lds_do[2][BM * D];
   __shared__ __attribute__((aligned(16))) float lds_lse[2][BM];
   __shared__ __attribute__((aligned(16))) float lds_dr[2][BM];
+  // key-split partial sums of the dQ tiles (head_dim 64: two waves per tile)
+  __shared__ __attribute__((aligned(16))) float lds_red[NW / DB > 1 ? DB * 64 * 16 : 1];
 
   ColItem w;
   if (!decode_col(a, w)) return;
@@ -269,11 +290,28 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
   const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
 
-  // the K and V blocks of the item in LDS (B operands of S = Q K^T and
-  // dP = dO V^T, and K for dQ = dS K); keys past the sequence read as zero
+  // The operands that stay fixed for the item live in registers: K and V of
+  // the wave's keys (B operands of S = Q K^T and dP = dO V^T, straight from
+  // global memory) and the K^T operand of the wave's dQ tile (read once by
+  // transposing reads from the K block staged in LDS).  Keys past the
+  // sequence read as zero.
+  constexpr int SPLIT = NW / DB;        // waves per dQ tile (1 at D=128, 2 at D=64)
+  constexpr int KEYS = BN / SPLIT;      // keys of a wave's dQ product
+  const int tile = wave % DB, part = wave / DB;
   lds_load_rows<D, BN>(lds_k, kbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
-  lds_load_rows<D, BN>(lds_v, vbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
-  const int krow = 32 * wave + l32;  // this lane's key row in the block
+  v8 kb[KSTEPS], vb[KSTEPS], kt[KEYS / 16];
+  {
+    const int rows = max(0, min(32, w.Lk - key0 - 32 * wave));
+    const int64_t off0 = (int64_t)(key0 + 32 * wave) * rsk;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + off0, tiling::head_rows_bytes(rows, rsk, D, 2));
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + off0, tiling::head_rows_bytes(rows, rsk, D, 2));
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const uint32_t off = ((uint32_t)l32 * (uint32_t)rsk + 16 * ks + 8 * g) * 2u;
+      kb[ks] = __builtin_bit_cast(v8, buffer_load16(rk, off));
+      vb[ks] = __builtin_bit_cast(v8, buffer_load16(rv, off));
+    }
+  }
 
   // query blocks that see a key of this block: rows q with q + shift >= key0
   const int i_begin = CAUSAL ? max(0, key0 - shift) / BM : 0;
@@ -298,6 +336,9 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     stage.store(lds_q[0], lds_do[0], lds_lse[0], lds_dr[0], tid);
   }
   __syncthreads();
+#pragma unroll
+  for (int kk = 0; kk < KEYS / 16; ++kk)
+    kt[kk] = tr_read8<v8, D>(lds_k, part * KEYS + 16 * kk + 8 * (lg >> 1), 32 * tile + 16 * (lg & 1), li);
 
   const int arow = tiling::key_of_arow(l32);
   for (int s = 0; s < nsteps; ++s) {
@@ -314,11 +355,10 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const v8 aq = *(const v8*)(qs + tiling::ks_index<D>(arow, 2 * ks + g));
       const v8 ad = *(const v8*)(dos + tiling::ks_index<D>(arow, 2 * ks + g));
-      const v8 bk = *(const v8*)(lds_k + tiling::ks_index<D>(krow, 2 * ks + g));
-      const v8 bv = *(const v8*)(lds_v + tiling::ks_index<D>(krow, 2 * ks + g));
-      sc = E::mfma(aq, bk, sc);
-      dp = E::mfma(ad, bv, dp);
+      sc = E::mfma(aq, kb[ks], sc);
+      dp = E::mfma(ad, vb[ks], dp);
     }
+    read_ahead_schedule<2 * KSTEPS, 2 * KSTEPS, 8>();
 
     // P and dS (softmax scale folded in) of the lane's 16 rows for its key
     float lse2[16], drr[16];
@@ -355,6 +395,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
         dvt[db] = E::mfma(adt, p16[t], dvt[db]);
         dkt[db] = E::mfma(aqt, ds16[t], dkt[db]);
       }
+    read_ahead_schedule<4 * DB, 8 * DB, 8>();
 
     // dS -> LDS, row-major [row][key].  The 16-bit values are taken from the
     // packed operand registers as whole words (element-wise access to the
@@ -371,19 +412,37 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // dQ rows r0..r0+31: wave -> (32-dim tile, key part); K^T operand by
-    // transposing reads of the row-major K block
+    // dQ rows r0..r0+31: wave -> (32-dim tile, key part)
     {
-      constexpr int SPLIT = NW / DB;        // waves per tile (1 at D=128, 2 at D=64)
-      constexpr int KEYS = BN / SPLIT;      // keys per wave
-      const int tile = wave % DB, part = wave / DB;
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KEYS / 16; ++kk) {
         const int k16 = part * KEYS + 16 * kk;
         const v8 ads = *(const v8*)(lds_ds + tiling::ks_index<BN>(l32, (k16 >> 3) + g));
-        const v8 bkt = tr_read8<v8, D>(lds_k, k16 + 8 * (lg >> 1), 32 * tile + 16 * (lg & 1), li);
-        acc = E::mfma(ads, bkt, acc);
+        acc = E::mfma(ads, kt[kk], acc);
+      }
+      // the next query block goes into the other buffer before the atomics are
+      // issued, so that waiting for its loads does not wait for them too
+      if (s + 1 < nsteps) stage.store(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_lse[buf ^ 1], lds_dr[buf ^ 1], tid);
+      if constexpr (SPLIT > 1) {
+        // two waves hold halves of the key sum of one tile: add them in LDS so
+        // that each dq element receives one atomic addition per key block
+        static_assert(SPLIT == 2, "key split of the dQ product");
+        if (part == 1) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *(f32x4*)(&lds_red[(tile * 64 + lane) * 16 + 4 * r4]) =
+                f32x4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+        }
+        __syncthreads();
+        if (part == 0) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 o = *(const f32x4*)(&lds_red[(tile * 64 + lane) * 16 + 4 * r4]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[4 * r4 + c] += o[c];
+          }
+        }
       }
       // accumulator register r of half g holds row 8*(r/4) + 4g + r%4, column 32*tile + l32.
       // Buffer atomics over the rows of this block that lie in the sequence:
@@ -391,14 +450,15 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
       const __amdgpu_buffer_rsrc_t racc =
           buffer_rsrc(a.dq_acc + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D,
                       tiling::head_rows_bytes(min(BM, w.Lq - r0), rs, D, 4));
+      if (part == 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t off = ((uint32_t)(8 * (r >> 2) + 4 * g + (r & 3)) * (uint32_t)rs + 32 * tile + l32) * 4u;
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], racc, (int)off, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t off = ((uint32_t)(8 * (r >> 2) + 4 * g + (r & 3)) * (uint32_t)rs + 32 * tile + l32) * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], racc, (int)off, 0, 0);
+        }
       }
     }
 
-    if (s + 1 < nsteps) stage.store(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_lse[buf ^ 1], lds_dr[buf ^ 1], tid);
     __syncthreads();
   }
 
