@@ -307,6 +307,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the sweep and dense rows")
     ap.add_argument("--pmc-pass", action="store_true", help="launch sequence for a rocprofv3 --pmc run")
+    ap.add_argument("--bwd-pass", action="store_true",
+                    help="only the backward pass of the 64k ragged causal batch (for profiling)")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="RESULTS_DB", help="print kernel stats of a rocprofv3 trace")
     args = ap.parse_args()
@@ -331,6 +333,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.bwd_pass:
+        print(json.dumps(measure_backward(workload_ragged64k(), True, iters=args.steps)), flush=True)
+        return 0
     if args.pmc_pass:
         pmc_pass(max(1, args.steps))
         return 0
