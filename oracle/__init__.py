@@ -12,6 +12,8 @@ Contents
   * :mod:`oracle.attention`      -- materialised fp64 attention (the definition)
   * :mod:`oracle.attention_grad` -- its gradients dq, dk, dv (chain rule on the
     materialised matrices)
+  * :mod:`oracle.kvcache`        -- attention against a (paged) key/value cache
+    with per-sequence lengths and left padding (the decode-shaped case)
   * :mod:`oracle.online_softmax` -- fp64 tile-by-tile emulation of the online
     softmax, used only to pin the claim that rescaled running statistics give
     the global softmax
@@ -23,6 +25,7 @@ from .cu_seqlens import lengths_from_cu, check_cu_seqlens, row_offset
 from .tile_map import tile_map, tile_items
 from .attention import attention_fwd, attention_rows, visible_mask, flops_visible_pairs, kv_head_of
 from .attention_grad import attention_bwd, attention_loss
+from .kvcache import attention_kvcache, cache_positions, gather_cache
 from .online_softmax import online_softmax_attention, blockwise_normalised_attention
 
 __all__ = [
@@ -38,6 +41,9 @@ __all__ = [
     "kv_head_of",
     "attention_bwd",
     "attention_loss",
+    "attention_kvcache",
+    "cache_positions",
+    "gather_cache",
     "online_softmax_attention",
     "blockwise_normalised_attention",
 ]
