@@ -302,3 +302,111 @@ def draw_qkv(wl: Workload, heads: Optional[Sequence[int]] = None) -> dict:
             x = np.ascontiguousarray(x[:, list(heads), :])
         out[name] = x
     return out
+
+
+# ---------------------------------------------------------------------------
+# key/value-cache (decode-shaped) workloads
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class KVWorkload:
+    """Packed queries against a key/value cache.
+
+    Sequence b has ``lengths_q[b]`` query rows and uses cache positions
+    ``leftpad[b] .. seqlens_k[b]-1``.  Without paging each sequence owns one
+    slot of ``cache_rows`` rows; with paging the cache holds blocks of
+    ``cache_rows`` rows and a block table maps a sequence's pages to shuffled
+    blocks.  Unused cache rows hold random values too."""
+    name: str
+    lengths_q: Tuple[int, ...]
+    seqlens_k: Tuple[int, ...]
+    leftpad: Optional[Tuple[int, ...]]
+    heads: int
+    kv_heads: int
+    head_dim: int
+    dtype: str
+    seed: int
+    cache_rows: int
+    paged: bool = False
+
+    @property
+    def batch(self) -> int:
+        return len(self.lengths_q)
+
+    @property
+    def cu_q(self) -> Tuple[int, ...]:
+        return tuple(int(x) for x in cu_from_lengths(self.lengths_q))
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.lengths_q))
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return max(self.lengths_q) if self.lengths_q else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return max(self.seqlens_k) if self.seqlens_k else 0
+
+    @property
+    def key_lengths(self) -> List[int]:
+        lp = self.leftpad or (0,) * self.batch
+        return [s - p for s, p in zip(self.seqlens_k, lp)]
+
+    @property
+    def blocks_per_seq(self) -> int:
+        return max(1, -(-self.max_seqlen_k // self.cache_rows)) if self.paged else 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def draw_kvcache(wl: KVWorkload) -> dict:
+    """q, k_cache, v_cache (float32 values and 16-bit bits) and, for a paged
+    cache, the int32 block table [batch, blocks_per_seq] (unused entries 0)."""
+    rng = np.random.default_rng(wl.seed)
+    to_bits, to_f32 = {"bf16": (bf16_rne_bits, bf16_bits_to_f32), "f16": (f16_rne_bits, f16_bits_to_f32)}[wl.dtype]
+    out = {}
+    if wl.paged:
+        need = [-(-s // wl.cache_rows) for s in wl.seqlens_k]
+        nblk = sum(need) + 3
+        order = rng.permutation(nblk)
+        table = np.zeros((wl.batch, wl.blocks_per_seq), dtype=np.int32)
+        n = 0
+        for b, k in enumerate(need):
+            table[b, :k] = order[n:n + k]
+            n += k
+        out["block_table"] = table
+        cache_shape = (nblk, wl.cache_rows, wl.kv_heads, wl.head_dim)
+    else:
+        cache_shape = (wl.batch, wl.cache_rows, wl.kv_heads, wl.head_dim)
+    for name, shape in (("q", (wl.total_q, wl.heads, wl.head_dim)), ("k_cache", cache_shape),
+                        ("v_cache", cache_shape)):
+        bits = to_bits(rng.standard_normal(shape, dtype=np.float32)).reshape(shape)
+        out[name + "_bits"] = bits
+        out[name] = to_f32(bits).reshape(shape)
+    return out
+
+
+def workload_decode(name: str, lengths_q, seqlens_k, heads: int, kv_heads: int, head_dim: int, dtype: str,
+                    seed: int, cache_rows: int, leftpad=None, paged: bool = False) -> KVWorkload:
+    if heads % kv_heads:
+        raise ValueError("kv_heads must divide heads")
+    if leftpad is not None and any(p > s for p, s in zip(leftpad, seqlens_k)):
+        raise ValueError("leftpad must not exceed seqlens_k")
+    if not paged and max(seqlens_k, default=0) > cache_rows:
+        raise ValueError("a sequence longer than its cache slot")
+    return KVWorkload(name, tuple(int(x) for x in lengths_q), tuple(int(x) for x in seqlens_k),
+                      None if leftpad is None else tuple(int(x) for x in leftpad), heads, kv_heads, head_dim,
+                      dtype, seed, cache_rows, paged)
+
+
+def workload_decode_bench(seed: int = 9) -> KVWorkload:
+    """Single-token decoding: 32 sequences with cached lengths log-uniform in
+    [1024, 16384], 32 query heads on 8 key/value heads, d=128, bf16, a paged
+    cache of 256-row blocks."""
+    rng = np.random.default_rng(seed)
+    seqlens = [int(round(math.exp(rng.uniform(math.log(1024), math.log(16384))))) for _ in range(32)]
+    return workload_decode(f"decode_b32_h32_kv8_d128_paged256_seed{seed}", [1] * 32, seqlens, 32, 8, 128, "bf16",
+                           seed, 256, paged=True)

@@ -233,6 +233,63 @@ int fa_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t num_hea
                                  size_t* bytes);
 
 /*
+ * Attention of packed queries against a key/value cache (the decode-shaped
+ * case: few query rows per sequence, long cached key ranges).
+ *
+ * The operation is the forward pass above with each sequence's keys and
+ * values taken from a cache (friki.work, "Mecanismo cu_seqlens en
+ * FlashAttention", sections "Lógica de cálculo de longitud" and
+ * "Optimización de acceso a memoria": per-sequence key lengths that are not
+ * cumulative, a batch-strided cache slot, a left padding subtracted from the
+ * length; section "Integración con máscaras causales y caché paginada": a
+ * paged cache).  Readings fixed here: sequence b's keys are cache positions
+ * leftpad_k[b] .. seqlens_k[b]-1 (key length seqlens_k[b] - leftpad_k[b]);
+ * without a block table position p of sequence b is row p of cache block b;
+ * with one it is row p % cache_rows of block block_table[b * blocks_per_seq
+ * + p / cache_rows]; the causal mask is bottom-right as above, so one new
+ * query token sees every cached key.
+ *
+ *   q, out        device [total_q, num_heads, head_dim] packed by
+ *                 cu_seqlens_q (out written for rows < cu_seqlens_q[batch])
+ *   k_cache, v_cache  device [cache_blocks, cache_rows, num_heads_k, head_dim]
+ *   cu_seqlens_q  device int32 [batch + 1], cumulative
+ *   seqlens_k     device int32 [batch], NOT cumulative
+ *   leftpad_k     device int32 [batch] or NULL (no left padding)
+ *   block_table   device int32 [batch, blocks_per_seq] or NULL (then
+ *                 cache_blocks >= batch and block b is sequence b's slot)
+ *   max_seqlen_q  >= every query length; max_seqlen_k >= every seqlens_k[b]
+ *                 and at most the positions a sequence can hold (cache_rows,
+ *                 or blocks_per_seq * cache_rows with a block table)
+ *   lse           device float32 [num_heads, total_q] as fa_varlen_fwd
+ *   num_splits    0 (chosen from the sizes) or 1..64 workgroups per
+ *                 (sequence, key/value head), each over a contiguous key range
+ *   workspace     device scratch of >= fa_varlen_kvcache_workspace_size
+ *                 bytes for this num_splits, 16-byte aligned, caller-owned
+ * Preconditions (not checked on the device): 0 <= leftpad_k[b] <=
+ * seqlens_k[b] <= max_seqlen_k and block table entries < cache_blocks.
+ * dtype FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_ERR_DTYPE), head_dim 64 or 128
+ * (FA_ERR_HEAD_DIM); other checks and errors as fa_varlen_fwd, plus
+ * FA_ERR_WORKSPACE and FA_ERR_ARG for num_splits out of range.
+ */
+int fa_varlen_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                          const int32_t* leftpad_k, const int32_t* block_table,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          float softmax_scale, int32_t causal, void* out, float* lse,
+                          int32_t batch, int32_t total_q, int32_t cache_blocks, int32_t cache_rows,
+                          int32_t blocks_per_seq, int32_t num_heads, int32_t num_heads_k,
+                          int32_t head_dim, int32_t dtype, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes of fa_varlen_fwd_kvcache: float32 partial outputs and
+ * (max, sum) pairs for every (query row, head, split, wavefront); num_splits
+ * 0 sizes for the largest automatic choice (64).  Host only.
+ */
+int fa_varlen_kvcache_workspace_size(int32_t total_q, int32_t num_heads, int32_t head_dim,
+                                     int32_t num_splits, size_t* bytes);
+
+/*
  * Device-side check of the cu_seqlens preconditions (friki.work, section
  * "Estructuras de datos clave": batch+1 cumulative offsets).  Writes to
  * `flags` (device int32 [1]) a bit mask, 0 when valid:

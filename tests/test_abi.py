@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["fa_status_string", "fa_varlen_block_sizes", "fa_varlen_tile_map",
                             "fa_varlen_fwd", "fa_varlen_fwd_mapped", "fa_varlen_check_cu_seqlens",
-                            "fa_varlen_bwd", "fa_varlen_bwd_workspace_size"])
+                            "fa_varlen_bwd", "fa_varlen_bwd_workspace_size", "fa_varlen_fwd_kvcache",
+                            "fa_varlen_kvcache_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -217,3 +218,49 @@ def test_bwd_workspace_size():
     # the exact size passes validation; one byte less does not
     need = size(1, 8, 2, 64)
     assert call_bwd(ws_bytes=need - 1) == 9
+
+
+# ---------------------------------------------------------------- key/value cache
+def call_kv(**over):
+    args = dict(q=A16, kc=A16, vc=A16, cu_q=A16, sk=A16, lp=None, bt=None, max_q=1, max_k=8, scale=0.125,
+                causal=0, out=A16, lse=A16, batch=1, total_q=1, blocks=1, rows=8, bps=0, heads=2, heads_k=1,
+                head_dim=64, dtype=1, splits=0, ws=A16, ws_bytes=1 << 24)
+    args.update(over)
+    lib = fa.load_library()
+    return lib.fa_varlen_fwd_kvcache(args["q"], args["kc"], args["vc"], args["cu_q"], args["sk"], args["lp"],
+                                     args["bt"], args["max_q"], args["max_k"], args["scale"], args["causal"],
+                                     args["out"], args["lse"], args["batch"], args["total_q"], args["blocks"],
+                                     args["rows"], args["bps"], args["heads"], args["heads_k"], args["head_dim"],
+                                     args["dtype"], args["splits"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(kc=None), 1), (dict(vc=None), 1), (dict(cu_q=None), 1), (dict(sk=None), 1),
+    (dict(out=None), 1), (dict(lse=None), 1),
+    (dict(dtype=0), 2), (dict(dtype=5), 2),
+    (dict(head_dim=96), 4), (dict(head_dim=256), 4),
+    (dict(heads_k=3), 3), (dict(max_q=2), 3), (dict(rows=0), 3), (dict(max_k=9), 3), (dict(blocks=0), 3),
+    (dict(bt=A16, bps=0), 3), (dict(bt=A16, bps=1, max_k=9), 3), (dict(batch=-1), 3),
+    (dict(scale=0.0), 6), (dict(causal=3), 6), (dict(splits=-1), 6), (dict(splits=65), 6),
+    (dict(q=A16 + 8), 5), (dict(kc=A16 + 4), 5), (dict(out=A16 + 2), 5), (dict(lp=A16 + 2), 5),
+    (dict(bt=A16 + 1, bps=1), 5), (dict(sk=A16 + 2), 5),
+    (dict(ws=None), 9), (dict(ws_bytes=16), 9),
+])
+def test_kvcache_validation(over, code):
+    assert call_kv(**over) == code
+
+
+def test_kvcache_workspace_size_and_empty():
+    lib = fa.load_library()
+    n = ctypes.c_size_t(0)
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for t, h, d, s in ((1, 2, 64, 1), (7, 32, 128, 4), (64, 8, 128, 0)):
+        assert lib.fa_varlen_kvcache_workspace_size(t, h, d, s, ctypes.byref(n)) == 0
+        p = (s if s else 64) * 4
+        assert n.value == r(t * h * p * d * 4) + r(t * h * p * 2 * 4)
+        assert fa.fa_varlen_kvcache_workspace_size(t, h, d, s) == n.value
+    assert lib.fa_varlen_kvcache_workspace_size(1, 2, 64, 65, ctypes.byref(n)) == 6
+    assert lib.fa_varlen_kvcache_workspace_size(1, 2, 64, 0, None) == 1
+    # no query rows: valid, nothing launched
+    assert call_kv(batch=0, total_q=0, max_q=0) == 0
+    assert call_kv(total_q=0, max_q=0) == 0

@@ -8,7 +8,8 @@ built every entry point raises :class:`FaVarlenError`.
 
 Functions carry the names of the C entry points:
   fa_varlen_fwd, fa_varlen_fwd_mapped, fa_varlen_bwd,
-  fa_varlen_bwd_workspace_size, fa_varlen_tile_map, fa_varlen_block_sizes,
+  fa_varlen_bwd_workspace_size, fa_varlen_fwd_kvcache,
+  fa_varlen_kvcache_workspace_size, fa_varlen_tile_map, fa_varlen_block_sizes,
   fa_varlen_check_cu_seqlens, fa_status_string.
 """
 from __future__ import annotations
@@ -32,6 +33,8 @@ __all__ = [
     "fa_varlen_fwd_mapped",
     "fa_varlen_bwd",
     "fa_varlen_bwd_workspace_size",
+    "fa_varlen_fwd_kvcache",
+    "fa_varlen_kvcache_workspace_size",
     "fa_varlen_check_cu_seqlens",
 ]
 
@@ -87,6 +90,12 @@ def load_library() -> ctypes.CDLL:
     lib.fa_varlen_bwd.restype = ctypes.c_int
     lib.fa_varlen_bwd_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_varlen_bwd_workspace_size.restype = ctypes.c_int
+    lib.fa_varlen_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp,
+                                          i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                          vp, ctypes.c_size_t, vp]
+    lib.fa_varlen_fwd_kvcache.restype = ctypes.c_int
+    lib.fa_varlen_kvcache_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_varlen_kvcache_workspace_size.restype = ctypes.c_int
     lib.fa_varlen_check_cu_seqlens.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.fa_varlen_check_cu_seqlens.restype = ctypes.c_int
     _LIB = lib
@@ -274,6 +283,69 @@ def fa_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
         workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
     _check(st, "fa_varlen_bwd")
     return dq, dk, dv
+
+
+def fa_varlen_kvcache_workspace_size(total_q: int, num_heads: int, head_dim: int, num_splits: int = 0) -> int:
+    """Bytes of device workspace fa_varlen_fwd_kvcache needs."""
+    n = ctypes.c_size_t(0)
+    _check(load_library().fa_varlen_kvcache_workspace_size(int(total_q), int(num_heads), int(head_dim),
+                                                           int(num_splits), ctypes.byref(n)),
+           "fa_varlen_kvcache_workspace_size")
+    return n.value
+
+
+def fa_varlen_fwd_kvcache(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                          softmax_scale: Optional[float] = None, causal: bool = False, leftpad_k=None,
+                          block_table=None, num_splits: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """Attention of packed queries against a key/value cache.
+
+    q [total_q, H, D] (bf16/fp16, CUDA) packed by cu_seqlens_q; k_cache,
+    v_cache [blocks, rows, Hk, D]; seqlens_k int32 [batch] (not cumulative);
+    optional leftpad_k int32 [batch] and block_table int32 [batch, blocks_per_seq]
+    (without one, block b is sequence b's slot).  Returns (out, lse).
+    """
+    torch = _torch()
+    q = q.contiguous()
+    k_cache, v_cache = k_cache.contiguous(), v_cache.contiguous()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("expected q [total_q, H, D] and caches [blocks, rows, Hk, D]")
+    if k_cache.shape[2] < 1 or q.shape[1] % k_cache.shape[2]:
+        raise ValueError("the key/value head count must divide the query head count")
+    if q.dtype != k_cache.dtype or q.dtype != v_cache.dtype or not (q.is_cuda and k_cache.is_cuda):
+        raise TypeError("q and the caches must be CUDA tensors of one dtype")
+    dt = _dtype_code(q)
+    cu_q = _dev_i32(cu_seqlens_q, "cu_seqlens_q")
+    batch = cu_q.numel() - 1
+    sk = _dev_i32(seqlens_k, "seqlens_k")
+    if sk.numel() != batch:
+        raise ValueError("seqlens_k must have one entry per sequence")
+    lp = None
+    if leftpad_k is not None:
+        lp = _dev_i32(leftpad_k, "leftpad_k")
+        if lp.numel() != batch:
+            raise ValueError("leftpad_k must have one entry per sequence")
+    bps = 0
+    if block_table is not None:
+        if not (block_table.is_cuda and block_table.dtype == torch.int32 and block_table.dim() == 2
+                and block_table.shape[0] == batch and block_table.is_contiguous()):
+            raise TypeError("block_table must be a contiguous int32 CUDA tensor [batch, blocks_per_seq]")
+        bps = block_table.shape[1]
+    total_q, H, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        workspace = torch.empty(max(fa_varlen_kvcache_workspace_size(total_q, H, D, num_splits), 1),
+                                dtype=torch.uint8, device=q.device)
+    st = load_library().fa_varlen_fwd_kvcache(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_q.data_ptr(), sk.data_ptr(),
+        None if lp is None else lp.data_ptr(), None if block_table is None else block_table.data_ptr(),
+        int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale), int(bool(causal)), out.data_ptr(),
+        lse.data_ptr(), batch, total_q, k_cache.shape[0], k_cache.shape[1], bps, H, k_cache.shape[2], D, dt,
+        int(num_splits), workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
+    _check(st, "fa_varlen_fwd_kvcache")
+    return out, lse
 
 
 def fa_varlen_check_cu_seqlens(cu_seqlens_q, cu_seqlens_k, total_q: int, total_k: int, max_seqlen_q: int,

@@ -105,6 +105,28 @@ BwdLayout bwd_layout(int64_t batch, int64_t total_q, int64_t heads, int64_t head
   return l;
 }
 
+// Key/value-cache attention: split count and workspace.
+constexpr int kMaxSplits = 64;
+
+int64_t dec_parts(int32_t num_splits) { return (int64_t)(num_splits > 0 ? num_splits : kMaxSplits) * fa::decode_waves(); }
+
+size_t dec_workspace(int64_t total_q, int64_t heads, int64_t head_dim, int32_t num_splits) {
+  const int64_t rows = total_q * heads * dec_parts(num_splits);
+  return round256((size_t)rows * head_dim * sizeof(float)) + round256((size_t)rows * 2 * sizeof(float));
+}
+
+// Splits when the caller leaves the choice: about eight workgroups per
+// compute unit (the pass streams the cache from HBM and needs many loads in
+// flight), at least one 32-key tile per wavefront of a split.
+int32_t auto_splits(int64_t batch, int64_t kv_heads, int64_t max_k) {
+  const int64_t items = batch * kv_heads;
+  int64_t s = items > 0 ? (8 * kComputeUnits + items - 1) / items : 1;
+  const int64_t by_keys = (max_k + 32 * 4 - 1) / (32 * 4);
+  if (s > by_keys) s = by_keys;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return (int32_t)(s < 1 ? 1 : s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,6 +281,74 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* out, 
     if (fa::launch_bwd(dtype, head_dim, causal != 0, (int)grid, a, s) != hipSuccess) return FA_ERR_HIP;
   }
   if (fa::launch_bwd_dq(dtype, head_dim, a, s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int fa_varlen_kvcache_workspace_size(int32_t total_q, int32_t num_heads, int32_t head_dim, int32_t num_splits,
+                                     size_t* bytes) {
+  if (!bytes) return FA_ERR_NULL;
+  if (total_q < 0 || num_heads < 1 || head_dim < 1) return FA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  *bytes = dec_workspace(total_q, num_heads, head_dim, num_splits);
+  return FA_OK;
+}
+
+int fa_varlen_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
+                          const int32_t* seqlens_k, const int32_t* leftpad_k, const int32_t* block_table,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                          void* out, float* lse, int32_t batch, int32_t total_q, int32_t cache_blocks,
+                          int32_t cache_rows, int32_t blocks_per_seq, int32_t num_heads, int32_t num_heads_k,
+                          int32_t head_dim, int32_t dtype, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !seqlens_k || !out || !lse) return FA_ERR_NULL;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_DTYPE;
+  if (head_dim != 64 && head_dim != 128) return FA_ERR_HEAD_DIM;
+  if (batch < 0 || total_q < 0 || num_heads < 1 || max_seqlen_q < 0 || max_seqlen_k < 0) return FA_ERR_SHAPE;
+  if (num_heads_k < 1 || num_heads % num_heads_k != 0) return FA_ERR_SHAPE;
+  if (max_seqlen_q > total_q || cache_rows < 1 || cache_blocks < 0) return FA_ERR_SHAPE;
+  if (block_table) {
+    if (blocks_per_seq < 1 || (int64_t)max_seqlen_k > (int64_t)blocks_per_seq * cache_rows) return FA_ERR_SHAPE;
+  } else {
+    if (cache_blocks < batch || max_seqlen_k > cache_rows) return FA_ERR_SHAPE;
+  }
+  if ((int64_t)num_heads * head_dim > (int64_t{1} << 22)) return FA_ERR_TOO_LARGE;
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16)) return FA_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(seqlens_k, 4)) return FA_ERR_ALIGN;
+  if ((leftpad_k && !aligned(leftpad_k, 4)) || (block_table && !aligned(block_table, 4))) return FA_ERR_ALIGN;
+  const int32_t splits = num_splits > 0 ? num_splits : auto_splits(batch, num_heads_k, max_seqlen_k);
+  if (!workspace || workspace_bytes < dec_workspace(total_q, num_heads, head_dim, splits)) return FA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+  if ((int64_t)batch * num_heads_k * splits > INT32_MAX) return FA_ERR_TOO_LARGE;
+  if (batch == 0 || total_q == 0) return FA_OK;  // no query rows
+
+  const int64_t rows = (int64_t)total_q * num_heads * splits * fa::decode_waves();
+  fa::DecArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.out = out;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.seqlens_k = seqlens_k;
+  a.leftpad_k = leftpad_k;
+  a.block_table = block_table;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)rows * head_dim * 4));
+  a.row_stride = (int64_t)num_heads * head_dim;
+  a.kv_row_stride = (int64_t)num_heads_k * head_dim;
+  a.scale_log2 = (float)((double)softmax_scale * kLog2e);
+  a.batch = batch;
+  a.total_q = total_q;
+  a.heads = num_heads;
+  a.kv_heads = num_heads_k;
+  a.head_group = num_heads / num_heads_k;
+  a.cache_rows = cache_rows;
+  a.blocks_per_seq = block_table ? blocks_per_seq : 0;
+  a.num_splits = splits;
+  if (fa::launch_decode(dtype, head_dim, causal != 0, a, (hipStream_t)stream) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 

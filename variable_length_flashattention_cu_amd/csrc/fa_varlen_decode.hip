@@ -1,0 +1,286 @@
+// fa_varlen_decode.hip -- gfx950 kernels for exact attention of packed queries
+// against a key/value cache: per-sequence key lengths that are not
+// cumulative, an optional left padding, an optional paged cache layout, and
+// the key range of each sequence split across workgroups (the decode-shaped
+// case: few query rows per sequence, long cached key ranges).
+//
+// Pages: friki.work "Mecanismo cu_seqlens en FlashAttention", sections "Lógica
+// de cálculo de longitud" and "Optimización de acceso a memoria" (with the
+// non-cumulative key format a sequence's keys sit at its batch index times a
+// batch stride and its usable key length is the given length minus the left
+// padding) and "Integración con máscaras causales y caché paginada" (a paged
+// key/value cache); slavadubrov.com "O que FlashAttention muda na
+// inferência", section "A implementação e a carga de trabalho continuam a
+// importar" (single-token decoding exposes different parallelism than
+// prefill).
+//
+// Layouts:
+//   q, out   [total_q, heads, D] packed by cu_seqlens_q (as the forward pass)
+//   caches   [cache_blocks, cache_rows, kv_heads, D]; without a block table
+//            block b is sequence b's slot; with one, position p of sequence b
+//            is row p % cache_rows of block block_table[b * blocks_per_seq +
+//            p / cache_rows]
+//   sequence b's keys are cache positions leftpad_k[b] .. seqlens_k[b]-1
+//
+// Work: one workgroup per (sequence, key/value head, split).  Its rows are all
+// query rows of the sequence for all query heads of the key/value head
+// (G * Lq rows, G = heads / kv_heads), so the cache is read once per group;
+// they are processed 32 at a time.  The split's 32-key tiles are dealt to the
+// 4 wavefronts round-robin; each wavefront streams its tiles straight from
+// global memory (K as the A operand of S^T = K Q^T, V through a wave-private
+// LDS tile read back with transposing reads as the A operand of O^T = V^T P^T),
+// keeps an online softmax per row and writes its partial (max, sum, O) to the
+// workspace.  decode_combine_kernel merges the partials of every row
+// (partials with max m_p, sum l_p and output O_p give out = sum_p 2^(m_p-m)
+// O_p / sum_p 2^(m_p-m) l_p with m = max_p m_p; the same rescaling identity
+// as the online softmax).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_varlen_device.h"
+#include "fa_varlen_launch.h"
+#include "fa_varlen_tiling.h"
+
+namespace fa {
+namespace {
+
+constexpr int kDecWaves = 4;  // wavefronts per workgroup
+constexpr int kDecTile = 32;  // keys per tile
+
+typedef short dec_s16x4 __attribute__((ext_vector_type(4)));
+
+// transposing read of 4 rows r0 .. r0+3 of column c0 + i (16-lane groups, see
+// ds_read_b64_tr_b16) from a row-major swizzled [rows][D] tile
+template <int D>
+__device__ __forceinline__ dec_s16x4 dec_tr_read4(const uint16_t* tile, int r0, int c0, int i) {
+  const int row = r0 + (i >> 2), col = c0 + 4 * (i & 3);
+  const uint16_t* p = tile + tiling::ks_index<D>(row, col >> 3) + (col & 7);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) dec_s16x4*)p);
+}
+template <typename V8, int D>
+__device__ __forceinline__ V8 dec_tr_read8(const uint16_t* tile, int r0, int c0, int i) {
+  const dec_s16x4 lo = dec_tr_read4<D>(tile, r0, c0, i);
+  const dec_s16x4 hi = dec_tr_read4<D>(tile, r0 + 4, c0, i);
+  const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(V8, v);
+}
+
+// Element offset of cache position p of sequence b, key/value head hk.
+__device__ __forceinline__ int64_t cache_offset(const DecArgs& a, int b, int p, int hk, int D) {
+  int64_t row;
+  if (a.block_table) {
+    const int blk = a.block_table[(int64_t)b * a.blocks_per_seq + p / a.cache_rows];
+    row = (int64_t)blk * a.cache_rows + p % a.cache_rows;
+  } else {
+    row = (int64_t)b * a.cache_rows + p;
+  }
+  return row * a.kv_row_stride + (int64_t)hk * D;
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  using E = Elem16<T>;
+  typedef typename E::v8 v8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kDecWaves][kDecTile * D];
+
+  // item: (sequence b, key/value head hk, split s)
+  const int item = blockIdx.x;
+  const int s = item % a.num_splits;
+  const int hk = (item / a.num_splits) % a.kv_heads;
+  const int b = item / (a.num_splits * a.kv_heads);
+  if (b >= a.batch) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int li = lane & 15, lg = lane >> 4;
+  const int G = a.head_group;
+  const int q_start = a.cu_q[b];
+  const int Lq = a.cu_q[b + 1] - q_start;
+  const int lp = a.leftpad_k ? a.leftpad_k[b] : 0;
+  const int Lk = a.seqlens_k[b] - lp;
+  const int shift = Lk - Lq;
+  const int rows = G * Lq;
+  const int ntiles = (max(Lk, 0) + kDecTile - 1) / kDecTile;
+  const int tps = (ntiles + a.num_splits - 1) / a.num_splits;
+  const int t_begin = s * tps, t_end = min(ntiles, t_begin + tps);
+  const int part = s * kDecWaves + wave;  // this wave's partial slot
+  const int npart = a.num_splits * kDecWaves;
+  uint16_t* vt = lds_v[wave];
+  const int arow = tiling::key_of_arow(l32);
+
+  for (int rt = 0; rt * 32 < rows; ++rt) {
+    // Q^T of the row tile as the B operand: lane l32 <-> row rt*32 + l32
+    const int r = rt * 32 + l32;
+    const bool rvalid = r < rows;
+    const int qi = rvalid ? r / G : 0, gi = rvalid ? r % G : 0;
+    const int h = hk * G + gi;
+    v8 qreg[KSTEPS];
+    {
+      const uint16_t* qp = (const uint16_t*)a.q + (int64_t)(q_start + qi) * a.row_stride + (int64_t)h * D;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (rvalid) x = *(const u32x4*)(qp + 16 * ks + 8 * g);
+        qreg[ks] = __builtin_bit_cast(v8, x);
+      }
+    }
+    const int lim = CAUSAL ? min(Lk - 1, qi + shift) : Lk - 1;  // last visible key of the row
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    float m_run = kNegInf, l_run = 0.f;
+
+    for (int t = t_begin + wave; t < t_end; t += kDecWaves) {
+      const int key0 = t * kDecTile;
+      // K rows of the tile in the permuted A-row order, V rows in natural order
+      const int kk = key0 + arow, kv = key0 + l32;
+      const uint16_t* kp = (const uint16_t*)a.k_cache + (kk < Lk ? cache_offset(a, b, lp + kk, hk, D) : 0);
+      const uint16_t* vp = (const uint16_t*)a.v_cache + (kv < Lk ? cache_offset(a, b, lp + kv, hk, D) : 0);
+      v8 ka[KSTEPS];
+      u32x4 vr[KSTEPS];
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+        if (kk < Lk) x = *(const u32x4*)(kp + 16 * ks + 8 * g);
+        if (kv < Lk) y = *(const u32x4*)(vp + 16 * ks + 8 * g);
+        ka[ks] = __builtin_bit_cast(v8, x);
+        vr[ks] = y;
+      }
+      // V tile into the wave's LDS buffer (row-major, swizzled)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) *(u32x4*)(vt + tiling::ks_index<D>(l32, 2 * ks + g)) = vr[ks];
+
+      // S^T = K Q^T: register e of half g holds key key0 + 16g + e of row l32
+      f32x16 sc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) sc = E::mfma(ka[ks], qreg[ks], sc);
+
+      float mx = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool vis = key0 + 16 * g + e <= lim;
+        sc[e] = vis ? sc[e] * a.scale_log2 : kNegInf;
+        mx = fmaxf(mx, sc[e]);
+      }
+      const float m_new = fmaxf(m_run, pair_max(mx));
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      v8 p[2];
+      float lsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = fast_exp2(sc[e] - m_use);
+        lsum += pe;
+        p[e >> 3][e & 7] = (T)pe;
+      }
+      l_run = l_run * alpha + lsum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+
+      // O^T += V^T P^T: V^T read back from the tile with transposing reads
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const v8 av = dec_tr_read8<v8, D>(vt, 16 * (lg >> 1) + 8 * tt, 32 * db + 16 * (lg & 1), li);
+          o[db] = E::mfma(av, p[tt], o[db]);
+        }
+    }
+
+    // partial of this wave for the rows of the tile
+    const float l = pair_sum(l_run);
+    if (rvalid) {
+      const int64_t pr = ((int64_t)(q_start + qi) * a.heads + h) * npart + part;
+      float* po = a.part_o + pr * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          *(f32x4*)(po + 32 * db + 8 * s4 + 4 * g) =
+              f32x4{o[db][4 * s4], o[db][4 * s4 + 1], o[db][4 * s4 + 2], o[db][4 * s4 + 3]};
+      if (g == 0) {
+        a.part_ml[2 * pr] = m_run;
+        a.part_ml[2 * pr + 1] = l;
+      }
+    }
+  }
+}
+
+// One wavefront per (row, head): merge its partials into out and lse.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row * heads + head
+  const int64_t nrows = a.cu_q[a.batch];
+  if (rh >= nrows * a.heads) return;
+  const int npart = a.num_splits * kDecWaves;
+  const float* ml = a.part_ml + rh * npart * 2;
+  float m = kNegInf;
+  for (int p = lane; p < npart; p += 64) m = fmaxf(m, ml[2 * p]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const float m_use = m == kNegInf ? 0.f : m;
+  constexpr int PER = D / 64;  // dims per lane (1 or 2)
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  float lsum = 0.f;
+  for (int p = 0; p < npart; ++p) {
+    const float w = fast_exp2(ml[2 * p] - m_use);  // 0 for an empty partial (m_p = -inf)
+    lsum += w * ml[2 * p + 1];
+    const float* po = a.part_o + (rh * npart + p) * D;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] += w * po[lane * PER + j];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  T* op = (T*)a.out + rh * D;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) op[lane * PER + j] = (T)(acc[j] * inv);
+  if (lane == 0) {
+    const int64_t row = rh / a.heads;
+    const int h = (int)(rh % a.heads);
+    a.lse[(int64_t)h * a.total_q + row] = lsum > 0.f ? (m + fast_log2(lsum)) * kLn2 : kNegInf;
+  }
+}
+
+template <typename F>
+hipError_t launch(F kernel, int64_t grid, hipStream_t stream, const DecArgs& a) {
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_decode_t(int head_dim, bool causal, int64_t grid, int64_t grid_c, const DecArgs& a,
+                           hipStream_t stream) {
+  hipError_t e;
+  if (head_dim == 128)
+    e = causal ? launch(decode16_kernel<T, 128, true>, grid, stream, a)
+               : launch(decode16_kernel<T, 128, false>, grid, stream, a);
+  else
+    e = causal ? launch(decode16_kernel<T, 64, true>, grid, stream, a)
+               : launch(decode16_kernel<T, 64, false>, grid, stream, a);
+  if (e != hipSuccess || grid_c == 0) return e;
+  return head_dim == 128 ? launch(decode_combine_kernel<T, 128>, grid_c, stream, a)
+                         : launch(decode_combine_kernel<T, 64>, grid_c, stream, a);
+}
+
+}  // namespace
+
+int decode_waves() { return kDecWaves; }
+
+hipError_t launch_decode(int dtype, int head_dim, bool causal, const DecArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.batch * a.kv_heads * a.num_splits;
+  const int64_t grid_c = ((int64_t)a.total_q * a.heads + 3) / 4;
+  if (grid == 0) return hipSuccess;
+  if (dtype == 1) return launch_decode_t<__bf16>(head_dim, causal, grid, grid_c, a, stream);
+  if (dtype == 2) return launch_decode_t<_Float16>(head_dim, causal, grid, grid_c, a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

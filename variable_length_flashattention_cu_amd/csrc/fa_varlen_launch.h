@@ -77,6 +77,36 @@ hipError_t launch_bwd(int dtype, int head_dim, bool causal, int grid, const BwdA
 // dq = softmax_scale * accumulator, in the input type
 hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream);
 
+// Kernel arguments of attention against a key/value cache (passed by value).
+struct DecArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  void* out;
+  float* lse;
+  const int32_t* cu_q;
+  const int32_t* seqlens_k;    // [batch], not cumulative
+  const int32_t* leftpad_k;    // [batch] or null
+  const int32_t* block_table;  // [batch, blocks_per_seq] or null (one slot per sequence)
+  float* part_o;               // [total_q, heads, num_splits * waves, head_dim] partial outputs
+  float* part_ml;              // [total_q, heads, num_splits * waves, 2] partial max (log2) and sum
+  int64_t row_stride;          // heads * head_dim
+  int64_t kv_row_stride;       // kv_heads * head_dim (elements between cache rows)
+  float scale_log2;
+  int32_t batch;
+  int32_t total_q;
+  int32_t heads;
+  int32_t kv_heads;
+  int32_t head_group;
+  int32_t cache_rows;          // rows per slot or per block
+  int32_t blocks_per_seq;
+  int32_t num_splits;
+};
+
+// wavefronts per decode workgroup (each writes one partial per row and split)
+int decode_waves();
+hipError_t launch_decode(int dtype, int head_dim, bool causal, const DecArgs& a, hipStream_t stream);
+
 hipError_t launch_tile_map(const int32_t* cu_q, int batch, int block_m, int32_t* blk_start, hipStream_t stream);
 hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, int total_q, int total_k,
