@@ -43,7 +43,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, Workload, draw_dout, draw_qkv, workload_dense,  # noqa: E402
-                      workload_ragged64k, workload_ragged64k_gqa, workload_sweep)
+                      workload_ragged64k, workload_ragged64k_gqa, workload_sweep, draw_kvcache,
+                      workload_decode_bench)
 
 METRIC = "varlen attention fwd TFLOP/s and % of bf16 MFMA peak, d=64/128, causal"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
@@ -189,6 +190,43 @@ def measure_backward(wl: Workload, causal: bool, iters: int = 10) -> dict:
             "tflops": round(fl / ms / 1e9, 1), "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
 
+def measure_decode(wl, iters: int = 20) -> dict:
+    """fa_varlen_fwd_kvcache (decode kernel and partial combine) on a cache batch.
+    Algorithmic bytes: the cached K and V rows each sequence uses (once per
+    key/value head), q read, out and lse written."""
+    import torch
+    import variable_length_flashattention_cu_amd as fa
+    data = draw_kvcache(wl)
+    tt = {"bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
+    dev = {n: torch.from_numpy(data[n + "_bits"].view(np.int16)).to("cuda").view(tt)
+           for n in ("q", "k_cache", "v_cache")}
+    bt = torch.from_numpy(data["block_table"]).to("cuda") if wl.paged else None
+    del data
+    cu_q = torch.tensor(wl.cu_q, dtype=torch.int32, device="cuda")
+    sk = torch.tensor(wl.seqlens_k, dtype=torch.int32, device="cuda")
+    lp = None if wl.leftpad is None else torch.tensor(wl.leftpad, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty((wl.heads, wl.total_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_varlen_kvcache_workspace_size(wl.total_q, wl.heads, wl.head_dim, 0), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        fa.fa_varlen_fwd_kvcache(dev["q"], dev["k_cache"], dev["v_cache"], cu_q, sk, wl.max_seqlen_q,
+                                 wl.max_seqlen_k, wl.scale, True, leftpad_k=lp, block_table=bt, out=out, lse=lse,
+                                 workspace=ws)
+    for _ in range(3):
+        step()
+    ms = time_events(step, iters)
+    es = 2
+    kv_bytes = 2.0 * sum(wl.key_lengths) * wl.kv_heads * wl.head_dim * es
+    qo_bytes = 2.0 * wl.total_q * wl.heads * wl.head_dim * es + 4.0 * wl.total_q * wl.heads
+    gbs = (kv_bytes + qo_bytes) / ms / 1e6
+    return {"workload": wl.name, "batch": wl.batch, "kv_tokens": int(sum(wl.key_lengths)), "heads": wl.heads,
+            "kv_heads": wl.kv_heads, "head_dim": wl.head_dim, "dtype": wl.dtype, "ms_per_call": round(ms, 4),
+            "algorithmic_bytes": round(kv_bytes + qo_bytes), "gb_per_s": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(wl: Workload, causal: bool, data: dict, heads=(0,)) -> dict:
     """The oracle (float64 numpy) on a bounded sample: one head, every sequence."""
     from threadpoolctl import threadpool_info
@@ -307,6 +345,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the sweep and dense rows")
     ap.add_argument("--pmc-pass", action="store_true", help="launch sequence for a rocprofv3 --pmc run")
+    ap.add_argument("--decode-pass", action="store_true",
+                    help="only the key/value-cache decode batch (for profiling)")
     ap.add_argument("--bwd-pass", action="store_true",
                     help="only the backward pass of the 64k ragged causal batch (for profiling)")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -333,6 +373,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.decode_pass:
+        print(json.dumps(measure_decode(workload_decode_bench(), iters=args.steps)), flush=True)
+        return 0
     if args.bwd_pass:
         print(json.dumps(measure_backward(workload_ragged64k(), True, iters=args.steps)), flush=True)
         return 0
@@ -420,6 +463,12 @@ def main() -> int:
             line["backward"].append(measure_backward(bwl, bc))
             print(f"# {line['backward'][-1]}", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        # decode-shaped attention against a paged key/value cache (HBM-bound)
+        line["decode"] = measure_decode(workload_decode_bench())
+        print(f"# {line['decode']}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, causal, data)

@@ -133,21 +133,41 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     float m_run = kNegInf, l_run = 0.f;
 
-    for (int t = t_begin + wave; t < t_end; t += kDecWaves) {
+    // Cache offsets of this lane's K row (permuted order) and V row of a tile.
+    // Keys past the sequence are pointed at its first key and their values
+    // zeroed after the load, so every load is issued without a branch.  The
+    // offsets of the wave's next tile (which may need block-table reads) are
+    // computed while the current tile's loads are in flight.
+    auto offsets = [](const DecArgs& da, int bb, int lpad, int key, int lk, int h_k) __attribute__((always_inline)) {
+      return cache_offset(da, bb, lpad + (key < lk ? key : 0), h_k, D);
+    };
+    int t = t_begin + wave;
+    int64_t ko = 0, vo = 0;
+    if (t < t_end) {
+      ko = offsets(a, b, lp, t * kDecTile + arow, Lk, hk);
+      vo = offsets(a, b, lp, t * kDecTile + l32, Lk, hk);
+    }
+    for (; t < t_end; t += kDecWaves) {
       const int key0 = t * kDecTile;
-      // K rows of the tile in the permuted A-row order, V rows in natural order
       const int kk = key0 + arow, kv = key0 + l32;
-      const uint16_t* kp = (const uint16_t*)a.k_cache + (kk < Lk ? cache_offset(a, b, lp + kk, hk, D) : 0);
-      const uint16_t* vp = (const uint16_t*)a.v_cache + (kv < Lk ? cache_offset(a, b, lp + kv, hk, D) : 0);
+      const uint16_t* kp = (const uint16_t*)a.k_cache + ko;
+      const uint16_t* vp = (const uint16_t*)a.v_cache + vo;
       v8 ka[KSTEPS];
       u32x4 vr[KSTEPS];
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-        if (kk < Lk) x = *(const u32x4*)(kp + 16 * ks + 8 * g);
-        if (kv < Lk) y = *(const u32x4*)(vp + 16 * ks + 8 * g);
-        ka[ks] = __builtin_bit_cast(v8, x);
-        vr[ks] = y;
+        ka[ks] = __builtin_bit_cast(v8, *(const u32x4*)(kp + 16 * ks + 8 * g));
+        vr[ks] = *(const u32x4*)(vp + 16 * ks + 8 * g);
+      }
+      if (t + kDecWaves < t_end) {
+        ko = offsets(a, b, lp, key0 + kDecWaves * kDecTile + arow, Lk, hk);
+        vo = offsets(a, b, lp, key0 + kDecWaves * kDecTile + l32, Lk, hk);
+      }
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        if (!(kk < Lk)) ka[ks] = __builtin_bit_cast(v8, zero);
+        if (!(kv < Lk)) vr[ks] = zero;
       }
       // V tile into the wave's LDS buffer (row-major, swizzled)
 #pragma unroll
