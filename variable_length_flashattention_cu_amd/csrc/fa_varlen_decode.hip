@@ -46,7 +46,7 @@ namespace fa {
 namespace {
 
 constexpr int kDecWaves = 4;  // wavefronts per workgroup
-constexpr int kDecTile = 32;  // keys per tile
+constexpr int kDecTile = 64;  // keys per tile
 
 typedef short dec_s16x4 __attribute__((ext_vector_type(4)));
 
@@ -78,9 +78,32 @@ __device__ __forceinline__ int64_t cache_offset(const DecArgs& a, int b, int p, 
   return row * a.kv_row_stride + (int64_t)hk * D;
 }
 
+// 16x16x32 MFMA of the 16-bit element type
+template <typename T>
+struct Mfma16;
+template <>
+struct Mfma16<__bf16> {
+  __device__ __forceinline__ static f32x4 run(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma16<_Float16> {
+  __device__ __forceinline__ static f32x4 run(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
-  constexpr int KSTEPS = D / 16, DB = D / 32;
+  // 16x16x32 MFMA layout (gfx950): lane l, group G = l/16, i = l%16:
+  //   A operand: row i, k = 8G..8G+7;  B operand: column i, k = 8G..8G+7;
+  //   accumulator register r: row 4G + r, column i.
+  constexpr int KS = D / 32;           // k-steps over head_dim
+  constexpr int DT = D / 16;           // 16-row tiles of O^T
+  constexpr int KT = kDecTile / 16;    // 16-key tiles of S^T per 64-key tile
+  constexpr int KK = kDecTile / 32;    // k-steps over the keys of a tile
+  constexpr int LOADS = kDecTile * D / 8 / 64;  // 16-byte loads per lane for one of K or V
   using E = Elem16<T>;
   typedef typename E::v8 v8;
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[kDecWaves][kDecTile * D];
@@ -94,7 +117,6 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, g = lane >> 5;
   const int li = lane & 15, lg = lane >> 4;
   const int G = a.head_group;
   const int q_start = a.cu_q[b];
@@ -104,127 +126,150 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
   const int shift = Lk - Lq;
   const int rows = G * Lq;
   const int ntiles = (max(Lk, 0) + kDecTile - 1) / kDecTile;
-  const int tps = (ntiles + a.num_splits - 1) / a.num_splits;
+  const int tps = (ntiles + a.num_splits - 1) / a.num_splits;  // tiles per split
   const int t_begin = s * tps, t_end = min(ntiles, t_begin + tps);
   const int part = s * kDecWaves + wave;  // this wave's partial slot
   const int npart = a.num_splits * kDecWaves;
   uint16_t* vt = lds_v[wave];
-  const int arow = tiling::key_of_arow(l32);
 
-  for (int rt = 0; rt * 32 < rows; ++rt) {
-    // Q^T of the row tile as the B operand: lane l32 <-> row rt*32 + l32
-    const int r = rt * 32 + l32;
+  for (int rt = 0; rt * 16 < rows; ++rt) {
+    // Q^T of the row tile as the B operand: lane column li <-> row rt*16 + li
+    const int r = rt * 16 + li;
     const bool rvalid = r < rows;
     const int qi = rvalid ? r / G : 0, gi = rvalid ? r % G : 0;
     const int h = hk * G + gi;
-    v8 qreg[KSTEPS];
+    v8 qreg[KS];
     {
       const uint16_t* qp = (const uint16_t*)a.q + (int64_t)(q_start + qi) * a.row_stride + (int64_t)h * D;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (rvalid) x = *(const u32x4*)(qp + 16 * ks + 8 * g);
+        if (rvalid) x = *(const u32x4*)(qp + 32 * ks + 8 * lg);
         qreg[ks] = __builtin_bit_cast(v8, x);
       }
     }
     const int lim = CAUSAL ? min(Lk - 1, qi + shift) : Lk - 1;  // last visible key of the row
-    f32x16 o[DB];
+    f32x4 o[DT];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = kNegInf, l_run = 0.f;
 
-    // Cache offsets of this lane's K row (permuted order) and V row of a tile.
-    // Keys past the sequence are pointed at its first key and their values
-    // zeroed after the load, so every load is issued without a branch.  The
-    // offsets of the wave's next tile (which may need block-table reads) are
-    // computed while the current tile's loads are in flight.
-    auto offsets = [](const DecArgs& da, int bb, int lpad, int key, int lk, int h_k) __attribute__((always_inline)) {
-      return cache_offset(da, bb, lpad + (key < lk ? key : 0), h_k, D);
-    };
+    // Lane (li, lg) loads K rows 16*kt + li (A operand, dims 32ks + 8lg ..)
+    // and V rows 16*kt + li (dims 32ks + 8lg ..) of each 64-key tile.  Keys
+    // past the sequence point at its first key and are zeroed after the load,
+    // so every load is issued without a branch; the next tile's offsets
+    // (block-table reads) are computed while the current loads are in flight.
+    int64_t off[KT];
     int t = t_begin + wave;
-    int64_t ko = 0, vo = 0;
     if (t < t_end) {
-      ko = offsets(a, b, lp, t * kDecTile + arow, Lk, hk);
-      vo = offsets(a, b, lp, t * kDecTile + l32, Lk, hk);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const int key = t * kDecTile + 16 * kt + li;
+        off[kt] = cache_offset(a, b, lp + (key < Lk ? key : 0), hk, D);
+      }
     }
     for (; t < t_end; t += kDecWaves) {
       const int key0 = t * kDecTile;
-      const int kk = key0 + arow, kv = key0 + l32;
-      const uint16_t* kp = (const uint16_t*)a.k_cache + ko;
-      const uint16_t* vp = (const uint16_t*)a.v_cache + vo;
-      v8 ka[KSTEPS];
-      u32x4 vr[KSTEPS];
+      v8 ka[KT][KS];
+      u32x4 vr[KT][KS];
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        ka[ks] = __builtin_bit_cast(v8, *(const u32x4*)(kp + 16 * ks + 8 * g));
-        vr[ks] = *(const u32x4*)(vp + 16 * ks + 8 * g);
-      }
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          ka[kt][ks] = __builtin_bit_cast(v8, *(const u32x4*)((const uint16_t*)a.k_cache + off[kt] + 32 * ks + 8 * lg));
+          vr[kt][ks] = *(const u32x4*)((const uint16_t*)a.v_cache + off[kt] + 32 * ks + 8 * lg);
+        }
       if (t + kDecWaves < t_end) {
-        ko = offsets(a, b, lp, key0 + kDecWaves * kDecTile + arow, Lk, hk);
-        vo = offsets(a, b, lp, key0 + kDecWaves * kDecTile + l32, Lk, hk);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const int key = key0 + kDecWaves * kDecTile + 16 * kt + li;
+          off[kt] = cache_offset(a, b, lp + (key < Lk ? key : 0), hk, D);
+        }
       }
       const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        if (!(kk < Lk)) ka[ks] = __builtin_bit_cast(v8, zero);
-        if (!(kv < Lk)) vr[ks] = zero;
+      for (int kt = 0; kt < KT; ++kt)
+        if (!(key0 + 16 * kt + li < Lk))
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            ka[kt][ks] = __builtin_bit_cast(v8, zero);
+            vr[kt][ks] = zero;
+          }
+      // V tile into the wave's LDS buffer (row-major, swizzled; 16-byte chunk
+      // 4ks + lg of key row 16kt + li)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          *(u32x4*)(vt + tiling::ks_index<D>(16 * kt + li, 4 * ks + lg)) = vr[kt][ks];
+
+      // S^T = K Q^T: register e of tile kt holds key key0 + 16kt + 4lg + e of row li
+      f32x4 sc[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sc[kt] = Mfma16<T>::run(ka[kt][ks], qreg[ks], sc[kt]);
       }
-      // V tile into the wave's LDS buffer (row-major, swizzled)
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) *(u32x4*)(vt + tiling::ks_index<D>(l32, 2 * ks + g)) = vr[ks];
-
-      // S^T = K Q^T: register e of half g holds key key0 + 16g + e of row l32
-      f32x16 sc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) sc = E::mfma(ka[ks], qreg[ks], sc);
-
       float mx = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const bool vis = key0 + 16 * g + e <= lim;
-        sc[e] = vis ? sc[e] * a.scale_log2 : kNegInf;
-        mx = fmaxf(mx, sc[e]);
-      }
-      const float m_new = fmaxf(m_run, pair_max(mx));
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool vis = key0 + 16 * kt + 4 * lg + e <= lim;
+          sc[kt][e] = vis ? sc[kt][e] * a.scale_log2 : kNegInf;
+          mx = fmaxf(mx, sc[kt][e]);
+        }
+      // the four 16-lane groups hold different keys of the same row
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m_run, mx);
       const float m_use = m_new == kNegInf ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
       m_run = m_new;
-      v8 p[2];
+      // P^T as the B operand: k-index 8lg + j of k-step kk <-> key 32kk + 16(j/4) + 4lg + j%4
+      v8 p[KK];
       float lsum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = fast_exp2(sc[e] - m_use);
-        lsum += pe;
-        p[e >> 3][e & 7] = (T)pe;
-      }
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pe = fast_exp2(sc[kt][e] - m_use);
+          lsum += pe;
+          p[kt >> 1][4 * (kt & 1) + e] = (T)pe;
+        }
       l_run = l_run * alpha + lsum;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        for (int e = 0; e < 4; ++e) o[dt][e] *= alpha;
 
-      // O^T += V^T P^T: V^T read back from the tile with transposing reads
+      // O^T += V^T P^T: the A operand of row d = 16dt + li holds keys
+      // 32kk + 4lg + 0..3 and 32kk + 16 + 4lg + 0..3 (two transposing reads)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const v8 av = dec_tr_read8<v8, D>(vt, 16 * (lg >> 1) + 8 * tt, 32 * db + 16 * (lg & 1), li);
-          o[db] = E::mfma(av, p[tt], o[db]);
+        for (int kk = 0; kk < KK; ++kk) {
+          const dec_s16x4 lo = dec_tr_read4<D>(vt, 32 * kk + 4 * lg, 16 * dt, li);
+          const dec_s16x4 hi = dec_tr_read4<D>(vt, 32 * kk + 16 + 4 * lg, 16 * dt, li);
+          const short __attribute__((ext_vector_type(8))) av = {lo[0], lo[1], lo[2], lo[3],
+                                                                 hi[0], hi[1], hi[2], hi[3]};
+          o[dt] = Mfma16<T>::run(__builtin_bit_cast(v8, av), p[kk], o[dt]);
         }
     }
 
-    // partial of this wave for the rows of the tile
-    const float l = pair_sum(l_run);
+    // partial of this wave for the rows of the tile: l summed over the four groups
+    float l = l_run + __shfl_xor(l_run, 16, 64);
+    l = pair_sum(l);
     if (rvalid) {
       const int64_t pr = ((int64_t)(q_start + qi) * a.heads + h) * npart + part;
       float* po = a.part_o + pr * D;
+      // a partial that saw no key (max -inf) is skipped by the combine: its O is not needed
+      if (m_run != kNegInf)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-          *(f32x4*)(po + 32 * db + 8 * s4 + 4 * g) =
-              f32x4{o[db][4 * s4], o[db][4 * s4 + 1], o[db][4 * s4 + 2], o[db][4 * s4 + 3]};
-      if (g == 0) {
+        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(po + 16 * dt + 4 * lg) = o[dt];
+      if (lg == 0) {
         a.part_ml[2 * pr] = m_run;
         a.part_ml[2 * pr + 1] = l;
       }
@@ -252,7 +297,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   float lsum = 0.f;
   for (int p = 0; p < npart; ++p) {
-    const float w = fast_exp2(ml[2 * p] - m_use);  // 0 for an empty partial (m_p = -inf)
+    if (ml[2 * p] == kNegInf) continue;  // empty partial: weight 0, O never written
+    const float w = fast_exp2(ml[2 * p] - m_use);
     lsum += w * ml[2 * p + 1];
     const float* po = a.part_o + (rh * npart + p) * D;
 #pragma unroll
