@@ -26,6 +26,11 @@ SOURCES = [os.path.join(CSRC, "fa_varlen_kernels.hip"), os.path.join(CSRC, "fa_v
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the generated code.
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source code generation options.  The backward kernel keeps its matrix
+# accumulators in architectural VGPRs: with accumulation registers the
+# allocator moved the dK/dV accumulators out and back every step to make room
+# for the score tiles.
+SOURCE_FLAGS = {"fa_varlen_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -40,22 +45,48 @@ def common_flags():
             "-Wall", "-Wno-unused-function"] + NO_PACKED_FP32
 
 
-def build(verbose: bool = False, asm_dir: str | None = None) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + common_flags() + ["-shared", "-o", tmp] + SOURCES
+def source_flags(src: str) -> list:
+    return SOURCE_FLAGS.get(os.path.basename(src), [])
+
+
+def run(cmd: list, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+
+
+def build(verbose: bool = False, asm_dir: str | None = None) -> str:
+    tmp = LIB_PATH + ".tmp"
+    objs = []
+    procs = []
+    for src in SOURCES:  # one object per source (own options), compiled in parallel
+        obj = LIB_PATH + "." + os.path.basename(src) + ".o"
+        cmd = [hipcc()] + common_flags() + source_flags(src) + ["-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True), obj))
+    failed = False
+    for proc, obj in procs:
+        out, err = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out + err)
+            failed = True
+        objs.append(obj)
+    if failed:
+        raise RuntimeError("hipcc failed")
+    run([hipcc()] + common_flags() + ["-shared", "-o", tmp] + objs, verbose)
+    for obj in objs:
+        os.remove(obj)
     os.replace(tmp, LIB_PATH)
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
         for src in SOURCES:
             if src.endswith(".hip"):
                 asm = os.path.join(asm_dir, os.path.basename(src)[:-4] + ".s")
-                cmd = [hipcc()] + common_flags() + ["--cuda-device-only", "-S", "-o", asm, src]
+                cmd = [hipcc()] + common_flags() + source_flags(src) + ["--cuda-device-only", "-S", "-o", asm, src]
                 subprocess.run(cmd, check=True, capture_output=True, text=True)
     return LIB_PATH
 

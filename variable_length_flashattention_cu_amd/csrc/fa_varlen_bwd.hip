@@ -25,11 +25,12 @@
 //
 // bwd16_kernel layout (4 wavefronts, wave w owns keys 32w..32w+31 of the
 // block; one 32-row query block per step):
-//   * K and V of the wave's keys stay in registers as the B operands of
-//     S = Q K^T and dP = dO V^T (contraction over head_dim); Q and dO rows are
-//     read from LDS in the permuted row order of the forward kernels, so that
-//     register r of lane half g of the 32x32 accumulators holds query row
-//     16g + r and lane l32 the key 32w + l32.
+//   * K and V of the block are staged in LDS once per item and give the B
+//     operands of S = Q K^T and dP = dO V^T (contraction over head_dim); Q and
+//     dO rows are read from LDS in the permuted row order of the forward
+//     kernels, so that register r of lane half g of the 32x32 accumulators
+//     holds query row 16g + r, and lane l32 takes key 32w + pi(l32) (pi: the
+//     same permutation, which keeps the swizzled K and V reads conflict-free).
 //   * That is the B-operand layout of dV^T = dO^T P and dK^T = Q^T dS
 //     (contraction over the 32 query rows), whose A operands Q^T and dO^T are
 //     staged transposed in LDS.  dK^T and dV^T accumulate in registers.
@@ -187,6 +188,12 @@ __device__ __forceinline__ void lds_load_rows(uint16_t* dst, const uint16_t* bas
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// The value, hidden from the optimiser (an empty asm that may modify it).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
 // lane i reads 8 bytes at row r0 + i/4, columns c0 + 4(i%4) .. +3 of a
 // row-major swizzled tile, and the hardware hands lane i the four elements
@@ -244,17 +251,22 @@ struct BlockStage {
     const uint16_t* doh = (const uint16_t*)a.dout + (int64_t)w.q_start * rs + (int64_t)h * D;
     tq.load_k(qh, rs, r0, w.Lq, tid);
     tdo.load_k(doh, rs, r0, w.Lq, tid);
-    const int q = r0 + (tid & (BM - 1));
-    const int64_t at = (int64_t)h * a.total_q + w.q_start + q;
-    if (tid < BM) lse_v = q < w.Lq ? a.lse[at] : 0.f;
-    else if (tid < 2 * BM) dr_v = q < w.Lq ? a.drow[at] : 0.f;
+    // lse and D of the block's rows: branch-free buffer loads whose range
+    // check (the rows of the sequence) reads rows past its end as zero
+    const int64_t at = (int64_t)h * a.total_q + w.q_start + r0;
+    const uint32_t bytes = (uint32_t)max(0, min(BM, w.Lq - r0)) * 4u;
+    const uint32_t off = (uint32_t)(tid & (BM - 1)) * 4u;
+    lse_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.lse + at, bytes), (int)off, 0, 0));
+    dr_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.drow + at, bytes), (int)off, 0, 0));
   }
   // lse is stored in log2 units
   __device__ __forceinline__ void store(uint16_t* qs, uint16_t* dos, float* lse, float* dr, int tid) const {
     tq.store_k(qs, tid);
     tdo.store_k(dos, tid);
-    if (tid < BM) lse[tid] = lse_v * kLog2eF;
-    else if (tid < 2 * BM) dr[tid - BM] = dr_v;
+    // every thread holds the values of row tid % BM: all write them (equal
+    // values), so no branch leaves the loads' wait off some path
+    lse[tid & (BM - 1)] = lse_v * kLog2eF;
+    dr[tid & (BM - 1)] = dr_v;
   }
 };
 
@@ -268,6 +280,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   typedef typename E::v8 v8;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[BN * D];       // K block, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[BN * D];       // V block, row-major
   __shared__ __attribute__((aligned(16))) uint16_t lds_ds[BM * BN];     // dS, row-major
   __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][BM * D];    // query block, row-major
   __shared__ __attribute__((aligned(16))) uint16_t lds_do[2][BM * D];
@@ -279,39 +292,31 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   ColItem w;
   if (!decode_col(a, w)) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, g = lane >> 5;
-  const int li = lane & 15, lg = lane >> 4;  // lane in its 16-lane group, group
+  const int tid0 = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+  int tid = tid0, lane = tid0 & 63;
+  int l32 = lane & 31, g = lane >> 5;
+  int li = lane & 15, lg = lane >> 4;  // lane in its 16-lane group, group
   const int key0 = w.j * BN;
-  const int kcol = key0 + 32 * wave + l32;  // this lane's key (in the sequence)
+  // this lane's key: the wave's 32 keys are taken in the row order whose
+  // swizzled LDS reads are free of bank conflicts
+  const int klane = 32 * wave + tiling::key_of_arow(l32);  // in the block
+  const int kcol = key0 + klane;                            // in the sequence
   const int shift = w.Lk - w.Lq;
   const int64_t rs = a.row_stride, rsk = a.kv_row_stride;
   const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
   const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
 
-  // The operands that stay fixed for the item live in registers: K and V of
-  // the wave's keys (B operands of S = Q K^T and dP = dO V^T, straight from
-  // global memory) and the K^T operand of the wave's dQ tile (read once by
-  // transposing reads from the K block staged in LDS).  Keys past the
+  // K and V of the block are staged in LDS for the item: the B operands of
+  // S = Q K^T and dP = dO V^T (contraction over head_dim) and, by transposing
+  // reads, the K^T operand of the wave's dQ tile are read from there every
+  // step, which keeps registers free for reads in flight.  Keys past the
   // sequence read as zero.
   constexpr int SPLIT = NW / DB;        // waves per dQ tile (1 at D=128, 2 at D=64)
   constexpr int KEYS = BN / SPLIT;      // keys of a wave's dQ product
   const int tile = wave % DB, part = wave / DB;
   lds_load_rows<D, BN>(lds_k, kbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
-  v8 kb[KSTEPS], vb[KSTEPS], kt[KEYS / 16];
-  {
-    const int rows = max(0, min(32, w.Lk - key0 - 32 * wave));
-    const int64_t off0 = (int64_t)(key0 + 32 * wave) * rsk;
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + off0, tiling::head_rows_bytes(rows, rsk, D, 2));
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + off0, tiling::head_rows_bytes(rows, rsk, D, 2));
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const uint32_t off = ((uint32_t)l32 * (uint32_t)rsk + 16 * ks + 8 * g) * 2u;
-      kb[ks] = __builtin_bit_cast(v8, buffer_load16(rk, off));
-      vb[ks] = __builtin_bit_cast(v8, buffer_load16(rv, off));
-    }
-  }
+  lds_load_rows<D, BN>(lds_v, vbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
 
   // query blocks that see a key of this block: rows q with q + shift >= key0
   const int i_begin = CAUSAL ? max(0, key0 - shift) / BM : 0;
@@ -336,29 +341,60 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     stage.store(lds_q[0], lds_do[0], lds_lse[0], lds_dr[0], tid);
   }
   __syncthreads();
-#pragma unroll
-  for (int kk = 0; kk < KEYS / 16; ++kk)
-    kt[kk] = tr_read8<v8, D>(lds_k, part * KEYS + 16 * kk + 8 * (lg >> 1), 32 * tile + 16 * (lg & 1), li);
 
-  const int arow = tiling::key_of_arow(l32);
+  // Every load issued so far (K, V operands, the first query block) has
+  // landed.  Without this wait the compiler keeps the operand loads pending
+  // at the loop head and places vmcnt waits inside the loop; those then also
+  // wait, every step, for the previous step's dQ atomics and for the next
+  // block's prefetch, since vector memory operations complete in order.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  int arow = tiling::key_of_arow(l32);
+  int klane_l = klane;
   for (int s = 0; s < nsteps; ++s) {
+    // lane-dependent address terms are re-derived every step instead of
+    // being kept as one register per LDS address across the loop
+    tid = opaque(tid0);
+    lane = tid & 63;
+    l32 = lane & 31;
+    g = lane >> 5;
+    li = lane & 15;
+    lg = lane >> 4;
+    arow = tiling::key_of_arow(l32);
+    klane_l = opaque(klane);
     const int buf = s & 1;
     const int h = w.hk * a.head_group + s / nblk;
     const int r0 = (i_begin + s % nblk) * BM;
-    if (s + 1 < nsteps) stage.load(a, w, s + 1, nblk, i_begin, tid);
+    // the next block (the last one again at the last step: loads and stores
+    // stay unconditional, so that no wait for them lands elsewhere in the loop)
+    stage.load(a, w, min(s + 1, nsteps - 1), nblk, i_begin, tid);
     const uint16_t* qs = lds_q[buf];
     const uint16_t* dos = lds_do[buf];
 
     // S = Q K^T and dP = dO V^T (rows permuted: register r of half g = row 16g + r)
     f32x16 sc = f32x16{}, dp = f32x16{};
+    {
+      // operands of k-step ks are read PF steps ahead of their MFMAs
+      constexpr int PF = 2;
+      v8 aq[PF + 1], ad[PF + 1], bk[PF + 1], bv[PF + 1];
+      auto fetch = [&](int ks) __attribute__((always_inline)) {
+        const int i = ks % (PF + 1);
+        aq[i] = *(const v8*)(qs + tiling::ks_index<D>(arow, 2 * ks + g));
+        ad[i] = *(const v8*)(dos + tiling::ks_index<D>(arow, 2 * ks + g));
+        bk[i] = *(const v8*)(lds_k + tiling::ks_index<D>(klane_l, 2 * ks + g));
+        bv[i] = *(const v8*)(lds_v + tiling::ks_index<D>(klane_l, 2 * ks + g));
+      };
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const v8 aq = *(const v8*)(qs + tiling::ks_index<D>(arow, 2 * ks + g));
-      const v8 ad = *(const v8*)(dos + tiling::ks_index<D>(arow, 2 * ks + g));
-      sc = E::mfma(aq, kb[ks], sc);
-      dp = E::mfma(ad, vb[ks], dp);
+      for (int ks = 0; ks < PF; ++ks) fetch(ks);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        if (ks + PF < KSTEPS) fetch(ks + PF);
+        const int i = ks % (PF + 1);
+        sc = E::mfma(aq[i], bk[i], sc);
+        dp = E::mfma(ad[i], bv[i], dp);
+      }
     }
-    read_ahead_schedule<2 * KSTEPS, 2 * KSTEPS, 8>();
+    __builtin_amdgcn_sched_barrier(0);
 
     // P and dS (softmax scale folded in) of the lane's 16 rows for its key
     float lse2[16], drr[16];
@@ -401,7 +437,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     // packed operand registers as whole words (element-wise access to the
     // 16-bit vector was miscompiled into one element per half).
     {
-      const int kk = 32 * wave + l32;
+      const int kk = klane_l;
       const u32x4 w0 = __builtin_bit_cast(u32x4, ds16[0]);
       const u32x4 w1 = __builtin_bit_cast(u32x4, ds16[1]);
 #pragma unroll
@@ -419,11 +455,13 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
       for (int kk = 0; kk < KEYS / 16; ++kk) {
         const int k16 = part * KEYS + 16 * kk;
         const v8 ads = *(const v8*)(lds_ds + tiling::ks_index<BN>(l32, (k16 >> 3) + g));
-        acc = E::mfma(ads, kt[kk], acc);
+        const v8 bkt = tr_read8<v8, D>(lds_k, k16 + 8 * (lg >> 1), 32 * tile + 16 * (lg & 1), li);
+        acc = E::mfma(ads, bkt, acc);
       }
+      read_ahead_schedule<KEYS / 16, 3 * (KEYS / 16), 9>();
       // the next query block goes into the other buffer before the atomics are
       // issued, so that waiting for its loads does not wait for them too
-      if (s + 1 < nsteps) stage.store(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_lse[buf ^ 1], lds_dr[buf ^ 1], tid);
+      stage.store(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_lse[buf ^ 1], lds_dr[buf ^ 1], tid);
       if constexpr (SPLIT > 1) {
         // two waves hold halves of the key sum of one tile: add them in LDS so
         // that each dq element receives one atomic addition per key block
