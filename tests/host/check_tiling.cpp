@@ -258,8 +258,9 @@ int main() {
     check_bf16<128, 64, 4>(H);
     check_bf16<96, 64, 4>(H);
     check_bf16<256, 32, 4>(H);
-    // backward: 32-row query blocks (row-major and transposed) and the
-    // transposed 128-key K block
+    // backward: query blocks of 64 rows (head_dim 128, 8 waves) and 32 rows
+    // (head_dim 64, 4 waves), and the 128-key K and V blocks
+    check_bf16<128, 128, 8>(H);
     check_bf16<128, 32, 4>(H);
     check_bf16<64, 32, 4>(H);
     check_bf16<128, 128, 4>(H);

@@ -23,20 +23,26 @@
 //                    dK, dV of the block and atomic dQ contributions;
 //   bwd_dq_kernel    dq = accumulator (already scaled) in the input type.
 //
-// bwd16_kernel layout (4 wavefronts, wave w owns keys 32w..32w+31 of the
-// block; one 32-row query block per step):
+// bwd16_kernel layout (wave w owns the 32 keys of key group w % 4 of the
+// block; head_dim 128 runs 8 wavefronts on 64-row query blocks, wave w taking
+// rows 32*(w/4) .. +31; head_dim 64 runs 4 wavefronts on 32-row blocks):
 //   * K and V of the block are staged in LDS once per item and give the B
 //     operands of S = Q K^T and dP = dO V^T (contraction over head_dim); Q and
 //     dO rows are read from LDS in the permuted row order of the forward
 //     kernels, so that register r of lane half g of the 32x32 accumulators
-//     holds query row 16g + r, and lane l32 takes key 32w + pi(l32) (pi: the
-//     same permutation, which keeps the swizzled K and V reads conflict-free).
+//     holds query row 16g + r of the wave's 32, and lane l32 takes key
+//     32*(w%4) + pi(l32) (pi: the same permutation, which keeps the swizzled K
+//     and V reads conflict-free).
 //   * That is the B-operand layout of dV^T = dO^T P and dK^T = Q^T dS
-//     (contraction over the 32 query rows), whose A operands Q^T and dO^T are
-//     staged transposed in LDS.  dK^T and dV^T accumulate in registers.
-//   * dS goes to LDS row-major; dQ = dS K reads it with K^T (staged once per
-//     item) and each wave adds one 32x32 output tile (or half of one) to the
-//     accumulator.
+//     (contraction over the 32 query rows), whose A operands Q^T and dO^T come
+//     from the row-major tiles by transposing LDS reads.  dK^T and dV^T
+//     accumulate in registers; the two waves of a key group add their sums
+//     through LDS at the end.
+//   * dS goes to LDS row-major; dQ = dS K reads it with K^T (transposing
+//     reads of the K block) and each wave adds one 32x32 output tile (or half
+//     of one) to the accumulator.  At head_dim 128 these float32 atomic
+//     additions (128 per query row and key block) set the kernel's pace: the
+//     L2 caches retire about one lane's atomic per channel and clock.
 //   * Q, dO, lse and D of the next query block are loaded into registers
 //     while the current one is computed and stored into the other LDS buffer.
 
@@ -51,8 +57,14 @@ namespace fa {
 namespace {
 
 constexpr float kLog2eF = 1.4426950408889634074f;
-constexpr int kBwdBN = 128;  // keys per work item (4 waves x 32)
-constexpr int kBwdBM = 32;   // query rows per step
+constexpr int kBwdBN = 128;  // keys per work item (4 key groups of 32)
+
+// Row halves per step: head_dim 128 runs 8 wavefronts, two per key group, on
+// the two 32-row halves of a 64-row query block (two waves per SIMD hide each
+// other's latencies); head_dim 64 runs 4 wavefronts on 32-row blocks and fits
+// two workgroups per CU instead.
+template <int D>
+constexpr int bwd_row_halves() { return D == 128 ? 2 : 1; }
 
 template <typename T>
 __device__ __forceinline__ float half_to_f32(uint32_t bits16);
@@ -166,12 +178,12 @@ __device__ __forceinline__ bool decode_col(const BwdArgs& a, ColItem& w) {
 // 16 bytes land at LDS chunk position p = 64 * instruction + lane, so the lane
 // loads the logical chunk that the swizzle stores there.  Rows at or past
 // `valid` read as zeros (buffer range check); no registers hold the data.
-template <int D, int ROWS>
+template <int D, int ROWS, int NW>
 __device__ __forceinline__ void lds_load_rows(uint16_t* dst, const uint16_t* base, int64_t row_stride, int valid,
                                               int wave, int lane) {
-  constexpr int CPR = D / 8;                // 16-byte chunks per row
-  constexpr int PER_WAVE = ROWS * CPR / 256;  // instructions per wave (4 waves)
-  static_assert(ROWS * CPR % 256 == 0, "tile must split into whole wave loads");
+  constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  constexpr int PER_WAVE = ROWS * CPR / (64 * NW);  // instructions per wave
+  static_assert(ROWS * CPR % (64 * NW) == 0, "tile must split into whole wave loads");
   const __amdgpu_buffer_rsrc_t r =
       buffer_rsrc(base, tiling::head_rows_bytes(max(0, min(ROWS, valid)), row_stride, D, 2));
 #pragma unroll
@@ -238,9 +250,9 @@ __device__ __forceinline__ void read_ahead_schedule() {
 // the previous block is computed, then stored into an LDS buffer.  Rows past
 // the sequence read as zeros.  Step s covers query head
 // kv_head * head_group + s / nblk and rows (i_begin + s % nblk) * BM ...
-template <int D, int BM>
+template <int D, int BM, int NW>
 struct BlockStage {
-  Tile16<D, BM, 4> tq, tdo;
+  Tile16<D, BM, NW> tq, tdo;
   float lse_v = 0.f, dr_v = 0.f;
 
   __device__ __forceinline__ void load(const BwdArgs& a, const ColItem& w, int s, int nblk, int i_begin, int tid) {
@@ -271,8 +283,9 @@ struct BlockStage {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
-  constexpr int BN = kBwdBN, BM = kBwdBM, NW = 4;
+__global__ __launch_bounds__(256 * bwd_row_halves<D>(), bwd_row_halves<D>()) void bwd16_kernel(BwdArgs a) {
+  constexpr int RH = bwd_row_halves<D>();
+  constexpr int BN = kBwdBN, BM = 32 * RH, NW = 4 * RH;
   constexpr int KSTEPS = D / 16;  // k-steps over head_dim
   constexpr int DB = D / 32;      // 32-dim tiles
   static_assert(D == 64 || D == 128, "backward head_dim");
@@ -287,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float lds_lse[2][BM];
   __shared__ __attribute__((aligned(16))) float lds_dr[2][BM];
   // key-split partial sums of the dQ tiles (head_dim 64: two waves per tile)
-  __shared__ __attribute__((aligned(16))) float lds_red[NW / DB > 1 ? DB * 64 * 16 : 1];
+  __shared__ __attribute__((aligned(16))) float lds_red[NW / (RH * DB) > 1 ? DB * 64 * 16 : 1];
 
   ColItem w;
   if (!decode_col(a, w)) return;
@@ -298,9 +311,10 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   int l32 = lane & 31, g = lane >> 5;
   int li = lane & 15, lg = lane >> 4;  // lane in its 16-lane group, group
   const int key0 = w.j * BN;
+  const int kg = wave & 3, rh = wave >> 2;  // key group (32 keys), row half of the query block
   // this lane's key: the wave's 32 keys are taken in the row order whose
   // swizzled LDS reads are free of bank conflicts
-  const int klane = 32 * wave + tiling::key_of_arow(l32);  // in the block
+  const int klane = 32 * kg + tiling::key_of_arow(l32);  // in the block
   const int kcol = key0 + klane;                            // in the sequence
   const int shift = w.Lk - w.Lq;
   const int64_t rs = a.row_stride, rsk = a.kv_row_stride;
@@ -312,11 +326,12 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   // reads, the K^T operand of the wave's dQ tile are read from there every
   // step, which keeps registers free for reads in flight.  Keys past the
   // sequence read as zero.
-  constexpr int SPLIT = NW / DB;        // waves per dQ tile (1 at D=128, 2 at D=64)
-  constexpr int KEYS = BN / SPLIT;      // keys of a wave's dQ product
-  const int tile = wave % DB, part = wave / DB;
-  lds_load_rows<D, BN>(lds_k, kbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
-  lds_load_rows<D, BN>(lds_v, vbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
+  constexpr int SPLIT = NW / (RH * DB);  // waves per dQ tile (1 at D=128, 2 at D=64)
+  constexpr int KEYS = BN / SPLIT;       // keys of a wave's dQ product
+  // dQ tile of the wave: 32 dims (tile), 32 rows (row tile rt), key part
+  const int tile = wave % DB, rt = (wave / DB) % RH, part = wave / (DB * RH);
+  lds_load_rows<D, BN, NW>(lds_k, kbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
+  lds_load_rows<D, BN, NW>(lds_v, vbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
 
   // query blocks that see a key of this block: rows q with q + shift >= key0
   const int i_begin = CAUSAL ? max(0, key0 - shift) / BM : 0;
@@ -327,7 +342,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   // Query block s (Q, dO, lse, D): loaded into registers while the previous
   // block is computed, then stored into an LDS buffer.  Rows past the
   // sequence read as zeros.
-  BlockStage<D, BM> stage;
+  BlockStage<D, BM, NW> stage;
 
   f32x16 dkt[DB], dvt[DB];
 #pragma unroll
@@ -379,8 +394,8 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
       v8 aq[PF + 1], ad[PF + 1], bk[PF + 1], bv[PF + 1];
       auto fetch = [&](int ks) __attribute__((always_inline)) {
         const int i = ks % (PF + 1);
-        aq[i] = *(const v8*)(qs + tiling::ks_index<D>(arow, 2 * ks + g));
-        ad[i] = *(const v8*)(dos + tiling::ks_index<D>(arow, 2 * ks + g));
+        aq[i] = *(const v8*)(qs + tiling::ks_index<D>(32 * rh + arow, 2 * ks + g));
+        ad[i] = *(const v8*)(dos + tiling::ks_index<D>(32 * rh + arow, 2 * ks + g));
         bk[i] = *(const v8*)(lds_k + tiling::ks_index<D>(klane_l, 2 * ks + g));
         bv[i] = *(const v8*)(lds_v + tiling::ks_index<D>(klane_l, 2 * ks + g));
       };
@@ -400,8 +415,8 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     float lse2[16], drr[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 l4 = *(const f32x4*)(&lds_lse[buf][16 * g + 4 * r4]);
-      const f32x4 d4 = *(const f32x4*)(&lds_dr[buf][16 * g + 4 * r4]);
+      const f32x4 l4 = *(const f32x4*)(&lds_lse[buf][32 * rh + 16 * g + 4 * r4]);
+      const f32x4 d4 = *(const f32x4*)(&lds_dr[buf][32 * rh + 16 * g + 4 * r4]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         lse2[4 * r4 + c] = l4[c];
@@ -411,7 +426,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     v8 p16[2], ds16[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int q = r0 + 16 * g + r;
+      const int q = r0 + 32 * rh + 16 * g + r;
       const bool vis = q < w.Lq && kcol < w.Lk && (!CAUSAL || kcol <= q + shift);
       const float pr = vis ? fast_exp2(__builtin_fmaf(sc[r], a.scale_log2, -lse2[r])) : 0.f;
       const float dsr = pr * (dp[r] - drr[r]) * a.scale;
@@ -425,7 +440,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int c0 = 32 * db + 16 * (lg & 1), rr = 16 * (lg >> 1) + 8 * t;
+        const int c0 = 32 * db + 16 * (lg & 1), rr = 32 * rh + 16 * (lg >> 1) + 8 * t;
         const v8 adt = tr_read8<v8, D>(dos, rr, c0, li);
         const v8 aqt = tr_read8<v8, D>(qs, rr, c0, li);
         dvt[db] = E::mfma(adt, p16[t], dvt[db]);
@@ -443,18 +458,19 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const uint32_t word = r < 8 ? w0[(r & 7) >> 1] : w1[(r & 7) >> 1];
-        lds_ds[tiling::ks_index<BN>(16 * g + r, kk >> 3) + (kk & 7)] = (uint16_t)((r & 1) ? (word >> 16) : word);
+        lds_ds[tiling::ks_index<BN>(32 * rh + 16 * g + r, kk >> 3) + (kk & 7)] =
+            (uint16_t)((r & 1) ? (word >> 16) : word);
       }
     }
     __syncthreads();
 
-    // dQ rows r0..r0+31: wave -> (32-dim tile, key part)
+    // dQ rows r0..r0+BM-1: wave -> (32-dim tile, 32-row tile, key part)
     {
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KEYS / 16; ++kk) {
         const int k16 = part * KEYS + 16 * kk;
-        const v8 ads = *(const v8*)(lds_ds + tiling::ks_index<BN>(l32, (k16 >> 3) + g));
+        const v8 ads = *(const v8*)(lds_ds + tiling::ks_index<BN>(32 * rt + l32, (k16 >> 3) + g));
         const v8 bkt = tr_read8<v8, D>(lds_k, k16 + 8 * (lg >> 1), 32 * tile + 16 * (lg & 1), li);
         acc = E::mfma(ads, bkt, acc);
       }
@@ -482,12 +498,13 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
           }
         }
       }
-      // accumulator register r of half g holds row 8*(r/4) + 4g + r%4, column 32*tile + l32.
-      // Buffer atomics over the rows of this block that lie in the sequence:
-      // the range check drops the additions of rows past its end.
+      // accumulator register r of half g holds row 32*rt + 8*(r/4) + 4g + r%4,
+      // column 32*tile + l32.  Buffer atomics over the rows of this block that
+      // lie in the sequence: the range check drops the additions of rows past its end.
+      const int rrow0 = r0 + 32 * rt;
       const __amdgpu_buffer_rsrc_t racc =
-          buffer_rsrc(a.dq_acc + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D,
-                      tiling::head_rows_bytes(min(BM, w.Lq - r0), rs, D, 4));
+          buffer_rsrc(a.dq_acc + (int64_t)(w.q_start + rrow0) * rs + (int64_t)h * D,
+                      tiling::head_rows_bytes(min(32, w.Lq - rrow0), rs, D, 4));
       if (part == 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -500,8 +517,41 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: dK (scale already in dS) and dV of this lane's key
-  if (kcol < w.Lk) {
+  // ---- epilogue: dK (scale already in dS) and dV of this lane's key.  With
+  // two row halves, the waves of half 1 hand their partial sums to the waves
+  // of half 0 through LDS (the K and V tiles are no longer read), one 32-dim
+  // block at a time.
+  if constexpr (RH == 2) {
+    float* red_k = (float*)lds_k;  // [key group][64 lanes][16] floats per block
+    float* red_v = (float*)lds_v;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (rh == 1) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          *(f32x4*)(&red_k[(kg * 64 + lane) * 16 + 4 * r4]) =
+              f32x4{dkt[db][4 * r4], dkt[db][4 * r4 + 1], dkt[db][4 * r4 + 2], dkt[db][4 * r4 + 3]};
+          *(f32x4*)(&red_v[(kg * 64 + lane) * 16 + 4 * r4]) =
+              f32x4{dvt[db][4 * r4], dvt[db][4 * r4 + 1], dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3]};
+        }
+      }
+      __syncthreads();
+      if (rh == 0) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 ok = *(const f32x4*)(&red_k[(kg * 64 + lane) * 16 + 4 * r4]);
+          const f32x4 ov = *(const f32x4*)(&red_v[(kg * 64 + lane) * 16 + 4 * r4]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            dkt[db][4 * r4 + c] += ok[c];
+            dvt[db][4 * r4 + c] += ov[c];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (rh == 0 && kcol < w.Lk) {
     T* dkp = (T*)a.dk + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
     T* dvp = (T*)a.dv + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
 #pragma unroll
@@ -530,11 +580,11 @@ hipError_t launch(F kernel, int grid, int threads, hipStream_t stream, const Bwd
 template <typename T>
 hipError_t launch_bwd_t(int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
   if (head_dim == 128)
-    return causal ? launch(bwd16_kernel<T, 128, true>, grid, 256, stream, a)
-                  : launch(bwd16_kernel<T, 128, false>, grid, 256, stream, a);
+    return causal ? launch(bwd16_kernel<T, 128, true>, grid, 256 * bwd_row_halves<128>(), stream, a)
+                  : launch(bwd16_kernel<T, 128, false>, grid, 256 * bwd_row_halves<128>(), stream, a);
   if (head_dim == 64)
-    return causal ? launch(bwd16_kernel<T, 64, true>, grid, 256, stream, a)
-                  : launch(bwd16_kernel<T, 64, false>, grid, 256, stream, a);
+    return causal ? launch(bwd16_kernel<T, 64, true>, grid, 256 * bwd_row_halves<64>(), stream, a)
+                  : launch(bwd16_kernel<T, 64, false>, grid, 256 * bwd_row_halves<64>(), stream, a);
   return hipErrorInvalidValue;
 }
 
