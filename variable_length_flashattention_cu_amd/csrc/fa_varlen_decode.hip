@@ -25,8 +25,8 @@
 // Work: one workgroup per (sequence, key/value head, split).  Its rows are all
 // query rows of the sequence for all query heads of the key/value head
 // (G * Lq rows, G = heads / kv_heads), so the cache is read once per group;
-// they are processed 32 at a time.  The split's 32-key tiles are dealt to the
-// 4 wavefronts round-robin; each wavefront streams its tiles straight from
+// they are processed 16 at a time (16x16x32 MFMAs).  The split's 64-key tiles
+// are dealt to the 4 wavefronts round-robin; each wavefront streams its tiles straight from
 // global memory (K as the A operand of S^T = K Q^T, V through a wave-private
 // LDS tile read back with transposing reads as the A operand of O^T = V^T P^T),
 // keeps an online softmax per row and writes its partial (max, sum, O) to the
@@ -277,7 +277,10 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
   }
 }
 
-// One wavefront per (row, head): merge its partials into out and lse.
+// One wavefront per (row, head): merge its partials into out and lse.  Lane
+// p % 64 weighs partials p; the partial outputs are then read without
+// dependent branches (empty partials, whose O was never written, enter through
+// a select with weight 0), so the loads of all partials are in flight together.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   const int lane = threadIdx.x & 63;
@@ -296,14 +299,39 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   float lsum = 0.f;
-  for (int p = 0; p < npart; ++p) {
-    if (ml[2 * p] == kNegInf) continue;  // empty partial: weight 0, O never written
-    const float w = fast_exp2(ml[2 * p] - m_use);
-    lsum += w * ml[2 * p + 1];
-    const float* po = a.part_o + (rh * npart + p) * D;
+  const float* po = a.part_o + rh * npart * D + lane * PER;
+  for (int p0 = 0; p0 < npart; p0 += 64) {
+    // weight of partial p0 + lane (0 for empty partials and past the end)
+    const int p = p0 + lane;
+    const float mp = p < npart ? ml[2 * p] : kNegInf;
+    const float wl = mp == kNegInf ? 0.f : fast_exp2(mp - m_use);
+    lsum += p < npart ? wl * ml[2 * p + 1] : 0.f;
+    const int n = min(64, npart - p0);
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {
+      float x[4][PER], wv[4];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] += w * po[lane * PER + j];
+      for (int u = 0; u < 4; ++u) {
+        wv[u] = __shfl(wl, i + u, 64);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) x[u][j] = po[(int64_t)(p0 + i + u) * D + j];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += wv[u] != 0.f ? wv[u] * x[u][j] : 0.f;
+    }
+    for (; i < n; ++i) {
+      const float wv = __shfl(wl, i, 64);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const float x = po[(int64_t)(p0 + i) * D + j];
+        acc[j] += wv != 0.f ? wv * x : 0.f;
+      }
+    }
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   T* op = (T*)a.out + rh * D;
 #pragma unroll
