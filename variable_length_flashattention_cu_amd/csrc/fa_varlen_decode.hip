@@ -25,7 +25,7 @@
 // Work: one workgroup per (sequence, key/value head, split).  Its rows are all
 // query rows of the sequence for all query heads of the key/value head
 // (G * Lq rows, G = heads / kv_heads), so the cache is read once per group;
-// they are processed 16 at a time (16x16x32 MFMAs).  The split's 64-key tiles
+// they are processed 16 at a time (16x16x32 MFMAs).  The split's 32-key tiles
 // are dealt to the 4 wavefronts round-robin; each wavefront streams its tiles straight from
 // global memory (K as the A operand of S^T = K Q^T, V through a wave-private
 // LDS tile read back with transposing reads as the A operand of O^T = V^T P^T),
@@ -46,7 +46,7 @@ namespace fa {
 namespace {
 
 constexpr int kDecWaves = 4;  // wavefronts per workgroup
-constexpr int kDecTile = 64;  // keys per tile
+constexpr int kDecTile = 32;  // keys per tile
 
 typedef short dec_s16x4 __attribute__((ext_vector_type(4)));
 
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
   //   accumulator register r: row 4G + r, column i.
   constexpr int KS = D / 32;           // k-steps over head_dim
   constexpr int DT = D / 16;           // 16-row tiles of O^T
-  constexpr int KT = kDecTile / 16;    // 16-key tiles of S^T per 64-key tile
+  constexpr int KT = kDecTile / 16;    // 16-key tiles of S^T per key tile
   constexpr int KK = kDecTile / 32;    // k-steps over the keys of a tile
   constexpr int LOADS = kDecTile * D / 8 / 64;  // 16-byte loads per lane for one of K or V
   using E = Elem16<T>;
@@ -155,11 +155,16 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
     float m_run = kNegInf, l_run = 0.f;
 
     // Lane (li, lg) loads K rows 16*kt + li (A operand, dims 32ks + 8lg ..)
-    // and V rows 16*kt + li (dims 32ks + 8lg ..) of each 64-key tile.  Keys
+    // and V rows 16*kt + li (dims 32ks + 8lg ..) of each key tile.  Keys
     // past the sequence point at its first key and are zeroed after the load,
-    // so every load is issued without a branch; the next tile's offsets
-    // (block-table reads) are computed while the current loads are in flight.
+    // so every load is issued without a branch.  The loads of the wave's next
+    // tile are issued as soon as the current tile's K and V registers are
+    // consumed (V stored to LDS, S computed), so they are in flight during the
+    // softmax and O += V^T P^T of the current tile; the offsets (block-table
+    // reads) run one more tile ahead.
     int64_t off[KT];
+    v8 ka[KT][KS];
+    u32x4 vr[KT][KS];
     int t = t_begin + wave;
     if (t < t_end) {
 #pragma unroll
@@ -167,11 +172,6 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
         const int key = t * kDecTile + 16 * kt + li;
         off[kt] = cache_offset(a, b, lp + (key < Lk ? key : 0), hk, D);
       }
-    }
-    for (; t < t_end; t += kDecWaves) {
-      const int key0 = t * kDecTile;
-      v8 ka[KT][KS];
-      u32x4 vr[KT][KS];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -182,10 +182,13 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
       if (t + kDecWaves < t_end) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
-          const int key = key0 + kDecWaves * kDecTile + 16 * kt + li;
+          const int key = t * kDecTile + kDecWaves * kDecTile + 16 * kt + li;
           off[kt] = cache_offset(a, b, lp + (key < Lk ? key : 0), hk, D);
         }
       }
+    }
+    for (; t < t_end; t += kDecWaves) {
+      const int key0 = t * kDecTile;
       const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
@@ -211,6 +214,24 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           sc[kt] = Mfma16<T>::run(ka[kt][ks], qreg[ks], sc[kt]);
+      }
+      // the next tile of this wave: loads into the registers just consumed
+      if (t + kDecWaves < t_end) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            ka[kt][ks] =
+                __builtin_bit_cast(v8, *(const u32x4*)((const uint16_t*)a.k_cache + off[kt] + 32 * ks + 8 * lg));
+            vr[kt][ks] = *(const u32x4*)((const uint16_t*)a.v_cache + off[kt] + 32 * ks + 8 * lg);
+          }
+        if (t + 2 * kDecWaves < t_end) {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            const int key = key0 + 2 * kDecWaves * kDecTile + 16 * kt + li;
+            off[kt] = cache_offset(a, b, lp + (key < Lk ? key : 0), hk, D);
+          }
+        }
       }
       float mx = kNegInf;
 #pragma unroll
