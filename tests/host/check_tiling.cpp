@@ -261,6 +261,8 @@ int main() {
     // backward: query blocks of 64 rows (head_dim 128, 8 waves) and 32 rows
     // (head_dim 64, 4 waves), and the 128-key K and V blocks
     check_bf16<128, 128, 8>(H);
+    check_bf16<128, 256, 8>(H);
+    check_bf16<128, 32, 8>(H);
     check_bf16<128, 32, 4>(H);
     check_bf16<64, 32, 4>(H);
     check_bf16<128, 128, 4>(H);

@@ -99,6 +99,7 @@ EDGE = [
     ("empty_seqs", [0, 37, 0, 200, 0], [5, 0, 0, 300, 0]),
     ("single_tokens", [1, 1, 1, 2], [1, 3, 1, 1]),
     ("ragged_tails", [129, 63, 65, 191, 257], [129, 63, 65, 191, 257]),
+    ("wide_block_tails", [255, 256, 513, 40], [255, 256, 513, 600]),
     ("q_longer_than_k", [824, 300, 40], [724, 33, 1]),
     ("k_longer_than_q", [200, 5, 77], [300, 500, 130]),
 ]

@@ -78,22 +78,6 @@ __device__ __forceinline__ int64_t cache_offset(const DecArgs& a, int b, int p, 
   return row * a.kv_row_stride + (int64_t)hk * D;
 }
 
-// 16x16x32 MFMA of the 16-bit element type
-template <typename T>
-struct Mfma16;
-template <>
-struct Mfma16<__bf16> {
-  __device__ __forceinline__ static f32x4 run(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct Mfma16<_Float16> {
-  __device__ __forceinline__ static f32x4 run(f16x8 a, f16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
   // 16x16x32 MFMA layout (gfx950): lane l, group G = l/16, i = l%16:

@@ -49,6 +49,22 @@ struct Elem16<_Float16> {
   }
 };
 
+// 16x16x32 MFMA of the 16-bit element type
+template <typename T>
+struct Mfma16;
+template <>
+struct Mfma16<__bf16> {
+  __device__ __forceinline__ static f32x4 run(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma16<_Float16> {
+  __device__ __forceinline__ static f32x4 run(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
