@@ -554,6 +554,27 @@ __device__ __forceinline__ int dq16_row(int i) {  // block row of A-row i of 16-
   return (i < 8 ? 0 : 8) + 8 * t + i;
 }
 
+// P and dS (softmax scale folded in) of the lane's 16 rows 16g + r.  lse (log2
+// units) and D of row 16g + r come from lane 16g + r (which holds row l % 32).
+// With MASKED, element r counts only if lo <= r < hi (the lane's key visible
+// to row 16g + r); blocks that lie wholly inside the visible region skip the test.
+template <bool MASKED, typename T>
+__device__ __forceinline__ void probs16(const f32x16& sc, const f32x16& dp, float cur_lse, float cur_dr, int g,
+                                        int lo, int hi, float scale_log2, float scale,
+                                        typename Elem16<T>::v8 (&p16)[2], typename Elem16<T>::v8 (&ds16)[2]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int src = 4 * (16 * g + r);
+    const float lse2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(cur_lse)));
+    const float drr = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(cur_dr)));
+    float pr = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -lse2));
+    if constexpr (MASKED) pr = (r >= lo && r < hi) ? pr : 0.f;
+    const float dsr = pr * (dp[r] - drr) * scale;
+    p16[r >> 3][r & 7] = (T)pr;
+    ds16[r >> 3][r & 7] = (T)dsr;
+  }
+}
+
 template <typename T, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   constexpr int D = 128, BN = kBwdBNWide, BM = 32, NW = 8;
@@ -651,20 +672,17 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // P and dS of the lane's 16 rows 16g + r; lse and D of row 16g + r come
-    // from lane 16g + r
+    // P and dS.  Row q = r0 + 16g + r sees the lane's key iff q < Lq, the key
+    // is in the sequence and (causal) key <= q + shift: lo <= r < hi below.
     v8 p16[2], ds16[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int src = 4 * (16 * g + r);
-      const float lse2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(cur_lse)));
-      const float drr = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(cur_dr)));
-      const int q = r0 + 16 * g + r;
-      const bool vis = q < w.Lq && kcol < w.Lk && (!CAUSAL || kcol <= q + shift);
-      const float pr = vis ? fast_exp2(__builtin_fmaf(sc[r], a.scale_log2, -lse2)) : 0.f;
-      const float dsr = pr * (dp[r] - drr) * a.scale;
-      p16[r >> 3][r & 7] = (T)pr;
-      ds16[r >> 3][r & 7] = (T)dsr;
+    const bool full = r0 + BM <= w.Lq && key0 + BN <= w.Lk && (!CAUSAL || key0 + BN - 1 <= r0 + shift);
+    if (full) {
+      probs16<false, T>(sc, dp, cur_lse, cur_dr, g, 0, 16, a.scale_log2, a.scale, p16, ds16);
+    } else {
+      const int qb = r0 + 16 * g;
+      const int lo = CAUSAL ? kcol - shift - qb : -1;
+      const int hi = kcol < w.Lk ? w.Lq - qb : lo;  // an empty range when the key is past the sequence
+      probs16<true, T>(sc, dp, cur_lse, cur_dr, g, lo, hi, a.scale_log2, a.scale, p16, ds16);
     }
 
     // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 rows)
