@@ -49,7 +49,10 @@ from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, Workload, draw_dout, draw_
 METRIC = "varlen attention fwd TFLOP/s and % of bf16 MFMA peak, d=64/128, causal"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-KERNEL_SRC = os.path.join(ROOT, "variable_length_flashattention_cu_amd", "csrc", "fa_varlen_kernels.hip")
+CSRC_DIR = os.path.join(ROOT, "variable_length_flashattention_cu_amd", "csrc")
+# the forward kernels' source and every header it includes
+KERNEL_SRCS = [os.path.join(CSRC_DIR, n) for n in
+               ("fa_varlen_kernels.hip", "fa_varlen_device.h", "fa_varlen_tiling.h", "fa_varlen_launch.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_ragged64k_causal_d128.json")
 COPY_BYTES = 1 << 30        # calibration copy: 1 GiB read + 1 GiB written
 
@@ -80,8 +83,11 @@ def algorithmic_bytes(wl: Workload) -> float:
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def to_device(wl: Workload, data: dict):
