@@ -242,7 +242,13 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* out, 
   // key blocks: sum_b ceil(Lk_b / bn) <= min(batch * ceil(max_k / bn), ceil(total_k / bn) + batch - 1)
   const int64_t by_max = (int64_t)batch * ((max_seqlen_k + bn - 1) / bn);
   const int64_t by_total = ((int64_t)total_k + bn - 1) / bn + (batch > 0 ? batch - 1 : 0);
-  const int64_t tmax = by_max < by_total ? by_max : by_total;
+  const int64_t compact = by_max < by_total ? by_max : by_total;
+  // Under a causal mask a sequence's first key blocks carry the most work.
+  // Block-major slots (block j of every sequence, then block j + 1) dispatch
+  // them first; slots of sequences shorter than j stay empty, so this order
+  // is used only while they are at most two thirds of the grid.
+  const bool by_block = causal != 0 && 4 * by_max <= 5 * compact;
+  const int64_t tmax = by_block ? by_max : compact;
   const int64_t grid = (tmax * num_heads_k + 7) / 8 * 8;
   if (grid > INT32_MAX) return FA_ERR_TOO_LARGE;
 
@@ -269,6 +275,7 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* out, 
   a.scale_log2 = (float)((double)softmax_scale * kLog2e);
   a.batch = batch;
   a.tmax = (int32_t)tmax;
+  a.by_block = by_block ? 1 : 0;
   a.n_work = (int32_t)(tmax * num_heads_k);
   a.total_q = total_q;
   a.heads = num_heads;
@@ -277,7 +284,7 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* out, 
   hipStream_t s = (hipStream_t)stream;
   if (fa::launch_bwd_prep(dtype, head_dim, a, s) != hipSuccess) return FA_ERR_HIP;
   if (grid > 0) {
-    if (fa::launch_tile_map(cu_seqlens_k, batch, bn, blk, s) != hipSuccess) return FA_ERR_HIP;
+    if (!by_block && fa::launch_tile_map(cu_seqlens_k, batch, bn, blk, s) != hipSuccess) return FA_ERR_HIP;
     if (fa::launch_bwd(dtype, head_dim, causal != 0, (int)grid, a, s) != hipSuccess) return FA_ERR_HIP;
   }
   if (fa::launch_bwd_dq(dtype, head_dim, a, s) != hipSuccess) return FA_ERR_HIP;

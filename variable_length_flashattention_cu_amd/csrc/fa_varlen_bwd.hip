@@ -142,6 +142,7 @@ struct ColItem {
   int q_start, Lq, k_start, Lk;
 };
 
+template <int BN>
 __device__ __forceinline__ bool decode_col(const BwdArgs& a, ColItem& w) {
   // each XCD (workgroup i runs on XCD i % 8) takes a contiguous slice of items
   const uint32_t per_xcd = gridDim.x >> 3;
@@ -149,19 +150,31 @@ __device__ __forceinline__ bool decode_col(const BwdArgs& a, ColItem& w) {
   if (work >= (uint32_t)a.n_work) return false;
   w.hk = (int)(work / (uint32_t)a.tmax);
   const int t = (int)(work % (uint32_t)a.tmax);
-  const int T = a.blk_start[a.batch];
-  if (t >= T) return false;
-  int lo = 0, hi = a.batch;  // invariant: blk_start[lo] <= t < blk_start[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.blk_start[mid] <= t) lo = mid; else hi = mid;
+  int b, j;
+  if (a.by_block) {
+    // key block j of every sequence before block j + 1 of any: under a causal
+    // mask the first key blocks see the most query rows, so the longest items
+    // are dispatched first and the short ones fill in at the end
+    j = t / a.batch;
+    b = t - j * a.batch;
+    if (j * BN >= a.cu_k[b + 1] - a.cu_k[b]) return false;
+  } else {
+    const int T = a.blk_start[a.batch];
+    if (t >= T) return false;
+    int lo = 0, hi = a.batch;  // invariant: blk_start[lo] <= t < blk_start[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.blk_start[mid] <= t) lo = mid; else hi = mid;
+    }
+    b = lo;
+    j = t - a.blk_start[lo];
   }
-  w.b = lo;
-  w.j = t - a.blk_start[lo];
-  w.q_start = a.cu_q[lo];
-  w.Lq = a.cu_q[lo + 1] - w.q_start;
-  w.k_start = a.cu_k[lo];
-  w.Lk = a.cu_k[lo + 1] - w.k_start;
+  w.b = b;
+  w.j = j;
+  w.q_start = a.cu_q[b];
+  w.Lq = a.cu_q[b + 1] - w.q_start;
+  w.k_start = a.cu_k[b];
+  w.Lk = a.cu_k[b + 1] - w.k_start;
   return true;
 }
 
@@ -297,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float lds_red[DB * 64 * 16];
 
   ColItem w;
-  if (!decode_col(a, w)) return;
+  if (!decode_col<BN>(a, w)) return;
 
   const int tid0 = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
@@ -590,7 +603,7 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_do[BM * D];
 
   ColItem w;
-  if (!decode_col(a, w)) return;
+  if (!decode_col<BN>(a, w)) return;
 
   const int tid0 = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);

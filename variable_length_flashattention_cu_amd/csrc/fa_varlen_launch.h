@@ -59,8 +59,11 @@ struct BwdArgs {
   float scale;             // softmax_scale
   float scale_log2;        // softmax_scale * log2(e)
   int32_t batch;
-  int32_t tmax;            // upper bound on key blocks per key/value head
+  int32_t tmax;            // work slots per key/value head (see by_block below)
   int32_t n_work;          // kv_heads * tmax
+  int32_t by_block;        // 1: slot t is key block t / batch of sequence t % batch (empty if
+                           // the sequence is shorter), so every sequence's first blocks come
+                           // first; 0: slot t is the t-th entry of the key-block map
   int32_t total_q;
   int32_t heads;
   int32_t head_group;      // query heads per key/value head
