@@ -262,6 +262,7 @@ int main() {
     // (head_dim 64, 4 waves), and the 128-key K and V blocks
     check_bf16<128, 128, 8>(H);
     check_bf16<128, 256, 8>(H);
+    check_bf16<64, 256, 8>(H);
     check_bf16<128, 32, 8>(H);
     check_bf16<128, 32, 4>(H);
     check_bf16<64, 32, 4>(H);

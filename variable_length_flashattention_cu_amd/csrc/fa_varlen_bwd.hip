@@ -19,14 +19,12 @@
 //
 // Three launches:
 //   bwd_prep_kernel  D_i for every (row, head) and a zeroed dQ accumulator;
-//   bwd16_kernel     (head_dim 64) or bwd16w_kernel (head_dim 128): one
-//                    workgroup per (key block, key/value head): dK, dV of the
-//                    block and atomic dQ contributions;
+//   bwd16w_kernel    one workgroup per (256-key block, key/value head): dK, dV
+//                    of the block and atomic dQ contributions;
 //   bwd_dq_kernel    dq = accumulator (already scaled) in the input type.
 //
-// Workgroup layout (wave w owns the 32 keys of key group w; head_dim 64: 4
-// wavefronts on 128-key blocks, head_dim 128: 8 wavefronts on 256-key blocks;
-// one 32-row query block per step):
+// Workgroup layout (8 wavefronts; wave w owns the 32 keys of key group w of
+// the 256-key block; one 32-row query block per step):
 //   * K and V of the block are staged in LDS once per item and give the B
 //     operands of S = Q K^T and dP = dO V^T (contraction over head_dim); Q and
 //     dO rows are read from LDS in the permuted row order of the forward
@@ -38,14 +36,13 @@
 //     from the row-major tiles by transposing LDS reads.  dK^T and dV^T
 //     accumulate in registers.
 //   * dS goes to LDS row-major; dQ = dS K reads it with K^T (transposing
-//     reads of the K block), contracted over all keys of the block, and adds
-//     it to the float32 accumulator.  These atomic additions (D per query row
-//     and key block) are what limits the 128-key kernel at head_dim 128: the
-//     L2 caches retire about one lane's atomic per channel and clock, hence
-//     the 256-key blocks there.
+//     reads of the K block), contracted over all 256 keys of the block, and
+//     adds it to the float32 accumulator.  These atomic additions (D per query
+//     row and key block) limited 128-key blocks at head_dim 128: the L2
+//     caches retire about one lane's atomic per channel and clock.
 //   * Q, dO, lse and D of the next query block are loaded into registers
-//     while the current one is computed and stored into LDS once no read of
-//     the current block remains.
+//     while the current one is computed and stored into LDS after the
+//     mid-step barrier, when no read of the current block remains.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,8 +55,7 @@ namespace fa {
 namespace {
 
 constexpr float kLog2eF = 1.4426950408889634074f;
-constexpr int kBwdBN = 128;      // keys per work item of bwd16_kernel (4 key groups of 32)
-constexpr int kBwdBNWide = 256;  // keys per work item of bwd16w_kernel (8 key groups of 32)
+constexpr int kBwdBNWide = 256;  // keys per work item (8 key groups of 32)
 
 template <typename T>
 __device__ __forceinline__ float half_to_f32(uint32_t bits16);
@@ -260,6 +256,9 @@ __device__ __forceinline__ void read_ahead_schedule() {
 // kv_head * head_group + s / nblk and rows (i_begin + s % nblk) * BM ...
 template <int D, int BM, int NW>
 struct BlockStage {
+  // NW staging wavefronts; with more threads in the workgroup, thread t
+  // stages as thread t % (64 NW) (the same chunks twice, equal values)
+  static constexpr int NT = 64 * NW;
   Tile16<D, BM, NW> tq, tdo;
   float lse_v = 0.f, dr_v = 0.f;
 
@@ -269,8 +268,8 @@ struct BlockStage {
     const int64_t rs = a.row_stride;
     const uint16_t* qh = (const uint16_t*)a.q + (int64_t)w.q_start * rs + (int64_t)h * D;
     const uint16_t* doh = (const uint16_t*)a.dout + (int64_t)w.q_start * rs + (int64_t)h * D;
-    tq.load_k(qh, rs, r0, w.Lq, tid);
-    tdo.load_k(doh, rs, r0, w.Lq, tid);
+    tq.load_k(qh, rs, r0, w.Lq, tid & (NT - 1));
+    tdo.load_k(doh, rs, r0, w.Lq, tid & (NT - 1));
     // lse and D of the block's rows: branch-free buffer loads whose range
     // check (the rows of the sequence) reads rows past its end as zero
     const int64_t at = (int64_t)h * a.total_q + w.q_start + r0;
@@ -281,8 +280,8 @@ struct BlockStage {
   }
   // lse is stored in log2 units
   __device__ __forceinline__ void store(uint16_t* qs, uint16_t* dos, float* lse, float* dr, int tid) const {
-    tq.store_k(qs, tid);
-    tdo.store_k(dos, tid);
+    tq.store_k(qs, tid & (NT - 1));
+    tdo.store_k(dos, tid & (NT - 1));
     // every thread holds the values of row tid % BM: all write them (equal
     // values), so no branch leaves the loads' wait off some path
     lse[tid & (BM - 1)] = lse_v * kLog2eF;
@@ -290,280 +289,26 @@ struct BlockStage {
   }
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd16_kernel(BwdArgs a) {
-  constexpr int BN = kBwdBN, BM = 32, NW = 4;
-  constexpr int KSTEPS = D / 16;  // k-steps over head_dim
-  constexpr int DB = D / 32;      // 32-dim tiles
-  static_assert(D == 64, "head_dim 128 runs bwd16w_kernel");
-  using E = Elem16<T>;
-  typedef typename E::v8 v8;
-
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[BN * D];       // K block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[BN * D];       // V block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_ds[BM * BN];     // dS, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][BM * D];    // query block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_do[2][BM * D];
-  __shared__ __attribute__((aligned(16))) float lds_lse[2][BM];
-  __shared__ __attribute__((aligned(16))) float lds_dr[2][BM];
-  // key-split partial sums of the dQ tiles (head_dim 64: two waves per tile)
-  __shared__ __attribute__((aligned(16))) float lds_red[DB * 64 * 16];
-
-  ColItem w;
-  if (!decode_col<BN>(a, w)) return;
-
-  const int tid0 = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
-  int tid = tid0, lane = tid0 & 63;
-  int l32 = lane & 31, g = lane >> 5;
-  int li = lane & 15, lg = lane >> 4;  // lane in its 16-lane group, group
-  const int key0 = w.j * BN;
-  // this lane's key: the wave's 32 keys are taken in the row order whose
-  // swizzled LDS reads are free of bank conflicts
-  const int klane = 32 * wave + tiling::key_of_arow(l32);  // in the block
-  const int kcol = key0 + klane;                            // in the sequence
-  const int shift = w.Lk - w.Lq;
-  const int64_t rs = a.row_stride, rsk = a.kv_row_stride;
-  const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
-  const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
-
-  // K and V of the block are staged in LDS for the item: the B operands of
-  // S = Q K^T and dP = dO V^T (contraction over head_dim) and, by transposing
-  // reads, the K^T operand of the wave's dQ tile are read from there every
-  // step, which keeps registers free for reads in flight.  Keys past the
-  // sequence read as zero.
-  constexpr int SPLIT = NW / DB;     // waves per dQ tile
-  constexpr int KEYS = BN / SPLIT;  // keys of a wave's dQ product
-  // dQ tile of the wave: 32 dims (tile), key part
-  const int tile = wave % DB, part = wave / DB;
-  lds_load_rows<D, BN, NW>(lds_k, kbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
-  lds_load_rows<D, BN, NW>(lds_v, vbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
-
-  // query blocks that see a key of this block: rows q with q + shift >= key0
-  const int i_begin = CAUSAL ? max(0, key0 - shift) / BM : 0;
-  const int i_end = (w.Lq + BM - 1) / BM;
-  const int nblk = max(0, i_end - i_begin);
-  const int nsteps = a.head_group * nblk;
-
-  // Query block s (Q, dO, lse, D): loaded into registers while the previous
-  // block is computed, then stored into an LDS buffer.  Rows past the
-  // sequence read as zeros.
-  BlockStage<D, BM, NW> stage;
-
-  f32x16 dkt[DB], dvt[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dkt[db] = f32x16{};
-    dvt[db] = f32x16{};
-  }
-
-  if (nsteps > 0) {
-    stage.load(a, w, 0, nblk, i_begin, tid);
-    stage.store(lds_q[0], lds_do[0], lds_lse[0], lds_dr[0], tid);
-  }
-  __syncthreads();
-
-  // Every load issued so far (K, V operands, the first query block) has
-  // landed.  Without this wait the compiler keeps the operand loads pending
-  // at the loop head and places vmcnt waits inside the loop; those then also
-  // wait, every step, for the previous step's dQ atomics and for the next
-  // block's prefetch, since vector memory operations complete in order.
-  __builtin_amdgcn_s_waitcnt(0);
-
-  int arow = tiling::key_of_arow(l32);
-  int klane_l = klane;
-  for (int s = 0; s < nsteps; ++s) {
-    // lane-dependent address terms are re-derived every step instead of
-    // being kept as one register per LDS address across the loop
-    tid = opaque(tid0);
-    lane = tid & 63;
-    l32 = lane & 31;
-    g = lane >> 5;
-    li = lane & 15;
-    lg = lane >> 4;
-    arow = tiling::key_of_arow(l32);
-    klane_l = opaque(klane);
-    const int buf = s & 1;
-    const int h = w.hk * a.head_group + s / nblk;
-    const int r0 = (i_begin + s % nblk) * BM;
-    // the next block (the last one again at the last step: loads and stores
-    // stay unconditional, so that no wait for them lands elsewhere in the loop)
-    stage.load(a, w, min(s + 1, nsteps - 1), nblk, i_begin, tid);
-    const uint16_t* qs = lds_q[buf];
-    const uint16_t* dos = lds_do[buf];
-
-    // S = Q K^T and dP = dO V^T (rows permuted: register r of half g = row 16g + r)
-    f32x16 sc = f32x16{}, dp = f32x16{};
-    {
-      // operands of k-step ks are read PF steps ahead of their MFMAs
-      constexpr int PF = 2;
-      v8 aq[PF + 1], ad[PF + 1], bk[PF + 1], bv[PF + 1];
-      auto fetch = [&](int ks) __attribute__((always_inline)) {
-        const int i = ks % (PF + 1);
-        aq[i] = *(const v8*)(qs + tiling::ks_index<D>(arow, 2 * ks + g));
-        ad[i] = *(const v8*)(dos + tiling::ks_index<D>(arow, 2 * ks + g));
-        bk[i] = *(const v8*)(lds_k + tiling::ks_index<D>(klane_l, 2 * ks + g));
-        bv[i] = *(const v8*)(lds_v + tiling::ks_index<D>(klane_l, 2 * ks + g));
-      };
-#pragma unroll
-      for (int ks = 0; ks < PF; ++ks) fetch(ks);
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        if (ks + PF < KSTEPS) fetch(ks + PF);
-        const int i = ks % (PF + 1);
-        sc = E::mfma(aq[i], bk[i], sc);
-        dp = E::mfma(ad[i], bv[i], dp);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // P and dS (softmax scale folded in) of the lane's 16 rows for its key
-    float lse2[16], drr[16];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 l4 = *(const f32x4*)(&lds_lse[buf][16 * g + 4 * r4]);
-      const f32x4 d4 = *(const f32x4*)(&lds_dr[buf][16 * g + 4 * r4]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        lse2[4 * r4 + c] = l4[c];
-        drr[4 * r4 + c] = d4[c];
-      }
-    }
-    v8 p16[2], ds16[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = r0 + 16 * g + r;
-      const bool vis = q < w.Lq && kcol < w.Lk && (!CAUSAL || kcol <= q + shift);
-      const float pr = vis ? fast_exp2(__builtin_fmaf(sc[r], a.scale_log2, -lse2[r])) : 0.f;
-      const float dsr = pr * (dp[r] - drr[r]) * a.scale;
-      p16[r >> 3][r & 7] = (T)pr;
-      ds16[r >> 3][r & 7] = (T)dsr;
-    }
-
-    // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 rows); the
-    // transposed A operands come from the row-major tiles by transposing reads
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int c0 = 32 * db + 16 * (lg & 1), rr = 16 * (lg >> 1) + 8 * t;
-        const v8 adt = tr_read8<v8, D>(dos, rr, c0, li);
-        const v8 aqt = tr_read8<v8, D>(qs, rr, c0, li);
-        dvt[db] = E::mfma(adt, p16[t], dvt[db]);
-        dkt[db] = E::mfma(aqt, ds16[t], dkt[db]);
-      }
-    read_ahead_schedule<4 * DB, 8 * DB, 8>();
-
-    // dS -> LDS, row-major [row][key].  The 16-bit values are taken from the
-    // packed operand registers as whole words (element-wise access to the
-    // 16-bit vector was miscompiled into one element per half).
-    {
-      const int kk = klane_l;
-      const u32x4 w0 = __builtin_bit_cast(u32x4, ds16[0]);
-      const u32x4 w1 = __builtin_bit_cast(u32x4, ds16[1]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t word = r < 8 ? w0[(r & 7) >> 1] : w1[(r & 7) >> 1];
-        lds_ds[tiling::ks_index<BN>(16 * g + r, kk >> 3) + (kk & 7)] = (uint16_t)((r & 1) ? (word >> 16) : word);
-      }
-    }
-    __syncthreads();
-
-    // dQ rows r0..r0+31: wave -> (32-dim tile, key part)
-    {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KEYS / 16; ++kk) {
-        const int k16 = part * KEYS + 16 * kk;
-        const v8 ads = *(const v8*)(lds_ds + tiling::ks_index<BN>(l32, (k16 >> 3) + g));
-        const v8 bkt = tr_read8<v8, D>(lds_k, k16 + 8 * (lg >> 1), 32 * tile + 16 * (lg & 1), li);
-        acc = E::mfma(ads, bkt, acc);
-      }
-      read_ahead_schedule<KEYS / 16, 3 * (KEYS / 16), 9>();
-      // the next query block goes into the other buffer before the atomics are
-      // issued, so that waiting for its loads does not wait for them too
-      stage.store(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_lse[buf ^ 1], lds_dr[buf ^ 1], tid);
-      if constexpr (SPLIT > 1) {
-        // two waves hold halves of the key sum of one tile: add them in LDS so
-        // that each dq element receives one atomic addition per key block
-        static_assert(SPLIT == 2, "key split of the dQ product");
-        if (part == 1) {
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            *(f32x4*)(&lds_red[(tile * 64 + lane) * 16 + 4 * r4]) =
-                f32x4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
-        }
-        __syncthreads();
-        if (part == 0) {
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 o = *(const f32x4*)(&lds_red[(tile * 64 + lane) * 16 + 4 * r4]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[4 * r4 + c] += o[c];
-          }
-        }
-      }
-      // accumulator register r of half g holds row 8*(r/4) + 4g + r%4, column
-      // 32*tile + l32.  Buffer atomics over the rows of this block that lie in
-      // the sequence: the range check drops the additions of rows past its end.
-      const __amdgpu_buffer_rsrc_t racc =
-          buffer_rsrc(a.dq_acc + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D,
-                      tiling::head_rows_bytes(min(BM, w.Lq - r0), rs, D, 4));
-      if (part == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t off = ((uint32_t)(8 * (r >> 2) + 4 * g + (r & 3)) * (uint32_t)rs + 32 * tile + l32) * 4u;
-          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], racc, (int)off, 0, 0);
-        }
-      }
-    }
-
-    __syncthreads();
-  }
-
-  // ---- epilogue: dK (scale already in dS) and dV of this lane's key
-  if (kcol < w.Lk) {
-    T* dkp = (T*)a.dk + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
-    T* dvp = (T*)a.dv + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        typename E::v4 k4, v4;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          k4[c] = (T)dkt[db][4 * s4 + c];
-          v4[c] = (T)dvt[db][4 * s4 + c];
-        }
-        const int d0 = 32 * db + 8 * s4 + 4 * g;
-        *(typename E::v4*)(dkp + d0) = k4;
-        *(typename E::v4*)(dvp + d0) = v4;
-      }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// the backward workgroup at head_dim 128: 256-key work items
+// the backward workgroup: 256-key work items
 // ---------------------------------------------------------------------------
-// Same arithmetic as bwd16_kernel, with 8 wavefronts, one per 32-key group of
-// a 256-key block, on 32-row query blocks.  The dQ contribution of a query
-// block is contracted over all 256 keys before it is added, which halves the
-// float32 atomic additions per (row, key) against 128-key items; those
-// additions, not the matrix cores, set the pace of the 128-key kernel.
-// LDS holds the K and V blocks (64 KB each), dS (16 KB) and one Q/dO block
-// (16 KB): 160 KB, all of it.  The next block's Q/dO are stored after the
+// 8 wavefronts, one per 32-key group of a 256-key block, on 32-row query
+// blocks.  The dQ contribution of a query block is contracted over all 256
+// keys before it is added, which halves the float32 atomic additions per
+// (row, key) against 128-key items.  At head_dim 128, LDS holds the K and V
+// blocks (64 KB each), dS (16 KB) and one Q/dO block (16 KB): 160 KB, all of
+// it (88 KB at head_dim 64).  The next block's Q/dO are stored after the
 // mid-step barrier (no Q/dO reads remain in the step), so one buffer
 // suffices; lse and D of the step's rows stay in registers (lane l holds row
 // l % 32) and reach the lanes that need them through ds_bpermute.
 //
 // dQ uses 16x16x32 MFMAs (gfx950 layout, lane l, i = l % 16, G = l / 16:
 // A row i, k = 8G..8G+7; B column i, k = 8G..8G+7; accumulator register r:
-// row 4G + r, column i): wave w owns dims 16w..16w+15 for both 16-row tiles of
-// the block, so no two waves add to the same element.  Row tile t takes the
-// query rows 8t..8t+7 and 16+8t..16+8t+7, whose swizzled dS rows sit in 16
-// distinct bank groups.
-template <int t>
-__device__ __forceinline__ int dq16_row(int i) {  // block row of A-row i of 16-row tile t
+// row 4G + r, column i), one 16x16 tile of dQ per (wave, tile) pair so that no
+// two waves add to the same element.  Row tile t takes the query rows
+// 8t..8t+7 and 16+8t..16+8t+7, whose swizzled dS rows sit in 16 distinct
+// bank groups.
+__device__ __forceinline__ int dq16_row(int t, int i) {  // block row of A-row i of 16-row tile t
   return (i < 8 ? 0 : 8) + 8 * t + i;
 }
 
@@ -588,11 +333,15 @@ __device__ __forceinline__ void probs16(const f32x16& sc, const f32x16& dp, floa
   }
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
-  constexpr int D = 128, BN = kBwdBNWide, BM = 32, NW = 8;
-  constexpr int KSTEPS = D / 16;  // k-steps over head_dim
-  constexpr int DB = D / 32;      // 32-dim tiles
+  constexpr int BN = kBwdBNWide, BM = 32, NW = 8;
+  constexpr int KSTEPS = D / 16;    // k-steps over head_dim
+  constexpr int DB = D / 32;        // 32-dim tiles
+  constexpr int CT = D / 16;        // 16-column tiles of dQ
+  constexpr int TPW = 2 * CT / NW;  // 16x16 dQ tiles per wave (2 at D=128, 1 at D=64)
+  constexpr int NWS = BM * D / 8 / 64 < NW ? BM * D / 8 / 64 : NW;  // staging wavefronts
+  static_assert(D == 64 || D == 128, "backward head_dim");
   using E = Elem16<T>;
   typedef typename E::v8 v8;
 
@@ -625,7 +374,7 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   const int nblk = max(0, i_end - i_begin);
   const int nsteps = a.head_group * nblk;
 
-  BlockStage<D, BM, NW> stage;
+  BlockStage<D, BM, NWS> stage;
   float cur_lse = 0.f, cur_dr = 0.f;  // lse (log2 units) and D of row l32 of the step
 
   f32x16 dkt[DB], dvt[DB];
@@ -637,18 +386,24 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
 
   if (nsteps > 0) {
     stage.load(a, w, 0, nblk, i_begin, tid);
-    stage.tq.store_k(lds_q, tid);
-    stage.tdo.store_k(lds_do, tid);
+    stage.tq.store_k(lds_q, tid & (64 * NWS - 1));
+    stage.tdo.store_k(lds_do, tid & (64 * NWS - 1));
     cur_lse = stage.lse_v * kLog2eF;
     cur_dr = stage.dr_v;
   }
   __syncthreads();
-  // every load issued so far has landed (see bwd16_kernel)
+  // Every load issued so far (K, V blocks, the first query block) has
+  // landed.  Without this wait the compiler keeps the pre-loop loads pending
+  // at the loop head and places vmcnt waits inside the loop; those then also
+  // wait, every step, for the previous step's dQ atomics, since vector memory
+  // operations complete in order.
   __builtin_amdgcn_s_waitcnt(0);
 
   int arow = tiling::key_of_arow(l32);
   int klane_l = klane;
   for (int s = 0; s < nsteps; ++s) {
+    // lane-dependent address terms are re-derived every step instead of
+    // being kept as one register per LDS address across the loop
     tid = opaque(tid0);
     lane = tid & 63;
     l32 = lane & 31;
@@ -711,7 +466,9 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
       }
     read_ahead_schedule<4 * DB, 8 * DB, 8>();
 
-    // dS -> LDS, row-major [row][key] (whole-word extraction, see bwd16_kernel)
+    // dS -> LDS, row-major [row][key].  The 16-bit values are taken from the
+    // packed operand registers as whole words (element-wise access to the
+    // 16-bit vector was miscompiled into one element per half).
     {
       const int kk = klane_l;
       const u32x4 w0 = __builtin_bit_cast(u32x4, ds16[0]);
@@ -724,36 +481,42 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // dQ rows r0..r0+31, dims 16*wave..+15: two 16x16 tiles over the 256 keys
+    // dQ rows r0..r0+31 over the 256 keys: 16x16 tiles (row tile rt, dims
+    // 16*ct..+15); D=128: wave w takes column tile w of both row tiles (one
+    // K^T operand feeds two MFMAs), D=64: column tile w % 4 of row tile w / 4
     {
-      f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int ct = wave % CT;
+      const int rt0 = TPW == 2 ? 0 : wave / CT;
+      f32x4 acc[TPW];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < BN / 32; ++kk) {
         const int k0 = 32 * kk;
-        const v8 a0 = *(const v8*)(lds_ds + tiling::ks_index<BN>(dq16_row<0>(li), (k0 >> 3) + lg));
-        const v8 a1 = *(const v8*)(lds_ds + tiling::ks_index<BN>(dq16_row<1>(li), (k0 >> 3) + lg));
-        const v8 bkt = tr_read8<v8, D>(lds_k, k0 + 8 * lg, 16 * wave, li);
-        acc0 = Mfma16<T>::run(a0, bkt, acc0);
-        acc1 = Mfma16<T>::run(a1, bkt, acc1);
+        const v8 bkt = tr_read8<v8, D>(lds_k, k0 + 8 * lg, 16 * ct, li);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const v8 av = *(const v8*)(lds_ds + tiling::ks_index<BN>(dq16_row(rt0 + u, li), (k0 >> 3) + lg));
+          acc[u] = Mfma16<T>::run(av, bkt, acc[u]);
+        }
       }
-      read_ahead_schedule<2 * (BN / 32), 4 * (BN / 32), 8>();
+      read_ahead_schedule<TPW * (BN / 32), (TPW + 2) * (BN / 32), 8>();
       // the next query block: no Q/dO reads remain in this step
-      stage.tq.store_k(lds_q, tid);
-      stage.tdo.store_k(lds_do, tid);
+      stage.tq.store_k(lds_q, tid & (64 * NWS - 1));
+      stage.tdo.store_k(lds_do, tid & (64 * NWS - 1));
       cur_lse = stage.lse_v * kLog2eF;
       cur_dr = stage.dr_v;
-      // register r: block row dq16_row<t>(4 lg + r), column 16*wave + li
+      // register r of tile u: block row dq16_row(rt0 + u, 4 lg + r), column 16*ct + li
       const __amdgpu_buffer_rsrc_t racc =
           buffer_rsrc(a.dq_acc + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D,
                       tiling::head_rows_bytes(min(BM, w.Lq - r0), rs, D, 4));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t c = 16 * wave + li;
-        const uint32_t off0 = ((uint32_t)dq16_row<0>(4 * lg + r) * (uint32_t)rs + c) * 4u;
-        const uint32_t off1 = ((uint32_t)dq16_row<1>(4 * lg + r) * (uint32_t)rs + c) * 4u;
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc0[r], racc, (int)off0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc1[r], racc, (int)off1, 0, 0);
-      }
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t off = ((uint32_t)dq16_row(rt0 + u, 4 * lg + r) * (uint32_t)rs + 16 * ct + li) * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[u][r], racc, (int)off, 0, 0);
+        }
     }
     __syncthreads();
   }
@@ -788,11 +551,11 @@ hipError_t launch(F kernel, int grid, int threads, hipStream_t stream, const Bwd
 template <typename T>
 hipError_t launch_bwd_t(int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
   if (head_dim == 128)
-    return causal ? launch(bwd16w_kernel<T, true>, grid, 512, stream, a)
-                  : launch(bwd16w_kernel<T, false>, grid, 512, stream, a);
+    return causal ? launch(bwd16w_kernel<T, 128, true>, grid, 512, stream, a)
+                  : launch(bwd16w_kernel<T, 128, false>, grid, 512, stream, a);
   if (head_dim == 64)
-    return causal ? launch(bwd16_kernel<T, 64, true>, grid, 256, stream, a)
-                  : launch(bwd16_kernel<T, 64, false>, grid, 256, stream, a);
+    return causal ? launch(bwd16w_kernel<T, 64, true>, grid, 512, stream, a)
+                  : launch(bwd16w_kernel<T, 64, false>, grid, 512, stream, a);
   return hipErrorInvalidValue;
 }
 
@@ -805,8 +568,7 @@ int64_t row_pairs_grid(const BwdArgs& a, int head_dim) {
 }  // namespace
 
 int bwd_block_n(int dtype, int head_dim) {
-  if ((dtype == 1 || dtype == 2) && head_dim == 64) return kBwdBN;
-  if ((dtype == 1 || dtype == 2) && head_dim == 128) return kBwdBNWide;
+  if ((dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 128)) return kBwdBNWide;
   return 0;
 }
 
