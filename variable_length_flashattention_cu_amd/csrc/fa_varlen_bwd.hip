@@ -399,6 +399,11 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   // operations complete in order.
   __builtin_amdgcn_s_waitcnt(0);
 
+  // the K operand of S = Q K^T is the same for every step: held in registers
+  v8 kreg[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) kreg[ks] = *(const v8*)(lds_k + tiling::ks_index<D>(klane, 2 * ks + g));
+
   int arow = tiling::key_of_arow(l32);
   int klane_l = klane;
   for (int s = 0; s < nsteps; ++s) {
@@ -420,12 +425,11 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
     f32x16 sc = f32x16{}, dp = f32x16{};
     {
       constexpr int PF = 2;
-      v8 aq[PF + 1], ad[PF + 1], bk[PF + 1], bv[PF + 1];
+      v8 aq[PF + 1], ad[PF + 1], bv[PF + 1];
       auto fetch = [&](int ks) __attribute__((always_inline)) {
         const int i = ks % (PF + 1);
         aq[i] = *(const v8*)(lds_q + tiling::ks_index<D>(arow, 2 * ks + g));
         ad[i] = *(const v8*)(lds_do + tiling::ks_index<D>(arow, 2 * ks + g));
-        bk[i] = *(const v8*)(lds_k + tiling::ks_index<D>(klane_l, 2 * ks + g));
         bv[i] = *(const v8*)(lds_v + tiling::ks_index<D>(klane_l, 2 * ks + g));
       };
 #pragma unroll
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
       for (int ks = 0; ks < KSTEPS; ++ks) {
         if (ks + PF < KSTEPS) fetch(ks + PF);
         const int i = ks % (PF + 1);
-        sc = E::mfma(aq[i], bk[i], sc);
+        sc = E::mfma(aq[i], kreg[ks], sc);
         dp = E::mfma(ad[i], bv[i], dp);
       }
     }
