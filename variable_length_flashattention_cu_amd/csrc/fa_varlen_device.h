@@ -95,6 +95,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   void* p = (void*)(((uint64_t)hi << 32) | lo);
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
+// The same descriptor as four scalar dwords, for inline assembly.
+__device__ __forceinline__ u32x4 buffer_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu;  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// LDS byte address of a pointer into a __shared__ array (wave-uniform).
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// Direct global -> LDS load (buffer_load_dwordx4 ... lds): lane i's 16 bytes
+// at byte offset `voffset` of the buffer land at LDS byte address
+// lds_base + 16 i, without passing through registers.  It is issued from
+// inline assembly so that the compiler does not track it (its wait analysis
+// cannot tell LDS buffers apart and would wait for the load before the next
+// LDS read of any buffer).  The caller waits for it itself (wait_vmcnt)
+// before the barrier after which the destination is read.  A load in flight
+// that the compiler does not know of only makes the compiler's own vmcnt
+// waits stricter: vector-memory loads complete in order.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N): at most N vector-memory loads of this wave still in
+// flight (export and LDS counters untouched).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_offset, 0, 0);
 }

@@ -291,6 +291,39 @@ struct GroupStage16 : tiling::Geom16<D, BN, NW> {
   }
 };
 
+// K tile staging by direct global -> LDS loads, shared by the 4 waves of one
+// group (256 lanes).  The tile lands in the swizzled K layout
+// (tiling::ks_index): LDS chunk slot p = 64 * instruction + lane holds the
+// logical chunk that the swizzle stores there, so each lane loads that chunk.
+// Keys at or past Lk read as zeros (buffer range check).  At head_dim 96 the
+// last 4 slots of a 128-element row hold no chunk; their lanes load a chunk of
+// the same row that is never read.
+template <int D, int BN>
+struct KDirect {
+  static constexpr int KS = tiling::k_stride<D>();
+  static constexpr int CPR = KS / 8;                 // 16-byte slots per LDS row
+  static constexpr int PER_WAVE = BN * CPR / 256;    // loads per wave per tile
+  static_assert(BN * CPR % 256 == 0, "tile must split into whole wave loads");
+  static_assert(PER_WAVE == 4, "the wait counts below assume 4 loads per tile");
+
+  __device__ __forceinline__ static void issue(uint16_t* dst, const uint16_t* __restrict__ kbase,
+                                               int64_t row_stride, int key0, int Lk, int gwave, int lane) {
+    const int rows = max(0, min(BN, Lk - key0));
+    const u32x4 r = buffer_rsrc_words(kbase + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
+    const uint32_t base = lds_address(dst);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int seg = gwave * PER_WAVE + i;
+      const int p = seg * 64 + lane;
+      const int row = p / CPR;
+      int ch = (p % CPR) ^ k_swz<KS>(row);
+      if (D == 96) ch = ch < D / 8 ? ch : ch - 8;  // slots 12..15: a chunk of the row, never read
+      const uint32_t off = ((uint32_t)row * (uint32_t)row_stride + (uint32_t)ch * 8u) * 2u;
+      lds_dma16(r, off, base + (uint32_t)seg * 1024u);
+    }
+  }
+};
+
 // Scheduling order of a block of NM MFMAs fed by NR LDS operand reads: the
 // first PRE reads, then one MFMA and one read alternately, then the
 // remaining MFMAs, so that PRE reads are in flight ahead of their use.
@@ -618,13 +651,16 @@ __device__ __forceinline__ void fwd16_item(const FwdArgs& a, const WorkItem& w,
 // into the buffer that V(n-2) left after slot 2n-1.  Each group loads the
 // next tile it stages from global memory right after storing the current one,
 // a slot pair ahead of its use.
+constexpr int kPingPongKBuffers = 3;
+
 template <typename T, int D, int BN, bool CAUSAL>
 __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const WorkItem& w,
-                                                    uint16_t (&lds_k)[2][BN * tiling::k_stride<D>()],
+                                                    uint16_t (&lds_k)[kPingPongKBuffers][BN * tiling::k_stride<D>()],
                                                     uint16_t (&lds_v)[2][D * BN]) {
   constexpr int NW = 8;
   constexpr int BM = 32 * NW;
-  using Stage = GroupStage16<D, BN, 4>;  // staging by one group of 4 waves
+  using Stage = GroupStage16<D, BN, 4>;  // V staging by group 0 (4 waves)
+  using KDma = KDirect<D, BN>;           // K staging by group 1 (4 waves)
   using Wave = Wave16<T, D, BN, 1>;
   constexpr int KB = Wave::KB;
 
@@ -645,6 +681,19 @@ __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const Work
   const int hk = w.h / a.head_group;
   const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)hk * D;
   const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)hk * D;
+
+  // The first tiles are requested before Q and one wait covers all of them:
+  // group 1 loads K(0..2) straight into the three K buffers, group 0 loads
+  // V(0) into registers.
+  Stage st;
+  if (n_end > 0) {
+    if (grp == 1) {
+      for (int j = 0; j < kPingPongKBuffers && j < n_end; ++j)
+        KDma::issue(lds_k[j], kbase, rsk, j * BN, w.Lk, wave - 4, lane);
+    } else {
+      st.load_v(vbase, rsk, 0, w.Lk, gtid);
+    }
+  }
 
   Wave wv;
   {  // Q rows past the end of the sequence load as zeros
@@ -676,31 +725,23 @@ __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const Work
   }
 
   const int arow = key_of_arow(l32);
-  Stage st;
-  if (n_end > 0) {
-    if (grp == 1) {
-      st.load_k(kbase, rsk, 0, w.Lk, gtid);
-      st.store_k(lds_k[0], gtid);
-      if (n_end > 1) st.load_k(kbase, rsk, BN, w.Lk, gtid);
-    } else {
-      st.load_v(vbase, rsk, 0, w.Lk, gtid);
-    }
-  }
+  wait_vmcnt<0>();  // Q, and K(0..2) or V(0)
   __syncthreads();
-  if (grp == 1) {  // group 1's idle first slot: stage K(1)
-    if (n_end > 1) {
-      st.store_k(lds_k[1], gtid);
-      if (n_end > 2) st.load_k(kbase, rsk, 2 * BN, w.Lk, gtid);
-    }
-    __syncthreads();
-  }
+  if (grp == 1) __syncthreads();  // group 1's idle first slot
 
   f32x16 s[1][KB];
   typename Wave::v8 p[1][KB][2];
+  int kbuf = 0;  // n % kPingPongKBuffers
   for (int n = 0; n <= n_end; ++n) {
     // matrix phase: S(n) = K(n) Q^T and O += V(n-1)^T P(n-1)
-    if (n < n_wave) wv.qk_ordered(lds_k[n & 1], s, arow, g);
+    if (n < n_wave) wv.qk_ordered(lds_k[kbuf], s, arow, g);
     if (n >= 1 && n - 1 < n_wave) wv.pv_ordered(lds_v[(n - 1) & 1], p, l32, g);
+    if (grp == 1) {
+      // K(n+1) is read after the coming barrier: it must have landed.  Loaded
+      // after it, only K(n+2) may still be in flight (4 loads per wave).
+      if (n + 2 < n_end) wait_vmcnt<KDma::PER_WAVE>();
+      else wait_vmcnt<0>();
+    }
     __syncthreads();
     // vector phase: masks, online softmax and the rare rescale of O for tile
     // n; group 0 stages V(n), group 1 stages K(n+2)
@@ -715,11 +756,10 @@ __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const Work
         if (n + 1 < n_end) st.load_v(vbase, rsk, (n + 1) * BN, w.Lk, gtid);
       }
     } else {
-      if (n + 2 < n_end) {
-        st.store_k(lds_k[n & 1], gtid);
-        if (n + 3 < n_end) st.load_k(kbase, rsk, (n + 3) * BN, w.Lk, gtid);
-      }
+      // K(n) was last read in the previous slot: its buffer takes K(n+3)
+      if (n + 3 < n_end) KDma::issue(lds_k[kbuf], kbase, rsk, (n + 3) * BN, w.Lk, wave - 4, lane);
     }
+    kbuf = kbuf == kPingPongKBuffers - 1 ? 0 : kbuf + 1;
     __syncthreads();
   }
   if (grp == 0) __syncthreads();  // group 0's idle last slot
@@ -785,7 +825,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(FwdArgs a) {
 
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void fwd16_pingpong_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * tiling::k_stride<D>()];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kPingPongKBuffers][BN * tiling::k_stride<D>()];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * BN];
   WorkItem w;
   if (!decode_work(a, w)) return;
