@@ -208,98 +208,25 @@ __global__ __launch_bounds__(256) void check_cu_kernel(const int32_t* __restrict
 // ---------------------------------------------------------------------------
 // LDS layouts (16-byte chunks are XOR-swizzled so that the MFMA operand reads
 // hit distinct banks within each group of 8 and of 16 lanes):
-//   Ks[key][d]   key-major, one row of D bf16 per key
+//   Ks[key][d]   key-major, one row of D bf16 per key (both kernels)
 //   Vt[d][key]   dimension-major (V transposed), one row of BN bf16 per d
+//                (head_dim 64 kernel: written transposed from registers)
+//   Vr[key][d]   key-major like Ks, read with transposing LDS reads
+//                (ping-pong kernel: loaded straight from global memory)
 //
 // Index arithmetic (swizzles, chunk/unit mappings, LDS indices, byte extents)
 // lives in fa_varlen_tiling.h, shared with the host-side bounds checker.
-// Staging for a kernel in which a thread stages either K tiles or V tiles:
-// one register set serves both roles.
-template <int D, int BN, int NW>
-struct GroupStage16 : tiling::Geom16<D, BN, NW> {
-  using G = tiling::Geom16<D, BN, NW>;
-  using G::K_PER_THREAD;
-  using G::THREADS;
-  using G::V_PER_THREAD;
 
-  // one register set serves either role: a thread stages K or V, not both
-  static constexpr int NREG = K_PER_THREAD > 4 * V_PER_THREAD ? K_PER_THREAD : 4 * V_PER_THREAD;
-  u32x4 reg[NREG];
-
-  // global -> registers; rows at or beyond Lk read as zero.  The resources
-  // start at the tile's first key (head slice) and end exactly at the end of
-  // the last valid row's head slice, so offsets stay below BN * row_stride * 2
-  // bytes (the host bounds heads * head_dim) and never reach past a tensor.
-  __device__ __forceinline__ void load_k(const uint16_t* __restrict__ kbase, int64_t row_stride, int key0, int Lk,
-                                         int tid) {
-    const int rows = max(0, min(BN, Lk - key0));
-    const __amdgpu_buffer_rsrc_t rk =
-        buffer_rsrc(kbase + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
-#pragma unroll
-    for (int i = 0; i < K_PER_THREAD; ++i) {
-      const int c = tid + i * THREADS;
-      reg[i] = buffer_load16(rk, ((uint32_t)G::k_row(c) * (uint32_t)row_stride + G::k_chunk(c) * 8) * 2u);
-    }
-  }
-  __device__ __forceinline__ void load_v(const uint16_t* __restrict__ vbase, int64_t row_stride, int key0, int Lk,
-                                         int tid) {
-    const int rows = max(0, min(BN, Lk - key0));
-    const __amdgpu_buffer_rsrc_t rv =
-        buffer_rsrc(vbase + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
-#pragma unroll
-    for (int i = 0; i < V_PER_THREAD; ++i) {
-      const int w = tid + i * THREADS;
-      const int u = G::v_group(w), dc = G::v_dchunk(w);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (G::v_owned(w)) x = buffer_load16(rv, ((uint32_t)(4 * u + r) * (uint32_t)row_stride + dc * 8) * 2u);
-        reg[4 * i + r] = x;
-      }
-    }
-  }
-
-  // registers -> LDS: K as is, V transposed
-  __device__ __forceinline__ void store_k(uint16_t* Ks, int tid) const {
-#pragma unroll
-    for (int i = 0; i < K_PER_THREAD; ++i) {
-      const int c = tid + i * THREADS;
-      *(u32x4*)(Ks + G::ks_index(G::k_row(c), G::k_chunk(c))) = reg[i];
-    }
-  }
-  __device__ __forceinline__ void store_v(uint16_t* Vt, int tid) const {
-#pragma unroll
-    for (int i = 0; i < V_PER_THREAD; ++i) {
-      const int w = tid + i * THREADS;
-      if (!G::v_owned(w)) continue;
-      const int u = G::v_group(w), dc = G::v_dchunk(w);
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        // dims 2*e2 and 2*e2+1 of the chunk, for keys 4u..4u+3
-        const uint32_t r0 = reg[4 * i][e2], r1 = reg[4 * i + 1][e2];
-        const uint32_t r2 = reg[4 * i + 2][e2], r3 = reg[4 * i + 3][e2];
-        u32x2 lo, hi;
-        lo[0] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // (key0, key1) of dim 2*e2
-        lo[1] = __builtin_amdgcn_perm(r3, r2, 0x05040100u);  // (key2, key3)
-        hi[0] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // dim 2*e2+1
-        hi[1] = __builtin_amdgcn_perm(r3, r2, 0x07060302u);
-        const int d0 = dc * 8 + 2 * e2;
-        *(u32x2*)(Vt + G::vt_index(d0, 4 * u)) = lo;
-        *(u32x2*)(Vt + G::vt_index(d0 + 1, 4 * u)) = hi;
-      }
-    }
-  }
-};
-
-// K tile staging by direct global -> LDS loads, shared by the 4 waves of one
+// Tile staging by direct global -> LDS loads, shared by the 4 waves of one
 // group (256 lanes).  The tile lands in the swizzled K layout
 // (tiling::ks_index): LDS chunk slot p = 64 * instruction + lane holds the
 // logical chunk that the swizzle stores there, so each lane loads that chunk.
 // Keys at or past Lk read as zeros (buffer range check).  At head_dim 96 the
 // last 4 slots of a 128-element row hold no chunk; their lanes load a chunk of
 // the same row that is never read.
-template <int D, int BN>
-struct KDirect {
+// V tiles use the same scheme with the row-major V swizzle (tiling::vr_index).
+template <int D, int BN, bool V_LAYOUT>
+struct RowDirect {
   static constexpr int KS = tiling::k_stride<D>();
   static constexpr int CPR = KS / 8;                 // 16-byte slots per LDS row
   static constexpr int PER_WAVE = BN * CPR / 256;    // loads per wave per tile
@@ -316,7 +243,7 @@ struct KDirect {
       const int seg = gwave * PER_WAVE + i;
       const int p = seg * 64 + lane;
       const int row = p / CPR;
-      int ch = (p % CPR) ^ k_swz<KS>(row);
+      int ch = (p % CPR) ^ (V_LAYOUT ? tiling::vrow_swz(row) : k_swz<KS>(row));
       if (D == 96) ch = ch < D / 8 ? ch : ch - 8;  // slots 12..15: a chunk of the row, never read
       const uint32_t off = ((uint32_t)row * (uint32_t)row_stride + (uint32_t)ch * 8u) * 2u;
       lds_dma16(r, off, base + (uint32_t)seg * 1024u);
@@ -337,6 +264,26 @@ __device__ __forceinline__ void operand_pipeline() {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, NM - NR + PRE, 0);
+}
+
+// Scheduling order of a block of NM MFMAs fed by NR LDS reads (NR a multiple
+// of NM): the first AHEAD reads, then each MFMA followed by the reads of a
+// later one, so that AHEAD reads are in flight ahead of their use.
+template <int I, int NM, int NR, int AHEAD>
+__device__ __forceinline__ void read_ahead_step() {
+  if constexpr (I < NM) {
+    constexpr int PER = NR / NM;
+    constexpr int LEFT = NR - AHEAD - I * PER;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (LEFT > 0) __builtin_amdgcn_sched_group_barrier(0x100, LEFT < PER ? LEFT : PER, 0);
+    read_ahead_step<I + 1, NM, NR, AHEAD>();
+  }
+}
+template <int NM, int NR, int AHEAD>
+__device__ __forceinline__ void read_ahead() {
+  static_assert(NR % NM == 0 && AHEAD <= NR, "reads per MFMA");
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // LDS reads
+  read_ahead_step<0, NM, NR, AHEAD>();
 }
 
 // Per-wave state and the three tile-level steps of the 16-bit forward pass.
@@ -468,6 +415,40 @@ struct Wave16 {
             o[qb][db] = Elem16<T>::mfma(av, p[qb][kb][t], o[qb][db]);
         }
     }
+  }
+
+  // O^T += V^T P^T with V row-major in LDS (tiling::vr_index).  The A operand
+  // of step (kb, t) -- keys kb*32 + 16g + 8t .. +7 of dimension db*32 + l32 --
+  // comes from two transposing reads: in each 16-lane group, lane i reads
+  // row r0 + i/4, dims c0 + 4(i%4) .. +3 (c0 = db*32 + 16*((lane/16)%2)) and
+  // receives dim c0 + i of rows r0 .. r0+3.
+  __device__ __forceinline__ void pv_rowmajor(const uint16_t* Vr, const v8 (&p)[QB][KB][2], int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const int i = lane & 15;
+    const int q = i >> 2;                          // row within a group of 4
+    const int cb = 2 * ((lane >> 4) & 1) + ((i >> 1) & 1);  // chunk within a quad
+    const int g = lane >> 5;
+    auto rd = [&](int row0, int db) {
+      const int row = row0 + q;
+      const uint16_t* a = Vr + row * tiling::k_stride<D>() + 8 * ((4 * db + cb) ^ tiling::vrow_swz(row)) + 4 * (i & 1);
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+    };
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int r0 = kb * 32 + 16 * g + 8 * t;
+          const s16x4 lo = rd(r0, db), hi = rd(r0 + 4, db);
+          const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const v8 av = __builtin_bit_cast(v8, v);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][db] = Elem16<T>::mfma(av, p[qb][kb][t], o[qb][db]);
+        }
+    read_ahead<DB * KB * 2 * QB, DB * KB * 4, 2 * AHEAD>();
   }
 
   // The same product with the output blocks innermost (independent
@@ -651,16 +632,16 @@ __device__ __forceinline__ void fwd16_item(const FwdArgs& a, const WorkItem& w,
 // into the buffer that V(n-2) left after slot 2n-1.  Each group loads the
 // next tile it stages from global memory right after storing the current one,
 // a slot pair ahead of its use.
-constexpr int kPingPongKBuffers = 3;
+constexpr int kPingPongBuffers = 3;  // K and V tiles in LDS, each
 
 template <typename T, int D, int BN, bool CAUSAL>
 __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const WorkItem& w,
-                                                    uint16_t (&lds_k)[kPingPongKBuffers][BN * tiling::k_stride<D>()],
-                                                    uint16_t (&lds_v)[2][D * BN]) {
+                                                    uint16_t (&lds_k)[kPingPongBuffers][BN * tiling::k_stride<D>()],
+                                                    uint16_t (&lds_v)[kPingPongBuffers][BN * tiling::k_stride<D>()]) {
   constexpr int NW = 8;
   constexpr int BM = 32 * NW;
-  using Stage = GroupStage16<D, BN, 4>;  // V staging by group 0 (4 waves)
-  using KDma = KDirect<D, BN>;           // K staging by group 1 (4 waves)
+  using KDma = RowDirect<D, BN, false>;  // K staging by group 1 (4 waves)
+  using VDma = RowDirect<D, BN, true>;   // V staging by group 0 (4 waves)
   using Wave = Wave16<T, D, BN, 1>;
   constexpr int KB = Wave::KB;
 
@@ -684,14 +665,13 @@ __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const Work
 
   // The first tiles are requested before Q and one wait covers all of them:
   // group 1 loads K(0..2) straight into the three K buffers, group 0 loads
-  // V(0) into registers.
-  Stage st;
+  // V(0).
   if (n_end > 0) {
     if (grp == 1) {
-      for (int j = 0; j < kPingPongKBuffers && j < n_end; ++j)
+      for (int j = 0; j < kPingPongBuffers && j < n_end; ++j)
         KDma::issue(lds_k[j], kbase, rsk, j * BN, w.Lk, wave - 4, lane);
     } else {
-      st.load_v(vbase, rsk, 0, w.Lk, gtid);
+      VDma::issue(lds_v[0], vbase, rsk, 0, w.Lk, wave, lane);
     }
   }
 
@@ -731,11 +711,18 @@ __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const Work
 
   f32x16 s[1][KB];
   typename Wave::v8 p[1][KB][2];
-  int kbuf = 0;  // n % kPingPongKBuffers
+  int kbuf = 0;  // n % kPingPongBuffers: K(n) and V(n)
+  int vprev = kPingPongBuffers - 1;  // (n - 1) % kPingPongBuffers: V(n-1)
   for (int n = 0; n <= n_end; ++n) {
+    // V(n-2) was last read in the previous slot: group 0 loads V(n+1) into
+    // its buffer
+    if (grp == 0 && n + 1 < n_end) {
+      const int vnext = kbuf == kPingPongBuffers - 1 ? 0 : kbuf + 1;
+      VDma::issue(lds_v[vnext], vbase, rsk, (n + 1) * BN, w.Lk, wave, lane);
+    }
     // matrix phase: S(n) = K(n) Q^T and O += V(n-1)^T P(n-1)
     if (n < n_wave) wv.qk_ordered(lds_k[kbuf], s, arow, g);
-    if (n >= 1 && n - 1 < n_wave) wv.pv_ordered(lds_v[(n - 1) & 1], p, l32, g);
+    if (n >= 1 && n - 1 < n_wave) wv.pv_rowmajor(lds_v[vprev], p, lane);
     if (grp == 1) {
       // K(n+1) is read after the coming barrier: it must have landed.  Loaded
       // after it, only K(n+2) may still be in flight (4 loads per wave).
@@ -751,15 +738,16 @@ __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const Work
       if (wv.softmax(s, p, alpha, a.scale_log2)) wv.rescale(alpha);
     }
     if (grp == 0) {
-      if (n < n_end) {
-        st.store_v(lds_v[n & 1], gtid);
-        if (n + 1 < n_end) st.load_v(vbase, rsk, (n + 1) * BN, w.Lk, gtid);
-      }
+      // V(n) is read after the coming barrier: it must have landed.  Loaded
+      // after it, only V(n+1) may still be in flight (4 loads per wave).
+      if (n + 1 < n_end) wait_vmcnt<VDma::PER_WAVE>();
+      else wait_vmcnt<0>();
     } else {
       // K(n) was last read in the previous slot: its buffer takes K(n+3)
       if (n + 3 < n_end) KDma::issue(lds_k[kbuf], kbase, rsk, (n + 3) * BN, w.Lk, wave - 4, lane);
     }
-    kbuf = kbuf == kPingPongKBuffers - 1 ? 0 : kbuf + 1;
+    vprev = kbuf;
+    kbuf = kbuf == kPingPongBuffers - 1 ? 0 : kbuf + 1;
     __syncthreads();
   }
   if (grp == 0) __syncthreads();  // group 0's idle last slot
@@ -825,8 +813,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(FwdArgs a) {
 
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void fwd16_pingpong_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kPingPongKBuffers][BN * tiling::k_stride<D>()];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * BN];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kPingPongBuffers][BN * tiling::k_stride<D>()];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kPingPongBuffers][BN * tiling::k_stride<D>()];
   WorkItem w;
   if (!decode_work(a, w)) return;
   run_work<256, CAUSAL>(a, w, [&](const WorkItem& wi) { fwd16_pingpong_item<T, D, BN, CAUSAL>(a, wi, lds_k, lds_v); });

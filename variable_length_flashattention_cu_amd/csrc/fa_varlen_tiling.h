@@ -57,6 +57,16 @@ FA_HD int ks_index(int row, int ch) {
 template <int BN>
 FA_HD int vt_index(int d, int key) { return d * BN + 8 * ((key >> 3) ^ v_swz<BN>(d)) + (key & 7); }
 
+// Row-major V tiles ([BN keys][k_stride<D>()], read by transposing LDS reads):
+// a transposing read of a 16-lane group covers rows r0..r0+3 (r0 a multiple
+// of 4) and two adjacent 16-byte chunks, and the two groups of a 32-lane half
+// cover the next two chunks of the same rows.  XORing the chunk index with
+// 4 * (row % 4) puts those 4 rows x 4 chunks on 16 distinct 16-byte bank
+// groups.
+FA_HD int vrow_swz(int row) { return 4 * (row & 3); }
+template <int D>
+FA_HD int vr_index(int row, int ch) { return row * k_stride<D>() + 8 * (ch ^ vrow_swz(row)); }
+
 // Byte extent, from the first element of one head's slice of a row, of that
 // head's slices in `rows` consecutive token rows: the last byte is the end of
 // the last row's slice, so nothing past the tensor is ever in range.
