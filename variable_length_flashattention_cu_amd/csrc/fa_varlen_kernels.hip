@@ -448,7 +448,9 @@ struct Wave16 {
           for (int qb = 0; qb < QB; ++qb)
             o[qb][db] = Elem16<T>::mfma(av, p[qb][kb][t], o[qb][db]);
         }
-    read_ahead<DB * KB * 2 * QB, DB * KB * 4, 2 * AHEAD>();
+    // fewer transposing reads in flight than operand reads of QK (measured:
+    // 4 ahead at head_dim <= 128 beat 8 and 16)
+    read_ahead<DB * KB * 2 * QB, DB * KB * 4, AHEAD / 2>();
   }
 
   // The same product with the output blocks innermost (independent
@@ -720,9 +722,9 @@ __device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const Work
       const int vnext = kbuf == kPingPongBuffers - 1 ? 0 : kbuf + 1;
       VDma::issue(lds_v[vnext], vbase, rsk, (n + 1) * BN, w.Lk, wave, lane);
     }
-    // matrix phase: S(n) = K(n) Q^T and O += V(n-1)^T P(n-1)
-    if (n < n_wave) wv.qk_ordered(lds_k[kbuf], s, arow, g);
+    // matrix phase: O += V(n-1)^T P(n-1) and S(n) = K(n) Q^T
     if (n >= 1 && n - 1 < n_wave) wv.pv_rowmajor(lds_v[vprev], p, lane);
+    if (n < n_wave) wv.qk_ordered(lds_k[kbuf], s, arow, g);
     if (grp == 1) {
       // K(n+1) is read after the coming barrier: it must have landed.  Loaded
       // after it, only K(n+2) may still be in flight (4 loads per wave).
