@@ -251,7 +251,91 @@ static void check_f32() {
   std::printf("f32 D=%d NW=%d: ok\n", D, NW);
 }
 
+// Ping-pong forward kernel: K and V tiles of BN keys loaded straight into LDS
+// (16 bytes per lane at LDS slot p = 64 * load + lane, 4 waves x 4 loads per
+// tile), K in the ks_index layout, V row-major (vr_index) and read with
+// transposing LDS reads for the PV product.
+template <int D, int BN, bool V_LAYOUT>
+static void check_direct(long H) {
+  constexpr int KS = k_stride<D>(), CPR = KS / 8, SLOTS = BN * CPR;
+  CHECK(SLOTS == 4 * 4 * 64, "D=%d BN=%d: %d slots are not 4 waves x 4 loads x 64 lanes", D, BN, SLOTS);
+  const long h = H - 1;
+  std::vector<int> placed(BN * KS, 0);
+  for (int rows : {BN, 1, BN / 2 + 3, BN - 1}) {  // valid keys in the tile
+    const Access a{rows + 5, H, D, h, 2, rows, head_rows_bytes(rows, H * D, D, 2)};
+    std::vector<int> seen(BN * D, 0);
+    for (int p = 0; p < SLOTS; ++p) {
+      int row, ch;
+      direct_slot_chunk<D, V_LAYOUT>(p, row, ch);
+      CHECK(row >= 0 && row < BN && ch >= 0 && ch < D / 8, "D=%d slot %d -> (%d,%d)", D, p, row, ch);
+      const unsigned off = (unsigned)((row * H * D + ch * 8) * 2);
+      const long first = touch(a, off, 2, 16);
+      const int idx = V_LAYOUT ? vr_index<D>(row, ch) : ks_index<D>(row, ch);
+      if (idx == 8 * p) {  // the slot holds this chunk in the read layout
+        if (rows == BN) placed[idx] += 1;
+        if (first >= 0)
+          for (int j = 0; j < 8; ++j) seen[row * D + ch * 8 + j]++;
+      } else {
+        CHECK(D == 96, "D=%d: slot %d holds (%d,%d) but the layout puts it at %d", D, p, row, ch, idx / 8);
+      }
+    }
+    for (int r = 0; r < BN; ++r)
+      for (int d = 0; d < D; ++d)
+        CHECK(seen[r * D + d] == (r < rows ? 1 : 0), "D=%d rows=%d: element (%d,%d) loaded %d times", D, rows, r,
+              d, seen[r * D + d]);
+  }
+  for (int r = 0; r < BN; ++r)
+    for (int ch = 0; ch < D / 8; ++ch) {
+      const int idx = V_LAYOUT ? vr_index<D>(r, ch) : ks_index<D>(r, ch);
+      CHECK(placed[idx] == 1, "D=%d chunk (%d,%d) placed %d times", D, r, ch, placed[idx]);
+    }
+  if (V_LAYOUT) {
+    // transposing reads of O^T += V^T P^T: step (kb, t) reads keys
+    // kb*32 + 16g + 8t + 4h .. +3 of dimensions 32 db + lane%32
+    for (int kb = 0; kb < BN / 32; ++kb)
+      for (int t = 0; t < 2; ++t)
+        for (int h2 = 0; h2 < 2; ++h2)
+          for (int db = 0; db < D / 32; ++db) {
+            std::vector<int> bank_use[2] = {std::vector<int>(16, 0), std::vector<int>(16, 0)};
+            for (int grp = 0; grp < 4; ++grp) {
+              const int g = grp / 2, r0 = kb * 32 + 16 * g + 8 * t + 4 * h2;
+              std::vector<int> got(4 * 16, 0);  // rows r0..r0+3 x the group's 16 dims
+              for (int i = 0; i < 16; ++i) {
+                const int lane = 16 * grp + i;
+                const int idx = vr_tr_index<D>(lane, r0, db);
+                CHECK(idx >= 0 && idx % 4 == 0 && idx + 4 <= BN * KS, "D=%d tr read index %d", D, idx);
+                // the 4 elements at idx are row r0 + i/4, dims c0 + 4(i%4) .. +3
+                const int row = r0 + (i >> 2), c0 = 32 * db + 16 * (grp & 1), col = c0 + 4 * (i & 3);
+                CHECK(idx == vr_index<D>(row, col >> 3) + (col & 7), "D=%d tr read lane %d at wrong element", D,
+                      lane);
+                for (int e = 0; e < 4; ++e) got[(i >> 2) * 16 + 4 * (i & 3) + e]++;
+                // lane i receives dim c0 + i: must be the output dim of this lane
+                CHECK(c0 + i == 32 * db + (lane & 31), "D=%d lane %d receives dim %d", D, lane, c0 + i);
+                bank_use[g][(idx * 2 / 16) % 16]++;
+              }
+              for (int e = 0; e < 64; ++e) CHECK(got[e] == 1, "D=%d tr group %d element %d read %d times", D, grp, e,
+                                                 got[e]);
+            }
+            for (int g = 0; g < 2; ++g)
+              for (int b = 0; b < 16; ++b)  // two lanes read the two halves of each 16-byte chunk
+                CHECK(bank_use[g][b] == 2, "D=%d tr read: bank group %d used by %d lanes of a 32-lane half", D, b,
+                      bank_use[g][b]);
+          }
+  }
+  std::printf("direct %s D=%d BN=%d H=%ld: ok\n", V_LAYOUT ? "V" : "K", D, BN, H);
+}
+
 int main() {
+  for (long H : {1L, 3L, 16L}) {
+    check_direct<64, 128, false>(H);
+    check_direct<64, 128, true>(H);
+    check_direct<96, 64, false>(H);
+    check_direct<96, 64, true>(H);
+    check_direct<128, 64, false>(H);
+    check_direct<128, 64, true>(H);
+    check_direct<256, 32, false>(H);
+    check_direct<256, 32, true>(H);
+  }
   // configurations the library instantiates (and neighbours it may use)
   for (long H : {1L, 3L, 16L}) {
     check_bf16<128, 64, 8>(H);

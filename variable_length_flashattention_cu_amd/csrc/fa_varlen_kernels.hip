@@ -7,13 +7,10 @@
 //                              iplexlaw.co.kr "FlashAttention-2 GPU work
 //                              partitioning", section "Tres mejoras en la
 //                              utilización de la GPU").
-//   * fwd16_pingpong_kernel -- 16-bit (bf16 or fp16) in/out, head_dim 96 and
-//                              128: two wave groups alternate MFMA and softmax
-//                              phases.
-//   * fwd16_kernel          -- 16-bit in/out, head_dim 64: one wave group with
-//                              a software pipeline inside each wave.
-//                              Both use 16-bit MFMA for the two contractions
-//                              and an fp32 online softmax.
+//   * fwd16_pingpong_kernel -- 16-bit (bf16 or fp16) in/out, head_dim 64, 96,
+//                              128 and 256: two wave groups alternate MFMA and
+//                              softmax phases; 16-bit MFMA for the two
+//                              contractions, fp32 online softmax.
 //   * fwd_f32_kernel        -- fp32 in/out, fp32 MFMA, same online softmax.
 //   * check_cu_kernel       -- optional device validation of the offsets.
 //
@@ -30,7 +27,7 @@
 // the waves share the K/V tiles and never exchange partial results, as the
 // pages describe for FlashAttention-2's forward pass, zepes.com "Comprendiendo
 // Flash-Atención y Flash-Atención-2", section "FlashAttention-2").  K/V tiles
-// of BN keys stream through double-buffered LDS; the score tile never leaves
+// of BN keys stream through LDS; the score tile never leaves
 // registers (slavadubrov.com "O que FlashAttention muda na inferência",
 // section "Separar o armazenamento do cálculo").
 //
@@ -45,8 +42,8 @@
 //   * the probabilities P^T are already in the B-operand layout of the second
 //     MFMA: no shuffle or LDS round trip between the two contractions.
 // The second contraction needs V^T as its A operand (8 consecutive keys per
-// lane), so V tiles are transposed in registers (v_perm) on their way into
-// LDS.
+// lane): the 16-bit kernels keep V row-major in LDS and read it with the
+// transposing LDS read; the fp32 kernel's operands are single elements.
 //
 // Online softmax per query row (iplexlaw.co.kr, section "Bloques pequeños,
 // normalización global"): with t = scale*log2(e)*s,
@@ -241,10 +238,8 @@ struct RowDirect {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int seg = gwave * PER_WAVE + i;
-      const int p = seg * 64 + lane;
-      const int row = p / CPR;
-      int ch = (p % CPR) ^ (V_LAYOUT ? tiling::vrow_swz(row) : k_swz<KS>(row));
-      if (D == 96) ch = ch < D / 8 ? ch : ch - 8;  // slots 12..15: a chunk of the row, never read
+      int row, ch;
+      tiling::direct_slot_chunk<D, V_LAYOUT>(seg * 64 + lane, row, ch);
       const uint32_t off = ((uint32_t)row * (uint32_t)row_stride + (uint32_t)ch * 8u) * 2u;
       lds_dma16(r, off, base + (uint32_t)seg * 1024u);
     }
@@ -299,26 +294,9 @@ struct Wave16 {
   f32x16 o[QB][DB];         // O^T accumulators
   float m_run[QB], l_run[QB];
 
-  // S^T = K Q^T for one key tile (K from LDS, swizzled rows)
-  __device__ __forceinline__ void qk(const uint16_t* Ks, f32x16 (&s)[QB][KB], int arow, int g) const {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int krow = kb * 32 + arow;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int ch = 2 * ks + g;
-        const v8 av = *(const v8*)(Ks + tiling::ks_index<D>(krow, ch));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const f32x16 c = ks == 0 ? f32x16{} : s[qb][kb];
-          s[qb][kb] = Elem16<T>::mfma(av, qreg[qb][ks], c);
-        }
-      }
-    }
-  }
-
-  // The same product with the two 32-key blocks interleaved (independent
-  // accumulation chains) and the LDS operand reads issued ahead of their use.
+  // S^T = K Q^T for one key tile (K from LDS, swizzled rows), the 32-key
+  // blocks interleaved (independent accumulation chains) and the LDS operand
+  // reads issued ahead of their use.
   __device__ __forceinline__ void qk_ordered(const uint16_t* Ks, f32x16 (&s)[QB][KB], int arow, int g) const {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -399,24 +377,6 @@ struct Wave16 {
         for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
   }
 
-  // O^T += V^T P^T for one key tile (V^T from LDS)
-  __device__ __forceinline__ void pv(const uint16_t* Vt, const v8 (&p)[QB][KB][2], int l32, int g) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = db * 32 + l32;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          // keys 32kb+16g+8t .. +7 of dimension d: one 16-byte chunk
-          const v8 av = *(const v8*)(Vt + tiling::vt_index<BN>(d, kb * 32 + 16 * g + 8 * t));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[qb][db] = Elem16<T>::mfma(av, p[qb][kb][t], o[qb][db]);
-        }
-    }
-  }
-
   // O^T += V^T P^T with V row-major in LDS (tiling::vr_index).  The A operand
   // of step (kb, t) -- keys kb*32 + 16g + 8t .. +7 of dimension db*32 + l32 --
   // comes from two transposing reads: in each 16-lane group, lane i reads
@@ -425,13 +385,9 @@ struct Wave16 {
   __device__ __forceinline__ void pv_rowmajor(const uint16_t* Vr, const v8 (&p)[QB][KB][2], int lane) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const int i = lane & 15;
-    const int q = i >> 2;                          // row within a group of 4
-    const int cb = 2 * ((lane >> 4) & 1) + ((i >> 1) & 1);  // chunk within a quad
     const int g = lane >> 5;
     auto rd = [&](int row0, int db) {
-      const int row = row0 + q;
-      const uint16_t* a = Vr + row * tiling::k_stride<D>() + 8 * ((4 * db + cb) ^ tiling::vrow_swz(row)) + 4 * (i & 1);
+      const uint16_t* a = Vr + tiling::vr_tr_index<D>(lane, row0, db);
       return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
     };
 #pragma unroll
@@ -452,167 +408,7 @@ struct Wave16 {
     // 4 ahead at head_dim <= 128 beat 8 and 16)
     read_ahead<DB * KB * 2 * QB, DB * KB * 4, AHEAD / 2>();
   }
-
-  // The same product with the output blocks innermost (independent
-  // accumulation chains) and the LDS operand reads issued ahead of their use.
-  __device__ __forceinline__ void pv_ordered(const uint16_t* Vt, const v8 (&p)[QB][KB][2], int l32, int g) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const v8 av = *(const v8*)(Vt + tiling::vt_index<BN>(db * 32 + l32, kb * 32 + 16 * g + 8 * t));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[qb][db] = Elem16<T>::mfma(av, p[qb][kb][t], o[qb][db]);
-        }
-    operand_pipeline<DB * KB * 2 * QB, DB * KB * 2, AHEAD>();
-  }
 };
-
-// Software pipeline (per wavefront): while the MFMAs of S(n+1) = K(n+1) Q^T
-// run, the VALU computes the softmax of tile n; then O += V(n)^T P(n).  K
-// therefore runs one tile ahead of V through the double buffers: at step n the
-// buffers hold K(n+1) and V(n) for reading while K(n+2) and V(n+1) are being
-// written into the slots that K(n) and V(n-1) left free.
-template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
-__device__ __forceinline__ void fwd16_item(const FwdArgs& a, const WorkItem& w,
-                                           uint16_t (&lds_k)[2][BN * tiling::k_stride<D>()],
-                                           uint16_t (&lds_v)[2][D * BN]) {
-  constexpr int BM = 32 * QB * NW;
-  using Tile = Tile16<D, BN, NW>;
-  using Wave = Wave16<T, D, BN, QB>;
-  constexpr int KB = Wave::KB;
-
-  int n_full, n_end;
-  key_tiles<BM, BN, CAUSAL>(w, n_full, n_end);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, g = lane >> 5;
-  const int wrow0 = w.m * BM + wave * 32 * QB;  // first query row of this wave (in sequence)
-  const int shift = w.Lk - w.Lq;
-  const int64_t rs = a.row_stride;
-
-  // key/value head of this query head; K/V rows hold kv_heads * D elements
-  const int64_t rsk = a.kv_row_stride;
-  const int hk = w.h / a.head_group;
-  const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)hk * D;
-  const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)hk * D;
-
-  Wave wv;
-  {  // Q rows past the end of the sequence load as zeros
-    const int qrows = max(0, min(32 * QB, w.Lq - wrow0));
-    const __amdgpu_buffer_rsrc_t rq =
-        buffer_rsrc((const uint16_t*)a.q + (int64_t)(w.q_start + wrow0) * rs + (int64_t)w.h * D,
-                    head_rows_bytes(qrows, rs, D, 2));
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int ks = 0; ks < Wave::KSTEPS; ++ks) {
-        const uint32_t off = ((uint32_t)(qb * 32 + l32) * (uint32_t)rs + 16 * ks + 8 * g) * 2u;
-        wv.qreg[qb][ks] = __builtin_bit_cast(typename Wave::v8, buffer_load16(rq, off));
-      }
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    wv.m_run[qb] = kNegInf;
-    wv.l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < Wave::DB; ++db) wv.o[qb][db] = f32x16{};
-  }
-
-  // Tiles this wave needs: all n < n_wave (rows past the sequence end need
-  // none; causal rows need keys up to their diagonal).
-  int n_wave = 0;
-  if (wrow0 < w.Lq) {
-    if (CAUSAL) {
-      const int last_key = wrow0 + 32 * QB - 1 + shift;
-      n_wave = last_key < 0 ? 0 : min(n_end, last_key / BN + 1);
-    } else {
-      n_wave = n_end;
-    }
-  }
-
-  const int arow = key_of_arow(l32);
-  Tile tile;
-  if (n_end > 0) {
-    tile.load_k(kbase, rsk, 0, w.Lk, tid);
-    tile.load_v(vbase, rsk, 0, w.Lk, tid);
-    tile.store_k(lds_k[0], tid);
-    tile.store_v(lds_v[0], tid);
-    if (n_end > 1) {
-      tile.load_k(kbase, rsk, BN, w.Lk, tid);
-      tile.store_k(lds_k[1], tid);
-    }
-  }
-  __syncthreads();
-
-  f32x16 s0[QB][KB], s1[QB][KB];
-  if (n_wave > 0) wv.qk(lds_k[0], s0, arow, g);
-
-  // One pipeline step for tile n (scores in s_cur).  With NEXT, the MFMAs of
-  // S(n+1) are issued into s_next in the same basic block as the softmax of
-  // tile n so that the scheduler can interleave them; a wave whose rows stop
-  // before tile n+1 computes that S once without using it.
-  auto step = [&](auto next_tag, int n, f32x16 (&s_cur)[QB][KB], f32x16 (&s_next)[QB][KB]) {
-    constexpr bool NEXT = decltype(next_tag)::value;
-    const bool more_k = n + 2 < n_end;
-    const bool more_v = n + 1 < n_end;
-    if (more_k) tile.load_k(kbase, rsk, (n + 2) * BN, w.Lk, tid);
-    if (more_v) tile.load_v(vbase, rsk, (n + 1) * BN, w.Lk, tid);
-    if (n < n_wave) {
-      if (n >= n_full) Wave::template mask<CAUSAL>(s_cur, n * BN, wrow0, l32, g, w.Lk, shift);
-      typename Wave::v8 p[QB][KB][2];
-      float alpha[QB];
-      if constexpr (NEXT) wv.qk(lds_k[(n + 1) & 1], s_next, arow, g);
-      const bool rescale = wv.softmax(s_cur, p, alpha, a.scale_log2);
-      if (rescale) wv.rescale(alpha);
-      wv.pv(lds_v[n & 1], p, l32, g);
-    }
-    if (more_k) tile.store_k(lds_k[n & 1], tid);
-    if (more_v) tile.store_v(lds_v[(n + 1) & 1], tid);
-    __syncthreads();
-  };
-  using Full = std::true_type;
-  using Last = std::false_type;
-  int n = 0;
-  for (; n + 2 < n_end; n += 2) {
-    step(Full{}, n, s0, s1);
-    step(Full{}, n + 1, s1, s0);
-  }
-  if (n + 1 < n_end) {
-    step(Full{}, n, s0, s1);
-    step(Last{}, n + 1, s1, s0);
-  } else if (n < n_end) {
-    step(Last{}, n, s0, s1);
-  }
-
-  // ---- epilogue: normalise, write out (16-bit, round to nearest even) and lse
-  T* __restrict__ op = (T*)a.out;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int i = wrow0 + qb * 32 + l32;
-    const float l = pair_sum(wv.l_run[qb]);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (i < w.Lq) {
-      T* dst = op + (int64_t)(w.q_start + i) * rs + (int64_t)w.h * D;
-#pragma unroll
-      for (int db = 0; db < Wave::DB; ++db)
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          typename Elem16<T>::v4 v4;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v4[c] = (T)(wv.o[qb][db][4 * s4 + c] * inv);
-          *(typename Elem16<T>::v4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
-        }
-      if (g == 0)
-        a.lse[(int64_t)w.h * a.total_q + w.q_start + i] =
-            l > 0.f ? (wv.m_run[qb] + fast_log2(l)) * kLn2 : kNegInf;
-    }
-  }
-}
 
 // Ping-pong schedule.  The workgroup's 8 wavefronts form two groups of 4
 // (waves 0-3 and 4-7); wave w runs on SIMD w % 4, so every SIMD holds one wave
@@ -802,17 +598,6 @@ __device__ __forceinline__ void run_work(const FwdArgs& a, WorkItem& w, Item&& i
   }
 }
 
-template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * tiling::k_stride<D>()];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * BN];
-  WorkItem w;
-  if (!decode_work(a, w)) return;
-  run_work<32 * QB * NW, CAUSAL>(a, w, [&](const WorkItem& wi) {
-    fwd16_item<T, D, BN, NW, QB, CAUSAL>(a, wi, lds_k, lds_v);
-  });
-}
-
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void fwd16_pingpong_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[kPingPongBuffers][BN * tiling::k_stride<D>()];
@@ -993,7 +778,7 @@ TileConfig tile_config(int dtype, int head_dim) {
   if (dtype == 1 || dtype == 2) {  // bf16, fp16
     if (head_dim == 128 || head_dim == 96) c = TileConfig{256, 64, 512};
     else if (head_dim == 256) c = TileConfig{256, 32, 512};
-    else if (head_dim == 64) c = TileConfig{128, 64, 256};
+    else if (head_dim == 64) c = TileConfig{256, 128, 512};
   } else if (dtype == 0) {  // f32
     if (head_dim == 128 || head_dim == 96 || head_dim == 64) c = TileConfig{128, 32, 256};
   }
@@ -1024,8 +809,8 @@ hipError_t launch_fwd16(int head_dim, bool causal, int grid, const FwdArgs& a, h
     return causal ? launch(fwd16_pingpong_kernel<T, 256, 32, true>, grid, 512, stream, a)
                   : launch(fwd16_pingpong_kernel<T, 256, 32, false>, grid, 512, stream, a);
   if (head_dim == 64)
-    return causal ? launch(fwd16_kernel<T, 64, 64, 4, 1, true>, grid, 256, stream, a)
-                  : launch(fwd16_kernel<T, 64, 64, 4, 1, false>, grid, 256, stream, a);
+    return causal ? launch(fwd16_pingpong_kernel<T, 64, 128, true>, grid, 512, stream, a)
+                  : launch(fwd16_pingpong_kernel<T, 64, 128, false>, grid, 512, stream, a);
   return hipErrorInvalidValue;
 }
 

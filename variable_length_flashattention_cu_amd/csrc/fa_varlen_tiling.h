@@ -60,12 +60,45 @@ FA_HD int vt_index(int d, int key) { return d * BN + 8 * ((key >> 3) ^ v_swz<BN>
 // Row-major V tiles ([BN keys][k_stride<D>()], read by transposing LDS reads):
 // a transposing read of a 16-lane group covers rows r0..r0+3 (r0 a multiple
 // of 4) and two adjacent 16-byte chunks, and the two groups of a 32-lane half
-// cover the next two chunks of the same rows.  XORing the chunk index with
-// 4 * (row % 4) puts those 4 rows x 4 chunks on 16 distinct 16-byte bank
-// groups.
-FA_HD int vrow_swz(int row) { return 4 * (row & 3); }
+// cover the next two chunks of the same rows (a quad of 4 chunks).  The
+// swizzle puts those 4 rows x 4 chunks on 16 distinct 16-byte bank groups:
+// rows of 16 or more chunks XOR the chunk index with 4 * (row % 4); rows of 8
+// chunks (head_dim 64) share a bank cycle in pairs, so rows r and r+2 take
+// opposite quads (XOR with 4 * ((row / 2) % 2)).
 template <int D>
-FA_HD int vr_index(int row, int ch) { return row * k_stride<D>() + 8 * (ch ^ vrow_swz(row)); }
+FA_HD int vrow_swz(int row) {
+  if constexpr (D == 64) return 4 * ((row >> 1) & 1);
+  else return 4 * (row & 3);
+}
+template <int D>
+FA_HD int vr_index(int row, int ch) { return row * k_stride<D>() + 8 * (ch ^ vrow_swz<D>(row)); }
+
+// Direct global -> LDS tile loads (16 bytes per lane, lane-consecutive in
+// LDS): LDS 16-byte slot p of a [rows][k_stride<D>()] tile receives logical
+// chunk `ch` of tile row `row` of the K-style (V_LAYOUT false: ks_index) or
+// row-major V (V_LAYOUT true: vr_index) layout.  At head_dim 96 the last 4
+// slots of a 128-element row hold no chunk; they are given a chunk of the same
+// row (in range, never read).
+template <int D, bool V_LAYOUT>
+FA_HD void direct_slot_chunk(int p, int& row, int& ch) {
+  constexpr int CPR = k_stride<D>() / 8;
+  row = p / CPR;
+  ch = (p % CPR) ^ (V_LAYOUT ? vrow_swz<D>(row) : k_swz<k_stride<D>()>(row));
+  if (D == 96 && ch >= D / 8) ch -= 8;
+}
+
+// Element index, in a row-major V tile, of lane `lane`'s transposing read of
+// tile rows r0 .. r0+3 (r0 a multiple of 4) for output dimension block db:
+// within each 16-lane group, lane i reads row r0 + i/4, dimensions
+// c0 + 4(i%4) .. +3 with c0 = 32 db + 16 ((lane/16) % 2), and receives
+// dimension c0 + i (= 32 db + lane % 32) of rows r0 .. r0+3.
+template <int D>
+FA_HD int vr_tr_index(int lane, int r0, int db) {
+  const int i = lane & 15;
+  const int row = r0 + (i >> 2);
+  const int ch = 4 * db + 2 * ((lane >> 4) & 1) + ((i >> 1) & 1);
+  return row * k_stride<D>() + 8 * (ch ^ vrow_swz<D>(row)) + 4 * (i & 1);
+}
 
 // Byte extent, from the first element of one head's slice of a row, of that
 // head's slices in `rows` consecutive token rows: the last byte is the end of
