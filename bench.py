@@ -339,6 +339,18 @@ def summarize_trace(db_path: str) -> str:
     lines = [f"{'calls':>6} {'total_ms':>10} {'avg_us':>10} {'pct':>6}  kernel"]
     for name, calls, tot, avg, pct in rows:
         lines.append(f"{calls:>6} {tot / 1e3:>10.3f} {avg:>10.2f} {pct:>6.2f}  {name}")
+    # per-dispatch durations of the attention kernel: the first launches of a
+    # process are cold (code and data not yet cached), so the median and the
+    # mean without the first two are what compares with the timed steps
+    con = sqlite3.connect(db_path)
+    durs = [r[0] for r in con.execute("select duration from kernels where name like '%fwd16_pingpong_kernel%' "
+                                      "order by start")]
+    con.close()
+    if durs:
+        us = np.asarray(durs, dtype=np.float64) / 1e3  # nanoseconds -> microseconds
+        warm = us[2:] if len(us) > 2 else us
+        lines.append(f"attention kernel, {len(us)} dispatches: first {us[0]:.1f} us, median {np.median(us):.1f} us, "
+                     f"mean without the first two {warm.mean():.1f} us")
     return "\n".join(lines)
 
 
