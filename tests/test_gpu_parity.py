@@ -115,6 +115,10 @@ EDGE = [
     ("ragged_tails", [129, 63, 65, 191, 257], [129, 63, 65, 191, 257]),
     ("q_longer_than_k", [824, 300, 40], [724, 33, 1]),
     ("k_longer_than_q", [200, 5, 77], [300, 500, 130]),
+    # key counts at and next to multiples of the 32-, 64- and 128-key tiles:
+    # 1 to 8 tiles per item, so every preamble and end-of-loop branch of the
+    # direct K/V loads (tiles still to load, tiles in flight) is taken
+    ("tile_boundaries", [64, 128, 192, 256, 383, 384, 385, 512], [64, 128, 192, 256, 383, 384, 385, 512]),
 ]
 
 
