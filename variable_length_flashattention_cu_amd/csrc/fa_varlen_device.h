@@ -1,7 +1,8 @@
 // fa_varlen_device.h -- device helpers shared by the forward and backward
 // kernels: vector types, the 16-bit element traits, fast exp2/log2, lane-pair
-// reductions, raw buffer resources, and the staging of K-style (row-major,
-// swizzled) and V-style (transposed) 16-bit tiles into LDS.
+// reductions, raw buffer resources, direct global -> LDS loads with explicit
+// waits, and the register staging of K-style (row-major, swizzled) and
+// V-style (transposed) 16-bit tiles into LDS.
 //
 // Included by the .hip sources only (inside namespace fa, an anonymous
 // namespace: every translation unit keeps its own copy).

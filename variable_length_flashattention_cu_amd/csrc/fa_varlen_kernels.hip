@@ -230,18 +230,19 @@ struct RowDirect {
   static_assert(BN * CPR % 256 == 0, "tile must split into whole wave loads");
   static_assert(PER_WAVE == 4, "the wait counts below assume 4 loads per tile");
 
-  __device__ __forceinline__ static void issue(uint16_t* dst, const uint16_t* __restrict__ kbase,
+  // keys key0 .. key0+BN-1 of the head slice at `base` into the LDS tile at dst
+  __device__ __forceinline__ static void issue(uint16_t* dst, const uint16_t* __restrict__ base,
                                                int64_t row_stride, int key0, int Lk, int gwave, int lane) {
     const int rows = max(0, min(BN, Lk - key0));
-    const u32x4 r = buffer_rsrc_words(kbase + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
-    const uint32_t base = lds_address(dst);
+    const u32x4 r = buffer_rsrc_words(base + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
+    const uint32_t lds = lds_address(dst);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int seg = gwave * PER_WAVE + i;
       int row, ch;
       tiling::direct_slot_chunk<D, V_LAYOUT>(seg * 64 + lane, row, ch);
       const uint32_t off = ((uint32_t)row * (uint32_t)row_stride + (uint32_t)ch * 8u) * 2u;
-      lds_dma16(r, off, base + (uint32_t)seg * 1024u);
+      lds_dma16(r, off, lds + (uint32_t)seg * 1024u);
     }
   }
 };
