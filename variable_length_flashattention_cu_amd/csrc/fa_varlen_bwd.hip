@@ -177,12 +177,42 @@ __device__ __forceinline__ bool decode_col(const BwdArgs& a, ColItem& w) {
 // ---------------------------------------------------------------------------
 // the backward workgroup
 // ---------------------------------------------------------------------------
+// Layout of the tiles that are read both with 16-byte operand reads and with
+// transposing reads (Q, dO and K; V is only read the first way and keeps the
+// K-style layout tiling::ks_index).  The operand reads of a 16-lane group take
+// one chunk of rows {0-3, 16-19, 4-7, 20-23} (+8): the chunk index is XORed
+// with two low bits that differ across those four row sets (row bit 2, and row
+// bits 3 and 4 combined).  A transposing read of a 32-lane half takes rows
+// r..r+3 (r a multiple of 4) and a quad of four chunks, or, for K^T, rows
+// r..r+3 and r+8..r+11 and a pair of chunks: the quad bits are XORed with
+// row % 4 and the low bits flip between r and r+8, so either read touches 16
+// distinct 16-byte bank groups (each was 4-way conflicted with the K-style
+// swizzle).  Rows of head_dim 64 keep the K-style layout.
+template <int D>
+__device__ __forceinline__ int tq_swz(int row) {
+  if constexpr (D == 128) return 4 * (row & 3) | ((row >> 2) & 1) | ((((row >> 3) ^ (row >> 4)) & 1) << 1);
+  else return tiling::k_swz<D>(row);
+}
+template <int D>
+__device__ __forceinline__ int tq_index(int row, int ch) { return row * D + 8 * (ch ^ tq_swz<D>(row)); }
+
+// Register-staged tile -> LDS in the tq_index layout
+template <int D, typename Tile>
+__device__ __forceinline__ void store_tq(const Tile& t, uint16_t* dst, int tid) {
+#pragma unroll
+  for (int i = 0; i < Tile::K_PER_THREAD; ++i) {
+    const int c = tid + i * Tile::THREADS;
+    *(u32x4*)(dst + tq_index<D>(Tile::k_row(c), Tile::k_chunk(c))) = t.kreg[i];
+  }
+}
+
 // Direct global -> LDS staging of a row-major tile of ROWS rows x D 16-bit
-// elements in the swizzled K-style layout (tiling::ks_index<D>): each lane's
-// 16 bytes land at LDS chunk position p = 64 * instruction + lane, so the lane
-// loads the logical chunk that the swizzle stores there.  Rows at or past
-// `valid` read as zeros (buffer range check); no registers hold the data.
-template <int D, int ROWS, int NW>
+// elements in the swizzled K-style layout (tiling::ks_index<D>), or with TQ in
+// the tq_index layout: each lane's 16 bytes land at LDS chunk position
+// p = 64 * instruction + lane, so the lane loads the logical chunk that the
+// swizzle stores there.  Rows at or past `valid` read as zeros (buffer range
+// check); no registers hold the data.
+template <int D, int ROWS, int NW, bool TQ>
 __device__ __forceinline__ void lds_load_rows(uint16_t* dst, const uint16_t* base, int64_t row_stride, int valid,
                                               int wave, int lane) {
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
@@ -195,7 +225,7 @@ __device__ __forceinline__ void lds_load_rows(uint16_t* dst, const uint16_t* bas
     const int seg = wave * PER_WAVE + i;
     const int p = seg * 64 + lane;
     const int row = p / CPR;
-    const int lc = (p % CPR) ^ tiling::k_swz<D>(row);
+    const int lc = (p % CPR) ^ (TQ ? tq_swz<D>(row) : tiling::k_swz<D>(row));
     const uint32_t off = ((uint32_t)row * (uint32_t)row_stride + (uint32_t)lc * 8u) * 2u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + seg * 512), 16, off,
                                              0, 0, 0);
@@ -217,7 +247,7 @@ __device__ __forceinline__ int opaque(int x) {
 template <int D>
 __device__ __forceinline__ s16x4 tr_read4(const uint16_t* tile, int r0, int c0, int i) {
   const int row = r0 + (i >> 2), col = c0 + 4 * (i & 3);
-  const uint16_t* p = tile + tiling::ks_index<D>(row, col >> 3) + (col & 7);
+  const uint16_t* p = tile + tq_index<D>(row, col >> 3) + (col & 7);
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
@@ -277,15 +307,6 @@ struct BlockStage {
     const uint32_t off = (uint32_t)(tid & (BM - 1)) * 4u;
     lse_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.lse + at, bytes), (int)off, 0, 0));
     dr_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.drow + at, bytes), (int)off, 0, 0));
-  }
-  // lse is stored in log2 units
-  __device__ __forceinline__ void store(uint16_t* qs, uint16_t* dos, float* lse, float* dr, int tid) const {
-    tq.store_k(qs, tid & (NT - 1));
-    tdo.store_k(dos, tid & (NT - 1));
-    // every thread holds the values of row tid % BM: all write them (equal
-    // values), so no branch leaves the loads' wait off some path
-    lse[tid & (BM - 1)] = lse_v * kLog2eF;
-    dr[tid & (BM - 1)] = dr_v;
   }
 };
 
@@ -366,8 +387,8 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   const int64_t rs = a.row_stride, rsk = a.kv_row_stride;
   const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
   const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
-  lds_load_rows<D, BN, NW>(lds_k, kbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
-  lds_load_rows<D, BN, NW>(lds_v, vbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
+  lds_load_rows<D, BN, NW, true>(lds_k, kbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
+  lds_load_rows<D, BN, NW, false>(lds_v, vbase + (int64_t)key0 * rsk, rsk, w.Lk - key0, wave, lane);
 
   const int i_begin = CAUSAL ? max(0, key0 - shift) / BM : 0;
   const int i_end = (w.Lq + BM - 1) / BM;
@@ -386,8 +407,8 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
 
   if (nsteps > 0) {
     stage.load(a, w, 0, nblk, i_begin, tid);
-    stage.tq.store_k(lds_q, tid & (64 * NWS - 1));
-    stage.tdo.store_k(lds_do, tid & (64 * NWS - 1));
+    store_tq<D>(stage.tq, lds_q, tid & (64 * NWS - 1));
+    store_tq<D>(stage.tdo, lds_do, tid & (64 * NWS - 1));
     cur_lse = stage.lse_v * kLog2eF;
     cur_dr = stage.dr_v;
   }
@@ -402,7 +423,7 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   // the K operand of S = Q K^T is the same for every step: held in registers
   v8 kreg[KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) kreg[ks] = *(const v8*)(lds_k + tiling::ks_index<D>(klane, 2 * ks + g));
+  for (int ks = 0; ks < KSTEPS; ++ks) kreg[ks] = *(const v8*)(lds_k + tq_index<D>(klane, 2 * ks + g));
 
   int arow = tiling::key_of_arow(l32);
   int klane_l = klane;
@@ -428,8 +449,8 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
       v8 aq[PF + 1], ad[PF + 1], bv[PF + 1];
       auto fetch = [&](int ks) __attribute__((always_inline)) {
         const int i = ks % (PF + 1);
-        aq[i] = *(const v8*)(lds_q + tiling::ks_index<D>(arow, 2 * ks + g));
-        ad[i] = *(const v8*)(lds_do + tiling::ks_index<D>(arow, 2 * ks + g));
+        aq[i] = *(const v8*)(lds_q + tq_index<D>(arow, 2 * ks + g));
+        ad[i] = *(const v8*)(lds_do + tq_index<D>(arow, 2 * ks + g));
         bv[i] = *(const v8*)(lds_v + tiling::ks_index<D>(klane_l, 2 * ks + g));
       };
 #pragma unroll
@@ -506,8 +527,8 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
       }
       read_ahead_schedule<TPW * (BN / 32), (TPW + 2) * (BN / 32), 8>();
       // the next query block: no Q/dO reads remain in this step
-      stage.tq.store_k(lds_q, tid & (64 * NWS - 1));
-      stage.tdo.store_k(lds_do, tid & (64 * NWS - 1));
+      store_tq<D>(stage.tq, lds_q, tid & (64 * NWS - 1));
+      store_tq<D>(stage.tdo, lds_do, tid & (64 * NWS - 1));
       cur_lse = stage.lse_v * kLog2eF;
       cur_dr = stage.dr_v;
       // register r of tile u: block row dq16_row(rt0 + u, 4 lg + r), column 16*ct + li
