@@ -55,6 +55,7 @@ KERNEL_SRCS = [os.path.join(CSRC_DIR, n) for n in
                ("fa_varlen_kernels.hip", "fa_varlen_device.h", "fa_varlen_tiling.h", "fa_varlen_launch.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_ragged64k_causal_d128.json")
 COPY_BYTES = 1 << 30        # calibration copy: 1 GiB read + 1 GiB written
+FWD_KERNEL_TAG = "fwd16_"   # name fragment of the 16-bit forward attention kernels
 
 
 def visible_pairs(wl: Workload, causal: bool) -> int:
@@ -103,35 +104,74 @@ def to_device(wl: Workload, data: dict):
 
 
 class Runner:
-    """Calls the C ABI with preallocated buffers on torch's current stream."""
+    """Calls the C ABI with preallocated buffers and descriptors on torch's current stream."""
 
     def __init__(self, wl: Workload, t: dict, causal: bool):
+        import ctypes
         import torch
         import variable_length_flashattention_cu_amd as fa
         self.fa, self.wl, self.t, self.causal = fa, wl, t, causal
         self.lib = fa.load_library()
         self.stream = torch.cuda.current_stream().cuda_stream
-        dt = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16}[wl.dtype]
-        self.bm = fa.fa_varlen_block_sizes(wl.head_dim, dt)[0]
-        self.blk = fa.fa_varlen_tile_map(t["cu_q"], self.bm)
-        self.common = (t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["cu_q"].data_ptr(),
-                       t["cu_k"].data_ptr(), wl.max_seqlen_q, wl.max_seqlen_k, wl.scale, int(causal),
-                       t["out"].data_ptr(), t["lse"].data_ptr(), wl.batch, wl.total_q, wl.total_k, wl.heads,
-                       wl.kv_heads, wl.head_dim, dt)
+        self.dt = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16}[wl.dtype]
+        self.blk = fa.fa_varlen_tile_map(t["cu_q"], wl.max_seqlen_q, wl.head_dim, self.dt)
+        self.descs = [fa.desc(t[n]) for n in ("q", "k", "v", "cu_q", "cu_k", "out", "lse")] + [fa.desc(self.blk)]
+        r = [ctypes.byref(d) for d in self.descs]
+        self.args = (r[0], r[1], r[2], r[3], r[4], wl.max_seqlen_q, wl.max_seqlen_k, ctypes.c_float(wl.scale),
+                     int(causal), r[5], r[6])
+        self.blk_ref = r[7]
 
     def step(self):
-        st = self.lib.fa_varlen_fwd(*self.common, self.stream)
+        st = self.lib.fa_varlen_fwd(*self.args, self.stream)
         if st:
             raise RuntimeError(f"fa_varlen_fwd failed: {self.fa.fa_status_string(st)}")
 
     def kernel_only(self):
-        st = self.lib.fa_varlen_fwd_mapped(*self.common, self.blk.data_ptr(), self.stream)
+        st = self.lib.fa_varlen_fwd_mapped(*self.args, self.blk_ref, self.stream)
         if st:
             raise RuntimeError(f"fa_varlen_fwd_mapped failed: {self.fa.fa_status_string(st)}")
 
 
-def time_events(fn, iters: int) -> float:
-    """Average milliseconds per call, HIP events on torch's current stream."""
+# ---------------------------------------------------------------------------
+# timing: a time-based pre-warm, then HIP events on torch's current stream
+# (the stream every call here is launched on)
+# ---------------------------------------------------------------------------
+PREWARM_MS = 200.0   # wall time of untimed calls before every timed loop
+MIN_TIMED_MS = 200.0
+MIN_TIMED_CALLS = 50
+
+
+def prewarm(fn, min_ms: float = PREWARM_MS) -> dict:
+    """Call fn until at least min_ms of wall time has passed (synchronised)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0 or n < 4:
+            torch.cuda.synchronize()
+            el = (time.perf_counter() - t0) * 1e3
+            if el >= min_ms:
+                return {"calls": n, "ms": round(el, 1)}
+
+
+def per_call_ms(fn, iters: int) -> np.ndarray:
+    """Per-call milliseconds: one event pair around every call."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev], dtype=np.float64)
+
+
+def bracketed_ms(fn, iters: int) -> float:
+    """Mean milliseconds per call of `iters` back-to-back calls between two events."""
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -143,30 +183,87 @@ def time_events(fn, iters: int) -> float:
     return start.elapsed_time(end) / iters
 
 
-def measure_secondary(wl: Workload, iters: int = 20, modes=(False, True)) -> list:
+def timed_iters(pw: dict) -> int:
+    """At least MIN_TIMED_CALLS calls and MIN_TIMED_MS of device time, from the pre-warm rate."""
+    per = pw["ms"] / max(pw["calls"], 1)
+    return int(max(MIN_TIMED_CALLS, math.ceil(MIN_TIMED_MS / max(per, 1e-3))))
+
+
+def call_stats(ms: np.ndarray) -> dict:
+    return {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(float(ms.min()), 4),
+            "mean_ms": round(float(ms.mean()), 4), "calls": int(ms.size)}
+
+
+# ---------------------------------------------------------------------------
+# sampled outputs for the parity check (rows chosen without the oracle)
+# ---------------------------------------------------------------------------
+def sample_rows(wl: Workload, block: int = 256, per_seq: int = 4, seed: int = 0) -> np.ndarray:
+    """Packed query rows: the first and last row of every sequence and of every
+    block of `block` rows (one query block of the forward kernel), plus a few
+    random rows per sequence."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(wl.batch):
+        s, L = wl.cu_q[b], wl.cu_q[b + 1] - wl.cu_q[b]
+        if L <= 0:
+            continue
+        cand = {0, L - 1} | {int(x) for x in rng.integers(0, L, size=per_seq)}
+        for m0 in range(0, L, block):
+            cand |= {m0, min(L - 1, m0 + block - 1)}
+        rows |= {s + c for c in cand}
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def take_sample(wl: Workload, t: dict, causal: bool, heads) -> dict:
+    import torch
+    rows = sample_rows(wl, seed=wl.seed)
+    idx = torch.from_numpy(rows).to(t["out"].device)
+    hs = torch.tensor(list(heads), device=t["out"].device)
+    out = t["out"].index_select(0, idx).index_select(1, hs).float().cpu().numpy()
+    lse = t["lse"].index_select(0, hs).index_select(1, idx).cpu().numpy()
+    return {"rows": rows, "heads": list(heads), "out": out, "lse": lse, "causal": causal}
+
+
+def measure_fwd(wl: Workload, t: dict, causal: bool) -> tuple:
+    """One forward workload: whole-call and kernel-only per-call times, and a
+    sample of the outputs for the parity check."""
+    r = Runner(wl, t, causal)
+    pw = prewarm(r.step)
+    n = timed_iters(pw)
+    call = call_stats(per_call_ms(r.step, n))
+    pwk = prewarm(r.kernel_only)
+    kern = call_stats(per_call_ms(r.kernel_only, n))
+    fl = algorithmic_flops(wl, causal)
+    by = algorithmic_bytes(wl)
+    row = {"workload": wl.name, "seq_len": wl.max_seqlen_q, "head_dim": wl.head_dim, "heads": wl.heads,
+           "kv_heads": wl.kv_heads, "dtype": wl.dtype, "causal": causal, "seed": wl.seed,
+           "gflop": round(fl / 1e9, 3), "algorithmic_mb": round(by / 1e6, 2),
+           "prewarm": pw, "call": call, "kernel": kern,
+           "tflops": round(fl / call["median_ms"] / 1e9, 1),
+           "kernel_tflops": round(fl / kern["median_ms"] / 1e9, 1),
+           "kernel_frac_bf16_peak": round(fl / kern["median_ms"] / 1e9 / PEAK_BF16_TFLOPS, 4),
+           "kernel_frac_hbm_peak": round(by / kern["median_ms"] / 1e6 / PEAK_HBM_GBS, 4),
+           "kernel_prewarm": pwk}
+    sample = take_sample(wl, t, causal, sorted({0, wl.heads - 1}))
+    del r
+    return row, sample
+
+
+def measure_secondary(wl: Workload, modes=(False, True), parity=None) -> list:
     """The given mask modes of one workload (inputs drawn once)."""
     data = draw_qkv(wl)
     t = to_device(wl, data)
-    del data
     rows = []
     for causal in modes:
-        r = Runner(wl, t, causal)
-        for _ in range(3):
-            r.step()
-        ms = time_events(r.step, iters)
-        kms = time_events(r.kernel_only, iters)
-        fl = algorithmic_flops(wl, causal)
-        rows.append({"workload": wl.name, "seq_len": wl.max_seqlen_q, "head_dim": wl.head_dim,
-                     "heads": wl.heads, "kv_heads": wl.kv_heads, "dtype": wl.dtype, "causal": causal, "ms_per_step": round(ms, 4),
-                     "tflops": round(fl / ms / 1e9, 1), "kernel_ms": round(kms, 4),
-                     "kernel_tflops": round(fl / kms / 1e9, 1),
-                     "kernel_frac_bf16_peak": round(fl / kms / 1e9 / PEAK_BF16_TFLOPS, 4)})
-        del r
-    del t
+        row, sample = measure_fwd(wl, t, causal)
+        if parity is not None:
+            row["parity"] = parity(wl, data, sample)
+        rows.append(row)
+    del t, data
     return rows
 
 
-def measure_backward(wl: Workload, causal: bool, iters: int = 10) -> dict:
+def measure_backward(wl: Workload, causal: bool) -> dict:
     """fa_varlen_bwd (all four launches) after one forward; 10*D flops per
     visible pair and head (S recomputed, dP, dV, dK, dQ: five products)."""
     import torch
@@ -187,16 +284,16 @@ def measure_backward(wl: Workload, causal: bool, iters: int = 10) -> dict:
     def step():
         fa.fa_varlen_bwd(t["q"], t["k"], t["v"], out, dout, lse, t["cu_q"], t["cu_k"], wl.max_seqlen_q,
                          wl.max_seqlen_k, wl.scale, causal, dq=dq, dk=dk, dv=dv, workspace=ws)
-    for _ in range(2):
-        step()
-    ms = time_events(step, iters)
+    pw = prewarm(step)
+    call = call_stats(per_call_ms(step, timed_iters(pw)))
     fl = 2.5 * algorithmic_flops(wl, causal)
     return {"workload": wl.name, "seq_len": wl.max_seqlen_q, "head_dim": wl.head_dim, "heads": wl.heads,
-            "kv_heads": wl.kv_heads, "dtype": wl.dtype, "causal": causal, "ms_per_call": round(ms, 4),
-            "tflops": round(fl / ms / 1e9, 1), "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+            "kv_heads": wl.kv_heads, "dtype": wl.dtype, "causal": causal, "prewarm": pw, "call": call,
+            "tflops": round(fl / call["median_ms"] / 1e9, 1),
+            "frac_bf16_peak": round(fl / call["median_ms"] / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
 
-def measure_decode(wl, iters: int = 20) -> dict:
+def measure_decode(wl) -> dict:
     """fa_varlen_fwd_kvcache (decode kernel and partial combine) on a cache batch.
     Algorithmic bytes: the cached K and V rows each sequence uses (once per
     key/value head), q read, out and lse written."""
@@ -220,17 +317,36 @@ def measure_decode(wl, iters: int = 20) -> dict:
         fa.fa_varlen_fwd_kvcache(dev["q"], dev["k_cache"], dev["v_cache"], cu_q, sk, wl.max_seqlen_q,
                                  wl.max_seqlen_k, wl.scale, True, leftpad_k=lp, block_table=bt, out=out, lse=lse,
                                  workspace=ws)
-    for _ in range(3):
-        step()
-    ms = time_events(step, iters)
+    pw = prewarm(step)
+    call = call_stats(per_call_ms(step, timed_iters(pw)))
+    ms = call["median_ms"]
     es = 2
     kv_bytes = 2.0 * sum(wl.key_lengths) * wl.kv_heads * wl.head_dim * es
     qo_bytes = 2.0 * wl.total_q * wl.heads * wl.head_dim * es + 4.0 * wl.total_q * wl.heads
     gbs = (kv_bytes + qo_bytes) / ms / 1e6
     return {"workload": wl.name, "batch": wl.batch, "kv_tokens": int(sum(wl.key_lengths)), "heads": wl.heads,
-            "kv_heads": wl.kv_heads, "head_dim": wl.head_dim, "dtype": wl.dtype, "ms_per_call": round(ms, 4),
+            "kv_heads": wl.kv_heads, "head_dim": wl.head_dim, "dtype": wl.dtype, "prewarm": pw, "call": call,
             "algorithmic_bytes": round(kv_bytes + qo_bytes), "gb_per_s": round(gbs, 1),
             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+# ---------------------------------------------------------------------------
+# cpu_baseline leg: the oracle on the host cores -- its timed sample, and the
+# sampled parity checks of the measured GPU outputs (only this leg runs it)
+# ---------------------------------------------------------------------------
+def cpu_parity(wl: Workload, data: dict, sample: dict) -> dict:
+    """Max-abs difference of the sampled GPU rows and heads against the oracle."""
+    from oracle import attention_rows
+    tol = {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-5}[wl.dtype]
+    ref_o, ref_l = attention_rows(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, sample["causal"],
+                                  sample["rows"], sample["heads"])
+    fin = np.isfinite(ref_l)
+    err_o = float(np.abs(sample["out"].astype(np.float64) - ref_o).max()) if ref_o.size else 0.0
+    err_l = float(np.abs(sample["lse"][fin].astype(np.float64) - ref_l[fin]).max()) if fin.any() else 0.0
+    pattern = bool(np.array_equal(np.isfinite(sample["lse"]), fin))
+    ok = err_o <= tol and err_l <= tol and pattern and not np.isnan(sample["out"]).any()
+    return {"rows": int(sample["rows"].size), "heads": sample["heads"], "max_abs_out": float(f"{err_o:.3e}"),
+            "max_abs_lse": float(f"{err_l:.3e}"), "tol": tol, "ok": bool(ok)}
 
 
 def cpu_baseline(wl: Workload, causal: bool, data: dict, heads=(0,)) -> dict:
@@ -243,11 +359,13 @@ def cpu_baseline(wl: Workload, causal: bool, data: dict, heads=(0,)) -> dict:
     dt = time.perf_counter() - t0
     fl = 4.0 * wl.head_dim * len(heads) * visible_pairs(wl, causal)
     blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
-    cores = max([p.get("num_threads", 1) for p in blas] or [1])
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "os_cpu_count": os.cpu_count(), "blas_threads": int(threads),
+            "blas": (blas[0].get("internal_api", "?") if blas else "?"),
             "sample": f"{wl.name}: head {list(heads)} of {wl.heads}, all {wl.batch} sequences "
-                      f"({fl / 1e9:.1f} GFLOP algorithmic, {dt:.1f} s, float64 numpy, "
-                      f"{blas[0].get('internal_api', '?') if blas else '?'} BLAS)"}
+                      f"({fl / 1e9:.1f} GFLOP algorithmic, {dt:.1f} s, float64 numpy on {threads} BLAS threads "
+                      f"of {os.cpu_count()} host cores)"}
 
 
 def stored_traffic() -> dict | None:
@@ -316,7 +434,7 @@ def parse_pmc(fetch_dir: str, write_dir: str) -> dict:
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per_disp = _counter_per_dispatch(d, counter)
         copy_vals = [v for (k, _), v in per_disp.items() if "elementwise" in k.lower()]
-        fwd_vals = [v for (k, _), v in per_disp.items() if "fwd16_pingpong_kernel" in k]
+        fwd_vals = [v for (k, _), v in per_disp.items() if FWD_KERNEL_TAG in k]
         if not copy_vals or not fwd_vals:
             raise RuntimeError(f"{counter}: calibration copy or attention dispatches not found in {d}")
         copy_kib = max(copy_vals)
@@ -330,7 +448,7 @@ def parse_pmc(fetch_dir: str, write_dir: str) -> dict:
     return out
 
 
-def summarize_trace(db_path: str) -> str:
+def summarize_trace(db_path: str, last: int = 100) -> str:
     """Per-kernel call count / total / average duration from a --kernel-trace run."""
     con = sqlite3.connect(db_path)
     rows = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels").fetchall()
@@ -343,14 +461,18 @@ def summarize_trace(db_path: str) -> str:
     # process are cold (code and data not yet cached), so the median and the
     # mean without the first two are what compares with the timed steps
     con = sqlite3.connect(db_path)
-    durs = [r[0] for r in con.execute("select duration from kernels where name like '%fwd16_pingpong_kernel%' "
+    durs = [r[0] for r in con.execute(f"select duration from kernels where name like '%{FWD_KERNEL_TAG}%' "
                                       "order by start")]
     con.close()
     if durs:
         us = np.asarray(durs, dtype=np.float64) / 1e3  # nanoseconds -> microseconds
-        warm = us[2:] if len(us) > 2 else us
-        lines.append(f"attention kernel, {len(us)} dispatches: first {us[0]:.1f} us, median {np.median(us):.1f} us, "
-                     f"mean without the first two {warm.mean():.1f} us")
+        warm = us[10:] if len(us) > 10 else us
+        lines.append(f"attention kernel, {len(us)} dispatches: first {us[0]:.1f} us; after the first ten: "
+                     f"median {np.median(warm):.1f} us, mean {warm.mean():.1f} us")
+        if len(us) >= last:
+            tail = us[-last:]
+            lines.append(f"the last {last} dispatches (the timed kernel-only loop of the bench run): "
+                         f"mean {tail.mean():.1f} us, median {np.median(tail):.1f} us, min {tail.min():.1f} us")
     return "\n".join(lines)
 
 
@@ -358,8 +480,8 @@ def summarize_trace(db_path: str) -> str:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the sweep and dense rows")
     ap.add_argument("--pmc-pass", action="store_true", help="launch sequence for a rocprofv3 --pmc run")
@@ -392,34 +514,48 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     if args.decode_pass:
-        print(json.dumps(measure_decode(workload_decode_bench(), iters=args.steps)), flush=True)
+        print(json.dumps(measure_decode(workload_decode_bench())), flush=True)
         return 0
     if args.bwd_pass:
-        print(json.dumps(measure_backward(workload_ragged64k(), True, iters=args.steps)), flush=True)
+        print(json.dumps(measure_backward(workload_ragged64k(), True)), flush=True)
         return 0
     if args.pmc_pass:
         pmc_pass(max(1, args.steps))
         return 0
 
+    import torch
     wl = workload_ragged64k()
     causal = True
     print(f"# bench: {wl.name} batch={wl.batch} tokens={wl.total_q} heads={wl.heads} d={wl.head_dim} "
           f"causal={causal}", file=sys.stderr, flush=True)
+    props = torch.cuda.get_device_properties(0)
+    gpu = {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", "?"),
+           "compute_units": props.multi_processor_count, "memory_gb": round(props.total_memory / 2**30, 1)}
+    ceiling = mfma_ceiling()
+    print(f"# gpu {gpu}; measured MFMA ceiling {ceiling}", file=sys.stderr, flush=True)
+
     data = draw_qkv(wl)
     t = to_device(wl, data)
+    torch.cuda.reset_peak_memory_stats()
     r = Runner(wl, t, causal)
     for _ in range(args.warmup):
         r.step()
+    pw = prewarm(r.step)
+    # the headline: exactly `steps` whole calls between two synchronisations
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ms = time_events(r.step, args.steps)
+    ms = bracketed_ms(r.step, args.steps)
     wall = (time.perf_counter() - w0) * 1e3 / args.steps
-    kms = time_events(r.kernel_only, max(args.steps, 10))
+    call = call_stats(per_call_ms(r.step, args.steps))
+    pwk = prewarm(r.kernel_only)
+    kern = call_stats(per_call_ms(r.kernel_only, args.steps))
+    peak_mem = torch.cuda.max_memory_allocated()
     fl = algorithmic_flops(wl, causal)
     value = fl / ms / 1e9
-    achieved = fl / kms / 1e9
-    print(f"# step {ms:.3f} ms ({value:.1f} TFLOP/s), attention kernel {kms:.3f} ms ({achieved:.1f} TFLOP/s)",
-          file=sys.stderr, flush=True)
+    achieved = fl / kern["mean_ms"] / 1e9
+    print(f"# step {ms:.3f} ms ({value:.1f} TFLOP/s), attention kernel mean {kern['mean_ms']:.4f} ms "
+          f"median {kern['median_ms']:.4f} ms ({achieved:.1f} TFLOP/s)", file=sys.stderr, flush=True)
+    sample = take_sample(wl, t, causal, [0, wl.heads // 2, wl.heads - 1])
 
     traffic = stored_traffic()
     line = {
@@ -443,22 +579,33 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": round(traffic["traffic_bytes"]) if traffic else None,
-                     "kernel": "fwd16_pingpong_kernel<__bf16, 128, 64, causal>", "kernel_ms": round(kms, 4),
-                     "algorithmic_bytes": round(algorithmic_bytes(wl))},
+                     "kernel": "fwd16 attention kernel <__bf16, 128, causal>", "kernel_ms": kern["mean_ms"],
+                     "kernel_ms_median": kern["median_ms"], "kernel_ms_min": kern["min_ms"],
+                     "algorithmic_bytes": round(algorithmic_bytes(wl)),
+                     "frac_of_measured_mfma_ceiling": (round(achieved / ceiling["tflops"], 4)
+                                                       if ceiling.get("tflops") else None)},
+        "timing": {"prewarm_call": pw, "prewarm_kernel": pwk, "call": call, "kernel": kern,
+                   "method": "HIP events on the launch stream after a >=200 ms pre-warm; value from `steps` "
+                             "back-to-back calls between two synchronisations"},
+        "gpu": gpu,
+        "mfma_ceiling": ceiling,
+        "peak_memory_bytes": int(peak_mem),
     }
-    del r, t
+    del r
+    t = None
     torch.cuda.empty_cache()
+    par = None if args.no_cpu_baseline else cpu_parity
 
     if not args.no_secondary:
         rows = []
         for d in SWEEP_HEAD_DIMS:
             for L in SWEEP_SEQLENS:
-                rows += measure_secondary(workload_sweep(L, d))
+                rows += measure_secondary(workload_sweep(L, d), parity=par)
                 for row in rows[-2:]:
                     print(f"# {row}", file=sys.stderr, flush=True)
                 torch.cuda.empty_cache()
         line["sweep_16k_tokens"] = rows
-        line["dense_8x2048"] = measure_secondary(workload_dense())
+        line["dense_8x2048"] = measure_secondary(workload_dense(), parity=par)
         torch.cuda.empty_cache()
         # the headline length mix with fp16 inputs, 8 shared key/value heads, head_dim 96 and 256
         base = workload_ragged64k()
@@ -469,11 +616,9 @@ def main() -> int:
                                         head_dim=256)]
         line["ragged64k_variants"] = []
         for v in variants:
-            line["ragged64k_variants"] += measure_secondary(v, modes=(True,))
+            line["ragged64k_variants"] += measure_secondary(v, modes=(True,), parity=par)
             print(f"# {line['ragged64k_variants'][-1]}", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
-
-    if not args.no_secondary:
         # backward pass (fa_varlen_bwd, after the forward that gives out and lse)
         line["backward"] = []
         for bwl, bc in ((workload_ragged64k(), True), (workload_sweep(4096, 128), False),
@@ -481,17 +626,39 @@ def main() -> int:
             line["backward"].append(measure_backward(bwl, bc))
             print(f"# {line['backward'][-1]}", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
-
-    if not args.no_secondary:
         # decode-shaped attention against a paged key/value cache (HBM-bound)
         line["decode"] = measure_decode(workload_decode_bench())
         print(f"# {line['decode']}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
+        line["parity"] = cpu_parity(wl, data, sample)
         line["cpu_baseline"] = cpu_baseline(wl, causal, data)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def mfma_ceiling() -> dict:
+    """Dense bf16 MFMA rate of a register-only loop on this device (libfa_probe.so)."""
+    import ctypes
+    path = os.path.join(ROOT, "variable_length_flashattention_cu_amd", "libfa_probe.so")
+    if not os.path.exists(path):
+        return {"tflops": None, "note": "libfa_probe.so not built"}
+    lib = ctypes.CDLL(path)
+    lib.fa_probe_mfma_peak.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double)]
+    lib.fa_probe_mfma_peak.restype = ctypes.c_int
+    tf, ghz = ctypes.c_double(0), ctypes.c_double(0)
+    best = None
+    for _ in range(3):
+        rc = lib.fa_probe_mfma_peak(20000, ctypes.byref(tf), ctypes.byref(ghz))
+        if rc != 0:
+            return {"tflops": None, "note": f"probe failed with status {rc}"}
+        if best is None or tf.value > best[0]:
+            best = (tf.value, ghz.value)
+    return {"tflops": round(best[0], 1), "clock_ghz": round(best[1], 3),
+            "frac_of_published_peak": round(best[0] / PEAK_BF16_TFLOPS, 4),
+            "method": "v_mfma_f32_32x32x16_bf16 on registers, 2 waves per SIMD on every CU, best of 3"}
 
 
 if __name__ == "__main__":

@@ -11,6 +11,11 @@ import numpy as np
 TOL = {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-5}
 
 
+def dtype_code(fa, name):
+    """fa_dtype code of a workload dtype name."""
+    return {"f32": fa.FA_DTYPE_F32, "bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16}[name]
+
+
 def say(msg):
     print(msg, flush=True)
     sys.stdout.flush()

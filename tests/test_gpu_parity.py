@@ -20,7 +20,7 @@ import pytest
 from fa_synth import (SWEEP_HEAD_DIMS, SWEEP_SEQLENS, draw_qkv, workload_custom, workload_dense,
                       workload_ragged64k, workload_ragged64k_gqa, workload_ragged_qk, workload_sweep, workload_tiny)
 from oracle import attention_fwd, attention_rows, tile_map
-from tests._gpu_util import TOL, compare, host, run_gpu, sample_rows, say, to_device
+from tests._gpu_util import TOL, compare, dtype_code, host, run_gpu, sample_rows, say, to_device
 
 torch = pytest.importorskip("torch")
 
@@ -54,12 +54,17 @@ def test_tile_map_bit_exact(fa):
         cases.append([0] + np.cumsum(lens).tolist())
     lens = rng.integers(0, 300, size=1000)  # several scan chunks of 256
     cases.append([0] + np.cumsum(lens).tolist())
-    bms = sorted({fa.fa_varlen_block_sizes(d, dt)[0] for d in (64, 128) for dt in (0, 1)} | {1, 64, 256})
+    # every block height the forward pass uses (fp32 and 16-bit kernels)
+    configs = [(d, dt) for d in (64, 96, 128) for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16)]
+    configs += [(256, fa.FA_DTYPE_BF16)]
+    assert len({fa.fa_varlen_block_sizes(d, dt)[0] for d, dt in configs}) >= 2
     for cu in cases:
         cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
-        for bm in bms:
-            got = fa.fa_varlen_tile_map(cu_t, bm).cpu().numpy()
-            assert np.array_equal(got, tile_map(cu, bm)), (cu[:5], bm)
+        max_q = int(np.diff(cu).max()) if len(cu) > 1 else 0
+        for d, dt in configs:
+            bm = fa.fa_varlen_block_sizes(d, dt)[0]
+            got = fa.fa_varlen_tile_map(cu_t, max_q, d, dt).cpu().numpy()
+            assert np.array_equal(got, tile_map(cu, bm)), (cu[:5], d, dt, bm)
 
 
 # ---------------------------------------------------------------- configurations, full comparison
@@ -82,17 +87,25 @@ def test_dense_8x2048(fa, causal):
 
 
 # ---------------------------------------------------------------- full sizes, sampled rows
-def sampled_parity(fa, wl, causal, heads, seed):
-    say(f"case {wl.name} causal={causal} (sampled rows, heads {heads})")
+def sampled_parity(fa, wl, causal, heads, seed, full_head=None):
+    """Sampled rows of `heads`; with `full_head`, also every row of that head
+    (every query block of every workgroup, whatever its place in the schedule)."""
+    say(f"case {wl.name} causal={causal} (sampled rows, heads {heads}; every row of head {full_head})")
     data = draw_qkv(wl)
     t = to_device(data, wl)
     o, l = host(*run_gpu(wl, t, causal))
-    bm = fa.fa_varlen_block_sizes(wl.head_dim, {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype])[0]
+    bm = fa.fa_varlen_block_sizes(wl.head_dim, dtype_code(fa, wl.dtype))[0]
     rows = sample_rows(wl, bm, np.random.default_rng(seed))
     ref_o, ref_l = attention_rows(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal, rows,
                                   heads)
     compare(o[rows][:, heads], l[heads][:, rows], ref_o, ref_l, TOL[wl.dtype], wl.name)
     assert not np.isnan(o[:wl.total_q]).any() and not np.isnan(l[:, :wl.total_q]).any()
+    if full_head is not None:
+        n = wl.total_q
+        ref_o, ref_l = attention_fwd(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal,
+                                     heads=[full_head])
+        compare(o[:n, full_head], l[full_head, :n], ref_o[:n, full_head], ref_l[full_head, :n], TOL[wl.dtype],
+                f"{wl.name} head {full_head}, all {n} rows")
 
 
 @pytest.mark.parametrize("seqlen", SWEEP_SEQLENS)
@@ -100,12 +113,13 @@ def sampled_parity(fa, wl, causal, heads, seed):
 @pytest.mark.parametrize("causal", [False, True])
 def test_sweep_sampled(fa, seqlen, head_dim, causal):
     wl = workload_sweep(seqlen, head_dim)
-    sampled_parity(fa, wl, causal, [0, wl.heads // 2, wl.heads - 1], seed=seqlen + head_dim)
+    sampled_parity(fa, wl, causal, [0, wl.heads // 2, wl.heads - 1], seed=seqlen + head_dim,
+                   full_head=wl.heads - 1 if seqlen >= 4096 else None)
 
 
 def test_ragged64k_sampled(fa):
     wl = workload_ragged64k()
-    sampled_parity(fa, wl, True, [0, 17, 31], seed=4)
+    sampled_parity(fa, wl, True, [0, 17, 31], seed=4, full_head=wl.heads - 1)
 
 
 # ---------------------------------------------------------------- edge cases
@@ -194,8 +208,7 @@ def test_deterministic_and_mapped_identical(fa):
     wl = workload_ragged_qk()
     data = draw_qkv(wl)
     t = to_device(data, wl)
-    bm = fa.fa_varlen_block_sizes(wl.head_dim, 1)[0]
-    blk = fa.fa_varlen_tile_map(t["cu_q"], bm)
+    blk = fa.fa_varlen_tile_map(t["cu_q"], wl.max_seqlen_q, wl.head_dim, fa.FA_DTYPE_BF16)
     for causal in (False, True):
         say(f"case determinism causal={causal}")
         o1, l1 = host(*run_gpu(wl, t, causal))

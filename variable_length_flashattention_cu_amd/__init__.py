@@ -24,6 +24,10 @@ __all__ = [
     "FA_DTYPE_F32",
     "FA_DTYPE_BF16",
     "FA_DTYPE_F16",
+    "FA_DTYPE_I32",
+    "FaTensor",
+    "make_desc",
+    "desc",
     "library_path",
     "load_library",
     "fa_status_string",
@@ -40,12 +44,14 @@ __all__ = [
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
-FA_DTYPE_F16 = 2
+FA_DTYPE_I32 = 2
+FA_DTYPE_F16 = 3
 
 FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_DTYPE", 3: "FA_ERR_SHAPE", 4: "FA_ERR_HEAD_DIM",
-    5: "FA_ERR_ALIGN", 6: "FA_ERR_ARG", 7: "FA_ERR_HIP", 8: "FA_ERR_TOO_LARGE", 9: "FA_ERR_WORKSPACE",
+    5: "FA_ERR_LAYOUT", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ARG", 8: "FA_ERR_HIP", 9: "FA_ERR_TOO_LARGE",
+    10: "FA_ERR_WORKSPACE",
 }
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +62,30 @@ class FaVarlenError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({_status_text(status)})")
+
+
+class FaTensor(ctypes.Structure):
+    """The fa_tensor descriptor of include/fa_varlen.h (element strides)."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 3), ("stride", ctypes.c_int64 * 3)]
+
+
+def make_desc(data: int, dtype: int, shape, stride=None) -> FaTensor:
+    """Descriptor from raw values; stride defaults to row-major contiguous."""
+    shape = [int(x) for x in shape]
+    if stride is None:
+        stride, acc = [0] * len(shape), 1
+        for i in range(len(shape) - 1, -1, -1):
+            stride[i] = acc
+            acc *= shape[i]
+    d = FaTensor()
+    d.data = int(data) if data else None
+    d.dtype = int(dtype)
+    d.ndim = len(shape)
+    for i, (n, st) in enumerate(zip(shape, stride)):
+        d.shape[i] = n
+        d.stride[i] = int(st)
+    return d
 
 
 def library_path() -> str:
@@ -72,32 +102,27 @@ def load_library() -> ctypes.CDLL:
         raise FaVarlenError(-1, f"HIP library not built: {path} is missing; run "
                                 "`python -m variable_length_flashattention_cu_amd.build`")
     lib = ctypes.CDLL(path)
-    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
-    i32p = ctypes.POINTER(ctypes.c_int32)
-    lib.fa_status_string.argtypes = [ctypes.c_int]
-    lib.fa_status_string.restype = ctypes.c_char_p
-    lib.fa_varlen_block_sizes.argtypes = [i32, i32, i32p, i32p]
-    lib.fa_varlen_block_sizes.restype = ctypes.c_int
-    lib.fa_varlen_tile_map.argtypes = [vp, i32, i32, vp, vp]
-    lib.fa_varlen_tile_map.restype = ctypes.c_int
-    fwd_args = [vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32]
-    lib.fa_varlen_fwd.argtypes = fwd_args + [vp]
-    lib.fa_varlen_fwd.restype = ctypes.c_int
-    lib.fa_varlen_fwd_mapped.argtypes = fwd_args + [vp, vp]
-    lib.fa_varlen_fwd_mapped.restype = ctypes.c_int
-    lib.fa_varlen_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp,
-                                  i32, i32, i32, i32, i32, i32, i32, vp, ctypes.c_size_t, vp]
-    lib.fa_varlen_bwd.restype = ctypes.c_int
-    lib.fa_varlen_bwd_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
-    lib.fa_varlen_bwd_workspace_size.restype = ctypes.c_int
-    lib.fa_varlen_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, vp, vp,
-                                          i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
-                                          vp, ctypes.c_size_t, vp]
-    lib.fa_varlen_fwd_kvcache.restype = ctypes.c_int
-    lib.fa_varlen_kvcache_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
-    lib.fa_varlen_kvcache_workspace_size.restype = ctypes.c_int
-    lib.fa_varlen_check_cu_seqlens.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
-    lib.fa_varlen_check_cu_seqlens.restype = ctypes.c_int
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    i32p, szp = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)
+    tp = ctypes.POINTER(FaTensor)
+    sigs = {
+        "fa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "fa_varlen_block_sizes": ([i32, i32, i32p, i32p], ctypes.c_int),
+        "fa_varlen_tile_map": ([tp, i32, i32, i32, tp, vp], ctypes.c_int),
+        "fa_varlen_fwd": ([tp, tp, tp, tp, tp, i32, i32, f32, i32, tp, tp, vp], ctypes.c_int),
+        "fa_varlen_fwd_mapped": ([tp, tp, tp, tp, tp, i32, i32, f32, i32, tp, tp, tp, vp], ctypes.c_int),
+        "fa_varlen_bwd": ([tp, tp, tp, tp, tp, tp, tp, tp, i32, i32, f32, i32, tp, tp, tp, vp, sz, vp],
+                          ctypes.c_int),
+        "fa_varlen_bwd_workspace_size": ([i32, i32, i32, i32, szp], ctypes.c_int),
+        "fa_varlen_fwd_kvcache": ([tp, tp, tp, tp, tp, tp, tp, i32, i32, f32, i32, i32, i32, tp, tp, vp, sz, vp],
+                                  ctypes.c_int),
+        "fa_varlen_kvcache_workspace_size": ([i32, i32, i32, i32, szp], ctypes.c_int),
+        "fa_varlen_check_cu_seqlens": ([tp, tp, i32, i32, i32, i32, tp, vp], ctypes.c_int),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
     _LIB = lib
     return lib
 
@@ -135,13 +160,24 @@ def _torch():
 
 def _dtype_code(t) -> int:
     torch = _torch()
-    if t.dtype == torch.float32:
-        return FA_DTYPE_F32
-    if t.dtype == torch.bfloat16:
-        return FA_DTYPE_BF16
-    if t.dtype == torch.float16:
-        return FA_DTYPE_F16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
+    codes = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16, torch.int32: FA_DTYPE_I32,
+             torch.float16: FA_DTYPE_F16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, float16 or int32)")
+    return codes[t.dtype]
+
+
+def desc(t) -> FaTensor:
+    """fa_tensor descriptor of a torch tensor (1 to 3 dimensions), or None for None."""
+    if t is None:
+        return None
+    if not 1 <= t.dim() <= 3:
+        raise ValueError(f"fa_tensor holds 1 to 3 dimensions, got {t.dim()}")
+    return make_desc(t.data_ptr(), _dtype_code(t), t.shape, t.stride())
+
+
+def _ref(d):
+    return None if d is None else ctypes.byref(d)
 
 
 def _stream_handle(stream) -> Optional[int]:
@@ -160,18 +196,17 @@ def _dev_i32(t, name: str):
     return t
 
 
-def fa_varlen_tile_map(cu_seqlens_q, block_m: int, blk_start=None, stream=None):
-    """int32 [batch+1] work-item map of the ragged batch (device tensor)."""
+def fa_varlen_tile_map(cu_seqlens_q, max_seqlen_q: int, head_dim: int, dtype: int, blk_start=None, stream=None):
+    """int32 [batch+1] work-item map of the ragged batch for (head_dim, dtype) (device tensor)."""
     torch = _torch()
     cu = _dev_i32(cu_seqlens_q, "cu_seqlens_q")
     batch = cu.numel() - 1
     if blk_start is None:
         blk_start = torch.empty(batch + 1, dtype=torch.int32, device=cu.device)
     _dev_i32(blk_start, "blk_start")
-    if blk_start.numel() != batch + 1:
-        raise ValueError("blk_start must have batch+1 entries")
-    _check(load_library().fa_varlen_tile_map(cu.data_ptr(), batch, int(block_m), blk_start.data_ptr(),
-                                             _stream_handle(stream)), "fa_varlen_tile_map")
+    d_cu, d_blk = desc(cu), desc(blk_start)
+    _check(load_library().fa_varlen_tile_map(ctypes.byref(d_cu), int(max_seqlen_q), int(head_dim), int(dtype),
+                                             ctypes.byref(d_blk), _stream_handle(stream)), "fa_varlen_tile_map")
     return blk_start
 
 
@@ -184,7 +219,7 @@ def _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse):
         raise ValueError("the key/value head count must divide the query head count")
     if not (q.is_cuda and k.is_cuda and v.is_cuda) or q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k, v must be CUDA tensors of one dtype")
-    dt = _dtype_code(q)
+    _dtype_code(q)
     cu_q = _dev_i32(cu_seqlens_q, "cu_seqlens_q")
     cu_k = _dev_i32(cu_seqlens_k, "cu_seqlens_k")
     if cu_q.numel() != cu_k.numel():
@@ -196,11 +231,11 @@ def _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse):
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
-    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor of shape [H, total_q]")
-    return q, k, v, cu_q, cu_k, float(softmax_scale), out, lse, dt
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous CUDA tensor shaped and typed like q")
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 CUDA tensor of shape [H, total_q]")
+    return q, k, v, cu_q, cu_k, float(softmax_scale), out, lse
 
 
 def fa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
@@ -213,13 +248,11 @@ def fa_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_se
     cu_seqlens_* int32 [batch+1] on the device.  Returns (out, lse) with
     out shaped like q and lse float32 [H, total_q].
     """
-    q, k, v, cu_q, cu_k, scale, out, lse, dt = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale,
-                                                        out, lse)
-    total_q, H, D = q.shape
-    st = load_library().fa_varlen_fwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), int(max_seqlen_q),
-        int(max_seqlen_k), scale, int(bool(causal)), out.data_ptr(), lse.data_ptr(), cu_q.numel() - 1,
-        total_q, k.shape[0], H, k.shape[1], D, dt, _stream_handle(stream))
+    q, k, v, cu_q, cu_k, scale, out, lse = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse)
+    ds = [desc(x) for x in (q, k, v, cu_q, cu_k, out, lse)]
+    st = load_library().fa_varlen_fwd(*map(ctypes.byref, ds[:5]), int(max_seqlen_q), int(max_seqlen_k), scale,
+                                      int(bool(causal)), ctypes.byref(ds[5]), ctypes.byref(ds[6]),
+                                      _stream_handle(stream))
     _check(st, "fa_varlen_fwd")
     return out, lse
 
@@ -228,14 +261,12 @@ def fa_varlen_fwd_mapped(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                          blk_start, softmax_scale: Optional[float] = None, causal: bool = False, out=None,
                          lse=None, stream=None):
     """fa_varlen_fwd with a work-item map built by fa_varlen_tile_map."""
-    q, k, v, cu_q, cu_k, scale, out, lse, dt = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale,
-                                                        out, lse)
+    q, k, v, cu_q, cu_k, scale, out, lse = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse)
     _dev_i32(blk_start, "blk_start")
-    total_q, H, D = q.shape
-    st = load_library().fa_varlen_fwd_mapped(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), int(max_seqlen_q),
-        int(max_seqlen_k), scale, int(bool(causal)), out.data_ptr(), lse.data_ptr(), cu_q.numel() - 1,
-        total_q, k.shape[0], H, k.shape[1], D, dt, blk_start.data_ptr(), _stream_handle(stream))
+    ds = [desc(x) for x in (q, k, v, cu_q, cu_k, out, lse, blk_start)]
+    st = load_library().fa_varlen_fwd_mapped(*map(ctypes.byref, ds[:5]), int(max_seqlen_q), int(max_seqlen_k),
+                                             scale, int(bool(causal)), ctypes.byref(ds[5]), ctypes.byref(ds[6]),
+                                             ctypes.byref(ds[7]), _stream_handle(stream))
     _check(st, "fa_varlen_fwd_mapped")
     return out, lse
 
@@ -248,6 +279,15 @@ def fa_varlen_bwd_workspace_size(batch: int, total_q: int, num_heads: int, head_
     return n.value
 
 
+def _workspace(workspace, need: int, device):
+    torch = _torch()
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not workspace.is_cuda:
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    return workspace
+
+
 def fa_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                   softmax_scale: Optional[float] = None, causal: bool = False, dq=None, dk=None, dv=None,
                   workspace=None, stream=None):
@@ -258,8 +298,7 @@ def fa_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
     fa_varlen_bwd_workspace_size bytes) is allocated when not given.
     """
     torch = _torch()
-    q, k, v, cu_q, cu_k, scale, out, lse, dt = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale,
-                                                        out, lse)
+    q, k, v, cu_q, cu_k, scale, out, lse = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse)
     dout = dout.contiguous()
     if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_cuda:
         raise ValueError("dout must be a CUDA tensor shaped and typed like q")
@@ -269,18 +308,13 @@ def fa_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like its input")
-    need = fa_varlen_bwd_workspace_size(batch, total_q, H, D)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not workspace.is_cuda:
-        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
-    st = load_library().fa_varlen_bwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-        cu_q.data_ptr(), cu_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale, int(bool(causal)),
-        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), batch, total_q, k.shape[0], H, k.shape[1], D, dt,
-        workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous CUDA tensor shaped and typed like its input")
+    workspace = _workspace(workspace, fa_varlen_bwd_workspace_size(batch, total_q, H, D), q.device)
+    ds = [desc(x) for x in (q, k, v, out, dout, lse, cu_q, cu_k, dq, dk, dv)]
+    st = load_library().fa_varlen_bwd(*map(ctypes.byref, ds[:8]), int(max_seqlen_q), int(max_seqlen_k), scale,
+                                      int(bool(causal)), *map(ctypes.byref, ds[8:]), workspace.data_ptr(),
+                                      workspace.numel(), _stream_handle(stream))
     _check(st, "fa_varlen_bwd")
     return dq, dk, dv
 
@@ -313,7 +347,7 @@ def fa_varlen_fwd_kvcache(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, max_seql
         raise ValueError("the key/value head count must divide the query head count")
     if q.dtype != k_cache.dtype or q.dtype != v_cache.dtype or not (q.is_cuda and k_cache.is_cuda):
         raise TypeError("q and the caches must be CUDA tensors of one dtype")
-    dt = _dtype_code(q)
+    _dtype_code(q)
     cu_q = _dev_i32(cu_seqlens_q, "cu_seqlens_q")
     batch = cu_q.numel() - 1
     sk = _dev_i32(seqlens_k, "seqlens_k")
@@ -324,26 +358,28 @@ def fa_varlen_fwd_kvcache(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, max_seql
         lp = _dev_i32(leftpad_k, "leftpad_k")
         if lp.numel() != batch:
             raise ValueError("leftpad_k must have one entry per sequence")
-    bps = 0
     if block_table is not None:
         if not (block_table.is_cuda and block_table.dtype == torch.int32 and block_table.dim() == 2
                 and block_table.shape[0] == batch and block_table.is_contiguous()):
             raise TypeError("block_table must be a contiguous int32 CUDA tensor [batch, blocks_per_seq]")
-        bps = block_table.shape[1]
     total_q, H, D = q.shape
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
-    if workspace is None:
-        workspace = torch.empty(max(fa_varlen_kvcache_workspace_size(total_q, H, D, num_splits), 1),
-                                dtype=torch.uint8, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous CUDA tensor shaped and typed like q")
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 CUDA tensor of shape [H, total_q]")
+    workspace = _workspace(workspace, fa_varlen_kvcache_workspace_size(total_q, H, D, num_splits), q.device)
+    blocks, rows, Hk = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    # the caches go over the ABI with their block and row dimensions merged
+    kc, vc = k_cache.view(blocks * rows, Hk, D), v_cache.view(blocks * rows, Hk, D)
+    ds = [desc(x) for x in (q, kc, vc, cu_q, sk, lp, block_table, out, lse)]
     st = load_library().fa_varlen_fwd_kvcache(
-        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_q.data_ptr(), sk.data_ptr(),
-        None if lp is None else lp.data_ptr(), None if block_table is None else block_table.data_ptr(),
-        int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale), int(bool(causal)), out.data_ptr(),
-        lse.data_ptr(), batch, total_q, k_cache.shape[0], k_cache.shape[1], bps, H, k_cache.shape[2], D, dt,
-        int(num_splits), workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
+        *map(_ref, ds[:7]), int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale), int(bool(causal)),
+        int(rows), int(num_splits), _ref(ds[7]), _ref(ds[8]), workspace.data_ptr(), workspace.numel(),
+        _stream_handle(stream))
     _check(st, "fa_varlen_fwd_kvcache")
     return out, lse
 
@@ -356,7 +392,8 @@ def fa_varlen_check_cu_seqlens(cu_seqlens_q, cu_seqlens_k, total_q: int, total_k
     cu_k = _dev_i32(cu_seqlens_k, "cu_seqlens_k")
     if flags is None:
         flags = torch.empty(1, dtype=torch.int32, device=cu_q.device)
+    d = [desc(x) for x in (cu_q, cu_k, flags)]
     _check(load_library().fa_varlen_check_cu_seqlens(
-        cu_q.data_ptr(), cu_k.data_ptr(), cu_q.numel() - 1, int(total_q), int(total_k), int(max_seqlen_q),
-        int(max_seqlen_k), flags.data_ptr(), _stream_handle(stream)), "fa_varlen_check_cu_seqlens")
+        ctypes.byref(d[0]), ctypes.byref(d[1]), int(total_q), int(total_k), int(max_seqlen_q), int(max_seqlen_k),
+        ctypes.byref(d[2]), _stream_handle(stream)), "fa_varlen_check_cu_seqlens")
     return flags

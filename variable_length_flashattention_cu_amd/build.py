@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_varlen.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+# measurement aid (include/fa_probe.h): the matrix-core ceiling probe
+PROBE_PATH = os.path.join(PKG_DIR, "libfa_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "fa_probe.hip")]
 
 SOURCES = [os.path.join(CSRC, "fa_varlen_kernels.hip"), os.path.join(CSRC, "fa_varlen_bwd.hip"),
            os.path.join(CSRC, "fa_varlen_decode.hip"), os.path.join(CSRC, "fa_varlen_api.cpp")]
@@ -59,11 +62,25 @@ def run(cmd: list, verbose: bool) -> None:
 
 
 def build(verbose: bool = False, asm_dir: str | None = None) -> str:
-    tmp = LIB_PATH + ".tmp"
+    """Build libfa_varlen.so and libfa_probe.so; returns the attention library's path."""
+    _link(LIB_PATH, SOURCES, verbose)
+    _link(PROBE_PATH, PROBE_SOURCES, verbose)
+    if asm_dir:
+        os.makedirs(asm_dir, exist_ok=True)
+        for src in SOURCES + PROBE_SOURCES:
+            if src.endswith(".hip"):
+                asm = os.path.join(asm_dir, os.path.basename(src)[:-4] + ".s")
+                cmd = [hipcc()] + common_flags() + source_flags(src) + ["--cuda-device-only", "-S", "-o", asm, src]
+                subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return LIB_PATH
+
+
+def _link(lib_path: str, sources: list, verbose: bool) -> None:
+    tmp = lib_path + ".tmp"
     objs = []
     procs = []
-    for src in SOURCES:  # one object per source (own options), compiled in parallel
-        obj = LIB_PATH + "." + os.path.basename(src) + ".o"
+    for src in sources:  # one object per source (own options), compiled in parallel
+        obj = lib_path + "." + os.path.basename(src) + ".o"
         cmd = [hipcc()] + common_flags() + source_flags(src) + ["-c", "-o", obj, src]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -80,15 +97,7 @@ def build(verbose: bool = False, asm_dir: str | None = None) -> str:
     run([hipcc()] + common_flags() + ["-shared", "-o", tmp] + objs, verbose)
     for obj in objs:
         os.remove(obj)
-    os.replace(tmp, LIB_PATH)
-    if asm_dir:
-        os.makedirs(asm_dir, exist_ok=True)
-        for src in SOURCES:
-            if src.endswith(".hip"):
-                asm = os.path.join(asm_dir, os.path.basename(src)[:-4] + ".s")
-                cmd = [hipcc()] + common_flags() + source_flags(src) + ["--cuda-device-only", "-S", "-o", asm, src]
-                subprocess.run(cmd, check=True, capture_output=True, text=True)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
 
 
 def main() -> None:

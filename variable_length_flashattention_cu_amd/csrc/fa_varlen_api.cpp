@@ -1,10 +1,11 @@
-// fa_varlen_api.cpp -- the C ABI declared in include/fa_varlen.h: argument
-// validation, launch sizing and the kernel launches of the forward and
-// backward passes.  Every check runs on the host before any HIP call, so a
-// validation error launches nothing.
+// fa_varlen_api.cpp -- the C ABI declared in include/fa_varlen.h: descriptor
+// validation, launch sizing and the kernel launches of the forward pass, the
+// backward pass and attention against a key/value cache.  Every check runs on
+// the host before any HIP call, so a validation error launches nothing.
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -14,48 +15,202 @@
 namespace {
 
 constexpr double kLog2e = 1.4426950408889634074;
-// Compute units of an MI355X; with at most kPairLimit workgroups per CU the
-// causal forward pairs query blocks (see run_work in the kernels).
-constexpr int64_t kComputeUnits = 256;
+// With at most kPairLimit workgroups per compute unit the causal forward pass
+// pairs query blocks (see run_work in the kernels).
 constexpr int64_t kPairLimit = 8;
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// ---------------------------------------------------------------------------
+// device properties
+// ---------------------------------------------------------------------------
+// Compute units of the current device, queried once per device and cached
+// (the query is a runtime call; the value never changes).
+int compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || n < 1)
+    n = 256;  // MI355X; only sizes the schedule, never correctness
+  if (dev >= 0) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// ---------------------------------------------------------------------------
+// descriptors
+// ---------------------------------------------------------------------------
+int elem_code(int32_t dtype) {
+  switch (dtype) {
+    case FA_DTYPE_F32: return fa::kElemF32;
+    case FA_DTYPE_BF16: return fa::kElemBF16;
+    case FA_DTYPE_F16: return fa::kElemF16;
+    default: return -1;
+  }
+}
+int elem_size(int32_t dtype) { return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16 ? 2 : 4; }
+
+bool rank_ok(const fa_tensor& t, int ndim) {
+  if (t.ndim != ndim) return false;
+  for (int i = 0; i < ndim; ++i)
+    if (t.shape[i] < 0) return false;
+  return true;
+}
+
+int64_t numel(const fa_tensor& t) {
+  int64_t n = 1;
+  for (int i = 0; i < t.ndim; ++i) n *= t.shape[i];
+  return n;
+}
+
+// Row-major contiguity; the stride of a dimension of extent <= 1 is not used
+// to address anything and is not looked at.
+bool contiguous(const fa_tensor& t) {
+  if (numel(t) == 0) return true;
+  int64_t expect = 1;
+  for (int i = t.ndim - 1; i >= 0; --i) {
+    if (t.shape[i] > 1 && t.stride[i] != expect) return false;
+    expect *= t.shape[i];
+  }
+  return true;
+}
+
+bool data_ok(const fa_tensor& t) { return t.data != nullptr || numel(t) == 0; }
+
+bool same_shape(const fa_tensor& a, const fa_tensor& b) {
+  if (a.ndim != b.ndim) return false;
+  for (int i = 0; i < a.ndim; ++i)
+    if (a.shape[i] != b.shape[i]) return false;
+  return true;
+}
+
+// head_dim support per entry point
+bool fwd_head_dim(int elem, int64_t d) {
+  return d == 64 || d == 96 || d == 128 || (d == 256 && elem != fa::kElemF32);
+}
+bool bwd_head_dim(int, int64_t d) { return d == 64 || d == 128; }
+
+// ---------------------------------------------------------------------------
+// the attention problem shared by the forward and backward entry points
+// ---------------------------------------------------------------------------
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t batch, total_q, total_k, heads, heads_k, head_dim, elem, dtype;
+};
+
+// q, k, v, offsets, out, lse, max_seqlen, scale and causal, in the documented
+// order of status codes.  `extra` holds further tensors shaped and typed like
+// q (first n_extra_q) or like k (the rest), checked with them.
+int check_problem(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* cu_q,
+                  const fa_tensor* cu_k, const fa_tensor* out, const fa_tensor* lse, int32_t max_q, int32_t max_k,
+                  float scale, int32_t causal, bool (*head_dim_ok)(int, int64_t), const fa_tensor* const* extra,
+                  int n_extra, int n_extra_q, Problem* p) {
+  if (!q || !k || !v || !cu_q || !cu_k || !out || !lse) return FA_ERR_NULL;
+  for (int i = 0; i < n_extra; ++i)
+    if (!extra[i]) return FA_ERR_NULL;
+  // element types
+  const int elem = elem_code(q->dtype);
+  if (elem < 0 || k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype) return FA_ERR_DTYPE;
+  for (int i = 0; i < n_extra; ++i)
+    if (extra[i]->dtype != q->dtype) return FA_ERR_DTYPE;
+  if (cu_q->dtype != FA_DTYPE_I32 || cu_k->dtype != FA_DTYPE_I32 || lse->dtype != FA_DTYPE_F32) return FA_ERR_DTYPE;
+  // ranks, then head_dim, then the remaining shape relations
+  if (!rank_ok(*q, 3) || !rank_ok(*k, 3) || !rank_ok(*v, 3) || !rank_ok(*out, 3) || !rank_ok(*cu_q, 1) ||
+      !rank_ok(*cu_k, 1) || !rank_ok(*lse, 2))
+    return FA_ERR_SHAPE;
+  for (int i = 0; i < n_extra; ++i)
+    if (!rank_ok(*extra[i], 3)) return FA_ERR_SHAPE;
+  const int64_t D = q->shape[2];
+  if (!head_dim_ok(elem, D)) return FA_ERR_HEAD_DIM;
+  const int64_t Tq = q->shape[0], H = q->shape[1], Tk = k->shape[0], Hk = k->shape[1];
+  if (H < 1 || Hk < 1 || H % Hk != 0 || k->shape[2] != D || !same_shape(*k, *v) || !same_shape(*q, *out))
+    return FA_ERR_SHAPE;
+  for (int i = 0; i < n_extra; ++i)
+    if (!same_shape(*extra[i], i < n_extra_q ? *q : *k)) return FA_ERR_SHAPE;
+  if (lse->shape[0] != H || lse->shape[1] != Tq) return FA_ERR_SHAPE;
+  if (cu_q->shape[0] < 1 || cu_k->shape[0] != cu_q->shape[0]) return FA_ERR_SHAPE;
+  if (max_q < 0 || max_k < 0 || max_q > Tq || max_k > Tk) return FA_ERR_SHAPE;
+  // layout, then data pointers
+  if (!contiguous(*q) || !contiguous(*k) || !contiguous(*v) || !contiguous(*out) || !contiguous(*lse) ||
+      !contiguous(*cu_q) || !contiguous(*cu_k))
+    return FA_ERR_LAYOUT;
+  for (int i = 0; i < n_extra; ++i)
+    if (!contiguous(*extra[i])) return FA_ERR_LAYOUT;
+  if (!data_ok(*q) || !data_ok(*k) || !data_ok(*v) || !data_ok(*out) || !data_ok(*lse) || !cu_q->data ||
+      !cu_k->data)
+    return FA_ERR_NULL;
+  for (int i = 0; i < n_extra; ++i)
+    if (!data_ok(*extra[i])) return FA_ERR_NULL;
+  // scalar arguments
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  // alignment
+  if (!aligned(q->data, 16) || !aligned(k->data, 16) || !aligned(v->data, 16) || !aligned(out->data, 16))
+    return FA_ERR_ALIGN;
+  for (int i = 0; i < n_extra; ++i)
+    if (!aligned(extra[i]->data, 16)) return FA_ERR_ALIGN;
+  if (!aligned(lse->data, 4) || !aligned(cu_q->data, 4) || !aligned(cu_k->data, 4)) return FA_ERR_ALIGN;
+  // sizes one launch addresses: 32-bit row counts, 32-bit in-tile byte offsets
+  if (Tq > INT32_MAX || Tk > INT32_MAX || H > INT32_MAX || cu_q->shape[0] - 1 > INT32_MAX) return FA_ERR_TOO_LARGE;
+  if (H * D > (int64_t{1} << 22) || Hk * D > (int64_t{1} << 22)) return FA_ERR_TOO_LARGE;
+  p->q = q->data;
+  p->k = k->data;
+  p->v = v->data;
+  p->out = out->data;
+  p->lse = static_cast<float*>(lse->data);
+  p->cu_q = static_cast<const int32_t*>(cu_q->data);
+  p->cu_k = static_cast<const int32_t*>(cu_k->data);
+  p->batch = (int32_t)(cu_q->shape[0] - 1);
+  p->total_q = (int32_t)Tq;
+  p->total_k = (int32_t)Tk;
+  p->heads = (int32_t)H;
+  p->heads_k = (int32_t)Hk;
+  p->head_dim = (int32_t)D;
+  p->elem = elem;
+  p->dtype = q->dtype;
+  return FA_OK;
+}
+
+// An int32 vector [n] (offsets, lengths, maps, flags).
+int check_i32_vector(const fa_tensor* t, int64_t n) {
+  if (!t) return FA_ERR_NULL;
+  if (t->dtype != FA_DTYPE_I32) return FA_ERR_DTYPE;
+  if (!rank_ok(*t, 1) || t->shape[0] != n) return FA_ERR_SHAPE;
+  if (!contiguous(*t)) return FA_ERR_LAYOUT;
+  if (!data_ok(*t)) return FA_ERR_NULL;
+  if (!aligned(t->data, 4)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// forward launch sizing
+// ---------------------------------------------------------------------------
 struct Plan {
   fa::TileConfig tc;
   int64_t tmax;
   int64_t grid;
 };
 
-// Validation shared by fa_varlen_fwd and fa_varlen_fwd_mapped.
-bool known_dtype(int32_t dtype) {
-  return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16;
-}
-
-int validate(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
-             int32_t max_q, int32_t max_k, float scale, int32_t causal, const void* out, const float* lse,
-             int32_t batch, int32_t total_q, int32_t total_k, int32_t heads, int32_t heads_k, int32_t head_dim,
-             int32_t dtype, Plan* plan) {
-  if (!q || !k || !v || !cu_q || !cu_k || !out || !lse) return FA_ERR_NULL;
-  if (!known_dtype(dtype)) return FA_ERR_DTYPE;
-  const fa::TileConfig tc = fa::tile_config(dtype, head_dim);
-  if (tc.block_m == 0) return FA_ERR_HEAD_DIM;
-  if (batch < 0 || total_q < 0 || total_k < 0 || heads < 1 || max_q < 0 || max_k < 0) return FA_ERR_SHAPE;
-  if (heads_k < 1 || heads % heads_k != 0) return FA_ERR_SHAPE;
-  if (max_q > total_q || max_k > total_k) return FA_ERR_SHAPE;
-  // In-tile byte offsets are 32-bit: bound the token row size.
-  if ((int64_t)heads * head_dim > (int64_t{1} << 22)) return FA_ERR_TOO_LARGE;
-  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
-  if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_ALIGN;
-  if (!aligned(lse, 4) || !aligned(cu_q, 4) || !aligned(cu_k, 4)) return FA_ERR_ALIGN;
+int plan_fwd(const Problem& p, int32_t max_q, Plan* plan) {
+  const fa::TileConfig tc = fa::tile_config(p.elem, p.head_dim);
   // Upper bound on the number of work items: sum_b ceil(Lq_b / BM) is at most
   // batch * ceil(max_seqlen_q / BM) and at most ceil(total_q / BM) + batch - 1.
   const int64_t bm = tc.block_m;
-  const int64_t by_max = (int64_t)batch * ((max_q + bm - 1) / bm);
-  const int64_t by_total = (total_q + bm - 1) / bm + (batch > 0 ? batch - 1 : 0);
+  const int64_t by_max = (int64_t)p.batch * ((max_q + bm - 1) / bm);
+  const int64_t by_total = (p.total_q + bm - 1) / bm + (p.batch > 0 ? p.batch - 1 : 0);
   const int64_t tmax = by_max < by_total ? by_max : by_total;
-  const int64_t work = tmax * heads;
+  const int64_t work = tmax * p.heads;
   const int64_t grid = (work + 7) / 8 * 8;
   if (grid > INT32_MAX || tmax > INT32_MAX) return FA_ERR_TOO_LARGE;
   plan->tc = tc;
@@ -64,32 +219,41 @@ int validate(const void* q, const void* k, const void* v, const int32_t* cu_q, c
   return FA_OK;
 }
 
-fa::FwdArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
-                      float scale, int32_t causal, void* out, float* lse, int32_t batch, int32_t total_q,
-                      int32_t heads, int32_t heads_k, int32_t head_dim, const int32_t* blk_start,
-                      const Plan& plan) {
+fa::FwdArgs make_fwd_args(const Problem& p, float scale, int32_t causal, const int32_t* blk_start, const Plan& plan) {
   fa::FwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.lse = lse;
-  a.cu_q = cu_q;
-  a.cu_k = cu_k;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.out = p.out;
+  a.lse = p.lse;
+  a.cu_q = p.cu_q;
+  a.cu_k = p.cu_k;
   a.blk_start = blk_start;
-  a.row_stride = (int64_t)heads * head_dim;
-  a.kv_row_stride = (int64_t)heads_k * head_dim;
-  a.head_group = heads / heads_k;
+  a.row_stride = (int64_t)p.heads * p.head_dim;
+  a.kv_row_stride = (int64_t)p.heads_k * p.head_dim;
+  a.head_group = p.heads / p.heads_k;
   a.scale_log2 = (float)((double)scale * kLog2e);
-  a.batch = batch;
+  a.batch = p.batch;
   a.tmax = (int32_t)plan.tmax;
-  a.n_work = (int32_t)(plan.tmax * heads);
-  a.total_q = total_q;
-  a.pair_blocks = (causal && plan.tmax * heads <= kPairLimit * kComputeUnits) ? 1 : 0;
+  a.n_work = (int32_t)(plan.tmax * p.heads);
+  a.total_q = p.total_q;
+  a.pair_blocks = (causal && plan.tmax * p.heads <= kPairLimit * compute_units()) ? 1 : 0;
   return a;
 }
 
-// Backward workspace: dq accumulator, row terms, key-block map (256-byte aligned parts).
+// The forward pass with the map in `blk_start` (built by the caller, or by
+// fwd_with_map below).
+int launch_fwd_mapped(const Problem& p, const Plan& plan, float scale, int32_t causal, const int32_t* blk_start,
+                      hipStream_t s) {
+  if (plan.grid == 0) return FA_OK;  // no query rows: nothing to compute
+  const fa::FwdArgs a = make_fwd_args(p, scale, causal, blk_start, plan);
+  if (fa::launch_fwd(p.elem, p.head_dim, causal != 0, (int)plan.grid, a, s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// backward workspace
+// ---------------------------------------------------------------------------
 struct BwdLayout {
   size_t dq_acc, drow, blk, total;
 };
@@ -105,7 +269,9 @@ BwdLayout bwd_layout(int64_t batch, int64_t total_q, int64_t heads, int64_t head
   return l;
 }
 
-// Key/value-cache attention: split count and workspace.
+// ---------------------------------------------------------------------------
+// key/value-cache attention: split count and workspace
+// ---------------------------------------------------------------------------
 constexpr int kMaxSplits = 64;
 
 int64_t dec_parts(int32_t num_splits) { return (int64_t)(num_splits > 0 ? num_splits : kMaxSplits) * fa::decode_waves(); }
@@ -120,7 +286,7 @@ size_t dec_workspace(int64_t total_q, int64_t heads, int64_t head_dim, int32_t n
 // flight), at least one 64-key tile per wavefront of a split.
 int32_t auto_splits(int64_t batch, int64_t kv_heads, int64_t max_k) {
   const int64_t items = batch * kv_heads;
-  int64_t s = items > 0 ? (8 * kComputeUnits + items - 1) / items : 1;
+  int64_t s = items > 0 ? (8 * (int64_t)compute_units() + items - 1) / items : 1;
   const int64_t by_keys = (max_k + 64 * 4 - 1) / (64 * 4);  // a 64-key tile per wavefront
   if (s > by_keys) s = by_keys;
   if (s > kMaxSplits) s = kMaxSplits;
@@ -134,83 +300,93 @@ extern "C" {
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
-    case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_DTYPE: return "unsupported dtype (expected FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16)";
+    case FA_ERR_NULL: return "a required tensor descriptor or pointer is NULL";
+    case FA_ERR_DTYPE: return "unsupported element type (attention tensors: FA_DTYPE_F32, FA_DTYPE_BF16 or "
+                              "FA_DTYPE_F16 as the entry point allows; offsets int32; lse float32)";
     case FA_ERR_SHAPE:
-      return "invalid sizes (negative, zero heads, key/value heads not dividing the query heads, or max_seqlen "
-             "above the row count)";
-    case FA_ERR_HEAD_DIM: return "unsupported head_dim (64, 96, 128; 256 with bf16/fp16)";
-    case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse and offsets 4 bytes)";
-    case FA_ERR_ARG: return "invalid argument (softmax_scale must be finite and > 0, causal 0 or 1, block_m 1..4096)";
+      return "invalid shape (wrong rank, negative or inconsistent sizes, key/value heads not dividing the query "
+             "heads, or max_seqlen above the row count)";
+    case FA_ERR_HEAD_DIM: return "unsupported head_dim for this dtype and entry point";
+    case FA_ERR_LAYOUT: return "tensor not contiguous in row-major order";
+    case FA_ERR_ALIGN: return "misaligned data (attention tensors need 16 bytes, lse and int32 arrays 4 bytes)";
+    case FA_ERR_ARG: return "invalid argument (softmax_scale must be finite and > 0, causal 0 or 1, num_splits "
+                            "0..64)";
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_TOO_LARGE: return "problem too large for one launch";
-    case FA_ERR_WORKSPACE: return "backward workspace missing or smaller than fa_varlen_bwd_workspace_size";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than the size function reports";
     default: return "unknown status";
   }
 }
 
 int fa_varlen_block_sizes(int32_t head_dim, int32_t dtype, int32_t* block_m, int32_t* block_n) {
   if (!block_m || !block_n) return FA_ERR_NULL;
-  if (!known_dtype(dtype)) return FA_ERR_DTYPE;
-  const fa::TileConfig tc = fa::tile_config(dtype, head_dim);
-  if (tc.block_m == 0) return FA_ERR_HEAD_DIM;
+  const int elem = elem_code(dtype);
+  if (elem < 0) return FA_ERR_DTYPE;
+  if (!fwd_head_dim(elem, head_dim)) return FA_ERR_HEAD_DIM;
+  const fa::TileConfig tc = fa::tile_config(elem, head_dim);
   *block_m = tc.block_m;
   *block_n = tc.block_n;
   return FA_OK;
 }
 
-int fa_varlen_tile_map(const int32_t* cu_seqlens_q, int32_t batch, int32_t block_m, int32_t* blk_start,
-                       void* stream) {
-  if (!cu_seqlens_q || !blk_start) return FA_ERR_NULL;
-  if (batch < 0) return FA_ERR_SHAPE;
-  if (block_m < 1 || block_m > 4096) return FA_ERR_ARG;
-  if (!aligned(cu_seqlens_q, 4) || !aligned(blk_start, 4)) return FA_ERR_ALIGN;
-  if (fa::launch_tile_map(cu_seqlens_q, batch, block_m, blk_start, (hipStream_t)stream) != hipSuccess)
-    return FA_ERR_HIP;
-  return FA_OK;
-}
-
-int fa_varlen_fwd_mapped(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
-                         const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                         float softmax_scale, int32_t causal, void* out, float* lse, int32_t batch,
-                         int32_t total_q, int32_t total_k, int32_t num_heads, int32_t num_heads_k,
-                         int32_t head_dim, int32_t dtype, const int32_t* blk_start, void* stream) {
-  Plan plan;
-  int st = validate(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
-                    out, lse, batch, total_q, total_k, num_heads, num_heads_k, head_dim, dtype, &plan);
+int fa_varlen_tile_map(const fa_tensor* cu_seqlens_q, int32_t max_seqlen_q, int32_t head_dim, int32_t dtype,
+                       fa_tensor* blk_start_out, hipStream_t stream) {
+  if (!cu_seqlens_q || !blk_start_out) return FA_ERR_NULL;
+  const int elem = elem_code(dtype);
+  if (elem < 0) return FA_ERR_DTYPE;
+  if (!fwd_head_dim(elem, head_dim)) return FA_ERR_HEAD_DIM;
+  if (cu_seqlens_q->dtype != FA_DTYPE_I32) return FA_ERR_DTYPE;
+  if (!rank_ok(*cu_seqlens_q, 1) || cu_seqlens_q->shape[0] < 1) return FA_ERR_SHAPE;
+  const int64_t batch = cu_seqlens_q->shape[0] - 1;
+  if (max_seqlen_q < 0) return FA_ERR_SHAPE;
+  int st = check_i32_vector(cu_seqlens_q, batch + 1);
   if (st != FA_OK) return st;
-  if (!blk_start) return FA_ERR_NULL;
-  if (!aligned(blk_start, 4)) return FA_ERR_ALIGN;
-  if (plan.grid == 0) return FA_OK;  // no query rows: nothing to compute
-  const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, causal, out, lse, batch,
-                                  total_q, num_heads, num_heads_k, head_dim, blk_start, plan);
-  if (fa::launch_fwd(dtype, head_dim, causal != 0, (int)plan.grid, a, (hipStream_t)stream) != hipSuccess)
+  st = check_i32_vector(blk_start_out, batch + 1);
+  if (st != FA_OK) return st;
+  if (batch > INT32_MAX - 1) return FA_ERR_TOO_LARGE;
+  const fa::TileConfig tc = fa::tile_config(elem, head_dim);
+  if (fa::launch_tile_map(static_cast<const int32_t*>(cu_seqlens_q->data), (int)batch, tc.block_m,
+                          static_cast<int32_t*>(blk_start_out->data), stream) != hipSuccess)
     return FA_ERR_HIP;
   return FA_OK;
 }
 
-int fa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
-                  const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
-                  int32_t causal, void* out, float* lse, int32_t batch, int32_t total_q, int32_t total_k,
-                  int32_t num_heads, int32_t num_heads_k, int32_t head_dim, int32_t dtype, void* stream) {
+int fa_varlen_fwd_mapped(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* cu_seqlens_q,
+                         const fa_tensor* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                         float softmax_scale, int32_t causal, fa_tensor* out, fa_tensor* lse,
+                         const fa_tensor* blk_start, hipStream_t stream) {
+  Problem p;
+  int st = check_problem(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, max_seqlen_q, max_seqlen_k, softmax_scale,
+                         causal, fwd_head_dim, nullptr, 0, 0, &p);
+  if (st != FA_OK) return st;
+  st = check_i32_vector(blk_start, (int64_t)p.batch + 1);
+  if (st != FA_OK) return st;
   Plan plan;
-  int st = validate(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
-                    out, lse, batch, total_q, total_k, num_heads, num_heads_k, head_dim, dtype, &plan);
+  st = plan_fwd(p, max_seqlen_q, &plan);
+  if (st != FA_OK) return st;
+  return launch_fwd_mapped(p, plan, softmax_scale, causal, static_cast<const int32_t*>(blk_start->data), stream);
+}
+
+int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* cu_seqlens_q,
+                  const fa_tensor* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                  int32_t causal, fa_tensor* out, fa_tensor* lse, hipStream_t stream) {
+  Problem p;
+  int st = check_problem(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, max_seqlen_q, max_seqlen_k, softmax_scale,
+                         causal, fwd_head_dim, nullptr, 0, 0, &p);
+  if (st != FA_OK) return st;
+  Plan plan;
+  st = plan_fwd(p, max_seqlen_q, &plan);
   if (st != FA_OK) return st;
   if (plan.grid == 0) return FA_OK;
-  hipStream_t s = (hipStream_t)stream;
   int32_t* blk_start = nullptr;
-  if (hipMallocAsync((void**)&blk_start, sizeof(int32_t) * ((size_t)batch + 1), s) != hipSuccess)
+  if (hipMallocAsync((void**)&blk_start, sizeof(int32_t) * ((size_t)p.batch + 1), stream) != hipSuccess)
     return FA_ERR_HIP;
   int rc = FA_OK;
-  if (fa::launch_tile_map(cu_seqlens_q, batch, plan.tc.block_m, blk_start, s) != hipSuccess) {
+  if (fa::launch_tile_map(p.cu_q, p.batch, plan.tc.block_m, blk_start, stream) != hipSuccess)
     rc = FA_ERR_HIP;
-  } else {
-    const fa::FwdArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, causal, out, lse, batch,
-                                    total_q, num_heads, num_heads_k, head_dim, blk_start, plan);
-    if (fa::launch_fwd(dtype, head_dim, causal != 0, (int)plan.grid, a, s) != hipSuccess) rc = FA_ERR_HIP;
-  }
-  if (hipFreeAsync(blk_start, s) != hipSuccess) rc = FA_ERR_HIP;
+  else
+    rc = launch_fwd_mapped(p, plan, softmax_scale, causal, blk_start, stream);
+  if (hipFreeAsync(blk_start, stream) != hipSuccess) rc = FA_ERR_HIP;
   return rc;
 }
 
@@ -222,72 +398,72 @@ int fa_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t num_hea
   return FA_OK;
 }
 
-int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
-                  int32_t max_seqlen_k, float softmax_scale, int32_t causal, void* dq, void* dk, void* dv,
-                  int32_t batch, int32_t total_q, int32_t total_k, int32_t num_heads, int32_t num_heads_k,
-                  int32_t head_dim, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
-  Plan plan;  // the forward's checks cover q, k, v, offsets, out, lse, sizes, scale, causal
-  int st = validate(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal, out,
-                    lse, batch, total_q, total_k, num_heads, num_heads_k, head_dim, dtype, &plan);
+int fa_varlen_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                  const fa_tensor* dout, const fa_tensor* lse, const fa_tensor* cu_seqlens_q,
+                  const fa_tensor* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                  int32_t causal, fa_tensor* dq, fa_tensor* dk, fa_tensor* dv, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  // dout and dq are shaped like q, dk and dv like k
+  const fa_tensor* extra[4] = {dout, dq, dk, dv};
+  Problem p;
+  int st = check_problem(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, max_seqlen_q, max_seqlen_k, softmax_scale,
+                         causal, bwd_head_dim, extra, 4, 2, &p);
   if (st != FA_OK) return st;
-  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_DTYPE;
-  const int bn = fa::bwd_block_n(dtype, head_dim);
+  if (p.elem != fa::kElemBF16 && p.elem != fa::kElemF16) return FA_ERR_DTYPE;
+  const int bn = fa::bwd_block_n(p.elem, p.head_dim);
   if (bn == 0) return FA_ERR_HEAD_DIM;
-  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16)) return FA_ERR_ALIGN;
-  const BwdLayout lay = bwd_layout(batch, total_q, num_heads, head_dim);
+  const BwdLayout lay = bwd_layout(p.batch, p.total_q, p.heads, p.head_dim);
   if (!workspace || workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
   // key blocks: sum_b ceil(Lk_b / bn) <= min(batch * ceil(max_k / bn), ceil(total_k / bn) + batch - 1)
-  const int64_t by_max = (int64_t)batch * ((max_seqlen_k + bn - 1) / bn);
-  const int64_t by_total = ((int64_t)total_k + bn - 1) / bn + (batch > 0 ? batch - 1 : 0);
+  const int64_t by_max = (int64_t)p.batch * ((max_seqlen_k + bn - 1) / bn);
+  const int64_t by_total = ((int64_t)p.total_k + bn - 1) / bn + (p.batch > 0 ? p.batch - 1 : 0);
   const int64_t compact = by_max < by_total ? by_max : by_total;
   // Under a causal mask a sequence's first key blocks carry the most work.
   // Block-major slots (block j of every sequence, then block j + 1) dispatch
   // them first; slots of sequences shorter than j stay empty, so this order
-  // is used only while they are at most two thirds of the grid.
+  // is used only while the grid has at most 25% more slots than the compact
+  // key-block map (4 * by_max <= 5 * compact).
   const bool by_block = causal != 0 && 4 * by_max <= 5 * compact;
   const int64_t tmax = by_block ? by_max : compact;
-  const int64_t grid = (tmax * num_heads_k + 7) / 8 * 8;
+  const int64_t grid = (tmax * p.heads_k + 7) / 8 * 8;
   if (grid > INT32_MAX) return FA_ERR_TOO_LARGE;
 
   char* ws = static_cast<char*>(workspace);
   int32_t* blk = reinterpret_cast<int32_t*>(ws + lay.blk);
   fa::BwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.dout = dout;
-  a.lse = lse;
-  a.cu_q = cu_seqlens_q;
-  a.cu_k = cu_seqlens_k;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.out = p.out;
+  a.dout = dout->data;
+  a.lse = p.lse;
+  a.cu_q = p.cu_q;
+  a.cu_k = p.cu_k;
   a.blk_start = blk;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
+  a.dq = dq->data;
+  a.dk = dk->data;
+  a.dv = dv->data;
   a.dq_acc = reinterpret_cast<float*>(ws + lay.dq_acc);
   a.drow = reinterpret_cast<float*>(ws + lay.drow);
-  a.row_stride = (int64_t)num_heads * head_dim;
-  a.kv_row_stride = (int64_t)num_heads_k * head_dim;
+  a.row_stride = (int64_t)p.heads * p.head_dim;
+  a.kv_row_stride = (int64_t)p.heads_k * p.head_dim;
   a.scale = softmax_scale;
   a.scale_log2 = (float)((double)softmax_scale * kLog2e);
-  a.batch = batch;
+  a.batch = p.batch;
   a.tmax = (int32_t)tmax;
   a.by_block = by_block ? 1 : 0;
-  a.n_work = (int32_t)(tmax * num_heads_k);
-  a.total_q = total_q;
-  a.heads = num_heads;
-  a.head_group = num_heads / num_heads_k;
+  a.n_work = (int32_t)(tmax * p.heads_k);
+  a.total_q = p.total_q;
+  a.heads = p.heads;
+  a.head_group = p.heads / p.heads_k;
 
-  hipStream_t s = (hipStream_t)stream;
-  if (fa::launch_bwd_prep(dtype, head_dim, a, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_prep(p.elem, p.head_dim, a, stream) != hipSuccess) return FA_ERR_HIP;
   if (grid > 0) {
-    if (!by_block && fa::launch_tile_map(cu_seqlens_k, batch, bn, blk, s) != hipSuccess) return FA_ERR_HIP;
-    if (fa::launch_bwd(dtype, head_dim, causal != 0, (int)grid, a, s) != hipSuccess) return FA_ERR_HIP;
+    if (!by_block && fa::launch_tile_map(p.cu_k, p.batch, bn, blk, stream) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_bwd(p.elem, p.head_dim, causal != 0, (int)grid, a, stream) != hipSuccess) return FA_ERR_HIP;
   }
-  if (fa::launch_bwd_dq(dtype, head_dim, a, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dq(p.elem, p.head_dim, a, stream) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 
@@ -300,73 +476,119 @@ int fa_varlen_kvcache_workspace_size(int32_t total_q, int32_t num_heads, int32_t
   return FA_OK;
 }
 
-int fa_varlen_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
-                          const int32_t* seqlens_k, const int32_t* leftpad_k, const int32_t* block_table,
-                          int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
-                          void* out, float* lse, int32_t batch, int32_t total_q, int32_t cache_blocks,
-                          int32_t cache_rows, int32_t blocks_per_seq, int32_t num_heads, int32_t num_heads_k,
-                          int32_t head_dim, int32_t dtype, int32_t num_splits, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+int fa_varlen_fwd_kvcache(const fa_tensor* q, const fa_tensor* k_cache, const fa_tensor* v_cache,
+                          const fa_tensor* cu_seqlens_q, const fa_tensor* seqlens_k, const fa_tensor* leftpad_k,
+                          const fa_tensor* block_table, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          float softmax_scale, int32_t causal, int32_t cache_rows, int32_t num_splits,
+                          fa_tensor* out, fa_tensor* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !seqlens_k || !out || !lse) return FA_ERR_NULL;
-  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_DTYPE;
-  if (head_dim != 64 && head_dim != 128) return FA_ERR_HEAD_DIM;
-  if (batch < 0 || total_q < 0 || num_heads < 1 || max_seqlen_q < 0 || max_seqlen_k < 0) return FA_ERR_SHAPE;
-  if (num_heads_k < 1 || num_heads % num_heads_k != 0) return FA_ERR_SHAPE;
-  if (max_seqlen_q > total_q || cache_rows < 1 || cache_blocks < 0) return FA_ERR_SHAPE;
+  // element types
+  const int elem = elem_code(q->dtype);
+  if (elem != fa::kElemBF16 && elem != fa::kElemF16) return FA_ERR_DTYPE;
+  if (k_cache->dtype != q->dtype || v_cache->dtype != q->dtype || out->dtype != q->dtype) return FA_ERR_DTYPE;
+  if (lse->dtype != FA_DTYPE_F32 || cu_seqlens_q->dtype != FA_DTYPE_I32 || seqlens_k->dtype != FA_DTYPE_I32)
+    return FA_ERR_DTYPE;
+  if ((leftpad_k && leftpad_k->dtype != FA_DTYPE_I32) || (block_table && block_table->dtype != FA_DTYPE_I32))
+    return FA_ERR_DTYPE;
+  // shapes
+  if (!rank_ok(*q, 3) || !rank_ok(*k_cache, 3) || !rank_ok(*out, 3) || !rank_ok(*lse, 2) ||
+      !rank_ok(*cu_seqlens_q, 1) || !rank_ok(*seqlens_k, 1))
+    return FA_ERR_SHAPE;
+  const int64_t D = q->shape[2];
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  const int64_t Tq = q->shape[0], H = q->shape[1], Hk = k_cache->shape[1];
+  const int64_t batch = cu_seqlens_q->shape[0] - 1;
+  if (batch < 0 || H < 1 || Hk < 1 || H % Hk != 0 || k_cache->shape[2] != D || !same_shape(*k_cache, *v_cache) ||
+      !same_shape(*q, *out) || lse->shape[0] != H || lse->shape[1] != Tq || seqlens_k->shape[0] != batch)
+    return FA_ERR_SHAPE;
+  if (leftpad_k && (!rank_ok(*leftpad_k, 1) || leftpad_k->shape[0] != batch)) return FA_ERR_SHAPE;
+  if (cache_rows < 1 || k_cache->shape[0] % cache_rows != 0) return FA_ERR_SHAPE;
+  const int64_t cache_blocks = k_cache->shape[0] / cache_rows;
+  int64_t blocks_per_seq = 0;
   if (block_table) {
-    if (blocks_per_seq < 1 || (int64_t)max_seqlen_k > (int64_t)blocks_per_seq * cache_rows) return FA_ERR_SHAPE;
+    if (!rank_ok(*block_table, 2) || block_table->shape[0] != batch || block_table->shape[1] < 1)
+      return FA_ERR_SHAPE;
+    blocks_per_seq = block_table->shape[1];
+    if ((int64_t)max_seqlen_k > blocks_per_seq * cache_rows) return FA_ERR_SHAPE;
   } else {
     if (cache_blocks < batch || max_seqlen_k > cache_rows) return FA_ERR_SHAPE;
   }
-  if ((int64_t)num_heads * head_dim > (int64_t{1} << 22)) return FA_ERR_TOO_LARGE;
+  if (max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > Tq) return FA_ERR_SHAPE;
+  // layout, data
+  if (!contiguous(*q) || !contiguous(*k_cache) || !contiguous(*v_cache) || !contiguous(*out) ||
+      !contiguous(*lse) || !contiguous(*cu_seqlens_q) || !contiguous(*seqlens_k) ||
+      (leftpad_k && !contiguous(*leftpad_k)) || (block_table && !contiguous(*block_table)))
+    return FA_ERR_LAYOUT;
+  if (!data_ok(*q) || !data_ok(*k_cache) || !data_ok(*v_cache) || !data_ok(*out) || !data_ok(*lse) ||
+      !cu_seqlens_q->data || !data_ok(*seqlens_k) || (leftpad_k && !data_ok(*leftpad_k)) ||
+      (block_table && !data_ok(*block_table)))
+    return FA_ERR_NULL;
+  // scalars
   if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return FA_ERR_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_ARG;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16)) return FA_ERR_ALIGN;
-  if (!aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(seqlens_k, 4)) return FA_ERR_ALIGN;
-  if ((leftpad_k && !aligned(leftpad_k, 4)) || (block_table && !aligned(block_table, 4))) return FA_ERR_ALIGN;
-  const int32_t splits = num_splits > 0 ? num_splits : auto_splits(batch, num_heads_k, max_seqlen_k);
-  if (!workspace || workspace_bytes < dec_workspace(total_q, num_heads, head_dim, splits)) return FA_ERR_WORKSPACE;
+  // alignment
+  if (!aligned(q->data, 16) || !aligned(k_cache->data, 16) || !aligned(v_cache->data, 16) ||
+      !aligned(out->data, 16))
+    return FA_ERR_ALIGN;
+  if (!aligned(lse->data, 4) || !aligned(cu_seqlens_q->data, 4) || !aligned(seqlens_k->data, 4) ||
+      (leftpad_k && !aligned(leftpad_k->data, 4)) || (block_table && !aligned(block_table->data, 4)))
+    return FA_ERR_ALIGN;
+  // sizes
+  if (Tq > INT32_MAX || H * D > (int64_t{1} << 22) || Hk * D > (int64_t{1} << 22) || cache_blocks > INT32_MAX ||
+      blocks_per_seq > INT32_MAX || batch > INT32_MAX)
+    return FA_ERR_TOO_LARGE;
+  const int32_t splits = num_splits > 0 ? num_splits : auto_splits(batch, Hk, max_seqlen_k);
+  if (batch * Hk * splits > INT32_MAX) return FA_ERR_TOO_LARGE;
+  if (!workspace || workspace_bytes < dec_workspace(Tq, H, D, splits)) return FA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
-  if ((int64_t)batch * num_heads_k * splits > INT32_MAX) return FA_ERR_TOO_LARGE;
-  if (batch == 0 || total_q == 0) return FA_OK;  // no query rows
+  if (batch == 0 || Tq == 0) return FA_OK;  // no query rows
 
-  const int64_t rows = (int64_t)total_q * num_heads * splits * fa::decode_waves();
+  const int64_t rows = Tq * H * splits * fa::decode_waves();
   fa::DecArgs a;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.out = out;
-  a.lse = lse;
-  a.cu_q = cu_seqlens_q;
-  a.seqlens_k = seqlens_k;
-  a.leftpad_k = leftpad_k;
-  a.block_table = block_table;
+  a.q = q->data;
+  a.k_cache = k_cache->data;
+  a.v_cache = v_cache->data;
+  a.out = out->data;
+  a.lse = static_cast<float*>(lse->data);
+  a.cu_q = static_cast<const int32_t*>(cu_seqlens_q->data);
+  a.seqlens_k = static_cast<const int32_t*>(seqlens_k->data);
+  a.leftpad_k = leftpad_k ? static_cast<const int32_t*>(leftpad_k->data) : nullptr;
+  a.block_table = block_table ? static_cast<const int32_t*>(block_table->data) : nullptr;
   a.part_o = static_cast<float*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)rows * head_dim * 4));
-  a.row_stride = (int64_t)num_heads * head_dim;
-  a.kv_row_stride = (int64_t)num_heads_k * head_dim;
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)rows * D * 4));
+  a.row_stride = H * D;
+  a.kv_row_stride = Hk * D;
   a.scale_log2 = (float)((double)softmax_scale * kLog2e);
-  a.batch = batch;
-  a.total_q = total_q;
-  a.heads = num_heads;
-  a.kv_heads = num_heads_k;
-  a.head_group = num_heads / num_heads_k;
+  a.batch = (int32_t)batch;
+  a.total_q = (int32_t)Tq;
+  a.heads = (int32_t)H;
+  a.kv_heads = (int32_t)Hk;
+  a.head_group = (int32_t)(H / Hk);
   a.cache_rows = cache_rows;
-  a.blocks_per_seq = block_table ? blocks_per_seq : 0;
+  a.blocks_per_seq = (int32_t)blocks_per_seq;
   a.num_splits = splits;
-  if (fa::launch_decode(dtype, head_dim, causal != 0, a, (hipStream_t)stream) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_decode(elem, (int)D, causal != 0, a, stream) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 
-int fa_varlen_check_cu_seqlens(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
-                               int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                               int32_t* flags, void* stream) {
+int fa_varlen_check_cu_seqlens(const fa_tensor* cu_seqlens_q, const fa_tensor* cu_seqlens_k, int32_t total_q,
+                               int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, fa_tensor* flags,
+                               hipStream_t stream) {
   if (!cu_seqlens_q || !cu_seqlens_k || !flags) return FA_ERR_NULL;
-  if (batch < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return FA_ERR_SHAPE;
-  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(flags, 4)) return FA_ERR_ALIGN;
-  if (fa::launch_check_cu(cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, flags,
-                          (hipStream_t)stream) != hipSuccess)
+  if (cu_seqlens_q->dtype != FA_DTYPE_I32) return FA_ERR_DTYPE;
+  if (!rank_ok(*cu_seqlens_q, 1) || cu_seqlens_q->shape[0] < 1) return FA_ERR_SHAPE;
+  const int64_t n = cu_seqlens_q->shape[0];
+  if (total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return FA_ERR_SHAPE;
+  int st = check_i32_vector(cu_seqlens_q, n);
+  if (st == FA_OK) st = check_i32_vector(cu_seqlens_k, n);
+  if (st == FA_OK) st = check_i32_vector(flags, 1);
+  if (st != FA_OK) return st;
+  if (n - 1 > INT32_MAX) return FA_ERR_TOO_LARGE;
+  if (fa::launch_check_cu(static_cast<const int32_t*>(cu_seqlens_q->data),
+                          static_cast<const int32_t*>(cu_seqlens_k->data), (int)(n - 1), total_q, total_k,
+                          max_seqlen_q, max_seqlen_k, static_cast<int32_t*>(flags->data), stream) != hipSuccess)
     return FA_ERR_HIP;
   return FA_OK;
 }

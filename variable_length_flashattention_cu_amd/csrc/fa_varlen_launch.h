@@ -8,6 +8,12 @@
 
 namespace fa {
 
+// Element codes of the `dtype` arguments below (the C ABI maps its fa_dtype
+// values onto these).
+constexpr int kElemF32 = 0;
+constexpr int kElemBF16 = 1;
+constexpr int kElemF16 = 2;
+
 // Kernel arguments of the forward pass (passed by value).
 struct FwdArgs {
   const void* q;
