@@ -64,7 +64,7 @@
  *
  * Status codes are checked in this order: NULL descriptor, element type,
  * rank and shape (head_dim separately), layout, NULL data, scalar
- * arguments, alignment, size limits, workspace.
+ * arguments, alignment, size limits, workspace (or static scratch).
  */
 #ifndef FA_VARLEN_H_
 #define FA_VARLEN_H_
@@ -110,7 +110,8 @@ typedef enum fa_status {
   FA_ERR_HIP = 8,        /* the HIP runtime reported an error (no device, launch failure) */
   FA_ERR_TOO_LARGE = 9,  /* sizes beyond what one launch addresses (grid above 2^31-1
                             workgroups, rows above 2^31-1, heads * head_dim above 2^22) */
-  FA_ERR_WORKSPACE = 10  /* workspace NULL or smaller than the size function reports */
+  FA_ERR_WORKSPACE = 10, /* workspace NULL or smaller than the size function reports */
+  FA_ERR_SCRATCH = 11    /* fa_varlen_fwd_noalloc: batch above its static map (65535 sequences) */
 } fa_status;
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -196,6 +197,28 @@ int fa_varlen_fwd_mapped(const fa_tensor* q, const fa_tensor* k, const fa_tensor
                          const fa_tensor* cu_seqlens_q, const fa_tensor* cu_seqlens_k,
                          int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
                          fa_tensor* out, fa_tensor* lse, const fa_tensor* blk_start, hipStream_t stream);
+
+/*
+ * The forward pass for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It computes exactly what fa_varlen_fwd computes (same kernels, same
+ * results) but calls no hipMalloc, hipMallocAsync, hipFree or other
+ * allocating routine: the (batch+1)-entry work-item map goes to a static
+ * device array of 65536 int32 (256 KiB) that the library holds on every GPU
+ * it runs on until the process ends.  The map kernel writes all batch+1
+ * entries before the attention kernel reads them, so nothing needs clearing
+ * between calls.
+ *   Arguments and errors as fa_varlen_fwd, plus FA_ERR_SCRATCH when batch
+ *   exceeds 65535.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or different host threads, without ordering
+ * between them) race on the map and may compute wrong rows.  Calls ordered on
+ * one stream do not.
+ */
+int fa_varlen_fwd_noalloc(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                          const fa_tensor* cu_seqlens_q, const fa_tensor* cu_seqlens_k,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                          fa_tensor* out, fa_tensor* lse, hipStream_t stream);
 
 /*
  * Backward pass: gradients of the attention of fa_varlen_fwd with respect to

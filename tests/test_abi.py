@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "fa_varlen.h")
 pytestmark = pytest.mark.skipif(not os.path.exists(fa.library_path()),
                                 reason="libfa_varlen.so not built (run __graft_entry__.build())")
 
-OK, NULL, DTYPE, SHAPE, HEAD_DIM, LAYOUT, ALIGN, ARG, HIP, TOO_LARGE, WORKSPACE = range(11)
+OK, NULL, DTYPE, SHAPE, HEAD_DIM, LAYOUT, ALIGN, ARG, HIP, TOO_LARGE, WORKSPACE, SCRATCH = range(12)
 F32, BF16, I32, F16 = fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16, fa.FA_DTYPE_I32, fa.FA_DTYPE_F16
 
 
@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["fa_status_string", "fa_varlen_block_sizes", "fa_varlen_tile_map",
-                            "fa_varlen_fwd", "fa_varlen_fwd_mapped", "fa_varlen_check_cu_seqlens",
+                            "fa_varlen_fwd", "fa_varlen_fwd_mapped", "fa_varlen_fwd_noalloc",
+                            "fa_varlen_check_cu_seqlens",
                             "fa_varlen_bwd", "fa_varlen_bwd_workspace_size", "fa_varlen_fwd_kvcache",
                             "fa_varlen_kvcache_workspace_size"])
 
@@ -55,7 +56,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(11):
+    for code in range(12):
         s = fa.fa_status_string(code)
         assert isinstance(s, str) and s and s != "unknown status"
     assert fa.fa_status_string(12345) == "unknown status"
@@ -111,9 +112,12 @@ def edit(t, name, **fields):
             setattr(d, f, val)
 
 
-def call_fwd(t, max_q=8, max_k=8, scale=0.125, causal=0, mapped=False, drop=None):
+def call_fwd(t, max_q=8, max_k=8, scale=0.125, causal=0, mapped=False, drop=None, noalloc=False):
     lib = fa.load_library()
     r = {n: (None if n == drop else ctypes.byref(d)) for n, d in t.items()}
+    if noalloc:
+        return lib.fa_varlen_fwd_noalloc(r["q"], r["k"], r["v"], r["cu_q"], r["cu_k"], max_q, max_k, scale, causal,
+                                         r["out"], r["lse"], None)
     if mapped:
         return lib.fa_varlen_fwd_mapped(r["q"], r["k"], r["v"], r["cu_q"], r["cu_k"], max_q, max_k, scale, causal,
                                         r["out"], r["lse"], r["blk"], None)
@@ -213,6 +217,20 @@ def test_empty_problems_launch_nothing():
     for n in ("q", "k", "v", "out", "lse"):
         edit(t, n, data=None)
     assert call_fwd(t, max_q=0, max_k=0) == OK
+
+
+def test_noalloc_validation():
+    """The no-allocation variant validates like fa_varlen_fwd and refuses
+    batches beyond its static map before any HIP call."""
+    assert call_fwd(tensors(), noalloc=True, drop="q") == NULL
+    t = tensors()
+    edit(t, "q", stride=(128, 1, 2))
+    assert call_fwd(t, noalloc=True) == LAYOUT
+    assert call_fwd(tensors(D=80), noalloc=True) == HEAD_DIM
+    assert call_fwd(tensors(), noalloc=True, causal=3) == ARG
+    assert call_fwd(tensors(B=65535, Tq=0), max_q=0, noalloc=True) == OK      # largest batch: empty, no launch
+    assert call_fwd(tensors(B=65536), noalloc=True) == SCRATCH
+    assert call_fwd(tensors(B=65536, Tq=0), max_q=0, noalloc=True) == SCRATCH
 
 
 def test_grid_too_large():

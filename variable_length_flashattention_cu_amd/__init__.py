@@ -7,7 +7,7 @@ memory and the stream; no CPU fallback exists -- when the library is not
 built every entry point raises :class:`FaVarlenError`.
 
 Functions carry the names of the C entry points:
-  fa_varlen_fwd, fa_varlen_fwd_mapped, fa_varlen_bwd,
+  fa_varlen_fwd, fa_varlen_fwd_mapped, fa_varlen_fwd_noalloc, fa_varlen_bwd,
   fa_varlen_bwd_workspace_size, fa_varlen_fwd_kvcache,
   fa_varlen_kvcache_workspace_size, fa_varlen_tile_map, fa_varlen_block_sizes,
   fa_varlen_check_cu_seqlens, fa_status_string.
@@ -35,6 +35,7 @@ __all__ = [
     "fa_varlen_tile_map",
     "fa_varlen_fwd",
     "fa_varlen_fwd_mapped",
+    "fa_varlen_fwd_noalloc",
     "fa_varlen_bwd",
     "fa_varlen_bwd_workspace_size",
     "fa_varlen_fwd_kvcache",
@@ -51,7 +52,7 @@ FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_DTYPE", 3: "FA_ERR_SHAPE", 4: "FA_ERR_HEAD_DIM",
     5: "FA_ERR_LAYOUT", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ARG", 8: "FA_ERR_HIP", 9: "FA_ERR_TOO_LARGE",
-    10: "FA_ERR_WORKSPACE",
+    10: "FA_ERR_WORKSPACE", 11: "FA_ERR_SCRATCH",
 }
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -111,6 +112,7 @@ def load_library() -> ctypes.CDLL:
         "fa_varlen_tile_map": ([tp, i32, i32, i32, tp, vp], ctypes.c_int),
         "fa_varlen_fwd": ([tp, tp, tp, tp, tp, i32, i32, f32, i32, tp, tp, vp], ctypes.c_int),
         "fa_varlen_fwd_mapped": ([tp, tp, tp, tp, tp, i32, i32, f32, i32, tp, tp, tp, vp], ctypes.c_int),
+        "fa_varlen_fwd_noalloc": ([tp, tp, tp, tp, tp, i32, i32, f32, i32, tp, tp, vp], ctypes.c_int),
         "fa_varlen_bwd": ([tp, tp, tp, tp, tp, tp, tp, tp, i32, i32, f32, i32, tp, tp, tp, vp, sz, vp],
                           ctypes.c_int),
         "fa_varlen_bwd_workspace_size": ([i32, i32, i32, i32, szp], ctypes.c_int),
@@ -268,6 +270,22 @@ def fa_varlen_fwd_mapped(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                                              scale, int(bool(causal)), ctypes.byref(ds[5]), ctypes.byref(ds[6]),
                                              ctypes.byref(ds[7]), _stream_handle(stream))
     _check(st, "fa_varlen_fwd_mapped")
+    return out, lse
+
+
+def fa_varlen_fwd_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, out, lse,
+                          softmax_scale: Optional[float] = None, causal: bool = False, stream=None):
+    """fa_varlen_fwd that allocates nothing: the caller passes out and lse,
+    and the library keeps the work-item map in its static per-GPU array (at
+    most 65535 sequences; overlapping calls on one GPU race on it)."""
+    if out is None or lse is None:
+        raise ValueError("fa_varlen_fwd_noalloc needs caller-allocated out and lse")
+    q, k, v, cu_q, cu_k, scale, out, lse = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse)
+    ds = [desc(x) for x in (q, k, v, cu_q, cu_k, out, lse)]
+    st = load_library().fa_varlen_fwd_noalloc(*map(ctypes.byref, ds[:5]), int(max_seqlen_q), int(max_seqlen_k),
+                                              scale, int(bool(causal)), ctypes.byref(ds[5]), ctypes.byref(ds[6]),
+                                              _stream_handle(stream))
+    _check(st, "fa_varlen_fwd_noalloc")
     return out, lse
 
 

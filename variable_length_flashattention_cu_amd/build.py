@@ -25,7 +25,8 @@ PROBE_PATH = os.path.join(PKG_DIR, "libfa_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "fa_probe.hip")]
 
 SOURCES = [os.path.join(CSRC, "fa_varlen_kernels.hip"), os.path.join(CSRC, "fa_varlen_bwd.hip"),
-           os.path.join(CSRC, "fa_varlen_decode.hip"), os.path.join(CSRC, "fa_varlen_api.cpp")]
+           os.path.join(CSRC, "fa_varlen_decode.hip"), os.path.join(CSRC, "fa_varlen_scratch.hip"),
+           os.path.join(CSRC, "fa_varlen_api.cpp")]
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the generated code.
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -314,6 +314,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_TOO_LARGE: return "problem too large for one launch";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than the size function reports";
+    case FA_ERR_SCRATCH: return "batch larger than the static work-item map of fa_varlen_fwd_noalloc (65535 sequences)";
     default: return "unknown status";
   }
 }
@@ -388,6 +389,26 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
     rc = launch_fwd_mapped(p, plan, softmax_scale, causal, blk_start, stream);
   if (hipFreeAsync(blk_start, stream) != hipSuccess) rc = FA_ERR_HIP;
   return rc;
+}
+
+int fa_varlen_fwd_noalloc(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* cu_seqlens_q,
+                          const fa_tensor* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          float softmax_scale, int32_t causal, fa_tensor* out, fa_tensor* lse, hipStream_t stream) {
+  Problem p;
+  int st = check_problem(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, max_seqlen_q, max_seqlen_k, softmax_scale,
+                         causal, fwd_head_dim, nullptr, 0, 0, &p);
+  if (st != FA_OK) return st;
+  if (p.batch > fa::kNoAllocMaxBatch) return FA_ERR_SCRATCH;
+  Plan plan;
+  st = plan_fwd(p, max_seqlen_q, &plan);
+  if (st != FA_OK) return st;
+  if (plan.grid == 0) return FA_OK;
+  // The map goes to this device's static array (written whole by the map
+  // kernel before the attention kernel reads it, both on `stream`).
+  int32_t* blk_start = nullptr;
+  if (fa::noalloc_map_scratch(&blk_start) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_tile_map(p.cu_q, p.batch, plan.tc.block_m, blk_start, stream) != hipSuccess) return FA_ERR_HIP;
+  return launch_fwd_mapped(p, plan, softmax_scale, causal, blk_start, stream);
 }
 
 int fa_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t num_heads, int32_t head_dim,

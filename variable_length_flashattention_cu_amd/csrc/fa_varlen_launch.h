@@ -116,6 +116,11 @@ struct DecArgs {
 int decode_waves();
 hipError_t launch_decode(int dtype, int head_dim, bool causal, const DecArgs& a, hipStream_t stream);
 
+// fa_varlen_fwd_noalloc: the largest batch its static work-item map holds,
+// and that map's device address on the current device (fa_varlen_scratch.hip).
+constexpr int kNoAllocMaxBatch = 65535;
+hipError_t noalloc_map_scratch(int32_t** ptr);
+
 hipError_t launch_tile_map(const int32_t* cu_q, int batch, int block_m, int32_t* blk_start, hipStream_t stream);
 hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, int total_q, int total_k,
