@@ -300,3 +300,33 @@ def test_ragged64k_d256_sampled(fa):
     wl = workload_custom("ragged64k_h16_d256", base.lengths_q, None, 16, 256, "bf16", seed=10)
     for causal in (False, True):
         sampled_parity(fa, wl, causal, [0, 7, 15], seed=10)
+
+
+# ---------------------------------------------------------------- score spikes
+SPIKE_CASES = [("bf16", 128), ("bf16", 64), ("bf16", 96), ("f16", 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,head_dim", SPIKE_CASES, ids=[f"{d}_d{h}" for d, h in SPIKE_CASES])
+def test_score_spikes_raise_reference(fa, causal, dtype, head_dim):
+    """Keys multiplied by 16 (exact in bf16 and fp16) in the middle of long
+    sequences give scores tens of log2 units above every earlier one, so the
+    kernels must raise their softmax references and rescale the partial
+    outputs in the middle of the key loop, not only in its first tiles."""
+    from fa_synth import bf16_rne_bits, f16_rne_bits
+    wl = workload_custom(f"spikes_{dtype}_d{head_dim}", [2048, 1500, 700], [2048, 1700, 900], 4, head_dim, dtype,
+                         seed=31)
+    say(f"case {wl.name} causal={causal}")
+    data = draw_qkv(wl)
+    k = data["k"].copy()
+    for b in range(wl.batch):
+        k0, Lk = wl.cu_k[b], wl.cu_k[b + 1] - wl.cu_k[b]
+        for frac in (0.37, 0.81):
+            k[k0 + int(frac * Lk)] *= 16.0
+    data["k"] = k
+    data["k_bits"] = bf16_rne_bits(k) if dtype == "bf16" else f16_rne_bits(k)
+    t = to_device(data, wl)
+    o, l = host(*run_gpu(wl, t, causal))
+    ref_o, ref_l = attention_fwd(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
+    n = wl.total_q
+    compare(o[:n], l[:, :n], ref_o[:n], ref_l[:, :n], TOL[dtype], wl.name)

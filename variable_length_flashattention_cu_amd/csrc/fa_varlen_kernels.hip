@@ -611,6 +611,386 @@ __global__ __launch_bounds__(512, 2) void fwd16_pingpong_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 16-bit forward, software-pipelined wavefronts
+// ---------------------------------------------------------------------------
+// The workgroup's 8 wavefronts (two per SIMD) each own 32 query rows and walk
+// the key range in 32-key slabs.  Stage j of a wavefront issues three pieces
+// of work that do not depend on each other:
+//   QK(j+1)    S^T of slab j+1 = K Q^T       8 MFMAs (head_dim 128), K from LDS
+//   softmax(j) the online softmax of slab j  vector ALU and exponentials
+//   PV(j-1)    O^T += V^T P^T of slab j-1    8 MFMAs, V^T by transposing LDS reads
+// so the matrix instructions of one wavefront run while its own vector
+// instructions issue, and both wavefronts of a SIMD always have both kinds of
+// work.  (A wavefront on its own issues vector instructions at about half the
+// rate two wavefronts reach together, and one MFMA of 32 cycles leaves room for
+// several vector instructions of the same wavefront.)  The softmax of slab j
+// needs S(j), computed in stage j-1; PV(j-1) needs P(j-1), produced in stage
+// j-1: each stage reads only results of the previous one.
+//
+// K and V tiles of BN keys go from global memory straight into LDS (direct
+// loads), four buffers each, tile m in buffer m % 4.  Iteration n of the
+// workgroup loop runs the stages of slabs of tile n; it reads K tiles n and
+// n+1 and V tiles n-1 and n, and issues the loads of K(n+3) and V(n+2), whose
+// buffers were last read in iteration n-1.  A load has two iterations to land;
+// each wavefront waits for its own loads before the barrier that ends the
+// iteration.
+constexpr int kPipeBuffers = 4;
+
+template <int D, int BN>
+struct PipeGeom {
+  static constexpr int KS = tiling::k_stride<D>();  // elements per LDS row
+  static constexpr int CPR = KS / 8;                 // 16-byte slots per LDS row
+  static constexpr int LOADS = BN * CPR / 64;        // wave-wide direct loads per tile
+  static constexpr int PER_WAVE = LOADS / 8;         // per wavefront (8 share a tile)
+  static constexpr int SPT = BN / 32;                // 32-key slabs per tile
+  static constexpr int TILE = BN * KS;               // elements per tile buffer
+  static_assert(LOADS % 8 == 0 && PER_WAVE >= 1 && PER_WAVE <= 4, "tile must split into whole wave loads");
+};
+
+// Direct loads of keys key0 .. key0+BN-1 of the head slice at `base` into the
+// LDS tile at dst, in the K-style (V_LAYOUT false) or row-major V layout; this
+// wavefront's share: slots 64 * (wave * PER_WAVE + i) + lane.  Keys at or past
+// Lk read as zeros (buffer range check).
+template <int D, int BN, bool V_LAYOUT>
+__device__ __forceinline__ void pipe_issue(uint16_t* dst, const uint16_t* __restrict__ base, int64_t row_stride,
+                                           int key0, int Lk, int wave, int lane) {
+  using G = PipeGeom<D, BN>;
+  const int rows = max(0, min(BN, Lk - key0));
+  const u32x4 r = buffer_rsrc_words(base + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
+  const uint32_t lds = lds_address(dst);
+#pragma unroll
+  for (int i = 0; i < G::PER_WAVE; ++i) {
+    const int seg = wave * G::PER_WAVE + i;
+    int row, ch;
+    tiling::direct_slot_chunk<D, V_LAYOUT>(seg * 64 + lane, row, ch);
+    const uint32_t off = ((uint32_t)row * (uint32_t)row_stride + (uint32_t)ch * 8u) * 2u;
+    lds_dma16(r, off, lds + (uint32_t)seg * 1024u);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  // s_waitcnt needs an immediate: the loads a wavefront may leave in flight
+  // are 0, PER_WAVE (V only) or 2 * PER_WAVE (K and V) per iteration
+  if (n >= 2 * N) wait_vmcnt<2 * N>();
+  else if (n >= N) wait_vmcnt<N>();
+  else wait_vmcnt<0>();
+}
+
+// Per-wavefront state and the three pieces of a stage.
+template <typename T, int D>
+struct PipeWave {
+  typedef typename Elem16<T>::v8 v8;
+  static constexpr int KSTEPS = D / 16;  // MFMA k-steps of Q K^T
+  static constexpr int DB = D / 32;      // 32-dimension blocks of the output
+  static constexpr int KS = tiling::k_stride<D>();
+
+  v8 q[KSTEPS];  // Q^T as the B operand
+  f32x16 o[DB];  // O^T accumulators (lane: query row, registers: dimensions)
+  float m_run, l_run;
+
+  // S^T of the slab whose first key row in the tile at Ks is `row0`.  A-row R
+  // reads key row key_of_arow(R), so register r of lane half g holds key
+  // 16 g + r of the slab.
+  __device__ __forceinline__ f32x16 qk(const uint16_t* Ks, int row0, int arow, int g) const {
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const v8 av = *(const v8*)(Ks + tiling::ks_index<D>(row0 + arow, 2 * ks + g));
+      s = Elem16<T>::mfma(av, q[ks], s);
+    }
+    return s;
+  }
+
+  // O^T += V^T P^T for the slab whose first key row in the tile at Vr is
+  // `row0`.  The A operand of k-step t (keys 16 g + 8 t .. +7 of the slab for
+  // lane half g, the keys of the probabilities in p[t]) comes from two
+  // transposing reads of 4 rows each.
+  __device__ __forceinline__ void pv(const uint16_t* Vr, int row0, const v8 (&p)[2], int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const int g = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int r0 = row0 + 16 * g + 8 * t;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(Vr + tiling::vr_tr_index<D>(lane, r0, db)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(Vr + tiling::vr_tr_index<D>(lane, r0 + 4, db)));
+        const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = Elem16<T>::mfma(__builtin_bit_cast(v8, v), p[t], o[db]);
+      }
+  }
+
+  // -inf for keys past the end of the sequence or (causal) above the diagonal;
+  // `key0` is the slab's first key, `row` this lane's query row.
+  template <bool CAUSAL>
+  __device__ __forceinline__ static void mask(f32x16& s, int key0, int row, int g, int Lk, int shift) {
+    const int lim = CAUSAL ? min(Lk - 1, row + shift) : (Lk - 1);  // last visible key
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (key0 + 16 * g + r > lim) s[r] = kNegInf;
+  }
+
+  // Online softmax of one slab: probabilities in the PV B-operand layout and
+  // the running statistics; returns whether some row of the wavefront raised
+  // its reference (then O must be scaled by alpha after the PV of the
+  // previous slab).  The reference is raised only when a row's maximum passes
+  // it by more than kRescaleSlack, which after the first slabs is rare.
+  __device__ __forceinline__ bool softmax(const f32x16& s, v8 (&p)[2], float& alpha, float scale_log2) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    const float m_tile = pair_max(mx) * scale_log2;
+    const bool need = wave_any(m_tile > m_run + kRescaleSlack);
+    const float m_new = need ? fmaxf(m_run, m_tile) : m_run;
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    alpha = fast_exp2(m_run - m_use);  // 1 when the reference is kept
+    m_run = m_new;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = fast_exp2(__builtin_fmaf(s[8 * t + e], scale_log2, -m_use));
+        part[e & 3] += pe;
+        p[t][e] = (T)pe;
+      }
+    const float lsum = (part[0] + part[1]) + (part[2] + part[3]);
+    l_run = l_run * alpha + lsum;
+    // The flag is formed from the row sums (never negative), so the rarely
+    // taken rescale branch cannot be placed ahead of the exponentials: they
+    // stay in one basic block with the MFMAs of the stage.
+    return wave_any(need && !(lsum < 0.f));
+  }
+
+  // Softmax of an unmasked slab against the current references, without the
+  // row maxima.  Used once every row of the wavefront has seen visible keys:
+  // each row's reference m_run is then an earlier maximum of its own scores.
+  // Any finite reference gives the same out = O / l and lse = m + log2(l):
+  // float32 and the 16-bit types keep their relative precision at any
+  // magnitude, and l and O share the reference.  The hazard is overflow when
+  // scores outgrow the reference: the probabilities are rounded to T before
+  // the second product, and fp16 ends at 65504.  The slab is accepted when
+  // every row's sum over it -- a bound on each of its probabilities -- stays
+  // at or below 2^15 (a NaN fails the test too); otherwise the caller redoes
+  // it with softmax() above, which raises the reference.  On acceptance l_run
+  // is updated and the probabilities are in p.
+  static constexpr float kFastSlabLimit = 32768.f;  // 2^15
+  __device__ __forceinline__ bool softmax_fast(const f32x16& s, v8 (&p)[2], float scale_log2) {
+    float part[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = fast_exp2(__builtin_fmaf(s[8 * t + e], scale_log2, -m_run));
+        part[e & 3] = (t == 0 && e < 4) ? pe : part[e & 3] + pe;
+        p[t][e] = (T)pe;
+      }
+    const float lsum = (part[0] + part[1]) + (part[2] + part[3]);
+    const bool ok = !wave_any(!(lsum <= kFastSlabLimit));
+    if (ok) l_run += lsum;
+    return ok;
+  }
+
+  __device__ __forceinline__ void rescale(float alpha) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+  }
+};
+
+template <typename T, int D, int BN, bool CAUSAL>
+__device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem& w,
+                                                uint16_t (&lds_k)[kPipeBuffers][BN * tiling::k_stride<D>()],
+                                                uint16_t (&lds_v)[kPipeBuffers][BN * tiling::k_stride<D>()]) {
+  using G = PipeGeom<D, BN>;
+  using Wave = PipeWave<T, D>;
+  typedef typename Wave::v8 v8;
+  constexpr int SPT = G::SPT;
+  constexpr int NB = kPipeBuffers;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int q0 = w.m * 256;               // first query row of the item (in its sequence)
+  const int wrow0 = q0 + wave * 32;       // first query row of this wavefront
+  const int shift = w.Lk - w.Lq;
+  const int64_t rs = a.row_stride, rsk = a.kv_row_stride;
+  const int hk = w.h / a.head_group;
+  const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)hk * D;
+  const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)hk * D;
+
+  // Slabs of this wavefront: j_end slabs hold a key some row sees, the first
+  // j_full slabs need no mask.  The workgroup walks the slabs of its last
+  // wavefront with rows (the most, under a causal mask).
+  int j_end = 0, j_full = 0;
+  if (wrow0 < w.Lq) {
+    const int hi = CAUSAL ? min(w.Lk, wrow0 + 32 + shift) : w.Lk;
+    const int full = CAUSAL ? min(w.Lk, wrow0 + 1 + shift) : w.Lk;
+    j_end = hi > 0 ? (hi + 31) / 32 : 0;
+    j_full = full > 0 ? full / 32 : 0;
+  }
+  int J = 0;
+  {
+    const int last_row = min(w.Lq, q0 + 256) - 1;
+    const int wlast = q0 + ((last_row - q0) & ~31);
+    const int hi = CAUSAL ? min(w.Lk, wlast + 32 + shift) : w.Lk;
+    J = hi > 0 ? (hi + 31) / 32 : 0;
+  }
+  const int NT = (J + SPT - 1) / SPT;  // K/V tiles the workgroup loads
+  const int NIT = J > 0 ? J / SPT + 1 : 0;  // iterations: stage J is in iteration J / SPT
+
+  // first tiles, then Q; one wait covers them all
+  if (NT > 0) {
+    pipe_issue<D, BN, false>(lds_k[0], kbase, rsk, 0, w.Lk, wave, lane);
+    pipe_issue<D, BN, true>(lds_v[0], vbase, rsk, 0, w.Lk, wave, lane);
+    if (NT > 1) pipe_issue<D, BN, false>(lds_k[1], kbase, rsk, BN, w.Lk, wave, lane);
+  }
+  Wave wv;
+  {  // Q rows past the end of the sequence load as zeros
+    const int qrows = max(0, min(32, w.Lq - wrow0));
+    const __amdgpu_buffer_rsrc_t rq =
+        buffer_rsrc((const uint16_t*)a.q + (int64_t)(w.q_start + wrow0) * rs + (int64_t)w.h * D,
+                    head_rows_bytes(qrows, rs, D, 2));
+#pragma unroll
+    for (int ks = 0; ks < Wave::KSTEPS; ++ks) {
+      const uint32_t off = ((uint32_t)l32 * (uint32_t)rs + 16 * ks + 8 * g) * 2u;
+      wv.q[ks] = __builtin_bit_cast(v8, buffer_load16(rq, off));
+    }
+  }
+  wv.m_run = kNegInf;
+  wv.l_run = 0.f;
+#pragma unroll
+  for (int db = 0; db < Wave::DB; ++db) wv.o[db] = f32x16{};
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const int arow = key_of_arow(l32);
+  const int row = wrow0 + l32;  // this lane's query row (in sequence)
+  f32x16 s_cur = {};
+  v8 p_prev[2] = {};
+  if (j_end > 0) s_cur = wv.qk(lds_k[0], 0, arow, g);  // S(0)
+
+  // K slab j+1 is in tile (j+1)/SPT, V slab j-1 in tile (j-1)/SPT
+  auto kslab = [&](int j) { return (const uint16_t*)lds_k[((j + 1) / SPT) % NB] + ((j + 1) % SPT) * 32 * Wave::KS; };
+  auto vslab = [&](int j) { return (const uint16_t*)lds_v[((j - 1) / SPT) % NB] + ((j - 1) % SPT) * 32 * Wave::KS; };
+  // loads of later tiles: issued at the start of iteration n, they fly
+  // during its work; returns the loads this wavefront may leave in flight
+  // at the end of the iteration
+  auto issue = [&](int n) {
+    int in_flight = 0;
+    if (n == 0) {
+      if (2 < NT) pipe_issue<D, BN, false>(lds_k[2], kbase, rsk, 2 * BN, w.Lk, wave, lane);
+      if (1 < NT) pipe_issue<D, BN, true>(lds_v[1], vbase, rsk, BN, w.Lk, wave, lane);
+    }
+    if (n + 3 < NT) {
+      pipe_issue<D, BN, false>(lds_k[(n + 3) % NB], kbase, rsk, (n + 3) * BN, w.Lk, wave, lane);
+      in_flight += G::PER_WAVE;
+    }
+    if (n + 2 < NT) {
+      pipe_issue<D, BN, true>(lds_v[(n + 2) % NB], vbase, rsk, (n + 2) * BN, w.Lk, wave, lane);
+      in_flight += G::PER_WAVE;
+    }
+    return in_flight;
+  };
+  // one iteration with every piece of every stage conditional (the first
+  // iteration, slabs that need a mask, the last slabs, finished wavefronts)
+  auto generic = [&](int n) {
+    for (int st = 0; st < SPT; ++st) {
+      const int j = n * SPT + st;
+      if (j > j_end) break;
+      v8 p_cur[2] = {};
+      float alpha = 1.f;
+      bool resc = false;
+      f32x16 s_next = {};
+      if (j + 1 < j_end) s_next = wv.qk(kslab(j), 0, arow, g);
+      if (j < j_end) {
+        if (j >= j_full) Wave::template mask<CAUSAL>(s_cur, 32 * j, row, g, w.Lk, shift);
+        resc = wv.softmax(s_cur, p_cur, alpha, a.scale_log2);
+      }
+      if (j >= 1) wv.pv(vslab(j), 0, p_prev, lane);
+      if (resc) wv.rescale(alpha);
+      s_cur = s_next;
+      p_prev[0] = p_cur[0];
+      p_prev[1] = p_cur[1];
+    }
+  };
+  // Iterations [1, n_steady) run only steady stages: QK, softmax and PV each
+  // present, no mask.
+  int n_steady = 1;
+  {
+    const int lim = min(j_end - 1, j_full);  // (n + 1) * SPT <= lim
+    if (lim >= 2 * SPT) n_steady = lim / SPT;
+  }
+  if (NIT > 0) {
+    const int fl = issue(0);
+    generic(0);
+    wait_vmcnt_dyn<G::PER_WAVE>(fl);
+    __syncthreads();
+  }
+  int n = 1;
+  for (; n < n_steady; ++n) {
+    const int fl = issue(n);
+#pragma unroll
+    for (int st = 0; st < SPT; ++st) {
+      const int j = n * SPT + st;
+      v8 p_cur[2];
+      const f32x16 s_next = wv.qk(kslab(j), 0, arow, g);
+      const bool ok = wv.softmax_fast(s_cur, p_cur, a.scale_log2);
+      wv.pv(vslab(j), 0, p_prev, lane);
+      if (__builtin_expect(!ok, 0)) {  // rare: redo the slab with raised references, O rescaled after PV(j-1)
+        asm volatile("" ::: "memory");  // a real branch: the redo must not be executed speculatively
+        float alpha;
+        if (wv.softmax(s_cur, p_cur, alpha, a.scale_log2)) wv.rescale(alpha);
+      }
+      s_cur = s_next;
+      p_prev[0] = p_cur[0];
+      p_prev[1] = p_cur[1];
+    }
+    wait_vmcnt_dyn<G::PER_WAVE>(fl);
+    __syncthreads();
+  }
+  for (; n < NIT; ++n) {
+    const int fl = issue(n);
+    generic(n);
+    wait_vmcnt_dyn<G::PER_WAVE>(fl);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, write out (16-bit, round to nearest even) and lse
+  T* __restrict__ op = (T*)a.out;
+  const float l = pair_sum(wv.l_run);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (row < w.Lq) {
+    T* dst = op + (int64_t)(w.q_start + row) * rs + (int64_t)w.h * D;
+#pragma unroll
+    for (int db = 0; db < Wave::DB; ++db)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        typename Elem16<T>::v4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = (T)(wv.o[db][4 * s4 + c] * inv);
+        *(typename Elem16<T>::v4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
+      }
+    if (g == 0)
+      a.lse[(int64_t)w.h * a.total_q + w.q_start + row] = l > 0.f ? (wv.m_run + fast_log2(l)) * kLn2 : kNegInf;
+  }
+}
+
+template <typename T, int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void fwd16_pipe_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kPipeBuffers][BN * tiling::k_stride<D>()];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kPipeBuffers][BN * tiling::k_stride<D>()];
+  WorkItem w;
+  if (!decode_work(a, w)) return;
+  run_work<256, CAUSAL>(a, w, [&](const WorkItem& wi) { fwd16_pipe_item<T, D, BN, CAUSAL>(a, wi, lds_k, lds_v); });
+}
+
+// ---------------------------------------------------------------------------
 // fp32 forward (fp32 MFMA 32x32x2; no reduced precision anywhere)
 // ---------------------------------------------------------------------------
 // A/B operands of the fp32 MFMA are single elements per lane, so neither K
@@ -803,8 +1183,8 @@ hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, 
 template <typename T>
 hipError_t launch_fwd16(int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream) {
   if (head_dim == 128)
-    return causal ? launch(fwd16_pingpong_kernel<T, 128, 64, true>, grid, 512, stream, a)
-                  : launch(fwd16_pingpong_kernel<T, 128, 64, false>, grid, 512, stream, a);
+    return causal ? launch(fwd16_pipe_kernel<T, 128, 64, true>, grid, 512, stream, a)
+                  : launch(fwd16_pipe_kernel<T, 128, 64, false>, grid, 512, stream, a);
   if (head_dim == 96)
     return causal ? launch(fwd16_pingpong_kernel<T, 96, 64, true>, grid, 512, stream, a)
                   : launch(fwd16_pingpong_kernel<T, 96, 64, false>, grid, 512, stream, a);
