@@ -933,10 +933,17 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
     __syncthreads();
   }
   int n = 1;
+  const bool lead_first = wave >= 4;  // wavefronts 4-7 (the younger on each SIMD) lead the first stage
   for (; n < n_steady; ++n) {
     const int fl = issue(n);
 #pragma unroll
     for (int st = 0; st < SPT; ++st) {
+      // Issue priority alternates between the two wavefronts of a SIMD:
+      // otherwise the older one always wins arbitration, finishes the
+      // iteration early and idles at the barrier while the younger one runs
+      // alone.
+      if (lead_first == (st == 0)) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
       const int j = n * SPT + st;
       v8 p_cur[2];
       const f32x16 s_next = wv.qk(kslab(j), 0, arow, g);
@@ -954,6 +961,7 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
     wait_vmcnt_dyn<G::PER_WAVE>(fl);
     __syncthreads();
   }
+  __builtin_amdgcn_s_setprio(0);
   for (; n < NIT; ++n) {
     const int fl = issue(n);
     generic(n);
