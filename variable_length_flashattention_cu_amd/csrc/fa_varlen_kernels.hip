@@ -635,6 +635,10 @@ __global__ __launch_bounds__(512, 2) void fwd16_pingpong_kernel(FwdArgs a) {
 // each wavefront waits for its own loads before the barrier that ends the
 // iteration.
 constexpr int kPipeBuffers = 4;
+// K fragments of the next slab that each steady stage reads ahead (half of
+// the slab's eight): their LDS latency then overlaps the end of the stage
+// instead of stalling the first products of the next one.
+constexpr int kPipeKPre = 4;
 
 template <int D, int BN>
 struct PipeGeom {
@@ -655,7 +659,9 @@ template <int D, int BN, bool V_LAYOUT>
 __device__ __forceinline__ void pipe_issue(uint16_t* dst, const uint16_t* __restrict__ base, int64_t row_stride,
                                            int key0, int Lk, int wave, int lane) {
   using G = PipeGeom<D, BN>;
-  const int rows = max(0, min(BN, Lk - key0));
+  // no clamp at zero: head_rows_bytes gives 0 bytes for rows <= 0 (and a
+  // min/max pair would be fused into a vector-only med3)
+  const int rows = min(BN, Lk - key0);
   const u32x4 r = buffer_rsrc_words(base + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
   const uint32_t lds = lds_address(dst);
 #pragma unroll
@@ -700,6 +706,25 @@ struct PipeWave {
       s = Elem16<T>::mfma(av, q[ks], s);
     }
     return s;
+  }
+
+  // The same product with its first NPRE K fragments already in registers
+  // (read by k_pre a stage earlier, so that their LDS latency is hidden).
+  template <int NPRE>
+  __device__ __forceinline__ f32x16 qk_pre(const uint16_t* Ks, const v8 (&pre)[NPRE], int arow, int g) const {
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const v8 av = ks < NPRE ? pre[ks < NPRE ? ks : 0]
+                              : *(const v8*)(Ks + tiling::ks_index<D>(arow, 2 * ks + g));
+      s = Elem16<T>::mfma(av, q[ks], s);
+    }
+    return s;
+  }
+  template <int NPRE>
+  __device__ __forceinline__ static void k_pre(const uint16_t* Ks, v8 (&pre)[NPRE], int arow, int g) {
+#pragma unroll
+    for (int ks = 0; ks < NPRE; ++ks) pre[ks] = *(const v8*)(Ks + tiling::ks_index<D>(arow, 2 * ks + g));
   }
 
   // O^T += V^T P^T for the slab whose first key row in the tile at Vr is
@@ -804,9 +829,19 @@ struct PipeWave {
 };
 
 template <typename T, int D, int BN, bool CAUSAL>
-__device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem& w,
+__device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem& wi,
                                                 uint16_t (&lds_k)[kPipeBuffers][BN * tiling::k_stride<D>()],
                                                 uint16_t (&lds_v)[kPipeBuffers][BN * tiling::k_stride<D>()]) {
+  // the item's fields are workgroup-uniform: keep them in scalar registers so
+  // that the per-iteration load set-up runs on the scalar unit
+  WorkItem w;
+  w.b = __builtin_amdgcn_readfirstlane(wi.b);
+  w.m = __builtin_amdgcn_readfirstlane(wi.m);
+  w.h = __builtin_amdgcn_readfirstlane(wi.h);
+  w.q_start = __builtin_amdgcn_readfirstlane(wi.q_start);
+  w.Lq = __builtin_amdgcn_readfirstlane(wi.Lq);
+  w.k_start = __builtin_amdgcn_readfirstlane(wi.k_start);
+  w.Lk = __builtin_amdgcn_readfirstlane(wi.Lk);
   using G = PipeGeom<D, BN>;
   using Wave = PipeWave<T, D>;
   typedef typename Wave::v8 v8;
@@ -933,6 +968,8 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
     __syncthreads();
   }
   int n = 1;
+  v8 kpre[kPipeKPre];
+  if (n < n_steady) Wave::k_pre(kslab(n * SPT), kpre, arow, g);
   const bool lead_first = wave >= 4;  // wavefronts 4-7 (the younger on each SIMD) lead the first stage
   for (; n < n_steady; ++n) {
     const int fl = issue(n);
@@ -946,9 +983,12 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
       else __builtin_amdgcn_s_setprio(0);
       const int j = n * SPT + st;
       v8 p_cur[2];
-      const f32x16 s_next = wv.qk(kslab(j), 0, arow, g);
+      const f32x16 s_next = wv.qk_pre(kslab(j), kpre, arow, g);
       const bool ok = wv.softmax_fast(s_cur, p_cur, a.scale_log2);
       wv.pv(vslab(j), 0, p_prev, lane);
+      // first K fragments of the next stage (its tile is resident: K tile
+      // n + 1 is read in this iteration already)
+      Wave::k_pre(kslab(j + 1), kpre, arow, g);
       if (__builtin_expect(!ok, 0)) {  // rare: redo the slab with raised references, O rescaled after PV(j-1)
         asm volatile("" ::: "memory");  // a real branch: the redo must not be executed speculatively
         float alpha;
