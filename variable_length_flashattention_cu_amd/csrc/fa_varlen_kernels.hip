@@ -979,7 +979,7 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
       // otherwise the older one always wins arbitration, finishes the
       // iteration early and idles at the barrier while the younger one runs
       // alone.
-      if (lead_first == (st == 0)) __builtin_amdgcn_s_setprio(1);
+      if (lead_first == ((st & 1) == 0)) __builtin_amdgcn_s_setprio(1);
       else __builtin_amdgcn_s_setprio(0);
       const int j = n * SPT + st;
       v8 p_cur[2];
@@ -1234,14 +1234,14 @@ hipError_t launch_fwd16(int head_dim, bool causal, int grid, const FwdArgs& a, h
     return causal ? launch(fwd16_pipe_kernel<T, 128, 64, true>, grid, 512, stream, a)
                   : launch(fwd16_pipe_kernel<T, 128, 64, false>, grid, 512, stream, a);
   if (head_dim == 96)
-    return causal ? launch(fwd16_pingpong_kernel<T, 96, 64, true>, grid, 512, stream, a)
-                  : launch(fwd16_pingpong_kernel<T, 96, 64, false>, grid, 512, stream, a);
+    return causal ? launch(fwd16_pipe_kernel<T, 96, 64, true>, grid, 512, stream, a)
+                  : launch(fwd16_pipe_kernel<T, 96, 64, false>, grid, 512, stream, a);
+  if (head_dim == 64)
+    return causal ? launch(fwd16_pipe_kernel<T, 64, 128, true>, grid, 512, stream, a)
+                  : launch(fwd16_pipe_kernel<T, 64, 128, false>, grid, 512, stream, a);
   if (head_dim == 256)
     return causal ? launch(fwd16_pingpong_kernel<T, 256, 32, true>, grid, 512, stream, a)
                   : launch(fwd16_pingpong_kernel<T, 256, 32, false>, grid, 512, stream, a);
-  if (head_dim == 64)
-    return causal ? launch(fwd16_pingpong_kernel<T, 64, 128, true>, grid, 512, stream, a)
-                  : launch(fwd16_pingpong_kernel<T, 64, 128, false>, grid, 512, stream, a);
   return hipErrorInvalidValue;
 }
 
