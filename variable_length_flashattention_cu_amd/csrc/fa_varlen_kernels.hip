@@ -1009,24 +1009,35 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
     __syncthreads();
   }
 
-  // ---- epilogue: normalise, write out (16-bit, round to nearest even) and lse
+  // ---- epilogue: normalise, write out (16-bit, round to nearest even) and lse.
+  // The wavefront's rows go through its own 32-row slice of the K buffers
+  // (free after the last barrier; every load has landed): registers hold 4
+  // columns per row and lane, LDS hands them back as 16-byte row pieces, so
+  // each global store writes whole rows instead of 8 bytes of 32 rows.
   T* __restrict__ op = (T*)a.out;
   const float l = pair_sum(wv.l_run);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (row < w.Lq) {
-    T* dst = op + (int64_t)(w.q_start + row) * rs + (int64_t)w.h * D;
+  uint16_t* stage = &lds_k[0][0] + wave * 32 * Wave::KS;
 #pragma unroll
-    for (int db = 0; db < Wave::DB; ++db)
+  for (int db = 0; db < Wave::DB; ++db)
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        typename Elem16<T>::v4 v4;
+    for (int s4 = 0; s4 < 4; ++s4) {
+      typename Elem16<T>::v4 v4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (T)(wv.o[db][4 * s4 + c] * inv);
-        *(typename Elem16<T>::v4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
-      }
-    if (g == 0)
-      a.lse[(int64_t)w.h * a.total_q + w.q_start + row] = l > 0.f ? (wv.m_run + fast_log2(l)) * kLn2 : kNegInf;
+      for (int c = 0; c < 4; ++c) v4[c] = (T)(wv.o[db][4 * s4 + c] * inv);
+      *(typename Elem16<T>::v4*)(stage + tiling::ks_index<D>(l32, 4 * db + s4) + 4 * g) = v4;
+    }
+  constexpr int CH = D / 8;  // 16-byte pieces per row
+  static_assert((32 * CH) % 64 == 0, "row pieces must fill whole wavefront passes");
+#pragma unroll
+  for (int it = 0; it < 32 * CH / 64; ++it) {
+    const int c = it * 64 + lane;
+    const int r = c / CH, ch = c % CH;
+    const v8 val = *(const v8*)(stage + tiling::ks_index<D>(r, ch));
+    if (wrow0 + r < w.Lq) *(v8*)(op + (int64_t)(w.q_start + wrow0 + r) * rs + (int64_t)w.h * D + 8 * ch) = val;
   }
+  if (row < w.Lq && g == 0)
+    a.lse[(int64_t)w.h * a.total_q + w.q_start + row] = l > 0.f ? (wv.m_run + fast_log2(l)) * kLn2 : kNegInf;
 }
 
 template <typename T, int D, int BN, bool CAUSAL>
