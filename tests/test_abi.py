@@ -374,7 +374,7 @@ def test_kvcache_validation():
     t = kv_tensors()
     edit(t, "kc", dtype=F16)
     assert call_kv(t) == DTYPE
-    for D in (96, 256):
+    for D in (32, 80, 160, 512):
         assert call_kv(kv_tensors(D=D)) == HEAD_DIM
     assert call_kv(kv_tensors(Hk=3)) == SHAPE
     assert call_kv(kv_tensors(), max_q=2) == SHAPE

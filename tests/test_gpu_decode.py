@@ -9,7 +9,7 @@ padding, empty and single-key sequences, key lengths around the 32-key tile,
 one and several query rows per sequence (up to several 32-row tiles of
 query-head x row), causal and not, MHA/GQA/MQA, explicit split counts
 including more splits than tiles, fp16, and the bench's decode batch at full
-size.
+size, and head_dim 64, 96 and 256 besides 128.
 """
 import numpy as np
 import pytest
@@ -68,6 +68,18 @@ def test_decode_leftpad(fa, causal):
     wl = workload_decode("dec_leftpad", [1, 2, 1, 3], [40, 300, 5, 129], 8, 2, 128, "bf16", seed=32, cache_rows=300,
                          leftpad=[7, 100, 5, 0])
     run_case(fa, wl, causal)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("head_dim", [64, 96, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_head_dims(fa, head_dim, dtype, causal):
+    # every head_dim the decode kernels take besides the 128 of the other
+    # cases: paged cache with left padding, GQA, several query rows per
+    # sequence, an empty and a single-key sequence, tile-edge key lengths
+    wl = workload_decode(f"dec_d{head_dim}_{dtype}", [1, 3, 1, 2, 1], [0, 300, 1, 64, 97], 6, 2, head_dim, dtype,
+                         seed=40 + head_dim, cache_rows=32, leftpad=[0, 17, 0, 3, 0], paged=True)
+    run_case(fa, wl, causal, num_splits=3)
 
 
 @pytest.mark.parametrize("page", [16, 256])

@@ -517,7 +517,7 @@ int fa_varlen_fwd_kvcache(const fa_tensor* q, const fa_tensor* k_cache, const fa
       !rank_ok(*cu_seqlens_q, 1) || !rank_ok(*seqlens_k, 1))
     return FA_ERR_SHAPE;
   const int64_t D = q->shape[2];
-  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 64 && D != 96 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   const int64_t Tq = q->shape[0], H = q->shape[1], Hk = k_cache->shape[1];
   const int64_t batch = cu_seqlens_q->shape[0] - 1;
   if (batch < 0 || H < 1 || Hk < 1 || H % Hk != 0 || k_cache->shape[2] != D || !same_shape(*k_cache, *v_cache) ||

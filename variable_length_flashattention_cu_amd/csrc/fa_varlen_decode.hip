@@ -78,8 +78,10 @@ __device__ __forceinline__ int64_t cache_offset(const DecArgs& a, int b, int p, 
   return row * a.kv_row_stride + (int64_t)hk * D;
 }
 
+// Two wavefronts per SIMD up to head_dim 128; at 256 the output and the
+// tile's K and V registers need more than half a SIMD's registers, so one.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void decode16_kernel(DecArgs a) {
   // 16x16x32 MFMA layout (gfx950): lane l, group G = l/16, i = l%16:
   //   A operand: row i, k = 8G..8G+7;  B operand: column i, k = 8G..8G+7;
   //   accumulator register r: row 4G + r, column i.
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
   constexpr int LOADS = kDecTile * D / 8 / 64;  // 16-byte loads per lane for one of K or V
   using E = Elem16<T>;
   typedef typename E::v8 v8;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kDecWaves][kDecTile * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kDecWaves][kDecTile * tiling::k_stride<D>()];
 
   // item: (sequence b, key/value head hk, split s)
   const int item = blockIdx.x;
@@ -299,12 +301,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   const float m_use = m == kNegInf ? 0.f : m;
-  constexpr int PER = D / 64;  // dims per lane (1 or 2)
+  // lane holds dimensions lane + 64 j (j < PER); the last group may be partial
+  constexpr int PER = (D + 63) / 64;
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   float lsum = 0.f;
-  const float* po = a.part_o + rh * npart * D + lane * PER;
+  const float* po = a.part_o + rh * npart * D + lane;
   for (int p0 = 0; p0 < npart; p0 += 64) {
     // weight of partial p0 + lane (0 for empty partials and past the end)
     const int p = p0 + lane;
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
       for (int u = 0; u < 4; ++u) {
         wv[u] = __shfl(wl, i + u, 64);
 #pragma unroll
-        for (int j = 0; j < PER; ++j) x[u][j] = po[(int64_t)(p0 + i + u) * D + j];
+        for (int j = 0; j < PER; ++j) x[u][j] = 64 * j + lane < D ? po[(int64_t)(p0 + i + u) * D + 64 * j] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
       const float wv = __shfl(wl, i, 64);
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        const float x = po[(int64_t)(p0 + i) * D + j];
+        const float x = 64 * j + lane < D ? po[(int64_t)(p0 + i) * D + 64 * j] : 0.f;
         acc[j] += wv != 0.f ? wv * x : 0.f;
       }
     }
@@ -340,7 +343,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   T* op = (T*)a.out + rh * D;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) op[lane * PER + j] = (T)(acc[j] * inv);
+  for (int j = 0; j < PER; ++j)
+    if (64 * j + lane < D) op[64 * j + lane] = (T)(acc[j] * inv);
   if (lane == 0) {
     const int64_t row = rh / a.heads;
     const int h = (int)(rh % a.heads);
@@ -358,15 +362,24 @@ template <typename T>
 hipError_t launch_decode_t(int head_dim, bool causal, int64_t grid, int64_t grid_c, const DecArgs& a,
                            hipStream_t stream) {
   hipError_t e;
-  if (head_dim == 128)
-    e = causal ? launch(decode16_kernel<T, 128, true>, grid, stream, a)
-               : launch(decode16_kernel<T, 128, false>, grid, stream, a);
-  else
-    e = causal ? launch(decode16_kernel<T, 64, true>, grid, stream, a)
-               : launch(decode16_kernel<T, 64, false>, grid, stream, a);
+  switch (head_dim) {
+    case 64: e = causal ? launch(decode16_kernel<T, 64, true>, grid, stream, a)
+                        : launch(decode16_kernel<T, 64, false>, grid, stream, a); break;
+    case 96: e = causal ? launch(decode16_kernel<T, 96, true>, grid, stream, a)
+                        : launch(decode16_kernel<T, 96, false>, grid, stream, a); break;
+    case 128: e = causal ? launch(decode16_kernel<T, 128, true>, grid, stream, a)
+                         : launch(decode16_kernel<T, 128, false>, grid, stream, a); break;
+    case 256: e = causal ? launch(decode16_kernel<T, 256, true>, grid, stream, a)
+                         : launch(decode16_kernel<T, 256, false>, grid, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   if (e != hipSuccess || grid_c == 0) return e;
-  return head_dim == 128 ? launch(decode_combine_kernel<T, 128>, grid_c, stream, a)
-                         : launch(decode_combine_kernel<T, 64>, grid_c, stream, a);
+  switch (head_dim) {
+    case 64: return launch(decode_combine_kernel<T, 64>, grid_c, stream, a);
+    case 96: return launch(decode_combine_kernel<T, 96>, grid_c, stream, a);
+    case 128: return launch(decode_combine_kernel<T, 128>, grid_c, stream, a);
+    default: return launch(decode_combine_kernel<T, 256>, grid_c, stream, a);
+  }
 }
 
 }  // namespace
