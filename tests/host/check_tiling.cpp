@@ -251,10 +251,10 @@ static void check_f32() {
   std::printf("f32 D=%d NW=%d: ok\n", D, NW);
 }
 
-// Ping-pong forward kernel: K and V tiles of BN keys loaded straight into LDS
-// (16 bytes per lane at LDS slot p = 64 * load + lane, 4 waves x 4 loads per
-// tile), K in the ks_index layout, V row-major (vr_index) and read with
-// transposing LDS reads for the PV product.
+// Forward kernel: K and V tiles of BN keys loaded straight into LDS (16 bytes
+// per lane at LDS slot p = 64 * load + lane; the NW wavefronts take 1024 / NW
+// consecutive slots each), K in the ks_index layout, V row-major (vr_index)
+// and read with transposing LDS reads for the PV product.
 template <int D, int BN, bool V_LAYOUT>
 static void check_direct(long H) {
   constexpr int KS = k_stride<D>(), CPR = KS / 8, SLOTS = BN * CPR;
@@ -325,7 +325,62 @@ static void check_direct(long H) {
   std::printf("direct %s D=%d BN=%d H=%ld: ok\n", V_LAYOUT ? "V" : "K", D, BN, H);
 }
 
+// The software-pipelined forward kernel's other LDS accesses: the K operand
+// reads of S^T = K Q^T from every 32-key slab of a tile, and the epilogue,
+// where wavefront w stages its 32 normalised rows in rows 32w .. 32w+31 of the
+// K buffers (ks_index layout, 4 columns per lane and write) and reads them
+// back as 16-byte row pieces for the global stores.
+template <int D, int BN, int NW>
+static void check_pipe() {
+  constexpr int KS = k_stride<D>(), TILE = BN * KS, NBUF = 4, CH = D / 8;
+  CHECK(NW * 32 * KS <= NBUF * TILE, "D=%d: %d waves' staging rows exceed the K buffers", D, NW);
+  for (int lane = 0; lane < 64; ++lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+    for (int row0 = 0; row0 < BN; row0 += 32)
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int idx = ks_index<D>(row0 + key_of_arow(l32), 2 * ks + g);
+        CHECK(idx >= 0 && idx % 8 == 0 && idx + 8 <= TILE, "D=%d K operand read %d", D, idx);
+      }
+  }
+  for (int w = 0; w < NW; ++w) {
+    const int base = w * 32 * KS;
+    std::vector<int> wrote(32 * D, 0), read(32 * D, 0);
+    std::vector<int> at(32 * KS, -1);  // element of the slice -> (row * D + col) written there
+    for (int lane = 0; lane < 64; ++lane) {
+      const int l32 = lane & 31, g = lane >> 5;
+      for (int db = 0; db < D / 32; ++db)
+        for (int s4 = 0; s4 < 4; ++s4)
+          for (int c = 0; c < 4; ++c) {
+            const int idx = ks_index<D>(l32, 4 * db + s4) + 4 * g + c;
+            const int col = 32 * db + 8 * s4 + 4 * g + c;
+            CHECK(idx >= 0 && idx < 32 * KS && base + idx < NBUF * TILE, "D=%d staging write %d", D, idx);
+            CHECK(at[idx] < 0, "D=%d staging element %d written twice", D, idx);
+            at[idx] = l32 * D + col;
+            wrote[l32 * D + col]++;
+          }
+    }
+    for (int it = 0; it < 32 * CH / 64; ++it)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int c = it * 64 + lane, r = c / CH, ch = c % CH;
+        for (int j = 0; j < 8; ++j) {
+          const int idx = ks_index<D>(r, ch) + j;
+          CHECK(idx >= 0 && idx < 32 * KS, "D=%d staging read %d", D, idx);
+          CHECK(at[idx] == r * D + 8 * ch + j, "D=%d staging read (%d,%d)+%d finds element %d", D, r, ch, j, at[idx]);
+          read[r * D + 8 * ch + j]++;
+        }
+      }
+    for (int e = 0; e < 32 * D; ++e)
+      CHECK(wrote[e] == 1 && read[e] == 1, "D=%d staging element %d written %d, read %d times", D, e, wrote[e],
+            read[e]);
+  }
+  std::printf("pipe D=%d BN=%d NW=%d: ok\n", D, BN, NW);
+}
+
 int main() {
+  check_pipe<64, 128, 8>();
+  check_pipe<96, 64, 8>();
+  check_pipe<128, 64, 8>();
+  check_pipe<256, 32, 4>();
   for (long H : {1L, 3L, 16L}) {
     check_direct<64, 128, false>(H);
     check_direct<64, 128, true>(H);

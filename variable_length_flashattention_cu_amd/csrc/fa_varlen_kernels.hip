@@ -7,10 +7,12 @@
 //                              iplexlaw.co.kr "FlashAttention-2 GPU work
 //                              partitioning", section "Tres mejoras en la
 //                              utilización de la GPU").
-//   * fwd16_pingpong_kernel -- 16-bit (bf16 or fp16) in/out, head_dim 64, 96,
-//                              128 and 256: two wave groups alternate MFMA and
-//                              softmax phases; 16-bit MFMA for the two
-//                              contractions, fp32 online softmax.
+//   * fwd16_pipe_kernel     -- 16-bit (bf16 or fp16) in/out, head_dim 64, 96,
+//                              128 and 256: software-pipelined wavefronts
+//                              (each stage: the first product of the next
+//                              slab, the softmax of this one, the second
+//                              product of the previous one); 16-bit MFMA for
+//                              the two contractions, fp32 online softmax.
 //   * fwd_f32_kernel        -- fp32 in/out, fp32 MFMA, same online softmax.
 //   * check_cu_kernel       -- optional device validation of the offsets.
 //
@@ -23,7 +25,7 @@
 // Forward-kernel organisation (all dtypes)
 // -----------------------------------------
 // One workgroup owns one (sequence b, query block m, head h) work item: BM
-// query rows split across NW wavefronts, 32*QB rows per wavefront (split-Q:
+// query rows split across NW wavefronts, 32 rows per wavefront (split-Q:
 // the waves share the K/V tiles and never exchange partial results, as the
 // pages describe for FlashAttention-2's forward pass, zepes.com "Comprendiendo
 // Flash-Atención y Flash-Atención-2", section "FlashAttention-2").  K/V tiles
@@ -201,378 +203,16 @@ __global__ __launch_bounds__(256) void check_cu_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// bf16 forward
+// 16-bit LDS layouts
 // ---------------------------------------------------------------------------
-// LDS layouts (16-byte chunks are XOR-swizzled so that the MFMA operand reads
-// hit distinct banks within each group of 8 and of 16 lanes):
-//   Ks[key][d]   key-major, one row of D bf16 per key (both kernels)
-//   Vt[d][key]   dimension-major (V transposed), one row of BN bf16 per d
-//                (head_dim 64 kernel: written transposed from registers)
-//   Vr[key][d]   key-major like Ks, read with transposing LDS reads
-//                (ping-pong kernel: loaded straight from global memory)
-//
-// Index arithmetic (swizzles, chunk/unit mappings, LDS indices, byte extents)
-// lives in fa_varlen_tiling.h, shared with the host-side bounds checker.
-
-// Tile staging by direct global -> LDS loads, shared by the 4 waves of one
-// group (256 lanes).  The tile lands in the swizzled K layout
-// (tiling::ks_index): LDS chunk slot p = 64 * instruction + lane holds the
-// logical chunk that the swizzle stores there, so each lane loads that chunk.
-// Keys at or past Lk read as zeros (buffer range check).  At head_dim 96 the
-// last 4 slots of a 128-element row hold no chunk; their lanes load a chunk of
-// the same row that is never read.
-// V tiles use the same scheme with the row-major V swizzle (tiling::vr_index).
-template <int D, int BN, bool V_LAYOUT>
-struct RowDirect {
-  static constexpr int KS = tiling::k_stride<D>();
-  static constexpr int CPR = KS / 8;                 // 16-byte slots per LDS row
-  static constexpr int PER_WAVE = BN * CPR / 256;    // loads per wave per tile
-  static_assert(BN * CPR % 256 == 0, "tile must split into whole wave loads");
-  static_assert(PER_WAVE == 4, "the wait counts below assume 4 loads per tile");
-
-  // keys key0 .. key0+BN-1 of the head slice at `base` into the LDS tile at dst
-  __device__ __forceinline__ static void issue(uint16_t* dst, const uint16_t* __restrict__ base,
-                                               int64_t row_stride, int key0, int Lk, int gwave, int lane) {
-    const int rows = max(0, min(BN, Lk - key0));
-    const u32x4 r = buffer_rsrc_words(base + (int64_t)key0 * row_stride, head_rows_bytes(rows, row_stride, D, 2));
-    const uint32_t lds = lds_address(dst);
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int seg = gwave * PER_WAVE + i;
-      int row, ch;
-      tiling::direct_slot_chunk<D, V_LAYOUT>(seg * 64 + lane, row, ch);
-      const uint32_t off = ((uint32_t)row * (uint32_t)row_stride + (uint32_t)ch * 8u) * 2u;
-      lds_dma16(r, off, lds + (uint32_t)seg * 1024u);
-    }
-  }
-};
-
-// Scheduling order of a block of NM MFMAs fed by NR LDS operand reads: the
-// first PRE reads, then one MFMA and one read alternately, then the
-// remaining MFMAs, so that PRE reads are in flight ahead of their use.
-template <int NM, int NR, int AHEAD = 8>
-__device__ __forceinline__ void operand_pipeline() {
-  constexpr int PRE = NR < AHEAD ? NR : AHEAD;
-  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);  // LDS reads
-#pragma unroll
-  for (int i = 0; i < NR - PRE; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR + PRE, 0);
-}
-
-// Scheduling order of a block of NM MFMAs fed by NR LDS reads (NR a multiple
-// of NM): the first AHEAD reads, then each MFMA followed by the reads of a
-// later one, so that AHEAD reads are in flight ahead of their use.
-template <int I, int NM, int NR, int AHEAD>
-__device__ __forceinline__ void read_ahead_step() {
-  if constexpr (I < NM) {
-    constexpr int PER = NR / NM;
-    constexpr int LEFT = NR - AHEAD - I * PER;
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    if constexpr (LEFT > 0) __builtin_amdgcn_sched_group_barrier(0x100, LEFT < PER ? LEFT : PER, 0);
-    read_ahead_step<I + 1, NM, NR, AHEAD>();
-  }
-}
-template <int NM, int NR, int AHEAD>
-__device__ __forceinline__ void read_ahead() {
-  static_assert(NR % NM == 0 && AHEAD <= NR, "reads per MFMA");
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // LDS reads
-  read_ahead_step<0, NM, NR, AHEAD>();
-}
-
-// Per-wave state and the three tile-level steps of the 16-bit forward pass.
-template <typename T, int D, int BN, int QB>
-struct Wave16 {
-  typedef typename Elem16<T>::v8 v8;
-  static constexpr int KSTEPS = D / 16;  // MFMA k-steps for Q K^T
-  static constexpr int KB = BN / 32;     // 32-key blocks per tile
-  static constexpr int DB = D / 32;      // 32-dim blocks of the output
-  static constexpr int AHEAD = D > 128 ? 4 : 8;  // operand reads in flight (registers at D=256)
-
-  v8 qreg[QB][KSTEPS];  // Q^T as the B operand
-  f32x16 o[QB][DB];         // O^T accumulators
-  float m_run[QB], l_run[QB];
-
-  // S^T = K Q^T for one key tile (K from LDS, swizzled rows), the 32-key
-  // blocks interleaved (independent accumulation chains) and the LDS operand
-  // reads issued ahead of their use.
-  __device__ __forceinline__ void qk_ordered(const uint16_t* Ks, f32x16 (&s)[QB][KB], int arow, int g) const {
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int krow = kb * 32 + arow;
-        const v8 av = *(const v8*)(Ks + tiling::ks_index<D>(krow, 2 * ks + g));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const f32x16 c = ks == 0 ? f32x16{} : s[qb][kb];
-          s[qb][kb] = Elem16<T>::mfma(av, qreg[qb][ks], c);
-        }
-      }
-    }
-    operand_pipeline<KSTEPS * KB * QB, KSTEPS * KB, AHEAD>();
-  }
-
-  // -inf for keys past the end of the sequence or (causal) above the diagonal
-  template <bool CAUSAL>
-  __device__ __forceinline__ static void mask(f32x16 (&s)[QB][KB], int key0, int row0, int l32, int g, int Lk,
-                                              int shift) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int i = row0 + qb * 32 + l32;
-      const int lim = CAUSAL ? min(Lk - 1, i + shift) : (Lk - 1);  // last visible key
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key0 + kb * 32 + 16 * g + r > lim) s[qb][kb][r] = kNegInf;
-    }
-  }
-
-  // Online softmax of one tile: probabilities (bf16, in the PV B-operand
-  // layout), running l; returns whether O must be rescaled by alpha[qb].
-  // The returned flag is formed from the tile's row sums, so the (rarely
-  // taken) rescale branch cannot be placed ahead of the exponentials: they
-  // stay in one basic block with the MFMAs of the next score tile.
-  __device__ __forceinline__ bool softmax(const f32x16 (&s)[QB][KB], v8 (&p)[QB][KB][2], float (&alpha)[QB],
-                                          float scale_log2) {
-    bool any_rescale = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-      const float m_tile = pair_max(mx) * scale_log2;
-      const bool need = wave_any(m_tile > m_run[qb] + kRescaleSlack);
-      const float m_new = need ? fmaxf(m_run[qb], m_tile) : m_run[qb];
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      alpha[qb] = fast_exp2(m_run[qb] - m_use);  // 1 when the reference is kept; branch-free
-      m_run[qb] = m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pe = fast_exp2(__builtin_fmaf(s[qb][kb][8 * t + e], scale_log2, -m_use));
-            lsum += pe;
-            p[qb][kb][t][e] = (T)pe;
-          }
-      l_run[qb] = l_run[qb] * alpha[qb] + lsum;
-      any_rescale |= wave_any(alpha[qb] != 1.f && !(lsum < 0.f));  // lsum >= 0: ties the flag to the exps
-    }
-    return any_rescale;
-  }
-
-  __device__ __forceinline__ void rescale(const float (&alpha)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
-  }
-
-  // O^T += V^T P^T with V row-major in LDS (tiling::vr_index).  The A operand
-  // of step (kb, t) -- keys kb*32 + 16g + 8t .. +7 of dimension db*32 + l32 --
-  // comes from two transposing reads: in each 16-lane group, lane i reads
-  // row r0 + i/4, dims c0 + 4(i%4) .. +3 (c0 = db*32 + 16*((lane/16)%2)) and
-  // receives dim c0 + i of rows r0 .. r0+3.
-  __device__ __forceinline__ void pv_rowmajor(const uint16_t* Vr, const v8 (&p)[QB][KB][2], int lane) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const int g = lane >> 5;
-    auto rd = [&](int row0, int db) {
-      const uint16_t* a = Vr + tiling::vr_tr_index<D>(lane, row0, db);
-      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
-    };
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int r0 = kb * 32 + 16 * g + 8 * t;
-          const s16x4 lo = rd(r0, db), hi = rd(r0 + 4, db);
-          const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const v8 av = __builtin_bit_cast(v8, v);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[qb][db] = Elem16<T>::mfma(av, p[qb][kb][t], o[qb][db]);
-        }
-    // fewer transposing reads in flight than operand reads of QK (measured:
-    // 4 ahead at head_dim <= 128 beat 8 and 16)
-    read_ahead<DB * KB * 2 * QB, DB * KB * 4, AHEAD / 2>();
-  }
-};
-
-// Ping-pong schedule.  The workgroup's 8 wavefronts form two groups of 4
-// (waves 0-3 and 4-7); wave w runs on SIMD w % 4, so every SIMD holds one wave
-// of each group.  Every wave runs the same loop of a matrix phase M(n) and a
-// vector phase V(n), each closed by a workgroup barrier, but group 1 runs one
-// phase behind group 0 (it passes one extra barrier first, group 0 one extra
-// barrier last).  Between two barriers one wave of each SIMD therefore issues
-// MFMAs while the other runs the softmax, and the matrix cores and the vector
-// ALU work at the same time:
-//
-//   slot        2n                          2n+1
-//   group 0     M(n): O += V(n-1)^T P(n-1), V(n): load V(n+1),
-//                     S(n) = K(n) Q^T             softmax S(n) -> P(n)
-//   group 1     V(n-1): load K(n+2),        M(n)
-//                     softmax S(n-1)
-//
-// K(n) is read in slots 2n and 2n+1, V(n-1) likewise.  Tiles go from global
-// memory straight into LDS, three buffers per operand: K(m) and V(m) live in
-// buffer m % 3.  Group 1 loads K(n+2) at the start of slot 2n (the buffer of
-// K(n-1), last read in slot 2n-1) and waits for K(n+1) at the end of slot
-// 2n+1; group 0 loads V(n+1) at the start of slot 2n+1 (the buffer of V(n-2))
-// and waits for V(n) at the end of that slot.  A K load has four slots to
-// land, a V load three.
-constexpr int kPingPongBuffers = 3;  // K and V tiles in LDS, each
-
-template <typename T, int D, int BN, bool CAUSAL>
-__device__ __forceinline__ void fwd16_pingpong_item(const FwdArgs& a, const WorkItem& w,
-                                                    uint16_t (&lds_k)[kPingPongBuffers][BN * tiling::k_stride<D>()],
-                                                    uint16_t (&lds_v)[kPingPongBuffers][BN * tiling::k_stride<D>()]) {
-  constexpr int NW = 8;
-  constexpr int BM = 32 * NW;
-  using KDma = RowDirect<D, BN, false>;  // K staging by group 1 (4 waves)
-  using VDma = RowDirect<D, BN, true>;   // V staging by group 0 (4 waves)
-  using Wave = Wave16<T, D, BN, 1>;
-  constexpr int KB = Wave::KB;
-
-  int n_full, n_end;
-  key_tiles<BM, BN, CAUSAL>(w, n_full, n_end);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int gtid = tid & 255;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int wrow0 = w.m * BM + wave * 32;  // first query row of this wave (in sequence)
-  const int shift = w.Lk - w.Lq;
-  const int64_t rs = a.row_stride;
-
-  // key/value head of this query head; K/V rows hold kv_heads * D elements
-  const int64_t rsk = a.kv_row_stride;
-  const int hk = w.h / a.head_group;
-  const uint16_t* __restrict__ kbase = (const uint16_t*)a.k + (int64_t)w.k_start * rsk + (int64_t)hk * D;
-  const uint16_t* __restrict__ vbase = (const uint16_t*)a.v + (int64_t)w.k_start * rsk + (int64_t)hk * D;
-
-  // The first tiles are requested before Q and one wait covers all of them:
-  // group 1 loads K(0..2) straight into the three K buffers, group 0 loads
-  // V(0).
-  if (n_end > 0) {
-    if (grp == 1) {
-      for (int j = 0; j < kPingPongBuffers && j < n_end; ++j)
-        KDma::issue(lds_k[j], kbase, rsk, j * BN, w.Lk, wave - 4, lane);
-    } else {
-      VDma::issue(lds_v[0], vbase, rsk, 0, w.Lk, wave, lane);
-    }
-  }
-
-  Wave wv;
-  {  // Q rows past the end of the sequence load as zeros
-    const int qrows = max(0, min(32, w.Lq - wrow0));
-    const __amdgpu_buffer_rsrc_t rq =
-        buffer_rsrc((const uint16_t*)a.q + (int64_t)(w.q_start + wrow0) * rs + (int64_t)w.h * D,
-                    head_rows_bytes(qrows, rs, D, 2));
-#pragma unroll
-    for (int ks = 0; ks < Wave::KSTEPS; ++ks) {
-      const uint32_t off = ((uint32_t)l32 * (uint32_t)rs + 16 * ks + 8 * g) * 2u;
-      wv.qreg[0][ks] = __builtin_bit_cast(typename Wave::v8, buffer_load16(rq, off));
-    }
-  }
-  wv.m_run[0] = kNegInf;
-  wv.l_run[0] = 0.f;
-#pragma unroll
-  for (int db = 0; db < Wave::DB; ++db) wv.o[0][db] = f32x16{};
-
-  // Tiles this wave needs: all n < n_wave (rows past the sequence end need
-  // none; causal rows need keys up to their diagonal).
-  int n_wave = 0;
-  if (wrow0 < w.Lq) {
-    if (CAUSAL) {
-      const int last_key = wrow0 + 31 + shift;
-      n_wave = last_key < 0 ? 0 : min(n_end, last_key / BN + 1);
-    } else {
-      n_wave = n_end;
-    }
-  }
-
-  const int arow = key_of_arow(l32);
-  wait_vmcnt<0>();  // Q, and K(0..2) or V(0)
-  __syncthreads();
-  if (grp == 1) __syncthreads();  // group 1's idle first slot
-
-  f32x16 s[1][KB];
-  typename Wave::v8 p[1][KB][2];
-  int kbuf = 0;  // n % kPingPongBuffers: K(n) and V(n)
-  int vprev = kPingPongBuffers - 1;  // (n - 1) % kPingPongBuffers: V(n-1)
-  for (int n = 0; n <= n_end; ++n) {
-    // matrix phase: O += V(n-1)^T P(n-1) and S(n) = K(n) Q^T
-    if (n >= 1 && n - 1 < n_wave) wv.pv_rowmajor(lds_v[vprev], p, lane);
-    if (n < n_wave) wv.qk_ordered(lds_k[kbuf], s, arow, g);
-    if (grp == 1) {
-      // K(n+1) is read after the coming barrier: it must have landed.  Loaded
-      // after it, only K(n+2) may still be in flight (4 loads per wave).
-      if (n + 2 < n_end) wait_vmcnt<KDma::PER_WAVE>();
-      else wait_vmcnt<0>();
-    }
-    __syncthreads();
-    // vector phase: first the loads of later tiles, which then fly during the
-    // softmax.  Group 1 loads K(n+3) into the buffer K(n) left (last read in
-    // the previous slot); group 0 loads V(n+1) into the buffer V(n-2) left
-    // (last read two slots ago).  Measured: issuing them here rather than
-    // after the softmax (K) or in the matrix phase (V) is 1-5% faster.
-    if (grp == 1 && n + 3 < n_end) KDma::issue(lds_k[kbuf], kbase, rsk, (n + 3) * BN, w.Lk, wave - 4, lane);
-    if (grp == 0 && n + 1 < n_end) {
-      const int vnext = kbuf == kPingPongBuffers - 1 ? 0 : kbuf + 1;
-      VDma::issue(lds_v[vnext], vbase, rsk, (n + 1) * BN, w.Lk, wave, lane);
-    }
-    // masks, online softmax and the rare rescale of O for tile n
-    if (n < n_wave) {
-      if (n >= n_full) Wave::template mask<CAUSAL>(s, n * BN, wrow0, l32, g, w.Lk, shift);
-      float alpha[1];
-      if (wv.softmax(s, p, alpha, a.scale_log2)) wv.rescale(alpha);
-    }
-    if (grp == 0) {
-      // V(n) is read after the coming barrier: it must have landed.  Loaded
-      // after it, only V(n+1) may still be in flight (4 loads per wave).
-      if (n + 1 < n_end) wait_vmcnt<VDma::PER_WAVE>();
-      else wait_vmcnt<0>();
-    }
-    vprev = kbuf;
-    kbuf = kbuf == kPingPongBuffers - 1 ? 0 : kbuf + 1;
-    __syncthreads();
-  }
-  if (grp == 0) __syncthreads();  // group 0's idle last slot
-
-  // ---- epilogue: normalise, write out (16-bit, round to nearest even) and lse
-  T* __restrict__ op = (T*)a.out;
-  const int i = wrow0 + l32;
-  const float l = pair_sum(wv.l_run[0]);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (i < w.Lq) {
-    T* dst = op + (int64_t)(w.q_start + i) * rs + (int64_t)w.h * D;
-#pragma unroll
-    for (int db = 0; db < Wave::DB; ++db)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        typename Elem16<T>::v4 v4;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (T)(wv.o[0][db][4 * s4 + c] * inv);
-        *(typename Elem16<T>::v4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
-      }
-    if (g == 0)
-      a.lse[(int64_t)w.h * a.total_q + w.q_start + i] = l > 0.f ? (wv.m_run[0] + fast_log2(l)) * kLn2 : kNegInf;
-  }
-}
+// 16-byte chunks are XOR-swizzled so that the MFMA operand reads hit distinct
+// banks within each group of 8 and of 16 lanes:
+//   Ks[key][d]   key-major, one row of k_stride<D>() elements per key
+//   Vr[key][d]   key-major like Ks (its own swizzle), read with transposing
+//                LDS reads as the A operand of O^T = V^T P^T
+// Both are loaded straight from global memory (direct loads).  Index
+// arithmetic (swizzles, chunk mappings, LDS indices, byte extents) lives in
+// fa_varlen_tiling.h, shared with the host-side bounds checker.
 
 // Work items of one workgroup.  Under a causal mask, query block m of a
 // sequence with M blocks reads about (m+1)/M of its keys, so blocks m and
@@ -599,15 +239,6 @@ __device__ __forceinline__ void run_work(const FwdArgs& a, WorkItem& w, Item&& i
   } else {
     item(w);
   }
-}
-
-template <typename T, int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void fwd16_pingpong_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kPingPongBuffers][BN * tiling::k_stride<D>()];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kPingPongBuffers][BN * tiling::k_stride<D>()];
-  WorkItem w;
-  if (!decode_work(a, w)) return;
-  run_work<256, CAUSAL>(a, w, [&](const WorkItem& wi) { fwd16_pingpong_item<T, D, BN, CAUSAL>(a, wi, lds_k, lds_v); });
 }
 
 // ---------------------------------------------------------------------------
@@ -640,25 +271,25 @@ constexpr int kPipeBuffers = 4;
 // instead of stalling the first products of the next one.
 constexpr int kPipeKPre = 4;
 
-template <int D, int BN>
+template <int D, int BN, int NW>
 struct PipeGeom {
   static constexpr int KS = tiling::k_stride<D>();  // elements per LDS row
   static constexpr int CPR = KS / 8;                 // 16-byte slots per LDS row
   static constexpr int LOADS = BN * CPR / 64;        // wave-wide direct loads per tile
-  static constexpr int PER_WAVE = LOADS / 8;         // per wavefront (8 share a tile)
+  static constexpr int PER_WAVE = LOADS / NW;        // per wavefront (NW share a tile)
   static constexpr int SPT = BN / 32;                // 32-key slabs per tile
   static constexpr int TILE = BN * KS;               // elements per tile buffer
-  static_assert(LOADS % 8 == 0 && PER_WAVE >= 1 && PER_WAVE <= 4, "tile must split into whole wave loads");
+  static_assert(LOADS % NW == 0 && PER_WAVE >= 1 && PER_WAVE <= 4, "tile must split into whole wave loads");
 };
 
 // Direct loads of keys key0 .. key0+BN-1 of the head slice at `base` into the
 // LDS tile at dst, in the K-style (V_LAYOUT false) or row-major V layout; this
 // wavefront's share: slots 64 * (wave * PER_WAVE + i) + lane.  Keys at or past
 // Lk read as zeros (buffer range check).
-template <int D, int BN, bool V_LAYOUT>
+template <int D, int BN, int NW, bool V_LAYOUT>
 __device__ __forceinline__ void pipe_issue(uint16_t* dst, const uint16_t* __restrict__ base, int64_t row_stride,
                                            int key0, int Lk, int wave, int lane) {
-  using G = PipeGeom<D, BN>;
+  using G = PipeGeom<D, BN, NW>;
   // no clamp at zero: head_rows_bytes gives 0 bytes for rows <= 0 (and a
   // min/max pair would be fused into a vector-only med3)
   const int rows = min(BN, Lk - key0);
@@ -828,7 +459,7 @@ struct PipeWave {
   }
 };
 
-template <typename T, int D, int BN, bool CAUSAL>
+template <typename T, int D, int BN, int NW, bool CAUSAL>
 __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem& wi,
                                                 uint16_t (&lds_k)[kPipeBuffers][BN * tiling::k_stride<D>()],
                                                 uint16_t (&lds_v)[kPipeBuffers][BN * tiling::k_stride<D>()]) {
@@ -842,8 +473,9 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
   w.Lq = __builtin_amdgcn_readfirstlane(wi.Lq);
   w.k_start = __builtin_amdgcn_readfirstlane(wi.k_start);
   w.Lk = __builtin_amdgcn_readfirstlane(wi.Lk);
-  using G = PipeGeom<D, BN>;
+  using G = PipeGeom<D, BN, NW>;
   using Wave = PipeWave<T, D>;
+  constexpr int BM = 32 * NW;
   typedef typename Wave::v8 v8;
   constexpr int SPT = G::SPT;
   constexpr int NB = kPipeBuffers;
@@ -851,7 +483,7 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int q0 = w.m * 256;               // first query row of the item (in its sequence)
+  const int q0 = w.m * BM;                // first query row of the item (in its sequence)
   const int wrow0 = q0 + wave * 32;       // first query row of this wavefront
   const int shift = w.Lk - w.Lq;
   const int64_t rs = a.row_stride, rsk = a.kv_row_stride;
@@ -871,7 +503,7 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
   }
   int J = 0;
   {
-    const int last_row = min(w.Lq, q0 + 256) - 1;
+    const int last_row = min(w.Lq, q0 + BM) - 1;
     const int wlast = q0 + ((last_row - q0) & ~31);
     const int hi = CAUSAL ? min(w.Lk, wlast + 32 + shift) : w.Lk;
     J = hi > 0 ? (hi + 31) / 32 : 0;
@@ -881,9 +513,9 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
 
   // first tiles, then Q; one wait covers them all
   if (NT > 0) {
-    pipe_issue<D, BN, false>(lds_k[0], kbase, rsk, 0, w.Lk, wave, lane);
-    pipe_issue<D, BN, true>(lds_v[0], vbase, rsk, 0, w.Lk, wave, lane);
-    if (NT > 1) pipe_issue<D, BN, false>(lds_k[1], kbase, rsk, BN, w.Lk, wave, lane);
+    pipe_issue<D, BN, NW, false>(lds_k[0], kbase, rsk, 0, w.Lk, wave, lane);
+    pipe_issue<D, BN, NW, true>(lds_v[0], vbase, rsk, 0, w.Lk, wave, lane);
+    if (NT > 1) pipe_issue<D, BN, NW, false>(lds_k[1], kbase, rsk, BN, w.Lk, wave, lane);
   }
   Wave wv;
   {  // Q rows past the end of the sequence load as zeros
@@ -919,15 +551,15 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
   auto issue = [&](int n) {
     int in_flight = 0;
     if (n == 0) {
-      if (2 < NT) pipe_issue<D, BN, false>(lds_k[2], kbase, rsk, 2 * BN, w.Lk, wave, lane);
-      if (1 < NT) pipe_issue<D, BN, true>(lds_v[1], vbase, rsk, BN, w.Lk, wave, lane);
+      if (2 < NT) pipe_issue<D, BN, NW, false>(lds_k[2], kbase, rsk, 2 * BN, w.Lk, wave, lane);
+      if (1 < NT) pipe_issue<D, BN, NW, true>(lds_v[1], vbase, rsk, BN, w.Lk, wave, lane);
     }
     if (n + 3 < NT) {
-      pipe_issue<D, BN, false>(lds_k[(n + 3) % NB], kbase, rsk, (n + 3) * BN, w.Lk, wave, lane);
+      pipe_issue<D, BN, NW, false>(lds_k[(n + 3) % NB], kbase, rsk, (n + 3) * BN, w.Lk, wave, lane);
       in_flight += G::PER_WAVE;
     }
     if (n + 2 < NT) {
-      pipe_issue<D, BN, true>(lds_v[(n + 2) % NB], vbase, rsk, (n + 2) * BN, w.Lk, wave, lane);
+      pipe_issue<D, BN, NW, true>(lds_v[(n + 2) % NB], vbase, rsk, (n + 2) * BN, w.Lk, wave, lane);
       in_flight += G::PER_WAVE;
     }
     return in_flight;
@@ -969,26 +601,32 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
   }
   int n = 1;
   v8 kpre[kPipeKPre];
-  if (n < n_steady) Wave::k_pre(kslab(n * SPT), kpre, arow, g);
+  if (SPT > 1 && n < n_steady) Wave::k_pre(kslab(n * SPT), kpre, arow, g);
   const bool lead_first = wave >= 4;  // wavefronts 4-7 (the younger on each SIMD) lead the first stage
+  constexpr bool kAlternate = NW == 8;  // two wavefronts of the workgroup share each SIMD
   for (; n < n_steady; ++n) {
     const int fl = issue(n);
+    // one slab per tile: the first slab of an iteration was only waited for
+    // at the barrier that began it
+    if (SPT == 1) Wave::k_pre(kslab(n), kpre, arow, g);
 #pragma unroll
     for (int st = 0; st < SPT; ++st) {
       // Issue priority alternates between the two wavefronts of a SIMD:
       // otherwise the older one always wins arbitration, finishes the
       // iteration early and idles at the barrier while the younger one runs
       // alone.
-      if (lead_first == ((st & 1) == 0)) __builtin_amdgcn_s_setprio(1);
-      else __builtin_amdgcn_s_setprio(0);
+      if (kAlternate) {
+        if (lead_first == ((st & 1) == 0)) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       const int j = n * SPT + st;
       v8 p_cur[2];
       const f32x16 s_next = wv.qk_pre(kslab(j), kpre, arow, g);
       const bool ok = wv.softmax_fast(s_cur, p_cur, a.scale_log2);
       wv.pv(vslab(j), 0, p_prev, lane);
-      // first K fragments of the next stage (its tile is resident: K tile
-      // n + 1 is read in this iteration already)
-      Wave::k_pre(kslab(j + 1), kpre, arow, g);
+      // first K fragments of the next stage: with two or more slabs per tile
+      // its slab is in K tile n + 1, which this iteration reads already
+      if (SPT > 1) Wave::k_pre(kslab(j + 1), kpre, arow, g);
       if (__builtin_expect(!ok, 0)) {  // rare: redo the slab with raised references, O rescaled after PV(j-1)
         asm volatile("" ::: "memory");  // a real branch: the redo must not be executed speculatively
         float alpha;
@@ -1040,13 +678,15 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
     a.lse[(int64_t)w.h * a.total_q + w.q_start + row] = l > 0.f ? (wv.m_run + fast_log2(l)) * kLn2 : kNegInf;
 }
 
-template <typename T, int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void fwd16_pipe_kernel(FwdArgs a) {
+// NW wavefronts of 32 query rows: 8 (two per SIMD), or 4 (one per SIMD,
+// which leaves a wavefront 512 registers: head_dim 256).
+template <typename T, int D, int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd16_pipe_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[kPipeBuffers][BN * tiling::k_stride<D>()];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[kPipeBuffers][BN * tiling::k_stride<D>()];
   WorkItem w;
   if (!decode_work(a, w)) return;
-  run_work<256, CAUSAL>(a, w, [&](const WorkItem& wi) { fwd16_pipe_item<T, D, BN, CAUSAL>(a, wi, lds_k, lds_v); });
+  run_work<32 * NW, CAUSAL>(a, w, [&](const WorkItem& wi) { fwd16_pipe_item<T, D, BN, NW, CAUSAL>(a, wi, lds_k, lds_v); });
 }
 
 // ---------------------------------------------------------------------------
@@ -1219,7 +859,7 @@ TileConfig tile_config(int dtype, int head_dim) {
   TileConfig c{0, 0, 0};
   if (dtype == 1 || dtype == 2) {  // bf16, fp16
     if (head_dim == 128 || head_dim == 96) c = TileConfig{256, 64, 512};
-    else if (head_dim == 256) c = TileConfig{256, 32, 512};
+    else if (head_dim == 256) c = TileConfig{128, 32, 256};
     else if (head_dim == 64) c = TileConfig{256, 128, 512};
   } else if (dtype == 0) {  // f32
     if (head_dim == 128 || head_dim == 96 || head_dim == 64) c = TileConfig{128, 32, 256};
@@ -1242,17 +882,17 @@ hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, 
 template <typename T>
 hipError_t launch_fwd16(int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream) {
   if (head_dim == 128)
-    return causal ? launch(fwd16_pipe_kernel<T, 128, 64, true>, grid, 512, stream, a)
-                  : launch(fwd16_pipe_kernel<T, 128, 64, false>, grid, 512, stream, a);
+    return causal ? launch(fwd16_pipe_kernel<T, 128, 64, 8, true>, grid, 512, stream, a)
+                  : launch(fwd16_pipe_kernel<T, 128, 64, 8, false>, grid, 512, stream, a);
   if (head_dim == 96)
-    return causal ? launch(fwd16_pipe_kernel<T, 96, 64, true>, grid, 512, stream, a)
-                  : launch(fwd16_pipe_kernel<T, 96, 64, false>, grid, 512, stream, a);
+    return causal ? launch(fwd16_pipe_kernel<T, 96, 64, 8, true>, grid, 512, stream, a)
+                  : launch(fwd16_pipe_kernel<T, 96, 64, 8, false>, grid, 512, stream, a);
   if (head_dim == 64)
-    return causal ? launch(fwd16_pipe_kernel<T, 64, 128, true>, grid, 512, stream, a)
-                  : launch(fwd16_pipe_kernel<T, 64, 128, false>, grid, 512, stream, a);
+    return causal ? launch(fwd16_pipe_kernel<T, 64, 128, 8, true>, grid, 512, stream, a)
+                  : launch(fwd16_pipe_kernel<T, 64, 128, 8, false>, grid, 512, stream, a);
   if (head_dim == 256)
-    return causal ? launch(fwd16_pingpong_kernel<T, 256, 32, true>, grid, 512, stream, a)
-                  : launch(fwd16_pingpong_kernel<T, 256, 32, false>, grid, 512, stream, a);
+    return causal ? launch(fwd16_pipe_kernel<T, 256, 32, 4, true>, grid, 256, stream, a)
+                  : launch(fwd16_pipe_kernel<T, 256, 32, 4, false>, grid, 256, stream, a);
   return hipErrorInvalidValue;
 }
 
