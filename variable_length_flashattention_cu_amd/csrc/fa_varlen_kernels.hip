@@ -270,6 +270,16 @@ constexpr int kPipeBuffers = 4;
 // the slab's eight): their LDS latency then overlaps the end of the stage
 // instead of stalling the first products of the next one.
 constexpr int kPipeKPre = 4;
+// At head_dim 256 a SIMD runs one wavefront, which has no partner to cover
+// LDS latency: there the whole K slab (16 fragments) is read ahead, right
+// after the barrier that makes it visible, and so are the V fragments of the
+// first k-step of the next stage's second product (8), read at the end of the
+// previous stage (the V tile of stage j+1 is resident during stage j).  12 or
+// 16 V fragments were slower, as were 4.
+template <int D>
+constexpr int pipe_kpre() { return D == 256 ? 16 : kPipeKPre; }
+template <int D>
+constexpr int pipe_vpre() { return D == 256 ? D / 32 : 0; }
 
 template <int D, int BN, int NW>
 struct PipeGeom {
@@ -378,6 +388,34 @@ struct PipeWave {
         const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[db] = Elem16<T>::mfma(__builtin_bit_cast(v8, v), p[t], o[db]);
       }
+  }
+
+  // V^T operand fragments of the product above, in its order (k-step t, then
+  // dimension block db: fragment t * DB + db); pv_pre takes the first NV of
+  // them already read by v_pre.
+  __device__ __forceinline__ static v8 v_frag(const uint16_t* Vr, int row0, int f, int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const int g = lane >> 5, t = f / DB, db = f % DB;
+    const int r0 = row0 + 16 * g + 8 * t;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(Vr + tiling::vr_tr_index<D>(lane, r0, db)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(Vr + tiling::vr_tr_index<D>(lane, r0 + 4, db)));
+    return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  template <int NV>
+  __device__ __forceinline__ static void v_pre(const uint16_t* Vr, v8 (&pre)[NV], int lane) {
+#pragma unroll
+    for (int f = 0; f < NV; ++f) pre[f] = v_frag(Vr, 0, f, lane);
+  }
+  template <int NV>
+  __device__ __forceinline__ void pv_pre(const uint16_t* Vr, const v8 (&p)[2], const v8 (&pre)[NV], int lane) {
+#pragma unroll
+    for (int f = 0; f < 2 * DB; ++f) {
+      const v8 av = f < NV ? pre[f < NV ? f : 0] : v_frag(Vr, 0, f, lane);
+      o[f % DB] = Elem16<T>::mfma(av, p[f / DB], o[f % DB]);
+    }
   }
 
   // -inf for keys past the end of the sequence or (causal) above the diagonal;
@@ -600,7 +638,10 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
     __syncthreads();
   }
   int n = 1;
-  v8 kpre[kPipeKPre];
+  v8 kpre[pipe_kpre<D>()];
+  constexpr int NVP = pipe_vpre<D>();
+  v8 vpre[NVP > 0 ? NVP : 1];
+  if (NVP > 0 && n < n_steady) Wave::v_pre(vslab(n * SPT), vpre, lane);
   if (SPT > 1 && n < n_steady) Wave::k_pre(kslab(n * SPT), kpre, arow, g);
   const bool lead_first = wave >= 4;  // wavefronts 4-7 (the younger on each SIMD) lead the first stage
   constexpr bool kAlternate = NW == 8;  // two wavefronts of the workgroup share each SIMD
@@ -623,7 +664,12 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
       v8 p_cur[2];
       const f32x16 s_next = wv.qk_pre(kslab(j), kpre, arow, g);
       const bool ok = wv.softmax_fast(s_cur, p_cur, a.scale_log2);
-      wv.pv(vslab(j), 0, p_prev, lane);
+      if constexpr (NVP > 0) {
+        wv.pv_pre(vslab(j), p_prev, vpre, lane);
+        Wave::v_pre(vslab(j + 1), vpre, lane);  // V tile of the next stage: resident (issued two iterations ago)
+      } else {
+        wv.pv(vslab(j), 0, p_prev, lane);
+      }
       // first K fragments of the next stage: with two or more slabs per tile
       // its slab is in K tile n + 1, which this iteration reads already
       if (SPT > 1) Wave::k_pre(kslab(j + 1), kpre, arow, g);
