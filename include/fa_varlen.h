@@ -174,7 +174,9 @@ int fa_varlen_tile_map(const fa_tensor* cu_seqlens_q, int32_t max_seqlen_q, int3
  * D must be 64, 96 or 128, or 256 with BF16/F16 inputs (FA_ERR_HEAD_DIM).
  * Alignment: q, k, v and out data 16 bytes; lse and the offsets 4 bytes (the
  * offsets are best kept 32-byte aligned, as any hipMalloc'd buffer is).
- * Scratch: a (batch+1)-entry int32 work-item map is allocated and freed
+ * Scratch: up to 64 sequences none (the attention kernel rebuilds the
+ * work-item map per wavefront from cu_seqlens_q and is the only launch);
+ * above that a (batch+1)-entry int32 map is allocated and freed
  * stream-ordered (hipMallocAsync / hipFreeAsync) on `stream`.
  * Reentrant: concurrent calls on different streams do not interfere.
  */

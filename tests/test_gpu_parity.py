@@ -154,6 +154,30 @@ def test_many_short_sequences(fa):
         full_parity(fa, wl, causal)
 
 
+@pytest.mark.parametrize("batch", [63, 64, 65])
+def test_map_boundary(fa, batch):
+    # fa_varlen_fwd rebuilds the work map inside the kernel up to 64 sequences
+    # and launches the map kernel above; both must match the oracle and the
+    # mapped entry point bit for bit (empty sequences at both ends included)
+    rng = np.random.default_rng(100 + batch)
+    lens = [int(x) for x in rng.integers(0, 600, size=batch)]
+    lens[0] = lens[-1] = 0
+    lens[batch // 2] = 0
+    wl = workload_custom(f"map_boundary_b{batch}", lens, lens, 2, 128, "bf16", seed=90 + batch)
+    data = draw_qkv(wl)
+    t = to_device(data, wl)
+    blk = fa.fa_varlen_tile_map(t["cu_q"], wl.max_seqlen_q, wl.head_dim, fa.FA_DTYPE_BF16)
+    for causal in (False, True):
+        say(f"case map boundary batch={batch} causal={causal}")
+        o1, l1 = host(*run_gpu(wl, t, causal))
+        o2, l2 = fa.fa_varlen_fwd_mapped(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], wl.max_seqlen_q,
+                                         wl.max_seqlen_k, blk, wl.scale, causal)
+        torch.cuda.synchronize()
+        o2, l2 = host(o2, l2)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        full_parity(fa, wl, causal)
+
+
 def test_single_long_sequence_fp32(fa):
     wl = workload_custom("long_fp32", [2000], [2300], 2, 128, "f32", seed=78)
     for causal in (False, True):

@@ -379,6 +379,8 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
   st = plan_fwd(p, max_seqlen_q, &plan);
   if (st != FA_OK) return st;
   if (plan.grid == 0) return FA_OK;
+  // small batches: the kernel rebuilds the map itself (no allocation, one launch)
+  if (p.batch <= fa::kMaplessBatch) return launch_fwd_mapped(p, plan, softmax_scale, causal, nullptr, stream);
   int32_t* blk_start = nullptr;
   if (hipMallocAsync((void**)&blk_start, sizeof(int32_t) * ((size_t)p.batch + 1), stream) != hipSuccess)
     return FA_ERR_HIP;

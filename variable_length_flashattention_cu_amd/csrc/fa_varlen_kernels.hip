@@ -96,6 +96,30 @@ struct WorkItem {
   int q_start, Lq, k_start, Lk;
 };
 
+// Without a map (a.blk_start null: at most kMaplessBatch sequences) every
+// wavefront rebuilds the scan itself: lane b holds sequence b's block count
+// ceil(Lq_b / BM), a wave-wide inclusive scan gives the map, and block t
+// belongs to the first sequence whose inclusive count exceeds t.  The same
+// (b, m) as the map path, without the map's allocation and launch.
+template <int BM>
+__device__ __forceinline__ void locate_block_mapless(const FwdArgs& a, int tr, int& T, int& b, int& m) {
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+  if (lane < a.batch) cnt = (a.cu_q[lane + 1] - a.cu_q[lane] + BM - 1) / BM;
+  int inc = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += y;
+  }
+  T = __shfl(inc, 63, 64);
+  const int t = T - 1 - tr;
+  const uint64_t past = __builtin_amdgcn_ballot_w64(inc > t);  // sequences ending after block t
+  b = past ? __builtin_ctzll(past) : 0;
+  m = t - __shfl(inc - cnt, b, 64);
+}
+
+template <int BM>
 __device__ __forceinline__ bool decode_work(const FwdArgs& a, WorkItem& w) {
   // hardware dispatch sends workgroup i to XCD i % 8; give each XCD a
   // contiguous slice of work ids (gridDim.x is a multiple of 8).
@@ -104,16 +128,24 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, WorkItem& w) {
   if (work >= (uint32_t)a.n_work) return false;
   w.h = (int)(work / (uint32_t)a.tmax);
   const int tr = (int)(work % (uint32_t)a.tmax);
-  const int T = a.blk_start[a.batch];
-  if (tr >= T) return false;
-  const int t = T - 1 - tr;
-  int lo = 0, hi = a.batch;  // invariant: blk_start[lo] <= t < blk_start[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.blk_start[mid] <= t) lo = mid; else hi = mid;
+  int lo = 0;
+  if (a.blk_start == nullptr) {
+    int T, m;
+    locate_block_mapless<BM>(a, tr, T, lo, m);
+    if (tr >= T) return false;
+    w.m = m;
+  } else {
+    const int T = a.blk_start[a.batch];
+    if (tr >= T) return false;
+    const int t = T - 1 - tr;
+    int hi = a.batch;  // invariant: blk_start[lo] <= t < blk_start[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.blk_start[mid] <= t) lo = mid; else hi = mid;
+    }
+    w.m = t - a.blk_start[lo];
   }
   w.b = lo;
-  w.m = t - a.blk_start[lo];
   w.q_start = a.cu_q[lo];
   w.Lq = a.cu_q[lo + 1] - w.q_start;
   w.k_start = a.cu_k[lo];
@@ -731,7 +763,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd16_pipe_kernel(FwdArgs a) 
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[kPipeBuffers][BN * tiling::k_stride<D>()];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[kPipeBuffers][BN * tiling::k_stride<D>()];
   WorkItem w;
-  if (!decode_work(a, w)) return;
+  if (!decode_work<32 * NW>(a, w)) return;
   run_work<32 * NW, CAUSAL>(a, w, [&](const WorkItem& wi) { fwd16_pipe_item<T, D, BN, NW, CAUSAL>(a, wi, lds_k, lds_v); });
 }
 
@@ -757,7 +789,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) float lds_v[2][BN * LD];
 
   WorkItem w;
-  if (!decode_work(a, w)) return;
+  if (!decode_work<BM>(a, w)) return;
   int n_full, n_end;
   key_tiles<BM, BN, CAUSAL>(w, n_full, n_end);
 

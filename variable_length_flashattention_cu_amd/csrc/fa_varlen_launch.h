@@ -23,7 +23,7 @@ struct FwdArgs {
   float* lse;
   const int32_t* cu_q;
   const int32_t* cu_k;
-  const int32_t* blk_start;
+  const int32_t* blk_start;  // the work-item map, or null: rebuilt per wavefront (batch <= kMaplessBatch)
   int64_t row_stride;     // elements between consecutive tokens of q/out: heads * head_dim
   int64_t kv_row_stride;  // elements between consecutive tokens of k/v: kv_heads * head_dim
   float scale_log2;    // softmax_scale * log2(e)
@@ -119,6 +119,9 @@ hipError_t launch_decode(int dtype, int head_dim, bool causal, const DecArgs& a,
 // fa_varlen_fwd_noalloc: the largest batch its static work-item map holds,
 // and that map's device address on the current device (fa_varlen_scratch.hip).
 constexpr int kNoAllocMaxBatch = 65535;
+// Batches of at most this many sequences need no map: the forward kernels
+// rebuild it per wavefront from cu_seqlens_q (one lane per sequence).
+constexpr int kMaplessBatch = 64;
 hipError_t noalloc_map_scratch(int32_t** ptr);
 
 hipError_t launch_tile_map(const int32_t* cu_q, int batch, int block_m, int32_t* blk_start, hipStream_t stream);
