@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "fa_varlen_device.h"
 #include "fa_varlen_launch.h"
 #include "fa_varlen_tiling.h"
@@ -304,7 +306,9 @@ struct BlockStage {
     // check (the rows of the sequence) reads rows past its end as zero
     const int64_t at = (int64_t)h * a.total_q + w.q_start + r0;
     const uint32_t bytes = (uint32_t)max(0, min(BM, w.Lq - r0)) * 4u;
-    const uint32_t off = (uint32_t)(tid & (BM - 1)) * 4u;
+    // lane l takes row (l % 16) + 16 * ((l / 32) % 2): each 16-lane row of the
+    // wave then holds the 16 rows that one lane half needs (see probs16)
+    const uint32_t off = (uint32_t)((tid & 15) | ((tid & 32) >> 1)) * 4u;
     lse_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.lse + at, bytes), (int)off, 0, 0));
     dr_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.drow + at, bytes), (int)off, 0, 0));
   }
@@ -334,24 +338,43 @@ __device__ __forceinline__ int dq16_row(int t, int i) {  // block row of A-row i
 }
 
 // P and dS (softmax scale folded in) of the lane's 16 rows 16g + r.  lse (log2
-// units) and D of row 16g + r come from lane 16g + r (which holds row l % 32).
+// units) and D of row 16g + r come from lane r of the lane's 16-lane row (lane
+// l holds row (l % 16) + 16 * ((l / 32) % 2)), by a DPP row broadcast: vector
+// ALU work instead of two LDS permutes per row.
 // With MASKED, element r counts only if lo <= r < hi (the lane's key visible
 // to row 16g + r); blocks that lie wholly inside the visible region skip the test.
+template <int R>
+__device__ __forceinline__ float row_bcast(float x) {
+  constexpr int kRowNewBcast = 0x150;  // DPP row_newbcast:n (lane n of each 16-lane row to the row)
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowNewBcast + R, 0xf, 0xf, false));
+}
+
+template <bool MASKED, typename T, int R>
+__device__ __forceinline__ void probs16_row(const f32x16& sc, const f32x16& dp, float cur_lse, float cur_dr, int lo,
+                                            int hi, float scale_log2, float scale, typename Elem16<T>::v8 (&p16)[2],
+                                            typename Elem16<T>::v8 (&ds16)[2]) {
+  const float lse2 = row_bcast<R>(cur_lse);
+  const float drr = row_bcast<R>(cur_dr);
+  float pr = fast_exp2(__builtin_fmaf(sc[R], scale_log2, -lse2));
+  if constexpr (MASKED) pr = (R >= lo && R < hi) ? pr : 0.f;
+  const float dsr = pr * (dp[R] - drr) * scale;
+  p16[R >> 3][R & 7] = (T)pr;
+  ds16[R >> 3][R & 7] = (T)dsr;
+}
+
+template <bool MASKED, typename T, int... R>
+__device__ __forceinline__ void probs16_rows(const f32x16& sc, const f32x16& dp, float cur_lse, float cur_dr, int lo,
+                                             int hi, float scale_log2, float scale, typename Elem16<T>::v8 (&p16)[2],
+                                             typename Elem16<T>::v8 (&ds16)[2], std::integer_sequence<int, R...>) {
+  (probs16_row<MASKED, T, R>(sc, dp, cur_lse, cur_dr, lo, hi, scale_log2, scale, p16, ds16), ...);
+}
+
 template <bool MASKED, typename T>
-__device__ __forceinline__ void probs16(const f32x16& sc, const f32x16& dp, float cur_lse, float cur_dr, int g,
+__device__ __forceinline__ void probs16(const f32x16& sc, const f32x16& dp, float cur_lse, float cur_dr, int /*g*/,
                                         int lo, int hi, float scale_log2, float scale,
                                         typename Elem16<T>::v8 (&p16)[2], typename Elem16<T>::v8 (&ds16)[2]) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int src = 4 * (16 * g + r);
-    const float lse2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(cur_lse)));
-    const float drr = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(cur_dr)));
-    float pr = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -lse2));
-    if constexpr (MASKED) pr = (r >= lo && r < hi) ? pr : 0.f;
-    const float dsr = pr * (dp[r] - drr) * scale;
-    p16[r >> 3][r & 7] = (T)pr;
-    ds16[r >> 3][r & 7] = (T)dsr;
-  }
+  probs16_rows<MASKED, T>(sc, dp, cur_lse, cur_dr, lo, hi, scale_log2, scale, p16, ds16,
+                          std::make_integer_sequence<int, 16>{});
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -396,7 +419,7 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   const int nsteps = a.head_group * nblk;
 
   BlockStage<D, BM, NWS> stage;
-  float cur_lse = 0.f, cur_dr = 0.f;  // lse (log2 units) and D of row l32 of the step
+  float cur_lse = 0.f, cur_dr = 0.f;  // lse (log2 units) and D of row (l % 16) + 16 ((l / 32) % 2) of the step
 
   f32x16 dkt[DB], dvt[DB];
 #pragma unroll
