@@ -337,7 +337,8 @@ __device__ __forceinline__ int dq16_row(int t, int i) {  // block row of A-row i
   return (i < 8 ? 0 : 8) + 8 * t + i;
 }
 
-// P and dS (softmax scale folded in) of the lane's 16 rows 16g + r.  lse (log2
+// P and dS / scale (dS without the softmax scale, which dK and dQ apply at
+// the end) of the lane's 16 rows 16g + r.  lse (log2
 // units) and D of row 16g + r come from lane r of the lane's 16-lane row (lane
 // l holds row (l % 16) + 16 * ((l / 32) % 2)), by a DPP row broadcast: vector
 // ALU work instead of two LDS permutes per row.
@@ -345,8 +346,10 @@ __device__ __forceinline__ int dq16_row(int t, int i) {  // block row of A-row i
 // to row 16g + r); blocks that lie wholly inside the visible region skip the test.
 template <int R>
 __device__ __forceinline__ float row_bcast(float x) {
-  constexpr int kRowNewBcast = 0x150;  // DPP row_newbcast:n (lane n of each 16-lane row to the row)
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowNewBcast + R, 0xf, 0xf, false));
+  // DPP row_newbcast:n writes lane n of each 16-lane row to every lane of the
+  // row, so no lane keeps an old value (none is materialised)
+  constexpr int kRowNewBcast = 0x150;
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kRowNewBcast + R, 0xf, 0xf, true));
 }
 
 template <bool MASKED, typename T, int R>
@@ -357,7 +360,7 @@ __device__ __forceinline__ void probs16_row(const f32x16& sc, const f32x16& dp, 
   const float drr = row_bcast<R>(cur_dr);
   float pr = fast_exp2(__builtin_fmaf(sc[R], scale_log2, -lse2));
   if constexpr (MASKED) pr = (R >= lo && R < hi) ? pr : 0.f;
-  const float dsr = pr * (dp[R] - drr) * scale;
+  const float dsr = pr * (dp[R] - drr);  // the softmax scale is applied to dK and dQ
   p16[R >> 3][R & 7] = (T)pr;
   ds16[R >> 3][R & 7] = (T)dsr;
 }
@@ -563,13 +566,13 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const uint32_t off = ((uint32_t)dq16_row(rt0 + u, 4 * lg + r) * (uint32_t)rs + 16 * ct + li) * 4u;
-          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[u][r], racc, (int)off, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[u][r] * a.scale, racc, (int)off, 0, 0);
         }
     }
     __syncthreads();
   }
 
-  // ---- epilogue: dK (scale already in dS) and dV of this lane's key
+  // ---- epilogue: dK (times the softmax scale, left out of dS) and dV of this lane's key
   if (kcol < w.Lk) {
     T* dkp = (T*)a.dk + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
     T* dvp = (T*)a.dv + (int64_t)(w.k_start + kcol) * rsk + (int64_t)w.hk * D;
@@ -580,7 +583,7 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
         typename E::v4 k4, v4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          k4[c] = (T)dkt[db][4 * s4 + c];
+          k4[c] = (T)(dkt[db][4 * s4 + c] * a.scale);
           v4[c] = (T)dvt[db][4 * s4 + c];
         }
         const int d0 = 32 * db + 8 * s4 + 4 * g;
