@@ -621,8 +621,10 @@ def main() -> int:
             torch.cuda.empty_cache()
         # backward pass (fa_varlen_bwd, after the forward that gives out and lse)
         line["backward"] = []
-        for bwl, bc in ((workload_ragged64k(), True), (workload_sweep(4096, 128), False),
-                        (workload_sweep(4096, 128), True), (workload_sweep(4096, 64), True)):
+        base = workload_ragged64k()
+        for bwl, bc in ((base, True), (workload_sweep(4096, 128), False),
+                        (workload_sweep(4096, 128), True), (workload_sweep(4096, 64), True),
+                        (dataclasses.replace(base, name=base.name.replace("_d128_", "_d96_"), head_dim=96), True)):
             line["backward"].append(measure_backward(bwl, bc))
             print(f"# {line['backward'][-1]}", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()

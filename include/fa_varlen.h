@@ -250,7 +250,7 @@ int fa_varlen_fwd_noalloc(const fa_tensor* q, const fa_tensor* k, const fa_tenso
  *                 owned by the caller; its contents on entry do not matter
  *                 and are undefined afterwards.  Calls that run at the same
  *                 time need separate workspaces.
- * dtype must be BF16 or F16 (FA_ERR_DTYPE otherwise) and D 64 or 128
+ * dtype must be BF16 or F16 (FA_ERR_DTYPE otherwise) and D 64, 96 or 128
  * (FA_ERR_HEAD_DIM otherwise); products use the 16-bit MFMA with float32
  * accumulation, P and dS are rounded to dtype before they enter a product,
  * dq is summed in float32.  Because dq is accumulated with atomic additions,

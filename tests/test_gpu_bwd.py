@@ -15,7 +15,8 @@ No NaN anywhere; rows that see no key have dq = 0 and keys no query sees
 have dk = dv = 0 exactly.
 
 Cases: ragged batches with empty sequences, single tokens, Lq != Lk under the
-causal mask, tails of every size; shared key/value heads; fp16; the
+causal mask, tails of every size; head_dim 64, 96 and 128; shared key/value
+heads; fp16; the
 bench's 64k-token length mix at full size with the oracle on a subset of
 sequences and heads.
 """
@@ -106,7 +107,8 @@ EDGE = [
 
 
 @pytest.mark.parametrize("name,lq,lk", EDGE, ids=[e[0] for e in EDGE])
-@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 128), ("f16", 64), ("f16", 128)])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 96), ("bf16", 128), ("f16", 64), ("f16", 96),
+                                             ("f16", 128)])
 def test_bwd_edge_cases(fa, name, lq, lk, dtype, head_dim):
     wl = workload_custom(f"bwd_{name}_{dtype}_d{head_dim}", lq, lk, 3, head_dim, dtype, seed=len(name) + head_dim)
     for causal in (False, True):
@@ -121,6 +123,13 @@ def test_bwd_ragged_qk(fa, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_bwd_dense_d96(fa, causal):
+    # head_dim 96: rows in 128-element LDS slots, dQ tiles on 6 of the 8 wavefronts
+    wl = workload_custom("bwd_dense_3x1024_h4_d96", [1024] * 3, None, 4, 96, "f16", seed=23)
+    full_case(fa, wl, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_bwd_dense_d128(fa, causal):
     wl = workload_custom("bwd_dense_4x1024_h4_d128", [1024] * 4, None, 4, 128, "bf16", seed=22)
     full_case(fa, wl, causal)
@@ -130,7 +139,7 @@ GQA = [(8, 1), (8, 2), (6, 3)]
 
 
 @pytest.mark.parametrize("heads,heads_k", GQA, ids=[f"h{h}kv{k}" for h, k in GQA])
-@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f16", 64), ("bf16", 96)])
 def test_bwd_shared_kv_heads(fa, heads, heads_k, dtype, head_dim):
     wl = workload_custom(f"bwd_gqa_h{heads}_kv{heads_k}_{dtype}_d{head_dim}", [300, 0, 129, 700],
                          [280, 5, 200, 700], heads, head_dim, dtype, seed=heads * 10 + heads_k, heads_k=heads_k)

@@ -93,7 +93,7 @@ bool same_shape(const fa_tensor& a, const fa_tensor& b) {
 bool fwd_head_dim(int elem, int64_t d) {
   return d == 64 || d == 96 || d == 128 || (d == 256 && elem != fa::kElemF32);
 }
-bool bwd_head_dim(int, int64_t d) { return d == 64 || d == 128; }
+bool bwd_head_dim(int, int64_t d) { return d == 64 || d == 96 || d == 128; }
 
 // ---------------------------------------------------------------------------
 // the attention problem shared by the forward and backward entry points

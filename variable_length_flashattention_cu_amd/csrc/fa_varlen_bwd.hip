@@ -77,17 +77,22 @@ __device__ __forceinline__ uint16_t f32_to_bits(float x) {
 // ---------------------------------------------------------------------------
 // D_i = rowsum(dout * out) and the zeroed dq accumulator
 // ---------------------------------------------------------------------------
+// Lanes per (row, head) pair: the row's 16-byte chunks rounded up to a power
+// of two (head_dim 96: 12 chunks on 16 lanes, the last 4 idle).
+template <int D>
+constexpr int pair_lanes() { return D / 8 <= 8 ? 8 : (D / 8 <= 16 ? 16 : 32); }
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-  constexpr int CH = D / 8;          // 16-byte chunks per (row, head)
-  constexpr int PAIRS = 256 / CH;    // (row, head) pairs per workgroup
-  static_assert((CH & (CH - 1)) == 0 && CH <= 64, "chunks of a row must form a power-of-two lane group");
+  constexpr int CH = D / 8;                // 16-byte chunks per (row, head)
+  constexpr int LP = pair_lanes<D>();      // lanes per pair
+  constexpr int PAIRS = 256 / LP;          // (row, head) pairs per workgroup
   const int tid = threadIdx.x;
-  const int64_t p = (int64_t)blockIdx.x * PAIRS + tid / CH;  // row * heads + head
-  const int c = tid % CH;
+  const int64_t p = (int64_t)blockIdx.x * PAIRS + tid / LP;  // row * heads + head
+  const int c = tid % LP;
   const int64_t npairs = (int64_t)a.total_q * a.heads;
   float dot = 0.f;
-  if (p < npairs) {
+  if (p < npairs && c < CH) {
     const u32x4 o = *(const u32x4*)((const uint16_t*)a.out + p * D + 8 * c);
     const u32x4 g = *(const u32x4*)((const uint16_t*)a.dout + p * D + 8 * c);
 #pragma unroll
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     *(f32x4*)(a.dq_acc + p * D + 8 * c + 4) = z;
   }
 #pragma unroll
-  for (int off = CH / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+  for (int off = LP / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
   if (p < npairs && c == 0) {
     const int64_t row = p / a.heads;
     const int h = (int)(p % a.heads);
@@ -114,12 +119,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int CH = D / 8;
-  constexpr int PAIRS = 256 / CH;
+  constexpr int LP = pair_lanes<D>();
+  constexpr int PAIRS = 256 / LP;
   const int tid = threadIdx.x;
-  const int64_t p = (int64_t)blockIdx.x * PAIRS + tid / CH;
-  const int c = tid % CH;
+  const int64_t p = (int64_t)blockIdx.x * PAIRS + tid / LP;
+  const int c = tid % LP;
   const int64_t rows = a.cu_q[a.batch];  // rows past the last sequence are not written
-  if (p < rows * a.heads) {
+  if (p < rows * a.heads && c < CH) {
     const f32x4 x0 = *(const f32x4*)(a.dq_acc + p * D + 8 * c);
     const f32x4 x1 = *(const f32x4*)(a.dq_acc + p * D + 8 * c + 4);
     u32x4 r;
@@ -190,13 +196,17 @@ __device__ __forceinline__ bool decode_col(const BwdArgs& a, ColItem& w) {
 // row % 4 and the low bits flip between r and r+8, so either read touches 16
 // distinct 16-byte bank groups (each was 4-way conflicted with the K-style
 // swizzle).  Rows of head_dim 64 keep the K-style layout.
+// Rows of head_dim 96 (12 chunks) sit in 128-element slots and take the
+// head_dim-128 swizzle; the slots' last four chunk positions hold no data.
 template <int D>
 __device__ __forceinline__ int tq_swz(int row) {
-  if constexpr (D == 128) return 4 * (row & 3) | ((row >> 2) & 1) | ((((row >> 3) ^ (row >> 4)) & 1) << 1);
+  if constexpr (D == 128 || D == 96) return 4 * (row & 3) | ((row >> 2) & 1) | ((((row >> 3) ^ (row >> 4)) & 1) << 1);
   else return tiling::k_swz<D>(row);
 }
 template <int D>
-__device__ __forceinline__ int tq_index(int row, int ch) { return row * D + 8 * (ch ^ tq_swz<D>(row)); }
+__device__ __forceinline__ int tq_index(int row, int ch) {
+  return row * tiling::k_stride<D>() + 8 * (ch ^ tq_swz<D>(row));
+}
 
 // Register-staged tile -> LDS in the tq_index layout
 template <int D, typename Tile>
@@ -217,7 +227,7 @@ __device__ __forceinline__ void store_tq(const Tile& t, uint16_t* dst, int tid) 
 template <int D, int ROWS, int NW, bool TQ>
 __device__ __forceinline__ void lds_load_rows(uint16_t* dst, const uint16_t* base, int64_t row_stride, int valid,
                                               int wave, int lane) {
-  constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  constexpr int CPR = tiling::k_stride<D>() / 8;  // 16-byte slots per LDS row
   constexpr int PER_WAVE = ROWS * CPR / (64 * NW);  // instructions per wave
   static_assert(ROWS * CPR % (64 * NW) == 0, "tile must split into whole wave loads");
   const __amdgpu_buffer_rsrc_t r =
@@ -227,7 +237,8 @@ __device__ __forceinline__ void lds_load_rows(uint16_t* dst, const uint16_t* bas
     const int seg = wave * PER_WAVE + i;
     const int p = seg * 64 + lane;
     const int row = p / CPR;
-    const int lc = (p % CPR) ^ (TQ ? tq_swz<D>(row) : tiling::k_swz<D>(row));
+    int lc = (p % CPR) ^ (TQ ? tq_swz<D>(row) : tiling::k_swz<tiling::k_stride<D>()>(row));
+    if (D == 96 && lc >= D / 8) lc -= 8;  // a padding slot: any chunk of the row (never read)
     const uint32_t off = ((uint32_t)row * (uint32_t)row_stride + (uint32_t)lc * 8u) * 2u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + seg * 512), 16, off,
                                              0, 0, 0);
@@ -300,8 +311,8 @@ struct BlockStage {
     const int64_t rs = a.row_stride;
     const uint16_t* qh = (const uint16_t*)a.q + (int64_t)w.q_start * rs + (int64_t)h * D;
     const uint16_t* doh = (const uint16_t*)a.dout + (int64_t)w.q_start * rs + (int64_t)h * D;
-    tq.load_k(qh, rs, r0, w.Lq, tid & (NT - 1));
-    tdo.load_k(doh, rs, r0, w.Lq, tid & (NT - 1));
+    tq.load_k(qh, rs, r0, w.Lq, tid % NT);
+    tdo.load_k(doh, rs, r0, w.Lq, tid % NT);
     // lse and D of the block's rows: branch-free buffer loads whose range
     // check (the rows of the sequence) reads rows past its end as zero
     const int64_t at = (int64_t)h * a.total_q + w.q_start + r0;
@@ -386,17 +397,22 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   constexpr int KSTEPS = D / 16;    // k-steps over head_dim
   constexpr int DB = D / 32;        // 32-dim tiles
   constexpr int CT = D / 16;        // 16-column tiles of dQ
-  constexpr int TPW = 2 * CT / NW;  // 16x16 dQ tiles per wave (2 at D=128, 1 at D=64)
+  // 16x16 dQ tiles per wave: at D=128 and 96 wave w < CT takes column tile w of
+  // both row tiles (one K^T operand feeds two MFMAs; at 96 waves 6 and 7 have
+  // none), at D=64 one tile per wave
+  constexpr int TPW = D == 64 ? 1 : 2;
+  constexpr int DQW = 2 * CT / TPW;  // wavefronts with dQ tiles
   constexpr int NWS = BM * D / 8 / 64 < NW ? BM * D / 8 / 64 : NW;  // staging wavefronts
-  static_assert(D == 64 || D == 128, "backward head_dim");
+  static_assert(D == 64 || D == 96 || D == 128, "backward head_dim");
+  constexpr int KSB = tiling::k_stride<D>();  // LDS row pitch of the K, V, Q and dO tiles
   using E = Elem16<T>;
   typedef typename E::v8 v8;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[BN * D];   // K block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[BN * D];   // V block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_ds[BM * BN];  // dS, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[BM * D];    // query block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_do[BM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[BN * KSB];   // K block, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[BN * KSB];   // V block, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ds[BM * BN];   // dS, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t lds_q[BM * KSB];   // query block, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t lds_do[BM * KSB];
 
   ColItem w;
   if (!decode_col<BN>(a, w)) return;
@@ -433,8 +449,8 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
 
   if (nsteps > 0) {
     stage.load(a, w, 0, nblk, i_begin, tid);
-    store_tq<D>(stage.tq, lds_q, tid & (64 * NWS - 1));
-    store_tq<D>(stage.tdo, lds_do, tid & (64 * NWS - 1));
+    store_tq<D>(stage.tq, lds_q, tid % (64 * NWS));
+    store_tq<D>(stage.tdo, lds_do, tid % (64 * NWS));
     cur_lse = stage.lse_v * kLog2eF;
     cur_dr = stage.dr_v;
   }
@@ -533,41 +549,47 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
     __syncthreads();
 
     // dQ rows r0..r0+31 over the 256 keys: 16x16 tiles (row tile rt, dims
-    // 16*ct..+15); D=128: wave w takes column tile w of both row tiles (one
-    // K^T operand feeds two MFMAs), D=64: column tile w % 4 of row tile w / 4
+    // 16*ct..+15); D=128 and 96: wave w < CT takes column tile w of both row
+    // tiles (one K^T operand feeds two MFMAs), D=64: column tile w % 4 of row
+    // tile w / 4
     {
+      const bool has_dq = DQW >= NW || wave < DQW;  // wave-uniform
       const int ct = wave % CT;
       const int rt0 = TPW == 2 ? 0 : wave / CT;
       f32x4 acc[TPW];
 #pragma unroll
       for (int u = 0; u < TPW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (has_dq) {
 #pragma unroll
-      for (int kk = 0; kk < BN / 32; ++kk) {
-        const int k0 = 32 * kk;
-        const v8 bkt = tr_read8<v8, D>(lds_k, k0 + 8 * lg, 16 * ct, li);
+        for (int kk = 0; kk < BN / 32; ++kk) {
+          const int k0 = 32 * kk;
+          const v8 bkt = tr_read8<v8, D>(lds_k, k0 + 8 * lg, 16 * ct, li);
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const v8 av = *(const v8*)(lds_ds + tiling::ks_index<BN>(dq16_row(rt0 + u, li), (k0 >> 3) + lg));
-          acc[u] = Mfma16<T>::run(av, bkt, acc[u]);
+          for (int u = 0; u < TPW; ++u) {
+            const v8 av = *(const v8*)(lds_ds + tiling::ks_index<BN>(dq16_row(rt0 + u, li), (k0 >> 3) + lg));
+            acc[u] = Mfma16<T>::run(av, bkt, acc[u]);
+          }
         }
+        read_ahead_schedule<TPW * (BN / 32), (TPW + 2) * (BN / 32), 8>();
       }
-      read_ahead_schedule<TPW * (BN / 32), (TPW + 2) * (BN / 32), 8>();
       // the next query block: no Q/dO reads remain in this step
-      store_tq<D>(stage.tq, lds_q, tid & (64 * NWS - 1));
-      store_tq<D>(stage.tdo, lds_do, tid & (64 * NWS - 1));
+      store_tq<D>(stage.tq, lds_q, tid % (64 * NWS));
+      store_tq<D>(stage.tdo, lds_do, tid % (64 * NWS));
       cur_lse = stage.lse_v * kLog2eF;
       cur_dr = stage.dr_v;
-      // register r of tile u: block row dq16_row(rt0 + u, 4 lg + r), column 16*ct + li
-      const __amdgpu_buffer_rsrc_t racc =
-          buffer_rsrc(a.dq_acc + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D,
-                      tiling::head_rows_bytes(min(BM, w.Lq - r0), rs, D, 4));
+      if (has_dq) {
+        // register r of tile u: block row dq16_row(rt0 + u, 4 lg + r), column 16*ct + li
+        const __amdgpu_buffer_rsrc_t racc =
+            buffer_rsrc(a.dq_acc + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D,
+                        tiling::head_rows_bytes(min(BM, w.Lq - r0), rs, D, 4));
 #pragma unroll
-      for (int u = 0; u < TPW; ++u)
+        for (int u = 0; u < TPW; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t off = ((uint32_t)dq16_row(rt0 + u, 4 * lg + r) * (uint32_t)rs + 16 * ct + li) * 4u;
-          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[u][r] * a.scale, racc, (int)off, 0, 0);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t off = ((uint32_t)dq16_row(rt0 + u, 4 * lg + r) * (uint32_t)rs + 16 * ct + li) * 4u;
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[u][r] * a.scale, racc, (int)off, 0, 0);
+          }
+      }
     }
     __syncthreads();
   }
@@ -604,6 +626,9 @@ hipError_t launch_bwd_t(int head_dim, bool causal, int grid, const BwdArgs& a, h
   if (head_dim == 128)
     return causal ? launch(bwd16w_kernel<T, 128, true>, grid, 512, stream, a)
                   : launch(bwd16w_kernel<T, 128, false>, grid, 512, stream, a);
+  if (head_dim == 96)
+    return causal ? launch(bwd16w_kernel<T, 96, true>, grid, 512, stream, a)
+                  : launch(bwd16w_kernel<T, 96, false>, grid, 512, stream, a);
   if (head_dim == 64)
     return causal ? launch(bwd16w_kernel<T, 64, true>, grid, 512, stream, a)
                   : launch(bwd16w_kernel<T, 64, false>, grid, 512, stream, a);
@@ -612,25 +637,36 @@ hipError_t launch_bwd_t(int head_dim, bool causal, int grid, const BwdArgs& a, h
 
 int64_t row_pairs_grid(const BwdArgs& a, int head_dim) {
   const int64_t pairs = (int64_t)a.total_q * a.heads;
-  const int64_t per = 256 / (head_dim / 8);
+  const int lanes = head_dim <= 64 ? 8 : (head_dim <= 128 ? 16 : 32);  // pair_lanes
+  const int64_t per = 256 / lanes;
   return (pairs + per - 1) / per;
 }
+
+template <template <typename, int> class K, typename T>
+hipError_t launch_rows(int head_dim, int grid, hipStream_t stream, const BwdArgs& a) {
+  switch (head_dim) {
+    case 64: return launch(K<T, 64>::fn, grid, 256, stream, a);
+    case 96: return launch(K<T, 96>::fn, grid, 256, stream, a);
+    default: return launch(K<T, 128>::fn, grid, 256, stream, a);
+  }
+}
+template <typename T, int D>
+struct PrepK { static constexpr auto fn = bwd_prep_kernel<T, D>; };
+template <typename T, int D>
+struct DqK { static constexpr auto fn = bwd_dq_kernel<T, D>; };
 
 }  // namespace
 
 int bwd_block_n(int dtype, int head_dim) {
-  if ((dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 128)) return kBwdBNWide;
+  if ((dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 96 || head_dim == 128)) return kBwdBNWide;
   return 0;
 }
 
 hipError_t launch_bwd_prep(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream) {
   const int grid = (int)row_pairs_grid(a, head_dim);
   if (grid == 0) return hipSuccess;
-  if (dtype == 1)
-    return head_dim == 128 ? launch(bwd_prep_kernel<__bf16, 128>, grid, 256, stream, a)
-                           : launch(bwd_prep_kernel<__bf16, 64>, grid, 256, stream, a);
-  return head_dim == 128 ? launch(bwd_prep_kernel<_Float16, 128>, grid, 256, stream, a)
-                         : launch(bwd_prep_kernel<_Float16, 64>, grid, 256, stream, a);
+  if (dtype == 1) return launch_rows<PrepK, __bf16>(head_dim, grid, stream, a);
+  return launch_rows<PrepK, _Float16>(head_dim, grid, stream, a);
 }
 
 hipError_t launch_bwd(int dtype, int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
@@ -642,11 +678,8 @@ hipError_t launch_bwd(int dtype, int head_dim, bool causal, int grid, const BwdA
 hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream) {
   const int grid = (int)row_pairs_grid(a, head_dim);
   if (grid == 0) return hipSuccess;
-  if (dtype == 1)
-    return head_dim == 128 ? launch(bwd_dq_kernel<__bf16, 128>, grid, 256, stream, a)
-                           : launch(bwd_dq_kernel<__bf16, 64>, grid, 256, stream, a);
-  return head_dim == 128 ? launch(bwd_dq_kernel<_Float16, 128>, grid, 256, stream, a)
-                         : launch(bwd_dq_kernel<_Float16, 64>, grid, 256, stream, a);
+  if (dtype == 1) return launch_rows<DqK, __bf16>(head_dim, grid, stream, a);
+  return launch_rows<DqK, _Float16>(head_dim, grid, stream, a);
 }
 
 }  // namespace fa
