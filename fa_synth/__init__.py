@@ -363,10 +363,14 @@ class KVWorkload:
 
 
 def draw_kvcache(wl: KVWorkload) -> dict:
-    """q, k_cache, v_cache (float32 values and 16-bit bits) and, for a paged
-    cache, the int32 block table [batch, blocks_per_seq] (unused entries 0)."""
+    """q, k_cache, v_cache as float32 values (exactly representable in the
+    workload's type) with, for bf16 and f16, the 16-bit bit arrays ``*_bits``
+    handed to the device, and, for a paged cache, the int32 block table
+    [batch, blocks_per_seq] (unused entries 0)."""
     rng = np.random.default_rng(wl.seed)
-    to_bits, to_f32 = {"bf16": (bf16_rne_bits, bf16_bits_to_f32), "f16": (f16_rne_bits, f16_bits_to_f32)}[wl.dtype]
+    rounders = {"bf16": (bf16_rne_bits, bf16_bits_to_f32), "f16": (f16_rne_bits, f16_bits_to_f32)}
+    if wl.dtype not in rounders and wl.dtype != "f32":
+        raise ValueError(f"unknown dtype {wl.dtype}")
     out = {}
     if wl.paged:
         need = [-(-s // wl.cache_rows) for s in wl.seqlens_k]
@@ -383,9 +387,13 @@ def draw_kvcache(wl: KVWorkload) -> dict:
         cache_shape = (wl.batch, wl.cache_rows, wl.kv_heads, wl.head_dim)
     for name, shape in (("q", (wl.total_q, wl.heads, wl.head_dim)), ("k_cache", cache_shape),
                         ("v_cache", cache_shape)):
-        bits = to_bits(rng.standard_normal(shape, dtype=np.float32)).reshape(shape)
-        out[name + "_bits"] = bits
-        out[name] = to_f32(bits).reshape(shape)
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if wl.dtype in rounders:
+            to_bits, to_f32 = rounders[wl.dtype]
+            bits = to_bits(x).reshape(shape)
+            out[name + "_bits"] = bits
+            x = to_f32(bits).reshape(shape)
+        out[name] = x
     return out
 
 

@@ -292,7 +292,7 @@ int fa_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t num_hea
  * every cached key.
  *
  *   q, out        [total_q, H, D] packed by cu_seqlens_q (out written for
- *                 rows < cu_seqlens_q[batch]), BF16 or F16
+ *                 rows < cu_seqlens_q[batch]), BF16, F16 or F32
  *   k_cache, v_cache  [cache_blocks * cache_rows, Hk, D], q's dtype: cache
  *                 blocks of cache_rows token rows each, stored back to back
  *                 (a [cache_blocks, cache_rows, Hk, D] tensor viewed with its
@@ -313,7 +313,8 @@ int fa_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t num_hea
  *                 bytes for this num_splits, 16-byte aligned, caller-owned
  * Preconditions (not checked on the device): 0 <= leftpad_k[b] <=
  * seqlens_k[b] <= max_seqlen_k and block table entries < cache_blocks.
- * D must be 64, 96, 128 or 256 (FA_ERR_HEAD_DIM); other checks and errors as
+ * D must be 64, 96, 128 or 256 for every dtype (FA_ERR_HEAD_DIM); other
+ * checks and errors as
  * fa_varlen_fwd, plus FA_ERR_WORKSPACE and FA_ERR_ARG for num_splits out of
  * range.
  */

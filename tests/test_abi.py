@@ -370,12 +370,17 @@ def test_kvcache_null_descriptor(name):
 
 
 def test_kvcache_validation():
-    assert call_kv(kv_tensors(dt=F32)) == DTYPE
-    t = kv_tensors()
-    edit(t, "kc", dtype=F16)
+    assert call_kv(kv_tensors(dt=I32)) == DTYPE
+    for other in (F16, F32):
+        t = kv_tensors()
+        edit(t, "kc", dtype=other)
+        assert call_kv(t) == DTYPE
+    t = kv_tensors(dt=F32)
+    edit(t, "out", dtype=BF16)
     assert call_kv(t) == DTYPE
-    for D in (32, 80, 160, 512):
-        assert call_kv(kv_tensors(D=D)) == HEAD_DIM
+    for dt in (BF16, F16, F32):
+        for D in (32, 80, 160, 512):
+            assert call_kv(kv_tensors(D=D, dt=dt)) == HEAD_DIM
     assert call_kv(kv_tensors(Hk=3)) == SHAPE
     assert call_kv(kv_tensors(), max_q=2) == SHAPE
     assert call_kv(kv_tensors(), rows=0) == SHAPE
@@ -421,5 +426,6 @@ def test_kvcache_workspace_size_and_empty():
     assert lib.fa_varlen_kvcache_workspace_size(1, 2, 64, 65, ctypes.byref(n)) == ARG
     assert lib.fa_varlen_kvcache_workspace_size(1, 2, 64, 0, None) == NULL
     # no query rows: valid, nothing launched
-    assert call_kv(kv_tensors(B=0, Tq=0), max_q=0) == OK
-    assert call_kv(kv_tensors(Tq=0), max_q=0) == OK
+    for dt in (BF16, F16, F32):
+        assert call_kv(kv_tensors(B=0, Tq=0, dt=dt), max_q=0) == OK
+        assert call_kv(kv_tensors(Tq=0, dt=dt), max_q=0) == OK

@@ -3,13 +3,13 @@ through the C ABI, against oracle.kvcache.
 
 Bar: as the forward pass (the same arithmetic: 16-bit MFMA products, fp32
 online softmax, P rounded to the input type): max-abs 2e-2 for bf16, 5e-3
-for fp16 on out and lse; rows with no visible key give out = 0 and lse = -inf
-exactly.  Cases: plain and paged caches (pages of 16 and 256 rows), left
+for fp16 and 1e-5 for fp32 (fp32 MFMA products, P kept in fp32) on out and
+lse; rows with no visible key give out = 0 and lse = -inf exactly.  Cases: plain and paged caches (pages of 16 and 256 rows), left
 padding, empty and single-key sequences, key lengths around the 32-key tile,
 one and several query rows per sequence (up to several 32-row tiles of
 query-head x row), causal and not, MHA/GQA/MQA, explicit split counts
-including more splits than tiles, fp16, and the bench's decode batch at full
-size, and head_dim 64, 96 and 256 besides 128.
+including more splits than tiles, fp16, fp32, and the bench's decode batch at
+full size, and head_dim 64, 96 and 256 besides 128.
 """
 import numpy as np
 import pytest
@@ -34,8 +34,12 @@ def fa():
 def run_case(fa, wl, causal, num_splits=0):
     say(f"case {wl.name} causal={causal} splits={num_splits}")
     data = draw_kvcache(wl)
-    tt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
-    dev = {n: torch.from_numpy(data[n + "_bits"].view(np.int16)).cuda().view(tt) for n in ("q", "k_cache", "v_cache")}
+    names = ("q", "k_cache", "v_cache")
+    if wl.dtype == "f32":
+        dev = {n: torch.from_numpy(data[n]).cuda() for n in names}
+    else:
+        tt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+        dev = {n: torch.from_numpy(data[n + "_bits"].view(np.int16)).cuda().view(tt) for n in names}
     cu_q = torch.tensor(wl.cu_q, dtype=torch.int32, device="cuda")
     sk = torch.tensor(wl.seqlens_k, dtype=torch.int32, device="cuda")
     lp = None if wl.leftpad is None else torch.tensor(wl.leftpad, dtype=torch.int32, device="cuda")
@@ -109,6 +113,25 @@ def test_decode_f16_d64(fa, causal):
     wl = workload_decode("dec_f16_d64", [1, 3, 1], [90, 257, 33], 8, 4, 64, "f16", seed=36, cache_rows=64,
                          leftpad=[0, 2, 1], paged=True)
     run_case(fa, wl, causal)
+
+
+@pytest.mark.parametrize("head_dim", [64, 96, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_f32(fa, head_dim, causal):
+    # fp32 caches (fp32 MFMA kernel): paged with left padding, GQA, several
+    # query rows per sequence, an empty and a single-key sequence, key lengths
+    # around the 32-key tile, 3 splits
+    wl = workload_decode(f"dec_f32_d{head_dim}", [1, 3, 1, 2, 1, 5], [0, 300, 1, 64, 97, 33], 6, 2, head_dim, "f32",
+                         seed=50 + head_dim, cache_rows=32, leftpad=[0, 17, 0, 3, 0, 1], paged=True)
+    run_case(fa, wl, causal, num_splits=3)
+
+
+@pytest.mark.parametrize("splits", [0, 1])
+def test_decode_f32_plain(fa, splits):
+    # fp32 without a block table, MQA, automatic and single split
+    wl = workload_decode("dec_f32_plain", [1, 2, 1, 1], [700, 129, 32, 0], 8, 1, 128, "f32", seed=58,
+                         cache_rows=704)
+    run_case(fa, wl, True, num_splits=splits)
 
 
 def test_decode_bench_batch(fa):

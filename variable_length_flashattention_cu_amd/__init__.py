@@ -351,7 +351,7 @@ def fa_varlen_fwd_kvcache(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, max_seql
                           block_table=None, num_splits: int = 0, out=None, lse=None, workspace=None, stream=None):
     """Attention of packed queries against a key/value cache.
 
-    q [total_q, H, D] (bf16/fp16, CUDA; D 64, 96, 128 or 256) packed by cu_seqlens_q; k_cache,
+    q [total_q, H, D] (bf16/fp16/fp32, CUDA; D 64, 96, 128 or 256) packed by cu_seqlens_q; k_cache,
     v_cache [blocks, rows, Hk, D]; seqlens_k int32 [batch] (not cumulative);
     optional leftpad_k int32 [batch] and block_table int32 [batch, blocks_per_seq]
     (without one, block b is sequence b's slot).  Returns (out, lse).

@@ -508,7 +508,7 @@ int fa_varlen_fwd_kvcache(const fa_tensor* q, const fa_tensor* k_cache, const fa
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !seqlens_k || !out || !lse) return FA_ERR_NULL;
   // element types
   const int elem = elem_code(q->dtype);
-  if (elem != fa::kElemBF16 && elem != fa::kElemF16) return FA_ERR_DTYPE;
+  if (elem < 0) return FA_ERR_DTYPE;
   if (k_cache->dtype != q->dtype || v_cache->dtype != q->dtype || out->dtype != q->dtype) return FA_ERR_DTYPE;
   if (lse->dtype != FA_DTYPE_F32 || cu_seqlens_q->dtype != FA_DTYPE_I32 || seqlens_k->dtype != FA_DTYPE_I32)
     return FA_ERR_DTYPE;

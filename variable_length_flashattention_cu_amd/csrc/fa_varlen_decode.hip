@@ -33,7 +33,8 @@
 // workspace.  decode_combine_kernel merges the partials of every row
 // (partials with max m_p, sum l_p and output O_p give out = sum_p 2^(m_p-m)
 // O_p / sum_p 2^(m_p-m) l_p with m = max_p m_p; the same rescaling identity
-// as the online softmax).
+// as the online softmax).  fp32 caches take decode_f32_kernel: the same work
+// split on the fp32 16x16x4 MFMA.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -284,6 +285,151 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void decode16_kernel(DecArgs 
   }
 }
 
+// fp32 caches: the same work split with the fp32 16x16x4 MFMA (lane l,
+// G = l/16, i = l%16: A row i, k = G; B column i, k = G; accumulator register
+// r: row 4G + r, column i), one element per lane and operand.
+//   * S^T = K Q^T contracts over head_dim in D/4 k-steps; k-step s of lane
+//     group G takes dimension G*D/4 + s, so each lane reads its K and Q
+//     elements as contiguous float4s.
+//   * The k-step s of O^T += V^T P^T over 16-key subtile kt takes keys
+//     16kt + 4G + s: register s of the lane's S^T subtile is then exactly its
+//     B operand (no shuffle).  V goes through a wave-private padded LDS tile
+//     (rows of D + 4 floats) and is read one element per lane.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void decode_f32_kernel(DecArgs a) {
+  constexpr int KQ = D / 4;                    // head dimensions per lane group in S^T = K Q^T
+  constexpr int NV = KQ / 4;                   // float4s per lane and row
+  constexpr int DT = D / 16;                   // 16-row tiles of O^T
+  constexpr int KT = kDecTile / 16;            // 16-key subtiles per key tile
+  constexpr int LD = D + 4;                    // LDS row of the V tile (floats)
+  constexpr int VCH = kDecTile * D / 4 / 64;   // float4s of the V tile per lane
+  static_assert((kDecTile * D / 4) % 64 == 0 && KQ % 4 == 0, "tile must split into whole float4 loads");
+  __shared__ __attribute__((aligned(16))) float lds_v[kDecWaves][kDecTile * LD];
+
+  const int item = blockIdx.x;
+  const int s_split = item % a.num_splits;
+  const int hk = (item / a.num_splits) % a.kv_heads;
+  const int b = item / (a.num_splits * a.kv_heads);
+  if (b >= a.batch) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int G = a.head_group;
+  const int q_start = a.cu_q[b];
+  const int Lq = a.cu_q[b + 1] - q_start;
+  const int lp = a.leftpad_k ? a.leftpad_k[b] : 0;
+  const int Lk = a.seqlens_k[b] - lp;
+  const int shift = Lk - Lq;
+  const int rows = G * Lq;
+  const int ntiles = (max(Lk, 0) + kDecTile - 1) / kDecTile;
+  const int tps = (ntiles + a.num_splits - 1) / a.num_splits;
+  const int t_begin = s_split * tps, t_end = min(ntiles, t_begin + tps);
+  const int part = s_split * kDecWaves + wave;
+  const int npart = a.num_splits * kDecWaves;
+  float* vt = lds_v[wave];
+
+  for (int rt = 0; rt * 16 < rows; ++rt) {
+    const int r = rt * 16 + li;
+    const bool rvalid = r < rows;
+    const int qi = rvalid ? r / G : 0, gi = rvalid ? r % G : 0;
+    const int h = hk * G + gi;
+    f32x4 qv[NV];
+    {
+      const float* qp = (const float*)a.q + (int64_t)(q_start + qi) * a.row_stride + (int64_t)h * D + lg * KQ;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) qv[n] = rvalid ? *(const f32x4*)(qp + 4 * n) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int lim = CAUSAL ? min(Lk - 1, qi + shift) : Lk - 1;
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kNegInf, l_run = 0.f;
+
+    for (int t = t_begin + wave; t < t_end; t += kDecWaves) {
+      const int key0 = t * kDecTile;
+      // V tile -> LDS (keys past the sequence as zeros)
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int c = lane + 64 * j;
+        const int row = c / (D / 4), c4 = c % (D / 4);
+        const int key = key0 + row;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (key < Lk) x = *(const f32x4*)((const float*)a.v_cache + cache_offset(a, b, lp + key, hk, D) + 4 * c4);
+        *(f32x4*)(vt + row * LD + 4 * c4) = x;
+      }
+      // S^T = K Q^T: register e of subtile kt holds key key0 + 16kt + 4lg + e of row li
+      f32x4 sc[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const int key = key0 + 16 * kt + li;
+        const bool kvalid = key < Lk;
+        const float* kp =
+            (const float*)a.k_cache + cache_offset(a, b, lp + (kvalid ? key : 0), hk, D) + lg * KQ;
+        sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+          const f32x4 kv = kvalid ? *(const f32x4*)(kp + 4 * n) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[c], qv[n][c], sc[kt], 0, 0, 0);
+        }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool vis = key0 + 16 * kt + 4 * lg + e <= lim;
+          sc[kt][e] = vis ? sc[kt][e] * a.scale_log2 : kNegInf;
+          mx = fmaxf(mx, sc[kt][e]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[kt][e] = fast_exp2(sc[kt][e] - m_use);
+          lsum += sc[kt][e];
+        }
+      l_run = l_run * alpha + lsum;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[dt][e] *= alpha;
+      // O^T += V^T P^T: k-step (kt, e) takes keys 16kt + 4G + e
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float* vrow = vt + (16 * kt + 4 * lg + e) * LD + li;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * dt], sc[kt][e], o[dt], 0, 0, 0);
+        }
+    }
+
+    float l = l_run + __shfl_xor(l_run, 16, 64);
+    l = pair_sum(l);
+    if (rvalid) {
+      const int64_t pr = ((int64_t)(q_start + qi) * a.heads + h) * npart + part;
+      float* po = a.part_o + pr * D;
+      if (m_run != kNegInf)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(po + 16 * dt + 4 * lg) = o[dt];
+      if (lg == 0) {
+        a.part_ml[2 * pr] = m_run;
+        a.part_ml[2 * pr + 1] = l;
+      }
+    }
+  }
+}
+
 // One wavefront per (row, head): merge its partials into out and lse.  Lane
 // p % 64 weighs partials p; the partial outputs are then read without
 // dependent branches (empty partials, whose O was never written, enter through
@@ -382,6 +528,29 @@ hipError_t launch_decode_t(int head_dim, bool causal, int64_t grid, int64_t grid
   }
 }
 
+hipError_t launch_decode_f32(int head_dim, bool causal, int64_t grid, int64_t grid_c, const DecArgs& a,
+                             hipStream_t stream) {
+  hipError_t e;
+  switch (head_dim) {
+    case 64: e = causal ? launch(decode_f32_kernel<64, true>, grid, stream, a)
+                        : launch(decode_f32_kernel<64, false>, grid, stream, a); break;
+    case 96: e = causal ? launch(decode_f32_kernel<96, true>, grid, stream, a)
+                        : launch(decode_f32_kernel<96, false>, grid, stream, a); break;
+    case 128: e = causal ? launch(decode_f32_kernel<128, true>, grid, stream, a)
+                         : launch(decode_f32_kernel<128, false>, grid, stream, a); break;
+    case 256: e = causal ? launch(decode_f32_kernel<256, true>, grid, stream, a)
+                         : launch(decode_f32_kernel<256, false>, grid, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess || grid_c == 0) return e;
+  switch (head_dim) {
+    case 64: return launch(decode_combine_kernel<float, 64>, grid_c, stream, a);
+    case 96: return launch(decode_combine_kernel<float, 96>, grid_c, stream, a);
+    case 128: return launch(decode_combine_kernel<float, 128>, grid_c, stream, a);
+    default: return launch(decode_combine_kernel<float, 256>, grid_c, stream, a);
+  }
+}
+
 }  // namespace
 
 int decode_waves() { return kDecWaves; }
@@ -390,6 +559,7 @@ hipError_t launch_decode(int dtype, int head_dim, bool causal, const DecArgs& a,
   const int64_t grid = (int64_t)a.batch * a.kv_heads * a.num_splits;
   const int64_t grid_c = ((int64_t)a.total_q * a.heads + 3) / 4;
   if (grid == 0) return hipSuccess;
+  if (dtype == 0) return launch_decode_f32(head_dim, causal, grid, grid_c, a, stream);
   if (dtype == 1) return launch_decode_t<__bf16>(head_dim, causal, grid, grid_c, a, stream);
   if (dtype == 2) return launch_decode_t<_Float16>(head_dim, causal, grid, grid_c, a, stream);
   return hipErrorInvalidValue;
