@@ -250,10 +250,11 @@ int fa_varlen_fwd_noalloc(const fa_tensor* q, const fa_tensor* k, const fa_tenso
  *                 owned by the caller; its contents on entry do not matter
  *                 and are undefined afterwards.  Calls that run at the same
  *                 time need separate workspaces.
- * dtype must be BF16 or F16 (FA_ERR_DTYPE otherwise) and D 64, 96 or 128
- * (FA_ERR_HEAD_DIM otherwise); products use the 16-bit MFMA with float32
- * accumulation, P and dS are rounded to dtype before they enter a product,
- * dq is summed in float32.  Because dq is accumulated with atomic additions,
+ * dtype and D as fa_varlen_fwd: BF16 or F16 with D 64, 96, 128 or 256, F32
+ * with D 64, 96 or 128 (FA_ERR_DTYPE / FA_ERR_HEAD_DIM otherwise).  16-bit
+ * products use the 16-bit MFMA with float32 accumulation, P and dS rounded
+ * to dtype before they enter a product; F32 uses the float32 MFMA
+ * throughout; dq is summed in float32.  Because dq is accumulated with atomic additions,
  * its low bits may differ from run to run.  Other checks as fa_varlen_fwd;
  * dout, dq, dk and dv need 16-byte alignment.  A workspace that is NULL or
  * too small gives FA_ERR_WORKSPACE.

@@ -316,9 +316,12 @@ def test_bwd_descriptor_validation(case, code):
 
 
 def test_bwd_validation():
-    assert call_bwd(bwd_tensors(dt=F32)) == DTYPE
-    for D in (256, 80, 32):
-        assert call_bwd(bwd_tensors(D=D)) == HEAD_DIM
+    assert call_bwd(bwd_tensors(dt=I32)) == DTYPE
+    # head_dim as the forward pass: 256 only for 16-bit inputs
+    assert call_bwd(bwd_tensors(dt=F32, D=256)) == HEAD_DIM
+    for dt in (BF16, F16, F32):
+        for D in (512, 80, 32):
+            assert call_bwd(bwd_tensors(D=D, dt=dt)) == HEAD_DIM
     assert call_bwd(bwd_tensors(Hk=3)) == SHAPE
     assert call_bwd(bwd_tensors(), max_q=9) == SHAPE
     assert call_bwd(bwd_tensors(), scale=0.0) == ARG

@@ -311,7 +311,8 @@ def fa_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
                   workspace=None, stream=None):
     """Gradients (dq, dk, dv) of fa_varlen_fwd given dout, the forward's out and lse.
 
-    bf16 or fp16 inputs, head_dim 64, 96 or 128.  dq is shaped like q, dk and dv
+    bf16 or fp16 inputs at head_dim 64, 96, 128 or 256, fp32 at 64, 96 or 128
+    (the forward pass's set).  dq is shaped like q, dk and dv
     like k.  ``workspace`` (a CUDA byte tensor of at least
     fa_varlen_bwd_workspace_size bytes) is allocated when not given.
     """

@@ -93,7 +93,6 @@ bool same_shape(const fa_tensor& a, const fa_tensor& b) {
 bool fwd_head_dim(int elem, int64_t d) {
   return d == 64 || d == 96 || d == 128 || (d == 256 && elem != fa::kElemF32);
 }
-bool bwd_head_dim(int, int64_t d) { return d == 64 || d == 96 || d == 128; }
 
 // ---------------------------------------------------------------------------
 // the attention problem shared by the forward and backward entry points
@@ -430,9 +429,8 @@ int fa_varlen_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
   const fa_tensor* extra[4] = {dout, dq, dk, dv};
   Problem p;
   int st = check_problem(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, max_seqlen_q, max_seqlen_k, softmax_scale,
-                         causal, bwd_head_dim, extra, 4, 2, &p);
+                         causal, fwd_head_dim, extra, 4, 2, &p);
   if (st != FA_OK) return st;
-  if (p.elem != fa::kElemBF16 && p.elem != fa::kElemF16) return FA_ERR_DTYPE;
   const int bn = fa::bwd_block_n(p.elem, p.head_dim);
   if (bn == 0) return FA_ERR_HEAD_DIM;
   const BwdLayout lay = bwd_layout(p.batch, p.total_q, p.heads, p.head_dim);

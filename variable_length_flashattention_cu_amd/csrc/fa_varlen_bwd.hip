@@ -47,6 +47,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "fa_varlen_device.h"
@@ -77,15 +78,38 @@ __device__ __forceinline__ uint16_t f32_to_bits(float x) {
 // ---------------------------------------------------------------------------
 // D_i = rowsum(dout * out) and the zeroed dq accumulator
 // ---------------------------------------------------------------------------
-// Lanes per (row, head) pair: the row's 16-byte chunks rounded up to a power
-// of two (head_dim 96: 12 chunks on 16 lanes, the last 4 idle).
-template <int D>
-constexpr int pair_lanes() { return D / 8 <= 8 ? 8 : (D / 8 <= 16 ? 16 : 32); }
+// Elements of T in 16 bytes, and lanes per (row, head) pair: the row's
+// 16-byte chunks rounded up to a power of two (16-bit head_dim 96: 12 chunks
+// on 16 lanes, the last 4 idle).
+template <typename T>
+constexpr int chunk_elems() { return 16 / (int)sizeof(T); }
+template <typename T, int D>
+constexpr int pair_lanes() {
+  constexpr int CH = D / chunk_elems<T>();
+  return CH <= 8 ? 8 : (CH <= 16 ? 16 : (CH <= 32 ? 32 : 64));
+}
+
+template <typename T>
+__device__ __forceinline__ float chunk_dot(u32x4 o, u32x4 g) {
+  float dot = 0.f;
+  if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dot += __uint_as_float(o[e]) * __uint_as_float(g[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dot += half_to_f32<T>(o[e] & 0xffffu) * half_to_f32<T>(g[e] & 0xffffu);
+      dot += half_to_f32<T>(o[e] >> 16) * half_to_f32<T>(g[e] >> 16);
+    }
+  }
+  return dot;
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-  constexpr int CH = D / 8;                // 16-byte chunks per (row, head)
-  constexpr int LP = pair_lanes<D>();      // lanes per pair
+  constexpr int EPC = chunk_elems<T>();
+  constexpr int CH = D / EPC;              // 16-byte chunks per (row, head)
+  constexpr int LP = pair_lanes<T, D>();   // lanes per pair
   constexpr int PAIRS = 256 / LP;          // (row, head) pairs per workgroup
   const int tid = threadIdx.x;
   const int64_t p = (int64_t)blockIdx.x * PAIRS + tid / LP;  // row * heads + head
@@ -93,16 +117,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   const int64_t npairs = (int64_t)a.total_q * a.heads;
   float dot = 0.f;
   if (p < npairs && c < CH) {
-    const u32x4 o = *(const u32x4*)((const uint16_t*)a.out + p * D + 8 * c);
-    const u32x4 g = *(const u32x4*)((const uint16_t*)a.dout + p * D + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dot += half_to_f32<T>(o[e] & 0xffffu) * half_to_f32<T>(g[e] & 0xffffu);
-      dot += half_to_f32<T>(o[e] >> 16) * half_to_f32<T>(g[e] >> 16);
-    }
+    const T* op = (const T*)a.out + p * D + EPC * c;
+    const T* gp = (const T*)a.dout + p * D + EPC * c;
+    dot = chunk_dot<T>(*(const u32x4*)op, *(const u32x4*)gp);
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)(a.dq_acc + p * D + 8 * c) = z;
-    *(f32x4*)(a.dq_acc + p * D + 8 * c + 4) = z;
+#pragma unroll
+    for (int e = 0; e < EPC; e += 4) *(f32x4*)(a.dq_acc + p * D + EPC * c + e) = z;
   }
 #pragma unroll
   for (int off = LP / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
@@ -118,23 +138,29 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int CH = D / 8;
-  constexpr int LP = pair_lanes<D>();
+  constexpr int EPC = chunk_elems<T>();
+  constexpr int CH = D / EPC;
+  constexpr int LP = pair_lanes<T, D>();
   constexpr int PAIRS = 256 / LP;
   const int tid = threadIdx.x;
   const int64_t p = (int64_t)blockIdx.x * PAIRS + tid / LP;
   const int c = tid % LP;
   const int64_t rows = a.cu_q[a.batch];  // rows past the last sequence are not written
   if (p < rows * a.heads && c < CH) {
-    const f32x4 x0 = *(const f32x4*)(a.dq_acc + p * D + 8 * c);
-    const f32x4 x1 = *(const f32x4*)(a.dq_acc + p * D + 8 * c + 4);
-    u32x4 r;
+    const float* src = a.dq_acc + p * D + EPC * c;
+    if constexpr (std::is_same<T, float>::value) {
+      *(f32x4*)((float*)a.dq + p * D + EPC * c) = *(const f32x4*)src;
+    } else {
+      const f32x4 x0 = *(const f32x4*)src;
+      const f32x4 x1 = *(const f32x4*)(src + 4);
+      u32x4 r;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      r[e] = (uint32_t)f32_to_bits<T>(x0[2 * e]) | ((uint32_t)f32_to_bits<T>(x0[2 * e + 1]) << 16);
-      r[e + 2] = (uint32_t)f32_to_bits<T>(x1[2 * e]) | ((uint32_t)f32_to_bits<T>(x1[2 * e + 1]) << 16);
+      for (int e = 0; e < 2; ++e) {
+        r[e] = (uint32_t)f32_to_bits<T>(x0[2 * e]) | ((uint32_t)f32_to_bits<T>(x0[2 * e + 1]) << 16);
+        r[e + 2] = (uint32_t)f32_to_bits<T>(x1[2 * e]) | ((uint32_t)f32_to_bits<T>(x1[2 * e + 1]) << 16);
+      }
+      *(u32x4*)((uint16_t*)a.dq + p * D + EPC * c) = r;
     }
-    *(u32x4*)((uint16_t*)a.dq + p * D + 8 * c) = r;
   }
 }
 
@@ -615,29 +641,342 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// the backward workgroup for fp32 inputs (head_dim 64, 96, 128) and for
+// 16-bit inputs at head_dim 256: 64-key work items, 4 wavefronts
+// ---------------------------------------------------------------------------
+// 16x16 MFMAs throughout (gfx950 layouts, lane l, i = l % 16, G = l / 16;
+// accumulator register r holds row 4G + r, column i): fp32 16x16x4 (A row i,
+// k = G; B column i, k = G) or 16-bit 16x16x32 (A row i, k = 8G..8G+7; B
+// column i, the same k).
+//   * Wave w owns keys 16w .. 16w+15 of the item.  Lane (i, G) holds K and V
+//     of key 16w + i, head dimensions G*D/4 .. G*D/4 + D/4 - 1, in registers
+//     for the whole item: the B operand of S = Q K^T and dP = dO V^T when the
+//     contraction index of lane group G runs over those dimensions (Q and dO
+//     rows read from LDS the same way as the A operand).
+//   * Each step takes 32 query rows of one query head, as two 16-row tiles u:
+//     register r of tile u holds row 16u + 4G + r and key 16w + i.  Those are
+//     the A operand of dV = P^T dO and dK = dS^T Q (row i = key, contraction
+//     over the 32 rows): fp32 takes k-step (u, r) with row 16u + 4G + r on lane
+//     group G; 16-bit takes one k-step whose 8 indices of group G are rows
+//     4G + 0..3 and 16 + 4G + 0..3, the B operand coming from two
+//     transposing reads of the row-major dO (or Q) tile.
+//   * dS goes to LDS (16-bit: transposed, [key][row], each lane's 2 x 4 rows
+//     as two 8-byte stores, read back by transposing reads); dQ = dS K
+//     (contraction over the item's 64 keys) is split into 16x16 tiles, 2D/64
+//     per wave, and added to the float32 accumulator with atomic additions.
+// P and dS are kept without the softmax scale, which dK and dQ apply at the
+// end, as in the 256-key workgroup.  Not tuned for speed: the 256-key
+// workgroup serves the 16-bit head dims up to 128.
+constexpr int kGenBN = 64;  // keys per work item
+constexpr int kGenBM = 32;  // query rows per step
+
+template <typename T, int D>
+struct GenGeom {
+  static constexpr bool F32 = std::is_same<T, float>::value;
+  static constexpr int EL = (int)sizeof(T);
+  static constexpr int EPC = 16 / EL;                   // elements per 16-byte chunk
+  static constexpr int QP = F32 ? D + 4 : D + 8;        // Q / dO LDS row pitch (elements)
+  static constexpr int KP = F32 ? D + 16 : D + 8;       // K LDS row pitch
+  // dS in LDS: fp32 row-major [rows][keys], 16-bit transposed [keys][rows]
+  static constexpr int SP = F32 ? kGenBN + 4 : kGenBM + 8;
+  static constexpr int DL = D / 4;                      // head dims of one lane group
+  static constexpr int NV = DL / EPC;                   // 16-byte chunks of K (or V) per lane
+  static constexpr int QBYTES = kGenBM * QP * EL;
+  static constexpr int KBYTES = kGenBN * KP * EL;
+  static constexpr int SBYTES = (F32 ? kGenBM : kGenBN) * SP * EL;
+  static_assert(DL % EPC == 0 && (QP * EL) % 16 == 0 && (KP * EL) % 16 == 0 && (SP * EL) % 16 == 0,
+                "rows must hold whole 16-byte chunks");
+};
+
+// transposing read of rows r0 .. r0+3 of column c0 + i from a row-major tile
+// of 16-bit elements with row pitch P (see tr_read4)
+template <int P>
+__device__ __forceinline__ s16x4 gen_tr4(const uint16_t* tile, int r0, int c0, int i) {
+  const uint16_t* p = tile + (r0 + (i >> 2)) * P + c0 + 4 * (i & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+template <typename V8, int P>
+__device__ __forceinline__ V8 gen_tr8(const uint16_t* tile, int ra, int rb, int c0, int i) {
+  const s16x4 lo = gen_tr4<P>(tile, ra, c0, i);
+  const s16x4 hi = gen_tr4<P>(tile, rb, c0, i);
+  const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(V8, v);
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_gen_kernel(BwdArgs a) {
+  using Geo = GenGeom<T, D>;
+  constexpr bool F32 = Geo::F32;
+  constexpr int BN = kGenBN, BM = kGenBM, EPC = Geo::EPC, QP = Geo::QP, KP = Geo::KP, SP = Geo::SP;
+  constexpr int DL = Geo::DL, NV = Geo::NV, DT = D / 16;
+  constexpr int DQT = 2 * D / 64;  // 16x16 dQ tiles per wave (2 row tiles x D/16 column tiles over 4 waves)
+  static_assert(F32 ? (D == 64 || D == 96 || D == 128) : D == 256, "generic backward shapes");
+
+  __shared__ __attribute__((aligned(16))) char lds_kb[Geo::KBYTES];
+  __shared__ __attribute__((aligned(16))) char lds_qb[Geo::QBYTES];
+  __shared__ __attribute__((aligned(16))) char lds_dob[Geo::QBYTES];
+  __shared__ __attribute__((aligned(16))) char lds_dsb[Geo::SBYTES];
+  __shared__ __attribute__((aligned(16))) float lds_lse[BM];
+  __shared__ __attribute__((aligned(16))) float lds_dr[BM];
+
+  ColItem w;
+  if (!decode_col<BN>(a, w)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int key0 = w.j * BN;
+  const int kc = key0 + 16 * wave + li;  // this lane's key (S, dP columns) in the sequence
+  const int shift = w.Lk - w.Lq;
+  const int64_t rs = a.row_stride, rsk = a.kv_row_stride;
+  const T* kbase = (const T*)a.k + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
+  const T* vbase = (const T*)a.v + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  // K and V of the lane's key: head dims lg*DL .. lg*DL + DL - 1
+  u32x4 kr[NV], vr[NV];
+#pragma unroll
+  for (int n = 0; n < NV; ++n) {
+    kr[n] = zero;
+    vr[n] = zero;
+    if (kc < w.Lk) {
+      kr[n] = *(const u32x4*)(kbase + (int64_t)kc * rsk + lg * DL + n * EPC);
+      vr[n] = *(const u32x4*)(vbase + (int64_t)kc * rsk + lg * DL + n * EPC);
+    }
+  }
+  // the item's K block in LDS (row-major, keys past the sequence as zeros): B operand of dQ = dS K
+  for (int c = tid; c < BN * D / EPC; c += 256) {
+    const int row = c / (D / EPC), ch = c % (D / EPC);
+    u32x4 x = zero;
+    if (key0 + row < w.Lk) x = *(const u32x4*)(kbase + (int64_t)(key0 + row) * rsk + ch * EPC);
+    *(u32x4*)(lds_kb + (row * KP + ch * EPC) * Geo::EL) = x;
+  }
+
+  f32x4 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int i_begin = CAUSAL ? max(0, key0 - shift) / BM : 0;
+  const int i_end = (w.Lq + BM - 1) / BM;
+  const int nblk = max(0, i_end - i_begin);
+  const int nsteps = a.head_group * nblk;
+
+  for (int st = 0; st < nsteps; ++st) {
+    const int h = w.hk * a.head_group + st / nblk;
+    const int r0 = (i_begin + st % nblk) * BM;
+    // ---- stage Q, dO, lse (log2 units) and D of rows r0 .. r0+31 (rows past the sequence as zeros)
+    {
+      const T* qh = (const T*)a.q + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D;
+      const T* doh = (const T*)a.dout + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D;
+      for (int c = tid; c < BM * D / EPC; c += 256) {
+        const int row = c / (D / EPC), ch = c % (D / EPC);
+        u32x4 x = zero, y = zero;
+        if (r0 + row < w.Lq) {
+          x = *(const u32x4*)(qh + (int64_t)row * rs + ch * EPC);
+          y = *(const u32x4*)(doh + (int64_t)row * rs + ch * EPC);
+        }
+        *(u32x4*)(lds_qb + (row * QP + ch * EPC) * Geo::EL) = x;
+        *(u32x4*)(lds_dob + (row * QP + ch * EPC) * Geo::EL) = y;
+      }
+      if (tid < BM) {
+        const bool ok = r0 + tid < w.Lq;
+        const int64_t at = (int64_t)h * a.total_q + w.q_start + r0 + tid;
+        lds_lse[tid] = ok ? a.lse[at] * kLog2eF : 0.f;
+        lds_dr[tid] = ok ? a.drow[at] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // ---- S = Q K^T and dP = dO V^T: tile u, register r <-> row 16u + 4lg + r, key kc
+    f32x4 s[2], dp[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char* qrow = lds_qb + ((16 * u + li) * QP + lg * DL) * Geo::EL;
+      const char* dorow = lds_dob + ((16 * u + li) * QP + lg * DL) * Geo::EL;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        if constexpr (F32) {
+          const f32x4 q4 = *(const f32x4*)(qrow + 16 * n), o4 = *(const f32x4*)(dorow + 16 * n);
+          const f32x4 k4 = __builtin_bit_cast(f32x4, kr[n]), v4 = __builtin_bit_cast(f32x4, vr[n]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            s[u] = mfma4(q4[c], k4[c], s[u]);
+            dp[u] = mfma4(o4[c], v4[c], dp[u]);
+          }
+        } else {
+          typedef typename Elem16<T>::v8 v8;
+          s[u] = Mfma16<T>::run(*(const v8*)(qrow + 16 * n), __builtin_bit_cast(v8, kr[n]), s[u]);
+          dp[u] = Mfma16<T>::run(*(const v8*)(dorow + 16 * n), __builtin_bit_cast(v8, vr[n]), dp[u]);
+        }
+      }
+    }
+
+    // ---- P = exp(S scale - lse) on visible pairs, dS / scale = P (dP - D)
+    float p[2][4], ds[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const f32x4 l4 = *(const f32x4*)(lds_lse + 16 * u + 4 * lg);
+      const f32x4 d4 = *(const f32x4*)(lds_dr + 16 * u + 4 * lg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 16 * u + 4 * lg + r;
+        const bool vis = row < w.Lq && kc < w.Lk && (!CAUSAL || kc <= row + shift);
+        const float pr = vis ? fast_exp2(__builtin_fmaf(s[u][r], a.scale_log2, -l4[r])) : 0.f;
+        p[u][r] = pr;
+        ds[u][r] = pr * (dp[u][r] - d4[r]);
+      }
+    }
+
+    // ---- dV += P^T dO, dK += dS^T Q; dS to LDS
+    if constexpr (F32) {
+      const float* qt = (const float*)lds_qb;
+      const float* dot = (const float*)lds_dob;
+      float* dst = (float*)lds_dsb;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * u + 4 * lg + r;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            dv[dt] = mfma4(p[u][r], dot[row * QP + 16 * dt + li], dv[dt]);
+            dk[dt] = mfma4(ds[u][r], qt[row * QP + 16 * dt + li], dk[dt]);
+          }
+          dst[row * SP + 16 * wave + li] = ds[u][r];
+        }
+    } else {
+      typedef typename Elem16<T>::v8 v8;
+      typedef typename Elem16<T>::v4 v4;
+      const uint16_t* qt = (const uint16_t*)lds_qb;
+      const uint16_t* dot = (const uint16_t*)lds_dob;
+      uint16_t* dst = (uint16_t*)lds_dsb;
+      v4 p0, p1, d0, d1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p0[r] = (T)p[0][r];
+        p1[r] = (T)p[1][r];
+        d0[r] = (T)ds[0][r];
+        d1[r] = (T)ds[1][r];
+      }
+      const v8 pa = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const v8 da = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7);
+      // dS^T row 16 wave + li (this lane's key): rows 4lg .. 4lg+3 and 16+4lg .. 16+4lg+3
+      // (whole-vector stores: scalar 16-bit LDS stores of these values were
+      // miscompiled into stores of one element)
+      *(v4*)(dst + (16 * wave + li) * SP + 4 * lg) = d0;
+      *(v4*)(dst + (16 * wave + li) * SP + 16 + 4 * lg) = d1;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dv[dt] = Mfma16<T>::run(pa, gen_tr8<v8, QP>(dot, 4 * lg, 16 + 4 * lg, 16 * dt, li), dv[dt]);
+        dk[dt] = Mfma16<T>::run(da, gen_tr8<v8, QP>(qt, 4 * lg, 16 + 4 * lg, 16 * dt, li), dk[dt]);
+      }
+    }
+    __syncthreads();
+
+    // ---- dQ = scale * dS K: tile t = wave + 4n takes row tile t % 2, column tile t / 2
+    const __amdgpu_buffer_rsrc_t racc =
+        buffer_rsrc(a.dq_acc + (int64_t)(w.q_start + r0) * rs + (int64_t)h * D,
+                    tiling::head_rows_bytes(min(BM, w.Lq - r0), rs, D, 4));
+#pragma unroll
+    for (int n = 0; n < DQT; ++n) {
+      const int t = wave + 4 * n, ru = t & 1, ct = t >> 1;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (F32) {
+        const float* dst = (const float*)lds_dsb;
+        const float* kt = (const float*)lds_kb;
+#pragma unroll
+        for (int s4 = 0; s4 < BN / 4; ++s4)
+          acc = mfma4(dst[(16 * ru + li) * SP + 4 * s4 + lg], kt[(4 * s4 + lg) * KP + 16 * ct + li], acc);
+      } else {
+        typedef typename Elem16<T>::v8 v8;
+        const uint16_t* dst = (const uint16_t*)lds_dsb;
+        const uint16_t* kt = (const uint16_t*)lds_kb;
+#pragma unroll
+        for (int s32 = 0; s32 < BN / 32; ++s32) {
+          // A: dS row 16ru + li, keys 32 s32 + 8lg .. +7 (transposing reads of dS^T)
+          const v8 av = gen_tr8<v8, SP>(dst, 32 * s32 + 8 * lg, 32 * s32 + 8 * lg + 4, 16 * ru, li);
+          acc = Mfma16<T>::run(av, gen_tr8<v8, KP>(kt, 32 * s32 + 8 * lg, 32 * s32 + 8 * lg + 4, 16 * ct, li), acc);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * ru + 4 * lg + r;
+        if (r0 + row < w.Lq) {
+          const uint32_t off = ((uint32_t)row * (uint32_t)rs + 16 * ct + li) * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r] * a.scale, racc, (int)off, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: dK (times the softmax scale) and dV of keys key0 + 16 wave + 4 lg + r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int kk = key0 + 16 * wave + 4 * lg + r;
+    if (kk < w.Lk) {
+      T* dkp = (T*)a.dk + (int64_t)(w.k_start + kk) * rsk + (int64_t)w.hk * D;
+      T* dvp = (T*)a.dv + (int64_t)(w.k_start + kk) * rsk + (int64_t)w.hk * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dkp[16 * dt + li] = (T)(dk[dt][r] * a.scale);
+        dvp[16 * dt + li] = (T)dv[dt][r];
+      }
+    }
+  }
+}
+
 template <typename F>
 hipError_t launch(F kernel, int grid, int threads, hipStream_t stream, const BwdArgs& a) {
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_bwd_t(int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
-  if (head_dim == 128)
-    return causal ? launch(bwd16w_kernel<T, 128, true>, grid, 512, stream, a)
-                  : launch(bwd16w_kernel<T, 128, false>, grid, 512, stream, a);
-  if (head_dim == 96)
-    return causal ? launch(bwd16w_kernel<T, 96, true>, grid, 512, stream, a)
-                  : launch(bwd16w_kernel<T, 96, false>, grid, 512, stream, a);
-  if (head_dim == 64)
-    return causal ? launch(bwd16w_kernel<T, 64, true>, grid, 512, stream, a)
-                  : launch(bwd16w_kernel<T, 64, false>, grid, 512, stream, a);
-  return hipErrorInvalidValue;
+template <typename T, int D>
+hipError_t launch_wide(bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
+  return causal ? launch(bwd16w_kernel<T, D, true>, grid, 512, stream, a)
+                : launch(bwd16w_kernel<T, D, false>, grid, 512, stream, a);
+}
+template <typename T, int D>
+hipError_t launch_gen(bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
+  return causal ? launch(bwd_gen_kernel<T, D, true>, grid, 256, stream, a)
+                : launch(bwd_gen_kernel<T, D, false>, grid, 256, stream, a);
 }
 
-int64_t row_pairs_grid(const BwdArgs& a, int head_dim) {
+template <typename T>
+hipError_t launch_bwd16(int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_wide<T, 64>(causal, grid, a, stream);
+    case 96: return launch_wide<T, 96>(causal, grid, a, stream);
+    case 128: return launch_wide<T, 128>(causal, grid, a, stream);
+    case 256: return launch_gen<T, 256>(causal, grid, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd32(int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_gen<float, 64>(causal, grid, a, stream);
+    case 96: return launch_gen<float, 96>(causal, grid, a, stream);
+    case 128: return launch_gen<float, 128>(causal, grid, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// (row, head) pairs per workgroup of the prep and dq kernels: 256 / pair_lanes
+int64_t row_pairs_grid(const BwdArgs& a, int dtype, int head_dim) {
   const int64_t pairs = (int64_t)a.total_q * a.heads;
-  const int lanes = head_dim <= 64 ? 8 : (head_dim <= 128 ? 16 : 32);  // pair_lanes
+  const int chunks = head_dim / (dtype == 0 ? 4 : 8);
+  const int lanes = chunks <= 8 ? 8 : (chunks <= 16 ? 16 : (chunks <= 32 ? 32 : 64));
   const int64_t per = 256 / lanes;
   return (pairs + per - 1) / per;
 }
@@ -647,7 +986,9 @@ hipError_t launch_rows(int head_dim, int grid, hipStream_t stream, const BwdArgs
   switch (head_dim) {
     case 64: return launch(K<T, 64>::fn, grid, 256, stream, a);
     case 96: return launch(K<T, 96>::fn, grid, 256, stream, a);
-    default: return launch(K<T, 128>::fn, grid, 256, stream, a);
+    case 128: return launch(K<T, 128>::fn, grid, 256, stream, a);
+    case 256: return launch(K<T, 256>::fn, grid, 256, stream, a);
+    default: return hipErrorInvalidValue;
   }
 }
 template <typename T, int D>
@@ -655,31 +996,40 @@ struct PrepK { static constexpr auto fn = bwd_prep_kernel<T, D>; };
 template <typename T, int D>
 struct DqK { static constexpr auto fn = bwd_dq_kernel<T, D>; };
 
+template <template <typename, int> class K>
+hipError_t launch_rows_dtype(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream) {
+  const int64_t grid = row_pairs_grid(a, dtype, head_dim);
+  if (grid == 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (dtype == 0) return launch_rows<K, float>(head_dim, (int)grid, stream, a);
+  if (dtype == 1) return launch_rows<K, __bf16>(head_dim, (int)grid, stream, a);
+  if (dtype == 2) return launch_rows<K, _Float16>(head_dim, (int)grid, stream, a);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 int bwd_block_n(int dtype, int head_dim) {
-  if ((dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 96 || head_dim == 128)) return kBwdBNWide;
+  const bool half = dtype == 1 || dtype == 2;
+  if (half && (head_dim == 64 || head_dim == 96 || head_dim == 128)) return kBwdBNWide;
+  if (half && head_dim == 256) return kGenBN;
+  if (dtype == 0 && (head_dim == 64 || head_dim == 96 || head_dim == 128)) return kGenBN;
   return 0;
 }
 
 hipError_t launch_bwd_prep(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream) {
-  const int grid = (int)row_pairs_grid(a, head_dim);
-  if (grid == 0) return hipSuccess;
-  if (dtype == 1) return launch_rows<PrepK, __bf16>(head_dim, grid, stream, a);
-  return launch_rows<PrepK, _Float16>(head_dim, grid, stream, a);
+  return launch_rows_dtype<PrepK>(dtype, head_dim, a, stream);
 }
 
 hipError_t launch_bwd(int dtype, int head_dim, bool causal, int grid, const BwdArgs& a, hipStream_t stream) {
-  if (dtype == 1) return launch_bwd_t<__bf16>(head_dim, causal, grid, a, stream);
-  if (dtype == 2) return launch_bwd_t<_Float16>(head_dim, causal, grid, a, stream);
+  if (dtype == 0) return launch_bwd32(head_dim, causal, grid, a, stream);
+  if (dtype == 1) return launch_bwd16<__bf16>(head_dim, causal, grid, a, stream);
+  if (dtype == 2) return launch_bwd16<_Float16>(head_dim, causal, grid, a, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdArgs& a, hipStream_t stream) {
-  const int grid = (int)row_pairs_grid(a, head_dim);
-  if (grid == 0) return hipSuccess;
-  if (dtype == 1) return launch_rows<DqK, __bf16>(head_dim, grid, stream, a);
-  return launch_rows<DqK, _Float16>(head_dim, grid, stream, a);
+  return launch_rows_dtype<DqK>(dtype, head_dim, a, stream);
 }
 
 }  // namespace fa
