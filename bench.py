@@ -624,7 +624,9 @@ def main() -> int:
         base = workload_ragged64k()
         for bwl, bc in ((base, True), (workload_sweep(4096, 128), False),
                         (workload_sweep(4096, 128), True), (workload_sweep(4096, 64), True),
-                        (dataclasses.replace(base, name=base.name.replace("_d128_", "_d96_"), head_dim=96), True)):
+                        (dataclasses.replace(base, name=base.name.replace("_d128_", "_d96_"), head_dim=96), True),
+                        (dataclasses.replace(base, name=base.name.replace("_h32_d128_", "_h16_d256_"), heads=16,
+                                             head_dim=256), True)):
             line["backward"].append(measure_backward(bwl, bc))
             print(f"# {line['backward'][-1]}", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()

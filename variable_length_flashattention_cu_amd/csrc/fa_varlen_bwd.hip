@@ -1,5 +1,6 @@
 // fa_varlen_bwd.hip -- gfx950 kernels for the backward pass of exact attention
-// over packed variable-length sequences (16-bit inputs, head_dim 64 and 128).
+// over packed variable-length sequences (bf16/fp16 at head_dim 64, 96, 128 and
+// 256; fp32 at 64, 96 and 128).
 //
 // Organisation (zepes.com "Comprendiendo Flash-Atención y Flash-Atención-2",
 // section "FashAttention v1" (sic)): each workgroup owns a block of key columns
@@ -20,7 +21,9 @@
 // Three launches:
 //   bwd_prep_kernel  D_i for every (row, head) and a zeroed dQ accumulator;
 //   bwd16w_kernel    one workgroup per (256-key block, key/value head): dK, dV
-//                    of the block and atomic dQ contributions;
+//                    of the block and atomic dQ contributions (16-bit inputs,
+//                    head_dim up to 128), or bwd_gen_kernel on 64-key blocks
+//                    (fp32 inputs, and 16-bit head_dim 256);
 //   bwd_dq_kernel    dq = accumulator (already scaled) in the input type.
 //
 // Workgroup layout (8 wavefronts; wave w owns the 32 keys of key group w of
