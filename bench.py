@@ -224,9 +224,23 @@ def take_sample(wl: Workload, t: dict, causal: bool, heads) -> dict:
     return {"rows": rows, "heads": list(heads), "out": out, "lse": lse, "causal": causal}
 
 
+def call_block_m(wl: Workload) -> int:
+    """Query rows per work item of a whole fa_varlen_fwd call: 128 for 16-bit
+    inputs at head_dim 64/128 with max_seqlen_q <= 1024 (the library's short
+    configuration), else the BM of fa_varlen_block_sizes, which the mapped
+    (kernel-only) entry point always uses."""
+    import variable_length_flashattention_cu_amd as fa
+    if wl.dtype in ("bf16", "f16") and wl.head_dim in (64, 128) and wl.max_seqlen_q <= 1024:
+        return 128
+    code = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16, "f32": fa.FA_DTYPE_F32}[wl.dtype]
+    return fa.fa_varlen_block_sizes(wl.head_dim, code)[0]
+
+
 def measure_fwd(wl: Workload, t: dict, causal: bool) -> tuple:
     """One forward workload: whole-call and kernel-only per-call times, and a
-    sample of the outputs for the parity check."""
+    sample of the outputs for the parity check.  The kernel-only figure times
+    fa_varlen_fwd_mapped (work items of fa_varlen_block_sizes' BM); for short
+    batches the whole call runs 128-row items instead (`call_block_m`)."""
     r = Runner(wl, t, causal)
     pw = prewarm(r.step)
     n = timed_iters(pw)
@@ -243,7 +257,9 @@ def measure_fwd(wl: Workload, t: dict, causal: bool) -> tuple:
            "kernel_tflops": round(fl / kern["median_ms"] / 1e9, 1),
            "kernel_frac_bf16_peak": round(fl / kern["median_ms"] / 1e9 / PEAK_BF16_TFLOPS, 4),
            "kernel_frac_hbm_peak": round(by / kern["median_ms"] / 1e6 / PEAK_HBM_GBS, 4),
-           "kernel_prewarm": pwk}
+           "kernel_prewarm": pwk,
+           "call_frac_bf16_peak": round(fl / call["median_ms"] / 1e9 / PEAK_BF16_TFLOPS, 4),
+           "call_block_m": call_block_m(wl)}
     sample = take_sample(wl, t, causal, sorted({0, wl.heads - 1}))
     del r
     return row, sample

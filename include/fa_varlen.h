@@ -174,6 +174,12 @@ int fa_varlen_tile_map(const fa_tensor* cu_seqlens_q, int32_t max_seqlen_q, int3
  * D must be 64, 96 or 128, or 256 with BF16/F16 inputs (FA_ERR_HEAD_DIM).
  * Alignment: q, k, v and out data 16 bytes; lse and the offsets 4 bytes (the
  * offsets are best kept 32-byte aligned, as any hipMalloc'd buffer is).
+ * Work items: with BF16/F16 inputs at D 64 or 128 and max_seqlen_q <= 1024
+ * the pass takes 128-row work items (four wavefronts; two workgroups share a
+ * compute unit) instead of the BM of fa_varlen_block_sizes; each query row
+ * goes through the same steps either way, but which key slabs take the
+ * full softmax (with row maxima) may differ, so its results can differ from
+ * fa_varlen_fwd_mapped's in the last bits.
  * Scratch: up to 64 sequences none (the attention kernel rebuilds the
  * work-item map per wavefront from cu_seqlens_q and is the only launch);
  * above that a (batch+1)-entry int32 map is allocated and freed
@@ -189,7 +195,7 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
  * The same forward pass with a work-item map the caller already built with
  * fa_varlen_tile_map for this head_dim and dtype, e.g. once per batch and
  * reused by every layer.  Launches only the attention kernel and allocates
- * nothing.
+ * nothing.  It always uses the BM of fa_varlen_block_sizes.
  *   blk_start     device int32 [batch + 1], 4-byte aligned, read only
  * Other arguments and errors as fa_varlen_fwd.  A map built for another
  * (head_dim, dtype) block height is a precondition violation (rows are then

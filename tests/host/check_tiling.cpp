@@ -258,7 +258,7 @@ static void check_f32() {
 template <int D, int BN, bool V_LAYOUT>
 static void check_direct(long H) {
   constexpr int KS = k_stride<D>(), CPR = KS / 8, SLOTS = BN * CPR;
-  CHECK(SLOTS == 4 * 4 * 64, "D=%d BN=%d: %d slots are not 4 waves x 4 loads x 64 lanes", D, BN, SLOTS);
+  CHECK(SLOTS % 64 == 0, "D=%d BN=%d: %d slots are not whole wavefront loads", D, BN, SLOTS);
   const long h = H - 1;
   std::vector<int> placed(BN * KS, 0);
   for (int rows : {BN, 1, BN / 2 + 3, BN - 1}) {  // valid keys in the tile
@@ -378,16 +378,22 @@ static void check_pipe() {
 
 int main() {
   check_pipe<64, 128, 8>();
+  check_pipe<64, 64, 4>();
   check_pipe<96, 64, 8>();
   check_pipe<128, 64, 8>();
+  check_pipe<128, 32, 4>();
   check_pipe<256, 32, 4>();
   for (long H : {1L, 3L, 16L}) {
     check_direct<64, 128, false>(H);
     check_direct<64, 128, true>(H);
+    check_direct<64, 64, false>(H);
+    check_direct<64, 64, true>(H);
     check_direct<96, 64, false>(H);
     check_direct<96, 64, true>(H);
     check_direct<128, 64, false>(H);
     check_direct<128, 64, true>(H);
+    check_direct<128, 32, false>(H);
+    check_direct<128, 32, true>(H);
     check_direct<256, 32, false>(H);
     check_direct<256, 32, true>(H);
   }

@@ -229,20 +229,49 @@ def test_poisoned_and_guarded_buffers(fa):
 
 
 def test_deterministic_and_mapped_identical(fa):
-    wl = workload_ragged_qk()
+    # queries longer than 1024 rows: fa_varlen_fwd takes the work items of
+    # fa_varlen_block_sizes, as the mapped entry point does, so the two are
+    # bit-identical; with 1024 rows or fewer (the 128-row items) they agree
+    # to the parity bar and each is deterministic
+    for wl in (workload_custom("mapped_long_d64", [1300, 200, 77], [1100, 300, 90], 6, 64, "bf16", seed=30),
+               workload_custom("mapped_long_d128", [1025, 3], None, 4, 128, "f16", seed=31), workload_ragged_qk()):
+        data = draw_qkv(wl)
+        t = to_device(data, wl)
+        code = fa.FA_DTYPE_BF16 if wl.dtype == "bf16" else fa.FA_DTYPE_F16
+        blk = fa.fa_varlen_tile_map(t["cu_q"], wl.max_seqlen_q, wl.head_dim, code)
+        for causal in (False, True):
+            say(f"case determinism {wl.name} causal={causal}")
+            o1, l1 = host(*run_gpu(wl, t, causal))
+            o2, l2 = host(*run_gpu(wl, t, causal))
+            o3, l3 = fa.fa_varlen_fwd_mapped(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], wl.max_seqlen_q,
+                                             wl.max_seqlen_k, blk, wl.scale, causal)
+            torch.cuda.synchronize()
+            o3, l3 = host(o3, l3)
+            assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+            if wl.max_seqlen_q > 1024:
+                assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+            else:
+                compare(o1, l1, o3, l3, TOL[wl.dtype], f"{wl.name}: short items vs mapped")
+
+
+SHORT = [("short_d64_bf16", [1024, 1, 129, 700, 64, 1000, 0, 33], None, 64, "bf16"),
+         ("short_d128_f16", [512, 1024, 255, 2, 97], [600, 1024, 100, 2, 300], 128, "f16"),
+         ("short_d128_bf16_qk", [1000, 31, 400], [1500, 31, 200], 128, "bf16")]
+
+
+@pytest.mark.parametrize("name,lq,lk,head_dim,dtype", SHORT, ids=[s[0] for s in SHORT])
+@pytest.mark.parametrize("causal", [False, True])
+def test_short_work_items(fa, name, lq, lk, head_dim, dtype, causal):
+    """max_seqlen_q <= 1024 at head_dim 64/128: fa_varlen_fwd's 128-row work
+    items (four wavefronts, 64- or 32-key tiles) against the oracle: ragged
+    tails, empty and single-token sequences, Lq != Lk."""
+    wl = workload_custom(name, lq, lk, 4, head_dim, dtype, seed=len(name) + head_dim, heads_k=2)
+    say(f"case {wl.name} causal={causal}")
     data = draw_qkv(wl)
     t = to_device(data, wl)
-    blk = fa.fa_varlen_tile_map(t["cu_q"], wl.max_seqlen_q, wl.head_dim, fa.FA_DTYPE_BF16)
-    for causal in (False, True):
-        say(f"case determinism causal={causal}")
-        o1, l1 = host(*run_gpu(wl, t, causal))
-        o2, l2 = host(*run_gpu(wl, t, causal))
-        o3, l3 = fa.fa_varlen_fwd_mapped(t["q"], t["k"], t["v"], t["cu_q"], t["cu_k"], wl.max_seqlen_q,
-                                         wl.max_seqlen_k, blk, wl.scale, causal)
-        torch.cuda.synchronize()
-        o3, l3 = host(o3, l3)
-        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
-        assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+    o, l = host(*run_gpu(wl, t, causal))
+    ref_o, ref_l = attention_fwd(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
+    compare(o[:wl.total_q], l[:, :wl.total_q], ref_o, ref_l, TOL[dtype], wl.name)
 
 
 def test_check_cu_seqlens_flags(fa):

@@ -197,12 +197,25 @@ int check_i32_vector(const fa_tensor* t, int64_t n) {
 // ---------------------------------------------------------------------------
 struct Plan {
   fa::TileConfig tc;
+  bool short_items;  // the 128-row configuration of tile_config_short
   int64_t tmax;
   int64_t grid;
 };
 
-int plan_fwd(const Problem& p, int32_t max_q, Plan* plan) {
-  const fa::TileConfig tc = fa::tile_config(p.elem, p.head_dim);
+// Longest query sequence for which the entry points that build their own map
+// take the 128-row items of tile_config_short: items of short sequences have
+// few key tiles, and smaller items with two workgroups per compute unit
+// overlap more of each item's start-up (at 2048 rows the larger items were
+// faster again).
+constexpr int32_t kShortMaxQ = 1024;
+
+// own_map: the caller of the plan builds the map itself (or needs none), so
+// it may take the short configuration; the mapped entry point keeps the BM of
+// fa_varlen_block_sizes.
+int plan_fwd(const Problem& p, int32_t max_q, bool own_map, Plan* plan) {
+  const fa::TileConfig ts = fa::tile_config_short(p.elem, p.head_dim);
+  const bool short_items = own_map && ts.block_m > 0 && max_q <= kShortMaxQ;
+  const fa::TileConfig tc = short_items ? ts : fa::tile_config(p.elem, p.head_dim);
   // Upper bound on the number of work items: sum_b ceil(Lq_b / BM) is at most
   // batch * ceil(max_seqlen_q / BM) and at most ceil(total_q / BM) + batch - 1.
   const int64_t bm = tc.block_m;
@@ -213,6 +226,7 @@ int plan_fwd(const Problem& p, int32_t max_q, Plan* plan) {
   const int64_t grid = (work + 7) / 8 * 8;
   if (grid > INT32_MAX || tmax > INT32_MAX) return FA_ERR_TOO_LARGE;
   plan->tc = tc;
+  plan->short_items = short_items;
   plan->tmax = tmax;
   plan->grid = grid;
   return FA_OK;
@@ -246,7 +260,8 @@ int launch_fwd_mapped(const Problem& p, const Plan& plan, float scale, int32_t c
                       hipStream_t s) {
   if (plan.grid == 0) return FA_OK;  // no query rows: nothing to compute
   const fa::FwdArgs a = make_fwd_args(p, scale, causal, blk_start, plan);
-  if (fa::launch_fwd(p.elem, p.head_dim, causal != 0, (int)plan.grid, a, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_fwd(p.elem, p.head_dim, causal != 0, plan.short_items, (int)plan.grid, a, s) != hipSuccess)
+    return FA_ERR_HIP;
   return FA_OK;
 }
 
@@ -362,7 +377,7 @@ int fa_varlen_fwd_mapped(const fa_tensor* q, const fa_tensor* k, const fa_tensor
   st = check_i32_vector(blk_start, (int64_t)p.batch + 1);
   if (st != FA_OK) return st;
   Plan plan;
-  st = plan_fwd(p, max_seqlen_q, &plan);
+  st = plan_fwd(p, max_seqlen_q, false, &plan);
   if (st != FA_OK) return st;
   return launch_fwd_mapped(p, plan, softmax_scale, causal, static_cast<const int32_t*>(blk_start->data), stream);
 }
@@ -375,7 +390,7 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
                          causal, fwd_head_dim, nullptr, 0, 0, &p);
   if (st != FA_OK) return st;
   Plan plan;
-  st = plan_fwd(p, max_seqlen_q, &plan);
+  st = plan_fwd(p, max_seqlen_q, true, &plan);
   if (st != FA_OK) return st;
   if (plan.grid == 0) return FA_OK;
   // small batches: the kernel rebuilds the map itself (no allocation, one launch)
@@ -401,7 +416,7 @@ int fa_varlen_fwd_noalloc(const fa_tensor* q, const fa_tensor* k, const fa_tenso
   if (st != FA_OK) return st;
   if (p.batch > fa::kNoAllocMaxBatch) return FA_ERR_SCRATCH;
   Plan plan;
-  st = plan_fwd(p, max_seqlen_q, &plan);
+  st = plan_fwd(p, max_seqlen_q, true, &plan);
   if (st != FA_OK) return st;
   if (plan.grid == 0) return FA_OK;
   // The map goes to this device's static array (written whole by the map

@@ -945,6 +945,12 @@ TileConfig tile_config(int dtype, int head_dim) {
   return c;
 }
 
+TileConfig tile_config_short(int dtype, int head_dim) {
+  if ((dtype == 1 || dtype == 2) && head_dim == 64) return TileConfig{128, 64, 256};
+  if ((dtype == 1 || dtype == 2) && head_dim == 128) return TileConfig{128, 32, 256};
+  return TileConfig{0, 0, 0};
+}
+
 hipError_t launch_tile_map(const int32_t* cu_q, int batch, int block_m, int32_t* blk_start, hipStream_t stream) {
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(256), 0, stream, cu_q, batch, block_m, blk_start);
   return hipGetLastError();
@@ -958,7 +964,16 @@ hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, 
 }
 
 template <typename T>
-hipError_t launch_fwd16(int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd16(int head_dim, bool causal, bool short_items, int grid, const FwdArgs& a, hipStream_t stream) {
+  if (short_items) {  // 128-row items of four wavefronts (tile_config_short)
+    if (head_dim == 128)
+      return causal ? launch(fwd16_pipe_kernel<T, 128, 32, 4, true>, grid, 256, stream, a)
+                    : launch(fwd16_pipe_kernel<T, 128, 32, 4, false>, grid, 256, stream, a);
+    if (head_dim == 64)
+      return causal ? launch(fwd16_pipe_kernel<T, 64, 64, 4, true>, grid, 256, stream, a)
+                    : launch(fwd16_pipe_kernel<T, 64, 64, 4, false>, grid, 256, stream, a);
+    return hipErrorInvalidValue;
+  }
   if (head_dim == 128)
     return causal ? launch(fwd16_pipe_kernel<T, 128, 64, 8, true>, grid, 512, stream, a)
                   : launch(fwd16_pipe_kernel<T, 128, 64, 8, false>, grid, 512, stream, a);
@@ -974,12 +989,14 @@ hipError_t launch_fwd16(int head_dim, bool causal, int grid, const FwdArgs& a, h
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd(int dtype, int head_dim, bool causal, bool short_items, int grid, const FwdArgs& a,
+                      hipStream_t stream) {
   if (dtype == 1) {
-    return launch_fwd16<__bf16>(head_dim, causal, grid, a, stream);
+    return launch_fwd16<__bf16>(head_dim, causal, short_items, grid, a, stream);
   } else if (dtype == 2) {
-    return launch_fwd16<_Float16>(head_dim, causal, grid, a, stream);
+    return launch_fwd16<_Float16>(head_dim, causal, short_items, grid, a, stream);
   } else if (dtype == 0) {
+    if (short_items) return hipErrorInvalidValue;
     if (head_dim == 128)
       return causal ? launch(fwd_f32_kernel<128, 4, true>, grid, 256, stream, a)
                     : launch(fwd_f32_kernel<128, 4, false>, grid, 256, stream, a);

@@ -43,6 +43,11 @@ struct TileConfig {
 
 // {0,0,0} for an unsupported (dtype, head_dim).
 TileConfig tile_config(int dtype, int head_dim);
+// Short sequences (16-bit inputs, head_dim 64 or 128): 128-row work items of
+// four wavefronts on 64-key (head_dim 64) or 32-key (head_dim 128) tiles, 64 KB
+// of LDS, so two workgroups share a compute unit.  Only the entry points that
+// build their own map use it; {0,0,0} where there is none.
+TileConfig tile_config_short(int dtype, int head_dim);
 
 // Kernel arguments of the backward pass (passed by value).
 struct BwdArgs {
@@ -125,7 +130,8 @@ constexpr int kMaplessBatch = 64;
 hipError_t noalloc_map_scratch(int32_t** ptr);
 
 hipError_t launch_tile_map(const int32_t* cu_q, int batch, int block_m, int32_t* blk_start, hipStream_t stream);
-hipError_t launch_fwd(int dtype, int head_dim, bool causal, int grid, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd(int dtype, int head_dim, bool causal, bool short_items, int grid, const FwdArgs& a,
+                      hipStream_t stream);
 hipError_t launch_check_cu(const int32_t* cu_q, const int32_t* cu_k, int batch, int total_q, int total_k,
                            int max_q, int max_k, int32_t* flags, hipStream_t stream);
 
