@@ -192,6 +192,15 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void decode16_kernel(DecArgs 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           *(u32x4*)(vt + tiling::ks_index<D>(16 * kt + li, 4 * ks + lg)) = vr[kt][ks];
+      const bool more = t + kDecWaves < t_end;
+      // the next tile's V: its registers are free once V is in LDS
+      if (more) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            vr[kt][ks] = *(const u32x4*)((const uint16_t*)a.v_cache + off[kt] + 32 * ks + 8 * lg);
+      }
 
       // S^T = K Q^T: register e of tile kt holds key key0 + 16kt + 4lg + e of row li
       f32x4 sc[KT];
@@ -202,16 +211,14 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void decode16_kernel(DecArgs 
         for (int ks = 0; ks < KS; ++ks)
           sc[kt] = Mfma16<T>::run(ka[kt][ks], qreg[ks], sc[kt]);
       }
-      // the next tile of this wave: loads into the registers just consumed
-      if (t + kDecWaves < t_end) {
+      // the next tile's K: into the registers the product above consumed
+      if (more) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
+          for (int ks = 0; ks < KS; ++ks)
             ka[kt][ks] =
                 __builtin_bit_cast(v8, *(const u32x4*)((const uint16_t*)a.k_cache + off[kt] + 32 * ks + 8 * lg));
-            vr[kt][ks] = *(const u32x4*)((const uint16_t*)a.v_cache + off[kt] + 32 * ks + 8 * lg);
-          }
         if (t + 2 * kDecWaves < t_end) {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
