@@ -646,51 +646,65 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // the backward workgroup for fp32 inputs (head_dim 64, 96, 128) and for
-// 16-bit inputs at head_dim 256: 64-key work items, 4 wavefronts
+// 16-bit inputs at head_dim 256: 4 wavefronts, 64 KW-key work items
 // ---------------------------------------------------------------------------
 // 16x16 MFMAs throughout (gfx950 layouts, lane l, i = l % 16, G = l / 16;
 // accumulator register r holds row 4G + r, column i): fp32 16x16x4 (A row i,
 // k = G; B column i, k = G) or 16-bit 16x16x32 (A row i, k = 8G..8G+7; B
 // column i, the same k).
-//   * Wave w owns keys 16w .. 16w+15 of the item.  Lane (i, G) holds K and V
-//     of key 16w + i, head dimensions G*D/4 .. G*D/4 + D/4 - 1, in registers
-//     for the whole item: the B operand of S = Q K^T and dP = dO V^T when the
-//     contraction index of lane group G runs over those dimensions (Q and dO
-//     rows read from LDS the same way as the A operand).
+//   * Wave w owns the KW 16-key subtiles KW w .. KW w + KW - 1 of the item.
+//     Lane (i, G) holds V (and with KW = 1 also K) of key i of each subtile,
+//     head dimensions G*D/4 .. G*D/4 + D/4 - 1, in registers for the whole
+//     item: the B operand of S = Q K^T and dP = dO V^T when the contraction
+//     index of lane group G runs over those dimensions (Q and dO rows read
+//     from LDS the same way as the A operand).  With KW = 2 the K operand is
+//     read from the item's K block in LDS instead, which the wave needs for
+//     dQ anyway.
 //   * Each step takes 32 query rows of one query head, as two 16-row tiles u:
-//     register r of tile u holds row 16u + 4G + r and key 16w + i.  Those are
-//     the A operand of dV = P^T dO and dK = dS^T Q (row i = key, contraction
-//     over the 32 rows): fp32 takes k-step (u, r) with row 16u + 4G + r on lane
-//     group G; 16-bit takes one k-step whose 8 indices of group G are rows
-//     4G + 0..3 and 16 + 4G + 0..3, the B operand coming from two
-//     transposing reads of the row-major dO (or Q) tile.
+//     register r of tile u holds row 16u + 4G + r and key i of the subtile.
+//     Those are the A operand of dV = P^T dO and dK = dS^T Q (row i = key,
+//     contraction over the 32 rows): fp32 takes k-step (u, r) with row
+//     16u + 4G + r on lane group G; 16-bit takes one k-step whose 8 indices of
+//     group G are rows 4G + 0..3 and 16 + 4G + 0..3, the B operand coming from
+//     two transposing reads of the row-major dO (or Q) tile, shared by the
+//     wave's subtiles.
 //   * dS goes to LDS (16-bit: transposed, [key][row], each lane's 2 x 4 rows
 //     as two 8-byte stores, read back by transposing reads); dQ = dS K
-//     (contraction over the item's 64 keys) is split into 16x16 tiles, 2D/64
-//     per wave, and added to the float32 accumulator with atomic additions.
+//     (contraction over the item's 64 KW keys) is split into 16x16 tiles,
+//     2D/64 per wave, and added to the float32 accumulator with atomic
+//     additions: D additions per query row and item, so larger items need
+//     fewer (at head_dim 256 they bound the pass).
 // P and dS are kept without the softmax scale, which dK and dQ apply at the
-// end, as in the 256-key workgroup.  Not tuned for speed: the 256-key
-// workgroup serves the 16-bit head dims up to 128.
-constexpr int kGenBN = 64;  // keys per work item
+// end, as in the 256-key workgroup.  The 256-key workgroup serves the 16-bit
+// head dims up to 128.
 constexpr int kGenBM = 32;  // query rows per step
+// 16-key subtiles per wavefront: 2 at 16-bit head_dim 256 (128-key items), 1
+// for fp32 (64-key items)
+template <typename T, int D>
+constexpr int gen_kw() { return std::is_same<T, float>::value ? 1 : 2; }
 
 template <typename T, int D>
 struct GenGeom {
   static constexpr bool F32 = std::is_same<T, float>::value;
+  static constexpr int KW = gen_kw<T, D>();
+  static constexpr int BN = 64 * KW;                    // keys per work item
   static constexpr int EL = (int)sizeof(T);
   static constexpr int EPC = 16 / EL;                   // elements per 16-byte chunk
   static constexpr int QP = F32 ? D + 4 : D + 8;        // Q / dO LDS row pitch (elements)
   static constexpr int KP = F32 ? D + 16 : D + 8;       // K LDS row pitch
   // dS in LDS: fp32 row-major [rows][keys], 16-bit transposed [keys][rows]
-  static constexpr int SP = F32 ? kGenBN + 4 : kGenBM + 8;
+  static constexpr int SP = F32 ? BN + 4 : kGenBM + 8;
   static constexpr int DL = D / 4;                      // head dims of one lane group
   static constexpr int NV = DL / EPC;                   // 16-byte chunks of K (or V) per lane
   static constexpr int QBYTES = kGenBM * QP * EL;
-  static constexpr int KBYTES = kGenBN * KP * EL;
-  static constexpr int SBYTES = (F32 ? kGenBM : kGenBN) * SP * EL;
+  static constexpr int KBYTES = BN * KP * EL;
+  static constexpr int SBYTES = (F32 ? kGenBM : BN) * SP * EL;
   static_assert(DL % EPC == 0 && (QP * EL) % 16 == 0 && (KP * EL) % 16 == 0 && (SP * EL) % 16 == 0,
                 "rows must hold whole 16-byte chunks");
+  static_assert(!F32 || KW == 1, "fp32 keeps one subtile per wavefront");
 };
+template <typename T, int D>
+constexpr int gen_block_n() { return GenGeom<T, D>::BN; }
 
 // transposing read of rows r0 .. r0+3 of column c0 + i from a row-major tile
 // of 16-bit elements with row pitch P (see tr_read4)
@@ -715,9 +729,11 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_gen_kernel(BwdArgs a) {
   using Geo = GenGeom<T, D>;
   constexpr bool F32 = Geo::F32;
-  constexpr int BN = kGenBN, BM = kGenBM, EPC = Geo::EPC, QP = Geo::QP, KP = Geo::KP, SP = Geo::SP;
+  constexpr int KW = Geo::KW, BN = Geo::BN, BM = kGenBM, EPC = Geo::EPC, QP = Geo::QP, KP = Geo::KP,
+                SP = Geo::SP;
   constexpr int DL = Geo::DL, NV = Geo::NV, DT = D / 16;
   constexpr int DQT = 2 * D / 64;  // 16x16 dQ tiles per wave (2 row tiles x D/16 column tiles over 4 waves)
+  constexpr bool KREG = KW == 1;   // K of the lane's key in registers (else read from the LDS block)
   static_assert(F32 ? (D == 64 || D == 96 || D == 128) : D == 256, "generic backward shapes");
 
   __shared__ __attribute__((aligned(16))) char lds_kb[Geo::KBYTES];
@@ -734,24 +750,32 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_gen_kernel(BwdArgs a
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int key0 = w.j * BN;
-  const int kc = key0 + 16 * wave + li;  // this lane's key (S, dP columns) in the sequence
+  int kr0[KW], kc[KW];  // key of the lane in the item's block / in the sequence, per subtile
+#pragma unroll
+  for (int kt = 0; kt < KW; ++kt) {
+    kr0[kt] = 16 * (KW * wave + kt) + li;
+    kc[kt] = key0 + kr0[kt];
+  }
   const int shift = w.Lk - w.Lq;
   const int64_t rs = a.row_stride, rsk = a.kv_row_stride;
   const T* kbase = (const T*)a.k + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
   const T* vbase = (const T*)a.v + (int64_t)w.k_start * rsk + (int64_t)w.hk * D;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  // K and V of the lane's key: head dims lg*DL .. lg*DL + DL - 1
-  u32x4 kr[NV], vr[NV];
+  // V (and K) of the lane's keys: head dims lg*DL .. lg*DL + DL - 1
+  u32x4 vr[KW][NV];
+  u32x4 kr[KREG ? KW : 1][NV];
 #pragma unroll
-  for (int n = 0; n < NV; ++n) {
-    kr[n] = zero;
-    vr[n] = zero;
-    if (kc < w.Lk) {
-      kr[n] = *(const u32x4*)(kbase + (int64_t)kc * rsk + lg * DL + n * EPC);
-      vr[n] = *(const u32x4*)(vbase + (int64_t)kc * rsk + lg * DL + n * EPC);
+  for (int kt = 0; kt < KW; ++kt)
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      vr[kt][n] = zero;
+      if (kc[kt] < w.Lk) vr[kt][n] = *(const u32x4*)(vbase + (int64_t)kc[kt] * rsk + lg * DL + n * EPC);
+      if constexpr (KREG) {
+        kr[kt][n] = zero;
+        if (kc[kt] < w.Lk) kr[kt][n] = *(const u32x4*)(kbase + (int64_t)kc[kt] * rsk + lg * DL + n * EPC);
+      }
     }
-  }
   // the item's K block in LDS (row-major, keys past the sequence as zeros): B operand of dQ = dS K
   for (int c = tid; c < BN * D / EPC; c += 256) {
     const int row = c / (D / EPC), ch = c % (D / EPC);
@@ -760,12 +784,14 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_gen_kernel(BwdArgs a
     *(u32x4*)(lds_kb + (row * KP + ch * EPC) * Geo::EL) = x;
   }
 
-  f32x4 dk[DT], dv[DT];
+  f32x4 dk[KW][DT], dv[KW][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int kt = 0; kt < KW; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dk[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   const int i_begin = CAUSAL ? max(0, key0 - shift) / BM : 0;
   const int i_end = (w.Lq + BM - 1) / BM;
@@ -798,46 +824,60 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_gen_kernel(BwdArgs a
     }
     __syncthreads();
 
-    // ---- S = Q K^T and dP = dO V^T: tile u, register r <-> row 16u + 4lg + r, key kc
-    f32x4 s[2], dp[2];
+    // ---- S = Q K^T and dP = dO V^T: subtile kt, tile u, register r <-> row 16u + 4lg + r, key kc[kt]
+    f32x4 s[KW][2], dp[KW][2];
+#pragma unroll
+    for (int kt = 0; kt < KW; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        s[kt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[kt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       const char* qrow = lds_qb + ((16 * u + li) * QP + lg * DL) * Geo::EL;
       const char* dorow = lds_dob + ((16 * u + li) * QP + lg * DL) * Geo::EL;
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
         if constexpr (F32) {
           const f32x4 q4 = *(const f32x4*)(qrow + 16 * n), o4 = *(const f32x4*)(dorow + 16 * n);
-          const f32x4 k4 = __builtin_bit_cast(f32x4, kr[n]), v4 = __builtin_bit_cast(f32x4, vr[n]);
+          const f32x4 k4 = __builtin_bit_cast(f32x4, kr[0][n]), v4 = __builtin_bit_cast(f32x4, vr[0][n]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            s[u] = mfma4(q4[c], k4[c], s[u]);
-            dp[u] = mfma4(o4[c], v4[c], dp[u]);
+            s[0][u] = mfma4(q4[c], k4[c], s[0][u]);
+            dp[0][u] = mfma4(o4[c], v4[c], dp[0][u]);
           }
         } else {
           typedef typename Elem16<T>::v8 v8;
-          s[u] = Mfma16<T>::run(*(const v8*)(qrow + 16 * n), __builtin_bit_cast(v8, kr[n]), s[u]);
-          dp[u] = Mfma16<T>::run(*(const v8*)(dorow + 16 * n), __builtin_bit_cast(v8, vr[n]), dp[u]);
+          const v8 qa = *(const v8*)(qrow + 16 * n), oa = *(const v8*)(dorow + 16 * n);
+#pragma unroll
+          for (int kt = 0; kt < KW; ++kt) {
+            v8 kb;
+            if constexpr (KREG) kb = __builtin_bit_cast(v8, kr[kt][n]);
+            else kb = *(const v8*)(lds_kb + (kr0[kt] * KP + lg * DL + 8 * n) * Geo::EL);
+            s[kt][u] = Mfma16<T>::run(qa, kb, s[kt][u]);
+            dp[kt][u] = Mfma16<T>::run(oa, __builtin_bit_cast(v8, vr[kt][n]), dp[kt][u]);
+          }
         }
       }
     }
 
     // ---- P = exp(S scale - lse) on visible pairs, dS / scale = P (dP - D)
-    float p[2][4], ds[2][4];
+    float p[KW][2][4], ds[KW][2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const f32x4 l4 = *(const f32x4*)(lds_lse + 16 * u + 4 * lg);
       const f32x4 d4 = *(const f32x4*)(lds_dr + 16 * u + 4 * lg);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = r0 + 16 * u + 4 * lg + r;
-        const bool vis = row < w.Lq && kc < w.Lk && (!CAUSAL || kc <= row + shift);
-        const float pr = vis ? fast_exp2(__builtin_fmaf(s[u][r], a.scale_log2, -l4[r])) : 0.f;
-        p[u][r] = pr;
-        ds[u][r] = pr * (dp[u][r] - d4[r]);
-      }
+      for (int kt = 0; kt < KW; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = r0 + 16 * u + 4 * lg + r;
+          const bool vis = row < w.Lq && kc[kt] < w.Lk && (!CAUSAL || kc[kt] <= row + shift);
+          const float pr = vis ? fast_exp2(__builtin_fmaf(s[kt][u][r], a.scale_log2, -l4[r])) : 0.f;
+          p[kt][u][r] = pr;
+          ds[kt][u][r] = pr * (dp[kt][u][r] - d4[r]);
+        }
     }
 
     // ---- dV += P^T dO, dK += dS^T Q; dS to LDS
@@ -852,10 +892,10 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_gen_kernel(BwdArgs a
           const int row = 16 * u + 4 * lg + r;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            dv[dt] = mfma4(p[u][r], dot[row * QP + 16 * dt + li], dv[dt]);
-            dk[dt] = mfma4(ds[u][r], qt[row * QP + 16 * dt + li], dk[dt]);
+            dv[0][dt] = mfma4(p[0][u][r], dot[row * QP + 16 * dt + li], dv[0][dt]);
+            dk[0][dt] = mfma4(ds[0][u][r], qt[row * QP + 16 * dt + li], dk[0][dt]);
           }
-          dst[row * SP + 16 * wave + li] = ds[u][r];
+          dst[row * SP + kr0[0]] = ds[0][u][r];
         }
     } else {
       typedef typename Elem16<T>::v8 v8;
@@ -863,25 +903,34 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_gen_kernel(BwdArgs a
       const uint16_t* qt = (const uint16_t*)lds_qb;
       const uint16_t* dot = (const uint16_t*)lds_dob;
       uint16_t* dst = (uint16_t*)lds_dsb;
-      v4 p0, p1, d0, d1;
+      v8 pa[KW], da[KW];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p0[r] = (T)p[0][r];
-        p1[r] = (T)p[1][r];
-        d0[r] = (T)ds[0][r];
-        d1[r] = (T)ds[1][r];
+      for (int kt = 0; kt < KW; ++kt) {
+        v4 p0, p1, d0, d1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p0[r] = (T)p[kt][0][r];
+          p1[r] = (T)p[kt][1][r];
+          d0[r] = (T)ds[kt][0][r];
+          d1[r] = (T)ds[kt][1][r];
+        }
+        pa[kt] = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+        da[kt] = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7);
+        // dS^T row kr0[kt] (this lane's key): rows 4lg .. 4lg+3 and 16+4lg .. 16+4lg+3
+        // (whole-vector stores: scalar 16-bit LDS stores of these values were
+        // miscompiled into stores of one element)
+        *(v4*)(dst + kr0[kt] * SP + 4 * lg) = d0;
+        *(v4*)(dst + kr0[kt] * SP + 16 + 4 * lg) = d1;
       }
-      const v8 pa = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
-      const v8 da = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7);
-      // dS^T row 16 wave + li (this lane's key): rows 4lg .. 4lg+3 and 16+4lg .. 16+4lg+3
-      // (whole-vector stores: scalar 16-bit LDS stores of these values were
-      // miscompiled into stores of one element)
-      *(v4*)(dst + (16 * wave + li) * SP + 4 * lg) = d0;
-      *(v4*)(dst + (16 * wave + li) * SP + 16 + 4 * lg) = d1;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        dv[dt] = Mfma16<T>::run(pa, gen_tr8<v8, QP>(dot, 4 * lg, 16 + 4 * lg, 16 * dt, li), dv[dt]);
-        dk[dt] = Mfma16<T>::run(da, gen_tr8<v8, QP>(qt, 4 * lg, 16 + 4 * lg, 16 * dt, li), dk[dt]);
+        const v8 bo = gen_tr8<v8, QP>(dot, 4 * lg, 16 + 4 * lg, 16 * dt, li);
+        const v8 bq = gen_tr8<v8, QP>(qt, 4 * lg, 16 + 4 * lg, 16 * dt, li);
+#pragma unroll
+        for (int kt = 0; kt < KW; ++kt) {
+          dv[kt][dt] = Mfma16<T>::run(pa[kt], bo, dv[kt][dt]);
+          dk[kt][dt] = Mfma16<T>::run(da[kt], bq, dk[kt][dt]);
+        }
       }
     }
     __syncthreads();
@@ -896,19 +945,20 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_gen_kernel(BwdArgs a
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (F32) {
         const float* dst = (const float*)lds_dsb;
-        const float* kt = (const float*)lds_kb;
+        const float* ktile = (const float*)lds_kb;
 #pragma unroll
         for (int s4 = 0; s4 < BN / 4; ++s4)
-          acc = mfma4(dst[(16 * ru + li) * SP + 4 * s4 + lg], kt[(4 * s4 + lg) * KP + 16 * ct + li], acc);
+          acc = mfma4(dst[(16 * ru + li) * SP + 4 * s4 + lg], ktile[(4 * s4 + lg) * KP + 16 * ct + li], acc);
       } else {
         typedef typename Elem16<T>::v8 v8;
         const uint16_t* dst = (const uint16_t*)lds_dsb;
-        const uint16_t* kt = (const uint16_t*)lds_kb;
+        const uint16_t* ktile = (const uint16_t*)lds_kb;
 #pragma unroll
         for (int s32 = 0; s32 < BN / 32; ++s32) {
           // A: dS row 16ru + li, keys 32 s32 + 8lg .. +7 (transposing reads of dS^T)
           const v8 av = gen_tr8<v8, SP>(dst, 32 * s32 + 8 * lg, 32 * s32 + 8 * lg + 4, 16 * ru, li);
-          acc = Mfma16<T>::run(av, gen_tr8<v8, KP>(kt, 32 * s32 + 8 * lg, 32 * s32 + 8 * lg + 4, 16 * ct, li), acc);
+          acc = Mfma16<T>::run(av, gen_tr8<v8, KP>(ktile, 32 * s32 + 8 * lg, 32 * s32 + 8 * lg + 4, 16 * ct, li),
+                               acc);
         }
       }
 #pragma unroll
@@ -922,20 +972,22 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void bwd_gen_kernel(BwdArgs a
     }
   }
 
-  // ---- epilogue: dK (times the softmax scale) and dV of keys key0 + 16 wave + 4 lg + r
+  // ---- epilogue: dK (times the softmax scale) and dV of keys key0 + 16 (KW wave + kt) + 4 lg + r
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int kk = key0 + 16 * wave + 4 * lg + r;
-    if (kk < w.Lk) {
-      T* dkp = (T*)a.dk + (int64_t)(w.k_start + kk) * rsk + (int64_t)w.hk * D;
-      T* dvp = (T*)a.dv + (int64_t)(w.k_start + kk) * rsk + (int64_t)w.hk * D;
+  for (int kt = 0; kt < KW; ++kt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        dkp[16 * dt + li] = (T)(dk[dt][r] * a.scale);
-        dvp[16 * dt + li] = (T)dv[dt][r];
+    for (int r = 0; r < 4; ++r) {
+      const int kk = key0 + 16 * (KW * wave + kt) + 4 * lg + r;
+      if (kk < w.Lk) {
+        T* dkp = (T*)a.dk + (int64_t)(w.k_start + kk) * rsk + (int64_t)w.hk * D;
+        T* dvp = (T*)a.dv + (int64_t)(w.k_start + kk) * rsk + (int64_t)w.hk * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dkp[16 * dt + li] = (T)(dk[kt][dt][r] * a.scale);
+          dvp[16 * dt + li] = (T)dv[kt][dt][r];
+        }
       }
     }
-  }
 }
 
 template <typename F>
@@ -1015,8 +1067,8 @@ hipError_t launch_rows_dtype(int dtype, int head_dim, const BwdArgs& a, hipStrea
 int bwd_block_n(int dtype, int head_dim) {
   const bool half = dtype == 1 || dtype == 2;
   if (half && (head_dim == 64 || head_dim == 96 || head_dim == 128)) return kBwdBNWide;
-  if (half && head_dim == 256) return kGenBN;
-  if (dtype == 0 && (head_dim == 64 || head_dim == 96 || head_dim == 128)) return kGenBN;
+  if (half && head_dim == 256) return gen_block_n<__bf16, 256>();
+  if (dtype == 0 && (head_dim == 64 || head_dim == 96 || head_dim == 128)) return gen_block_n<float, 64>();
   return 0;
 }
 
