@@ -22,8 +22,8 @@
 //   bwd_prep_kernel  D_i for every (row, head) and a zeroed dQ accumulator;
 //   bwd16w_kernel    one workgroup per (256-key block, key/value head): dK, dV
 //                    of the block and atomic dQ contributions (16-bit inputs,
-//                    head_dim up to 128), or bwd_gen_kernel on 64-key blocks
-//                    (fp32 inputs, and 16-bit head_dim 256);
+//                    head_dim up to 128), or bwd_gen_kernel (fp32 inputs on
+//                    64-key blocks, 16-bit head_dim 256 on 128-key blocks);
 //   bwd_dq_kernel    dq = accumulator (already scaled) in the input type.
 //
 // Workgroup layout (8 wavefronts; wave w owns the 32 keys of key group w of
