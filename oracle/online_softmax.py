@@ -14,7 +14,7 @@ cálculo").
 These functions exist only so that tests can pin that equivalence claim:
 ``online_softmax_attention`` must equal :func:`oracle.attention.attention_fwd`
 to float64 rounding, and ``blockwise_normalised_attention`` (normalise every
-key block separately, then add) must not.  Neither is used to judge the GPU.
+key block separately, then add) must not.  Neither is used to check the GPU.
 
 Running statistics for one query row, key blocks n = 0, 1, ...:
     m_n   = max(m_{n-1}, max_j s_j)               (row maximum so far)
