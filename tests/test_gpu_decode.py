@@ -137,3 +137,43 @@ def test_decode_f32_plain(fa, splits):
 def test_decode_bench_batch(fa):
     """The bench's decode batch at full size (32 sequences, 1k-16k cached keys, paged)."""
     run_case(fa, workload_decode_bench(), True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_nan_inputs_stay_local(fa, causal):
+    """NaN propagation through the split key ranges and their merge: a NaN in
+    a query row makes that (row, head) NaN, a NaN in a cached key makes NaN
+    exactly the rows that see it (the oracle's row-wise definition); every
+    other row matches at the usual bar."""
+    from fa_synth import bf16_rne_bits
+    wl = workload_decode("dec_nan", [1, 3, 1], [400, 300, 90], 8, 2, 128, "bf16", seed=37, cache_rows=32,
+                         leftpad=[0, 5, 0], paged=True)
+    say(f"case {wl.name} causal={causal}")
+    data = draw_kvcache(wl)
+    q, kc = data["q"].copy(), data["k_cache"].copy()
+    q[2, 3, :] = np.nan                                   # sequence 1, its second row, head 3
+    tbl = data["block_table"]
+    blk, row = int(tbl[2, 50 // 32]), 50 % 32             # sequence 2, cache position 50, key/value head 1
+    kc[blk, row, 1, 7] = np.nan
+    data["q"], data["k_cache"] = q, kc
+    data["q_bits"], data["k_cache_bits"] = bf16_rne_bits(q).reshape(q.shape), bf16_rne_bits(kc).reshape(kc.shape)
+    dev = {n: torch.from_numpy(data[n + "_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+           for n in ("q", "k_cache", "v_cache")}
+    cu_q = torch.tensor(wl.cu_q, dtype=torch.int32, device="cuda")
+    sk = torch.tensor(wl.seqlens_k, dtype=torch.int32, device="cuda")
+    lp = torch.tensor(wl.leftpad, dtype=torch.int32, device="cuda")
+    bt = torch.from_numpy(tbl).cuda()
+    out, lse = fa.fa_varlen_fwd_kvcache(dev["q"], dev["k_cache"], dev["v_cache"], cu_q, sk, wl.max_seqlen_q,
+                                        wl.max_seqlen_k, wl.scale, causal, leftpad_k=lp, block_table=bt,
+                                        num_splits=3)
+    torch.cuda.synchronize()
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    ref_o, ref_l = attention_kvcache(data["q"], data["k_cache"], data["v_cache"], wl.cu_q, wl.seqlens_k, wl.scale,
+                                     causal, leftpad_k=wl.leftpad, block_table=tbl, page_size=wl.cache_rows)
+    bad = np.isnan(ref_l)
+    assert bad.sum() >= 2
+    assert np.array_equal(np.isnan(l), bad), "NaN lse pattern differs from the oracle"
+    assert np.isnan(o.transpose(1, 0, 2)[bad]).all(), "out of a NaN row must be NaN"
+    keep = ~bad.T[:, :, None]
+    compare(np.where(keep, o, 0.0), np.where(bad, 0.0, l), np.where(keep, ref_o, 0.0), np.where(bad, 0.0, ref_l),
+            TOL["bf16"], wl.name)

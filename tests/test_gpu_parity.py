@@ -383,3 +383,41 @@ def test_score_spikes_raise_reference(fa, causal, dtype, head_dim):
     ref_o, ref_l = attention_fwd(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
     n = wl.total_q
     compare(o[:n], l[:, :n], ref_o[:n], ref_l[:, :n], TOL[dtype], wl.name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f16", 64)])
+def test_nan_inputs_stay_local(fa, causal, dtype, head_dim):
+    """NaN propagation (the pages leave it open; the reading here is the
+    oracle's row-wise definition): a NaN anywhere in a query row makes that
+    (row, head)'s out and lse NaN and nothing else; a NaN in a key makes NaN
+    exactly the rows that see that key, under the causal mask too.  Every
+    other row matches the oracle at the usual bar.  (NaN in V is not covered:
+    a product of a zero probability and a NaN value is NaN in any matrix
+    product, so which rows it reaches depends on how keys are blocked.)"""
+    from fa_synth import bf16_rne_bits, f16_rne_bits
+    wl = workload_custom(f"nan_{dtype}_d{head_dim}", [300, 200, 64], [300, 250, 64], 4, head_dim, dtype, seed=34)
+    say(f"case {wl.name} causal={causal}")
+    data = draw_qkv(wl)
+    q, k = data["q"].copy(), data["k"].copy()
+    q[17, 1, :] = np.nan                  # a whole query row, sequence 0, head 1
+    q[300 + 50, 2, 5] = np.nan            # one element of a query row, sequence 1, head 2
+    k[500 + 40, 0, 3] = np.nan            # one element of key 40 of sequence 2 (key/value head 0)
+    data["q"], data["k"] = q, k
+    rnd = bf16_rne_bits if dtype == "bf16" else f16_rne_bits
+    data["q_bits"], data["k_bits"] = rnd(q), rnd(k)
+    t = to_device(data, wl)
+    o, l = host(*run_gpu(wl, t, causal))
+    ref_o, ref_l = attention_fwd(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
+    n = wl.total_q
+    o, l, ref_o, ref_l = o[:n], l[:, :n], ref_o[:n], ref_l[:, :n]
+    bad = np.isnan(ref_l)                 # (head, row) pairs the definition makes NaN
+    assert bad.sum() > 2, "the planted NaNs must reach the key's rows too"
+    for h in range(wl.heads):
+        assert np.array_equal(np.isnan(l[h]), bad[h]), f"head {h}: NaN lse pattern differs from the oracle"
+        assert np.isnan(o[:, h][bad[h]]).all(), f"head {h}: out of a NaN row must be NaN"
+    o_ok = np.where(bad.T[:, :, None], 0.0, o)
+    r_ok = np.where(bad.T[:, :, None], 0.0, ref_o)
+    l_ok = np.where(bad, 0.0, l)
+    lr_ok = np.where(bad, 0.0, ref_l)
+    compare(o_ok, l_ok, r_ok, lr_ok, TOL[dtype], wl.name)

@@ -493,7 +493,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  // lsum is exactly 0 only for a row that saw no key; a NaN score gives a NaN
+  // sum, which must reach out and lse rather than read as an empty row
+  const float inv = lsum != 0.f ? 1.f / lsum : 0.f;
   T* op = (T*)a.out + rh * D;
 #pragma unroll
   for (int j = 0; j < PER; ++j)
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   if (lane == 0) {
     const int64_t row = rh / a.heads;
     const int h = (int)(rh % a.heads);
-    a.lse[(int64_t)h * a.total_q + row] = lsum > 0.f ? (m + fast_log2(lsum)) * kLn2 : kNegInf;
+    a.lse[(int64_t)h * a.total_q + row] = lsum != 0.f ? (m + fast_log2(lsum)) * kLn2 : kNegInf;
   }
 }
 

@@ -731,8 +731,10 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
   // columns per row and lane, LDS hands them back as 16-byte row pieces, so
   // each global store writes whole rows instead of 8 bytes of 32 rows.
   T* __restrict__ op = (T*)a.out;
+  // l is exactly 0 only for a row that saw no key; a NaN score gives a NaN
+  // sum, which must reach out and lse rather than read as an empty row
   const float l = pair_sum(wv.l_run);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = l != 0.f ? 1.f / l : 0.f;
   uint16_t* stage = &lds_k[0][0] + wave * 32 * Wave::KS;
 #pragma unroll
   for (int db = 0; db < Wave::DB; ++db)
@@ -753,7 +755,7 @@ __device__ __forceinline__ void fwd16_pipe_item(const FwdArgs& a, const WorkItem
     if (wrow0 + r < w.Lq) *(v8*)(op + (int64_t)(w.q_start + wrow0 + r) * rs + (int64_t)w.h * D + 8 * ch) = val;
   }
   if (row < w.Lq && g == 0)
-    a.lse[(int64_t)w.h * a.total_q + w.q_start + row] = l > 0.f ? (wv.m_run + fast_log2(l)) * kLn2 : kNegInf;
+    a.lse[(int64_t)w.h * a.total_q + w.q_start + row] = l != 0.f ? (wv.m_run + fast_log2(l)) * kLn2 : kNegInf;
 }
 
 // NW wavefronts of 32 query rows: 8 (two per SIMD), or 4 (one per SIMD,
@@ -905,7 +907,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdArgs a) {
   }
 
   const float l = pair_sum(l_run);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = l != 0.f ? 1.f / l : 0.f;  // NaN sums propagate (see the 16-bit kernel)
   if (i < w.Lq) {
     float* dst = (float*)a.out + (int64_t)(w.q_start + i) * a.row_stride + (int64_t)w.h * D;
 #pragma unroll
@@ -917,7 +919,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdArgs a) {
         for (int c = 0; c < 4; ++c) v4[c] = o[db][4 * s4 + c] * inv;
         *(f32x4*)(dst + db * 32 + 8 * s4 + 4 * g) = v4;
       }
-    if (g == 0) a.lse[(int64_t)w.h * a.total_q + w.q_start + i] = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
+    if (g == 0) a.lse[(int64_t)w.h * a.total_q + w.q_start + i] = l != 0.f ? (m_run + fast_log2(l)) * kLn2 : kNegInf;
   }
 }
 
