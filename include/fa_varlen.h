@@ -334,7 +334,7 @@ int fa_varlen_fwd_kvcache(const fa_tensor* q, const fa_tensor* k_cache, const fa
 
 /*
  * Workspace bytes of fa_varlen_fwd_kvcache: float32 partial outputs and
- * (max, sum) pairs for every (query row, head, split, wavefront); num_splits
+ * (max, sum) pairs for every (query row, head, split); num_splits
  * 0 sizes for the largest automatic choice (64).  Host only.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_ARG (num_splits outside 0..64).
  */

@@ -423,7 +423,7 @@ def test_kvcache_workspace_size_and_empty():
     r = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for t, h, d, s in ((1, 2, 64, 1), (7, 32, 128, 4), (64, 8, 128, 0)):
         assert lib.fa_varlen_kvcache_workspace_size(t, h, d, s, ctypes.byref(n)) == OK
-        p = (s if s else 64) * 4
+        p = s if s else 64
         assert n.value == r(t * h * p * d * 4) + r(t * h * p * 2 * 4)
         assert fa.fa_varlen_kvcache_workspace_size(t, h, d, s) == n.value
     assert lib.fa_varlen_kvcache_workspace_size(1, 2, 64, 65, ctypes.byref(n)) == ARG

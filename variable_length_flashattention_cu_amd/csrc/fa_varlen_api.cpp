@@ -288,7 +288,9 @@ BwdLayout bwd_layout(int64_t batch, int64_t total_q, int64_t heads, int64_t head
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplits = 64;
 
-int64_t dec_parts(int32_t num_splits) { return (int64_t)(num_splits > 0 ? num_splits : kMaxSplits) * fa::decode_waves(); }
+int64_t dec_parts(int32_t num_splits) {
+  return (int64_t)(num_splits > 0 ? num_splits : kMaxSplits) * fa::decode_parts_per_split();
+}
 
 size_t dec_workspace(int64_t total_q, int64_t heads, int64_t head_dim, int32_t num_splits) {
   const int64_t rows = total_q * heads * dec_parts(num_splits);
@@ -581,7 +583,7 @@ int fa_varlen_fwd_kvcache(const fa_tensor* q, const fa_tensor* k_cache, const fa
   if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
   if (batch == 0 || Tq == 0) return FA_OK;  // no query rows
 
-  const int64_t rows = Tq * H * splits * fa::decode_waves();
+  const int64_t rows = Tq * H * splits * fa::decode_parts_per_split();
   fa::DecArgs a;
   a.q = q->data;
   a.k_cache = k_cache->data;

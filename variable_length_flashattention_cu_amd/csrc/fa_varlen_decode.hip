@@ -29,8 +29,9 @@
 // are dealt to the 4 wavefronts round-robin; each wavefront streams its tiles straight from
 // global memory (K as the A operand of S^T = K Q^T, V through a wave-private
 // LDS tile read back with transposing reads as the A operand of O^T = V^T P^T),
-// keeps an online softmax per row and writes its partial (max, sum, O) to the
-// workspace.  decode_combine_kernel merges the partials of every row
+// keeps an online softmax per row; the four wavefronts' (max, sum, O) are
+// merged in LDS into the split's partial, which goes to the workspace.
+// decode_combine_kernel merges the partials of every row
 // (partials with max m_p, sum l_p and output O_p give out = sum_p 2^(m_p-m)
 // O_p / sum_p 2^(m_p-m) l_p with m = max_p m_p; the same rescaling identity
 // as the online softmax).  fp32 caches take decode_f32_kernel: the same work
@@ -79,6 +80,62 @@ __device__ __forceinline__ int64_t cache_offset(const DecArgs& a, int b, int p, 
   return row * a.kv_row_stride + (int64_t)hk * D;
 }
 
+// The four wavefronts' results for the 16 rows of a row tile are merged in
+// LDS before anything is written (the rescaling identity of the combine:
+// weights 2^(m_w - M), M the largest m_w), so each split writes one partial
+// per (row, head).  On entry lane (i, G) of wave w holds o[dt][r] = O^T(dim
+// 16dt + 4G + r, row i) and the row's m and l (equal on the four lane
+// groups); `ob` is LDS room for 4 x 16 x D floats (the waves' V tiles, free
+// once every wave has left its key loop) and `mlb` for 4 x 16 (m, l) pairs.
+// Wave w then merges dims w D/4 .. (w+1) D/4 - 1 of the tile, lane (i, G)
+// the D/16 of them from w D/4 + G D/16 on.  Ends with a barrier, so the next
+// row tile may overwrite the V tiles.
+template <int D>
+__device__ __forceinline__ void dec_merge_store(const DecArgs& a, const f32x4 (&o)[D / 16], float m_run, float l,
+                                                float* ob, float (*mlb)[16][2], int wave, int li, int lg,
+                                                bool rvalid, int64_t pr) {
+  constexpr int DT = D / 16, DW = D / 4, DL = D / 16;
+  __syncthreads();  // every wave has left its key loop: the V tiles are free
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) *(f32x4*)(ob + (wave * 16 + li) * D + 16 * dt + 4 * lg) = o[dt];
+  if (lg == 0) {
+    mlb[wave][li][0] = m_run;
+    mlb[wave][li][1] = l;
+  }
+  __syncthreads();
+  float mw[kDecWaves], M = kNegInf;
+#pragma unroll
+  for (int v = 0; v < kDecWaves; ++v) {
+    mw[v] = mlb[v][li][0];
+    M = fmaxf(M, mw[v]);
+  }
+  float wgt[kDecWaves], L = 0.f;
+#pragma unroll
+  for (int v = 0; v < kDecWaves; ++v) {
+    wgt[v] = mw[v] == kNegInf ? 0.f : fast_exp2(mw[v] - M);
+    L += wgt[v] * mlb[v][li][1];  // a NaN sum stays NaN, even at weight 0
+  }
+  if (rvalid) {
+    // a split that saw no key (M = -inf) writes only its (m, l): the combine skips its O
+    if (M != kNegInf) {
+      float* po = a.part_o + pr * D + wave * DW + lg * DL;
+      const float* src = ob + li * D + wave * DW + lg * DL;
+#pragma unroll
+      for (int c = 0; c < DL; ++c) {
+        float x = 0.f;
+#pragma unroll
+        for (int v = 0; v < kDecWaves; ++v) x += wgt[v] != 0.f ? wgt[v] * src[v * 16 * D + c] : 0.f;
+        po[c] = x;
+      }
+    }
+    if (wave == 0 && lg == 0) {
+      a.part_ml[2 * pr] = M;
+      a.part_ml[2 * pr + 1] = L;
+    }
+  }
+  __syncthreads();  // the merge has read the V-tile room
+}
+
 // Two wavefronts per SIMD up to head_dim 128; at 256 the output and the
 // tile's K and V registers need more than half a SIMD's registers, so one.
 template <typename T, int D, bool CAUSAL>
@@ -115,8 +172,8 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void decode16_kernel(DecArgs 
   const int ntiles = (max(Lk, 0) + kDecTile - 1) / kDecTile;
   const int tps = (ntiles + a.num_splits - 1) / a.num_splits;  // tiles per split
   const int t_begin = s * tps, t_end = min(ntiles, t_begin + tps);
-  const int part = s * kDecWaves + wave;  // this wave's partial slot
-  const int npart = a.num_splits * kDecWaves;
+  const int npart = a.num_splits;  // one partial per (row, head, split)
+  __shared__ float lds_ml[kDecWaves][16][2];
   uint16_t* vt = lds_v[wave];
 
   for (int rt = 0; rt * 16 < rows; ++rt) {
@@ -274,21 +331,12 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void decode16_kernel(DecArgs 
         }
     }
 
-    // partial of this wave for the rows of the tile: l summed over the four groups
+    // this wave's (m, l, O) for the rows of the tile, l summed over the four
+    // groups; merged with the other waves' into the split's partial
     float l = l_run + __shfl_xor(l_run, 16, 64);
     l = pair_sum(l);
-    if (rvalid) {
-      const int64_t pr = ((int64_t)(q_start + qi) * a.heads + h) * npart + part;
-      float* po = a.part_o + pr * D;
-      // a partial that saw no key (max -inf) is skipped by the combine: its O is not needed
-      if (m_run != kNegInf)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(po + 16 * dt + 4 * lg) = o[dt];
-      if (lg == 0) {
-        a.part_ml[2 * pr] = m_run;
-        a.part_ml[2 * pr + 1] = l;
-      }
-    }
+    const int64_t pr = ((int64_t)(q_start + qi) * a.heads + h) * npart + s;
+    dec_merge_store<D>(a, o, m_run, l, reinterpret_cast<float*>(&lds_v[0][0]), lds_ml, wave, li, lg, rvalid, pr);
   }
 }
 
@@ -332,8 +380,8 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void decode_f32_kernel(DecArg
   const int ntiles = (max(Lk, 0) + kDecTile - 1) / kDecTile;
   const int tps = (ntiles + a.num_splits - 1) / a.num_splits;
   const int t_begin = s_split * tps, t_end = min(ntiles, t_begin + tps);
-  const int part = s_split * kDecWaves + wave;
-  const int npart = a.num_splits * kDecWaves;
+  const int npart = a.num_splits;
+  __shared__ float lds_ml[kDecWaves][16][2];
   float* vt = lds_v[wave];
 
   for (int rt = 0; rt * 16 < rows; ++rt) {
@@ -423,17 +471,8 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void decode_f32_kernel(DecArg
 
     float l = l_run + __shfl_xor(l_run, 16, 64);
     l = pair_sum(l);
-    if (rvalid) {
-      const int64_t pr = ((int64_t)(q_start + qi) * a.heads + h) * npart + part;
-      float* po = a.part_o + pr * D;
-      if (m_run != kNegInf)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(po + 16 * dt + 4 * lg) = o[dt];
-      if (lg == 0) {
-        a.part_ml[2 * pr] = m_run;
-        a.part_ml[2 * pr + 1] = l;
-      }
-    }
+    const int64_t pr = ((int64_t)(q_start + qi) * a.heads + h) * npart + s_split;
+    dec_merge_store<D>(a, o, m_run, l, &lds_v[0][0], lds_ml, wave, li, lg, rvalid, pr);
   }
 }
 
@@ -447,7 +486,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row * heads + head
   const int64_t nrows = a.cu_q[a.batch];
   if (rh >= nrows * a.heads) return;
-  const int npart = a.num_splits * kDecWaves;
+  const int npart = a.num_splits;
   const float* ml = a.part_ml + rh * npart * 2;
   float m = kNegInf;
   for (int p = lane; p < npart; p += 64) m = fmaxf(m, ml[2 * p]);
@@ -562,7 +601,7 @@ hipError_t launch_decode_f32(int head_dim, bool causal, int64_t grid, int64_t gr
 
 }  // namespace
 
-int decode_waves() { return kDecWaves; }
+int decode_parts_per_split() { return 1; }
 
 hipError_t launch_decode(int dtype, int head_dim, bool causal, const DecArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.batch * a.kv_heads * a.num_splits;
