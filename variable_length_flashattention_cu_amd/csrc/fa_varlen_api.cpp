@@ -288,12 +288,10 @@ BwdLayout bwd_layout(int64_t batch, int64_t total_q, int64_t heads, int64_t head
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplits = 64;
 
-int64_t dec_parts(int32_t num_splits) {
-  return (int64_t)(num_splits > 0 ? num_splits : kMaxSplits) * fa::decode_parts_per_split();
-}
-
+// One fp32 partial (O, max, sum) per (query row, head, split): the
+// workgroup's wavefronts merge theirs before writing.
 size_t dec_workspace(int64_t total_q, int64_t heads, int64_t head_dim, int32_t num_splits) {
-  const int64_t rows = total_q * heads * dec_parts(num_splits);
+  const int64_t rows = total_q * heads * (num_splits > 0 ? num_splits : kMaxSplits);
   return round256((size_t)rows * head_dim * sizeof(float)) + round256((size_t)rows * 2 * sizeof(float));
 }
 
@@ -583,7 +581,7 @@ int fa_varlen_fwd_kvcache(const fa_tensor* q, const fa_tensor* k_cache, const fa
   if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
   if (batch == 0 || Tq == 0) return FA_OK;  // no query rows
 
-  const int64_t rows = Tq * H * splits * fa::decode_parts_per_split();
+  const int64_t rows = Tq * H * splits;
   fa::DecArgs a;
   a.q = q->data;
   a.k_cache = k_cache->data;

@@ -601,8 +601,6 @@ hipError_t launch_decode_f32(int head_dim, bool causal, int64_t grid, int64_t gr
 
 }  // namespace
 
-int decode_parts_per_split() { return 1; }
-
 hipError_t launch_decode(int dtype, int head_dim, bool causal, const DecArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.batch * a.kv_heads * a.num_splits;
   const int64_t grid_c = ((int64_t)a.total_q * a.heads + 3) / 4;

@@ -117,9 +117,6 @@ struct DecArgs {
   int32_t num_splits;
 };
 
-// partials per (row, head, split) in the decode workspace (the workgroup's
-// wavefronts merge theirs before writing)
-int decode_parts_per_split();
 hipError_t launch_decode(int dtype, int head_dim, bool causal, const DecArgs& a, hipStream_t stream);
 
 // fa_varlen_fwd_noalloc: the largest batch its static work-item map holds,
