@@ -1,5 +1,6 @@
 // check_tiling.cpp -- host-side bounds and consistency check of the forward
-// kernels' index arithmetic (fa_varlen_tiling.h), built with g++ by
+// kernels' index arithmetic (fa_varlen_tiling.h, and the backward's
+// fa_varlen_bwd_tiling.h), built with g++ by
 // tests/test_host_tiling.py.  For every thread of a workgroup it enumerates:
 //   * the byte offsets of the K/V/Q buffer loads against the resource extents,
 //     under a conservative model of the hardware range check (a load whose
@@ -17,6 +18,7 @@
 #include <vector>
 
 #include "fa_varlen_tiling.h"
+#include "fa_varlen_bwd_tiling.h"
 
 using namespace fa::tiling;
 
@@ -376,6 +378,76 @@ static void check_pipe() {
   std::printf("pipe D=%d BN=%d NW=%d: ok\n", D, BN, NW);
 }
 
+
+// Backward (256-key workgroup, 32-row query blocks): every main-loop LDS
+// address written as (lane part ^ chunk term) + offset must equal the
+// element-index form, stay inside its tile and keep its alignment; the chunk
+// terms must stay below bit 10, the alignment of the tiles' base addresses.
+template <int D>
+static void check_bwd_addr() {
+  namespace B = fa::bwdt;
+  constexpr int KS = k_stride<D>(), BM = 32, BN = 256, CT = D / 16;
+  const unsigned qtile = 2u * BM * KS, ktile = 2u * BN * KS, dstile = 2u * BM * BN;
+  for (int g = 0; g < 2; ++g)
+    for (int ks = 0; ks < D / 16; ++ks) {
+      CHECK(B::op_xor(ks) < 1024u, "op xor");
+      for (int row = 0; row < BM; ++row) {
+        const unsigned a = B::op_lane_tq<D>(row, g) ^ B::op_xor(ks);
+        CHECK(a == 2u * (unsigned)B::tq_index<D>(row, 2 * ks + g), "D=%d Q/dO operand row %d ks %d g %d", D, row, ks, g);
+        CHECK(a % 16 == 0 && a + 16 <= qtile, "D=%d Q/dO operand out of tile", D);
+      }
+      for (int row = 0; row < BN; ++row) {
+        const unsigned a = B::op_lane_ks<D>(row, g) ^ B::op_xor(ks);
+        CHECK(a == 2u * (unsigned)ks_index<D>(row, 2 * ks + g), "D=%d V operand row %d ks %d g %d", D, row, ks, g);
+        CHECK(a % 16 == 0 && a + 16 <= ktile, "D=%d V operand out of tile", D);
+      }
+    }
+  for (int li = 0; li < 16; ++li)
+    for (int lg = 0; lg < 4; ++lg) {
+      for (int db = 0; db < D / 32; ++db)
+        for (int t = 0; t < 2; ++t)
+          for (int h = 0; h < 2; ++h) {
+            CHECK(B::trq_xor<D>(db, t, h) < 1024u, "trq xor");
+            const unsigned a = (B::trq_lane<D>(li, lg) ^ B::trq_xor<D>(db, t, h)) + B::trq_add<D>(t, h);
+            CHECK(a == B::trq_orig<D>(li, lg, db, t, h), "D=%d dV/dK read li %d lg %d db %d t %d h %d", D, li, lg, db,
+                  t, h);
+            CHECK(a % 8 == 0 && a + 8 <= qtile, "D=%d dV/dK read out of tile", D);
+          }
+      for (int kk = 0; kk < BN / 32; ++kk)
+        for (int ct = 0; ct < CT; ++ct)
+          for (int h = 0; h < 2; ++h) {
+            CHECK(B::trk_xor(ct, h) < 1024u, "trk xor");
+            const unsigned a = (B::trk_lane<D>(li, lg) ^ B::trk_xor(ct, h)) + B::trk_add<D>(kk, h);
+            CHECK(a == B::trk_orig<D>(li, lg, kk, ct, h), "D=%d K^T read li %d lg %d kk %d ct %d h %d", D, li, lg, kk,
+                  ct, h);
+            CHECK(a % 8 == 0 && a + 8 <= ktile, "D=%d K^T read out of tile", D);
+          }
+      for (int kk = 0; kk < BN / 32; ++kk)
+        for (int rt = 0; rt < 2; ++rt) {
+          CHECK(B::dsa_xor(kk) < 1024u, "dsa xor");
+          const unsigned a = (B::dsa_lane(li, lg) ^ B::dsa_xor(kk)) + B::dsa_add(rt);
+          const unsigned b = (B::dsa_lane(li, lg) + B::dsa_add(rt)) ^ B::dsa_xor(kk);
+          CHECK(a == B::dsa_orig(li, lg, kk, rt) && b == a, "dS read li %d lg %d kk %d rt %d", li, lg, kk, rt);
+          CHECK(a % 16 == 0 && a + 16 <= dstile, "dS read out of tile");
+        }
+    }
+  for (int key = 0; key < BN; ++key)
+    for (int g = 0; g < 2; ++g)
+      for (int r = 0; r < 16; ++r) {
+        CHECK(B::dss_xor(r) < 1024u, "dss xor");
+        const unsigned a = (B::dss_lane(key, g) ^ B::dss_xor(r)) + B::dss_add(r);
+        CHECK(a == B::dss_orig(key, g, r), "dS store key %d g %d r %d", key, g, r);
+        CHECK(a % 2 == 0 && a + 2 <= dstile, "dS store out of tile");
+      }
+  // the dS stores of one step (32 keys per wave x 8 waves, 32 rows) cover the tile once
+  std::vector<int> hit(BM * BN, 0);
+  for (int key = 0; key < BN; ++key)
+    for (int g = 0; g < 2; ++g)
+      for (int r = 0; r < 16; ++r) ++hit[B::dss_orig(key, g, r) / 2];
+  for (int e = 0; e < BM * BN; ++e) CHECK(hit[e] == 1, "dS element %d stored %d times", e, hit[e]);
+  std::printf("backward addresses D=%d: ok\n", D);
+}
+
 int main() {
   check_pipe<64, 128, 8>();
   check_pipe<64, 64, 4>();
@@ -416,6 +488,9 @@ int main() {
     check_bf16<64, 64, 8>(H);
     check_bf16<64, 128, 4>(H);
   }
+  check_bwd_addr<64>();
+  check_bwd_addr<96>();
+  check_bwd_addr<128>();
   check_f32<64, 4>();
   check_f32<96, 4>();
   check_f32<128, 4>();

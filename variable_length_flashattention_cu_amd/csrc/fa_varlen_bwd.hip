@@ -56,6 +56,7 @@
 #include "fa_varlen_device.h"
 #include "fa_varlen_launch.h"
 #include "fa_varlen_tiling.h"
+#include "fa_varlen_bwd_tiling.h"
 
 namespace fa {
 namespace {
@@ -214,28 +215,11 @@ __device__ __forceinline__ bool decode_col(const BwdArgs& a, ColItem& w) {
 // ---------------------------------------------------------------------------
 // the backward workgroup
 // ---------------------------------------------------------------------------
-// Layout of the tiles that are read both with 16-byte operand reads and with
-// transposing reads (Q, dO and K; V is only read the first way and keeps the
-// K-style layout tiling::ks_index).  The operand reads of a 16-lane group take
-// one chunk of rows {0-3, 16-19, 4-7, 20-23} (+8): the chunk index is XORed
-// with two low bits that differ across those four row sets (row bit 2, and row
-// bits 3 and 4 combined).  A transposing read of a 32-lane half takes rows
-// r..r+3 (r a multiple of 4) and a quad of four chunks, or, for K^T, rows
-// r..r+3 and r+8..r+11 and a pair of chunks: the quad bits are XORed with
-// row % 4 and the low bits flip between r and r+8, so either read touches 16
-// distinct 16-byte bank groups (each was 4-way conflicted with the K-style
-// swizzle).  Rows of head_dim 64 keep the K-style layout.
-// Rows of head_dim 96 (12 chunks) sit in 128-element slots and take the
-// head_dim-128 swizzle; the slots' last four chunk positions hold no data.
-template <int D>
-__device__ __forceinline__ int tq_swz(int row) {
-  if constexpr (D == 128 || D == 96) return 4 * (row & 3) | ((row >> 2) & 1) | ((((row >> 3) ^ (row >> 4)) & 1) << 1);
-  else return tiling::k_swz<D>(row);
-}
-template <int D>
-__device__ __forceinline__ int tq_index(int row, int ch) {
-  return row * tiling::k_stride<D>() + 8 * (ch ^ tq_swz<D>(row));
-}
+// Layout of the Q, dO and K tiles (read both with 16-byte operand reads and
+// with transposing reads; V keeps the K-style layout tiling::ks_index):
+// bwdt::tq_index, with the reasoning in fa_varlen_bwd_tiling.h.
+using bwdt::tq_index;
+using bwdt::tq_swz;
 
 // Register-staged tile -> LDS in the tq_index layout
 template <int D, typename Tile>
@@ -291,6 +275,28 @@ __device__ __forceinline__ s16x4 tr_read4(const uint16_t* tile, int r0, int c0, 
   const int row = r0 + (i >> 2), col = c0 + 4 * (i & 3);
   const uint16_t* p = tile + tq_index<D>(row, col >> 3) + (col & 7);
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+// LDS accesses at absolute LDS byte addresses (the 256-key workgroup's main
+// loop, fa_varlen_bwd_tiling.h): a constant added to the address becomes the
+// instruction's offset field.
+template <typename V>
+__device__ __forceinline__ V lds_rd(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) V*)(uintptr_t)addr;
+}
+__device__ __forceinline__ void lds_wr16(uint32_t addr, uint16_t v) {
+  *(__attribute__((address_space(3))) uint16_t*)(uintptr_t)addr = v;
+}
+__device__ __forceinline__ s16x4 lds_rd_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
+}
+// two transposing reads (rows r0..r0+3 and r0+4..r0+7) as one MFMA operand
+template <typename V8>
+__device__ __forceinline__ V8 lds_rd_tr8(uint32_t lo_addr, uint32_t hi_addr) {
+  const s16x4 lo = lds_rd_tr(lo_addr);
+  const s16x4 hi = lds_rd_tr(hi_addr);
+  const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(V8, v);
 }
 
 // 8 consecutive rows r0 .. r0+7 of column c0 + i as one MFMA operand
@@ -437,11 +443,15 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
   using E = Elem16<T>;
   typedef typename E::v8 v8;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[BN * KSB];   // K block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[BN * KSB];   // V block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_ds[BM * BN];   // dS, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[BM * KSB];   // query block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t lds_do[BM * KSB];
+  // 1024-byte alignment: the chunk XOR terms of the main loop's addresses
+  // (bits 4-8) must not meet bits of a tile's base address
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[BN * KSB];   // K block, row-major
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[BN * KSB];   // V block, row-major
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_ds[BM * BN];   // dS, row-major
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_qdo[2][BM * KSB];  // query block: Q, then dO
+  uint16_t* const lds_q = lds_qdo[0];
+  uint16_t* const lds_do = lds_qdo[1];
+  constexpr uint32_t kDoOff = 2 * BM * KSB;  // bytes from the Q tile to the dO tile
 
   ColItem w;
   if (!decode_col<BN>(a, w)) return;
@@ -496,19 +506,27 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) kreg[ks] = *(const v8*)(lds_k + tq_index<D>(klane, 2 * ks + g));
 
-  int arow = tiling::key_of_arow(l32);
-  int klane_l = klane;
+  // Lane parts of the main loop's LDS addresses (fa_varlen_bwd_tiling.h):
+  // every access there is (lane part ^ loop-index chunk term) + loop-index
+  // offset.  They pass through an empty asm each step, so the compiler keeps
+  // these six registers rather than one register per address.
+  // The tiles' base addresses are included (their bits below 10 are zero).
+  const uint32_t at_qdo = lds_address(lds_qdo), at_v = lds_address(lds_v), at_k = lds_address(lds_k),
+                 at_ds = lds_address(lds_ds);
+  const uint32_t a_op_q0 = at_qdo + bwdt::op_lane_tq<D>(tiling::key_of_arow(l32), g);  // Q, dO operand reads
+  const uint32_t a_op_v0 = at_v + bwdt::op_lane_ks<D>(klane, g);                       // V operand reads
+  const uint32_t a_trq0 = at_qdo + bwdt::trq_lane<D>(li, lg);                          // dO^T, Q^T reads
+  const uint32_t a_trk0 = at_k + bwdt::trk_lane<D>(li, lg);                            // K^T reads (dQ)
+  const uint32_t a_dsa0 = at_ds + bwdt::dsa_lane(li, lg);                              // dS reads (dQ)
+  const uint32_t a_dss0 = at_ds + bwdt::dss_lane(klane, g);                            // dS stores
   for (int s = 0; s < nsteps; ++s) {
-    // lane-dependent address terms are re-derived every step instead of
-    // being kept as one register per LDS address across the loop
     tid = opaque(tid0);
     lane = tid & 63;
-    l32 = lane & 31;
     g = lane >> 5;
     li = lane & 15;
     lg = lane >> 4;
-    arow = tiling::key_of_arow(l32);
-    klane_l = opaque(klane);
+    const uint32_t a_op_q = opaque(a_op_q0), a_op_v = opaque(a_op_v0), a_trq = opaque(a_trq0),
+                   a_trk = opaque(a_trk0), a_dsa = opaque(a_dsa0), a_dss = opaque(a_dss0);
     const int h = w.hk * a.head_group + s / nblk;
     const int r0 = (i_begin + s % nblk) * BM;
     stage.load(a, w, min(s + 1, nsteps - 1), nblk, i_begin, tid);
@@ -520,9 +538,9 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
       v8 aq[PF + 1], ad[PF + 1], bv[PF + 1];
       auto fetch = [&](int ks) __attribute__((always_inline)) {
         const int i = ks % (PF + 1);
-        aq[i] = *(const v8*)(lds_q + tq_index<D>(arow, 2 * ks + g));
-        ad[i] = *(const v8*)(lds_do + tq_index<D>(arow, 2 * ks + g));
-        bv[i] = *(const v8*)(lds_v + tiling::ks_index<D>(klane_l, 2 * ks + g));
+        aq[i] = lds_rd<v8>(a_op_q ^ bwdt::op_xor(ks));
+        ad[i] = lds_rd<v8>((a_op_q ^ bwdt::op_xor(ks)) + kDoOff);
+        bv[i] = lds_rd<v8>(a_op_v ^ bwdt::op_xor(ks));
       };
 #pragma unroll
       for (int ks = 0; ks < PF; ++ks) fetch(ks);
@@ -554,9 +572,10 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int c0 = 32 * db + 16 * (lg & 1), rr = 16 * (lg >> 1) + 8 * t;
-        const v8 adt = tr_read8<v8, D>(lds_do, rr, c0, li);
-        const v8 aqt = tr_read8<v8, D>(lds_q, rr, c0, li);
+        const uint32_t lo = (a_trq ^ bwdt::trq_xor<D>(db, t, 0)) + bwdt::trq_add<D>(t, 0);
+        const uint32_t hi = (a_trq ^ bwdt::trq_xor<D>(db, t, 1)) + bwdt::trq_add<D>(t, 1);
+        const v8 adt = lds_rd_tr8<v8>(lo + kDoOff, hi + kDoOff);
+        const v8 aqt = lds_rd_tr8<v8>(lo, hi);
         dvt[db] = E::mfma(adt, p16[t], dvt[db]);
         dkt[db] = E::mfma(aqt, ds16[t], dkt[db]);
       }
@@ -566,13 +585,12 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
     // packed operand registers as whole words (element-wise access to the
     // 16-bit vector was miscompiled into one element per half).
     {
-      const int kk = klane_l;
       const u32x4 w0 = __builtin_bit_cast(u32x4, ds16[0]);
       const u32x4 w1 = __builtin_bit_cast(u32x4, ds16[1]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const uint32_t word = r < 8 ? w0[(r & 7) >> 1] : w1[(r & 7) >> 1];
-        lds_ds[tiling::ks_index<BN>(16 * g + r, kk >> 3) + (kk & 7)] = (uint16_t)((r & 1) ? (word >> 16) : word);
+        lds_wr16((a_dss ^ bwdt::dss_xor(r)) + bwdt::dss_add(r), (uint16_t)((r & 1) ? (word >> 16) : word));
       }
     }
     __syncthreads();
@@ -589,13 +607,19 @@ __global__ __launch_bounds__(512, 2) void bwd16w_kernel(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < TPW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (has_dq) {
+        // K^T of column tile ct: the chunk terms of the two row halves are
+        // wave-uniform, so each costs one XOR per step
+        const uint32_t k_lo = a_trk ^ bwdt::trk_xor(ct, 0), k_hi = a_trk ^ bwdt::trk_xor(ct, 1);
+        // at D=64 the row tile is wave-uniform but not a constant: fold its
+        // offset (bit 12, clear of the chunk terms) into the lane part
+        const uint32_t a_ds = TPW == 2 ? a_dsa : a_dsa + bwdt::dsa_add(rt0);
 #pragma unroll
         for (int kk = 0; kk < BN / 32; ++kk) {
-          const int k0 = 32 * kk;
-          const v8 bkt = tr_read8<v8, D>(lds_k, k0 + 8 * lg, 16 * ct, li);
+          const v8 bkt = lds_rd_tr8<v8>(k_lo + bwdt::trk_add<D>(kk, 0), k_hi + bwdt::trk_add<D>(kk, 1));
 #pragma unroll
           for (int u = 0; u < TPW; ++u) {
-            const v8 av = *(const v8*)(lds_ds + tiling::ks_index<BN>(dq16_row(rt0 + u, li), (k0 >> 3) + lg));
+            const uint32_t off = TPW == 2 ? (a_ds ^ bwdt::dsa_xor(kk)) + bwdt::dsa_add(u) : a_ds ^ bwdt::dsa_xor(kk);
+            const v8 av = lds_rd<v8>(off);
             acc[u] = Mfma16<T>::run(av, bkt, acc[u]);
           }
         }
