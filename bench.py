@@ -599,7 +599,10 @@ def main() -> int:
                      "kernel_ms_median": kern["median_ms"], "kernel_ms_min": kern["min_ms"],
                      "algorithmic_bytes": round(algorithmic_bytes(wl)),
                      "frac_of_measured_mfma_ceiling": (round(achieved / ceiling["tflops"], 4)
-                                                       if ceiling.get("tflops") else None)},
+                                                       if ceiling.get("tflops") else None),
+                     "frac_of_random_operand_mfma_ceiling": (
+                         round(achieved / ceiling["random_operands"]["tflops"], 4)
+                         if ceiling.get("random_operands", {}).get("tflops") else None)},
         "timing": {"prewarm_call": pw, "prewarm_kernel": pwk, "call": call, "kernel": kern,
                    "method": "HIP events on the launch stream after a >=200 ms pre-warm; value from `steps` "
                              "back-to-back calls between two synchronisations"},
@@ -668,17 +671,27 @@ def mfma_ceiling() -> dict:
     lib.fa_probe_mfma_peak.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_double)]
     lib.fa_probe_mfma_peak.restype = ctypes.c_int
+    lib.fa_probe_mfma_peak_random.argtypes = [ctypes.c_int32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_double),
+                                              ctypes.POINTER(ctypes.c_double)]
+    lib.fa_probe_mfma_peak_random.restype = ctypes.c_int
     tf, ghz = ctypes.c_double(0), ctypes.c_double(0)
-    best = None
-    for _ in range(3):
-        rc = lib.fa_probe_mfma_peak(20000, ctypes.byref(tf), ctypes.byref(ghz))
-        if rc != 0:
-            return {"tflops": None, "note": f"probe failed with status {rc}"}
-        if best is None or tf.value > best[0]:
-            best = (tf.value, ghz.value)
-    return {"tflops": round(best[0], 1), "clock_ghz": round(best[1], 3),
-            "frac_of_published_peak": round(best[0] / PEAK_BF16_TFLOPS, 4),
-            "method": "v_mfma_f32_32x32x16_bf16 on registers, 2 waves per SIMD on every CU, best of 3"}
+    best = {}
+    for name, call in (("constant", lambda: lib.fa_probe_mfma_peak(20000, ctypes.byref(tf), ctypes.byref(ghz))),
+                       ("random", lambda: lib.fa_probe_mfma_peak_random(20000, 12345, ctypes.byref(tf),
+                                                                         ctypes.byref(ghz)))):
+        for _ in range(3):
+            rc = call()
+            if rc != 0:
+                return {"tflops": None, "note": f"probe failed with status {rc}"}
+            if name not in best or tf.value > best[name][0]:
+                best[name] = (tf.value, ghz.value)
+    c, r = best["constant"], best["random"]
+    return {"tflops": round(c[0], 1), "clock_ghz": round(c[1], 3),
+            "frac_of_published_peak": round(c[0] / PEAK_BF16_TFLOPS, 4),
+            "method": "v_mfma_f32_32x32x16_bf16 on registers, 2 waves per SIMD on every CU, best of 3",
+            "random_operands": {"tflops": round(r[0], 1), "clock_ghz": round(r[1], 3),
+                                "frac_of_published_peak": round(r[0] / PEAK_BF16_TFLOPS, 4),
+                                "method": "the same loop on pseudo-random bf16 operands, 8 operand pairs per wave"}}
 
 
 if __name__ == "__main__":

@@ -34,6 +34,17 @@ extern "C" {
  */
 int fa_probe_mfma_peak(int32_t iters, double* tflops, double* ghz);
 
+/*
+ * The same loop with operands that switch: every wavefront holds eight A and
+ * eight B fragments of pseudo-random bf16 values in +-[1, 2) (random sign and
+ * mantissa bits from a hash of `seed` and the thread), and each of its 8
+ * chains multiplies a different pair.  Attention feeds the matrix cores data
+ * of this kind; the constant-operand loop above switches few operand bits
+ * and so draws less power at the same rate.  Arguments, outputs, behaviour
+ * and return codes as fa_probe_mfma_peak.
+ */
+int fa_probe_mfma_peak_random(int32_t iters, uint32_t seed, double* tflops, double* ghz);
+
 #ifdef __cplusplus
 }
 #endif

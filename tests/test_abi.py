@@ -55,6 +55,19 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_probe_library_exports_its_header():
+    """libfa_probe.so (the measurement aid bench.py uses) exports what include/fa_probe.h declares."""
+    path = os.path.join(os.path.dirname(fa.library_path()), "libfa_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libfa_probe.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "fa_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+    assert names == ["fa_probe_mfma_peak", "fa_probe_mfma_peak_random"]
+    lib = ctypes.CDLL(path)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
 def test_status_strings():
     for code in range(12):
         s = fa.fa_status_string(code)
