@@ -297,11 +297,11 @@ size_t dec_workspace(int64_t total_q, int64_t heads, int64_t head_dim, int32_t n
 
 // Splits when the caller leaves the choice: about eight workgroups per
 // compute unit (the pass streams the cache from HBM and needs many loads in
-// flight), at least one 64-key tile per wavefront of a split.
+// flight), at least 64 keys (two 32-key tiles) per wavefront of a split.
 int32_t auto_splits(int64_t batch, int64_t kv_heads, int64_t max_k) {
   const int64_t items = batch * kv_heads;
   int64_t s = items > 0 ? (8 * (int64_t)compute_units() + items - 1) / items : 1;
-  const int64_t by_keys = (max_k + 64 * 4 - 1) / (64 * 4);  // a 64-key tile per wavefront
+  const int64_t by_keys = (max_k + 64 * 4 - 1) / (64 * 4);  // 64 keys for each of the 4 wavefronts
   if (s > by_keys) s = by_keys;
   if (s > kMaxSplits) s = kMaxSplits;
   return (int32_t)(s < 1 ? 1 : s);
