@@ -178,6 +178,36 @@ def test_map_boundary(fa, batch):
         full_parity(fa, wl, causal)
 
 
+def test_single_64k_sequence_sampled(fa):
+    # one sequence of 65,536 tokens: the longest work items (1024 key tiles),
+    # causal pairing of its 256 query blocks, and 64-bit offsets over the
+    # whole K/V walk; 40 sampled rows per head (block edges included), both masks
+    wl = workload_custom("long_64k_h2_d128", [65536], None, 2, 128, "bf16", seed=81)
+    data = draw_qkv(wl)
+    t = to_device(data, wl)
+    rng = np.random.default_rng(81)
+    rows = np.unique(np.concatenate([[0, 255, 256, 32767, 32768, 65279, 65280, 65535],
+                                     rng.integers(0, 65536, size=32)])).astype(np.int64)
+    for causal in (False, True):
+        say(f"case {wl.name} causal={causal} ({len(rows)} sampled rows, both heads)")
+        o, l = host(*run_gpu(wl, t, causal))
+        ref_o, ref_l = attention_rows(data["q"], data["k"], data["v"], wl.cu_q, wl.cu_k, wl.scale, causal, rows,
+                                      [0, 1])
+        compare(o[rows], l[:, rows], ref_o, ref_l, TOL["bf16"], wl.name)
+        assert not np.isnan(o).any() and not np.isnan(l).any()
+
+
+def test_70k_sequences(fa):
+    # 70,000 sequences of 0-8 tokens (280k tokens): the map kernel's scan over
+    # many chunks, ~70k work items per head, beyond the no-allocation entry
+    # point's 65,535-sequence limit; every row against the oracle
+    rng = np.random.default_rng(82)
+    lens = [int(x) for x in rng.integers(0, 9, size=70000)]
+    wl = workload_custom("many_70k_seqs_h2_d64", lens, None, 2, 64, "bf16", seed=82)
+    for causal in (False, True):
+        full_parity(fa, wl, causal)
+
+
 def test_single_long_sequence_fp32(fa):
     wl = workload_custom("long_fp32", [2000], [2300], 2, 128, "f32", seed=78)
     for causal in (False, True):
