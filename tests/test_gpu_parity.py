@@ -386,7 +386,7 @@ def test_ragged64k_d256_sampled(fa):
 
 
 # ---------------------------------------------------------------- score spikes
-SPIKE_CASES = [("bf16", 128), ("bf16", 64), ("bf16", 96), ("f16", 128)]
+SPIKE_CASES = [("bf16", 128), ("bf16", 64), ("bf16", 96), ("f16", 128), ("f16", 64), ("bf16", 256), ("f16", 256)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -396,9 +396,20 @@ def test_score_spikes_raise_reference(fa, causal, dtype, head_dim):
     sequences give scores tens of log2 units above every earlier one, so the
     kernels must raise their softmax references and rescale the partial
     outputs in the middle of the key loop, not only in its first tiles."""
+    spikes_case(fa, causal, dtype, head_dim, [2048, 1500, 700], [2048, 1700, 900])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f16", 64)], ids=["bf16_d128", "f16_d64"])
+def test_score_spikes_short_items(fa, causal, dtype, head_dim):
+    """The same with every query length at most 1024, where fa_varlen_fwd
+    takes 128-row work items (four wavefronts, 32- or 64-key tiles)."""
+    spikes_case(fa, causal, dtype, head_dim, [1024, 700, 301], [1024, 900, 501])
+
+
+def spikes_case(fa, causal, dtype, head_dim, lq, lk):
     from fa_synth import bf16_rne_bits, f16_rne_bits
-    wl = workload_custom(f"spikes_{dtype}_d{head_dim}", [2048, 1500, 700], [2048, 1700, 900], 4, head_dim, dtype,
-                         seed=31)
+    wl = workload_custom(f"spikes_{dtype}_d{head_dim}_q{max(lq)}", lq, lk, 4, head_dim, dtype, seed=31)
     say(f"case {wl.name} causal={causal}")
     data = draw_qkv(wl)
     k = data["k"].copy()
