@@ -51,9 +51,9 @@
 // normalización global"): with t = scale*log2(e)*s,
 //   m' = max(m, max_j t_j), alpha = 2^(m - m'), l' = alpha l + sum_j 2^(t_j - m'),
 //   O' = alpha O + sum_j 2^(t_j - m') v_j;  out = O / l,  lse = (m + log2 l) ln 2.
-// The reference m need not be the exact running max: any m >= the max seen so
-// far (up to a bounded slack) gives the same out and lse, because l and O are
-// accumulated against the same m.  The kernel therefore raises m (and pays
+// The reference m need not be the exact running max: any finite m close
+// enough to it that 2^(t - m) neither overflows nor loses all precision gives
+// the same out and lse, because l and O are accumulated against the same m.  The kernel therefore raises m (and pays
 // the rescale of O) only when some row of the wavefront outgrows it by more
 // than 2^8, which after the first tiles is rare.
 // A row that has seen no visible key keeps m = -inf and is guarded so that no
