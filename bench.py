@@ -365,21 +365,30 @@ def cpu_parity(wl: Workload, data: dict, sample: dict) -> dict:
             "max_abs_lse": float(f"{err_l:.3e}"), "tol": tol, "ok": bool(ok)}
 
 
-def cpu_baseline(wl: Workload, causal: bool, data: dict, heads=(0,)) -> dict:
-    """The oracle (float64 numpy) on a bounded sample: one head, every sequence."""
+def cpu_baseline(wl: Workload, causal: bool, data: dict, min_seconds: float = 10.0) -> dict:
+    """The oracle (float64 numpy) on a bounded sample: whole heads (every
+    sequence), one at a time, until about `min_seconds` of CPU work."""
     from threadpoolctl import threadpool_info
     from oracle import attention_fwd
-    sub = {n: np.ascontiguousarray(data[n][:, list(heads), :]) for n in "qkv"}
-    t0 = time.perf_counter()
-    attention_fwd(sub["q"], sub["k"], sub["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
-    dt = time.perf_counter() - t0
+    group = wl.heads // (wl.heads_k or wl.heads)
+    heads, dt = [], 0.0
+    for h in range(wl.heads):
+        sub = {"q": np.ascontiguousarray(data["q"][:, [h], :])}
+        for n in "kv":
+            sub[n] = np.ascontiguousarray(data[n][:, [h // group], :])
+        t0 = time.perf_counter()
+        attention_fwd(sub["q"], sub["k"], sub["v"], wl.cu_q, wl.cu_k, wl.scale, causal)
+        dt += time.perf_counter() - t0
+        heads.append(h)
+        if dt >= min_seconds:
+            break
     fl = 4.0 * wl.head_dim * len(heads) * visible_pairs(wl, causal)
     blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
     threads = max([p.get("num_threads", 1) for p in blas] or [1])
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "os_cpu_count": os.cpu_count(), "blas_threads": int(threads),
             "blas": (blas[0].get("internal_api", "?") if blas else "?"),
-            "sample": f"{wl.name}: head {list(heads)} of {wl.heads}, all {wl.batch} sequences "
+            "sample": f"{wl.name}: heads {heads[0]}-{heads[-1]} of {wl.heads}, all {wl.batch} sequences "
                       f"({fl / 1e9:.1f} GFLOP algorithmic, {dt:.1f} s, float64 numpy on {threads} BLAS threads "
                       f"of {os.cpu_count()} host cores)"}
 
